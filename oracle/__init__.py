@@ -1,0 +1,191 @@
+"""Plain CPU oracle for causal GQA attention over a per-layer KV cache.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path (the HIP library and its
+Python binding) never imports this package, and this package never imports the
+product: the two share no code.
+
+`oracle.c` holds every step, written from the pages (see its header for sources);
+this module only compiles it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM = 0, 1, 2, 3, 4, 5
+ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+          "-std=c11", "-Wall", "-Wextra"]
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib = None
+
+
+def _bind(lib):
+    i32, f32, p = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    sig = {
+        "orc_rope_inv_freq": (ctypes.c_int, [i32, f32, f32, p]),
+        "orc_rope_cos_sin": (ctypes.c_int, [i32, f32, f32, i32, p, p]),
+        "orc_rope": (ctypes.c_int, [p, i32, i32, i32, p, f32, f32, i32]),
+        "orc_cache_new": (p, [i32, i32, i32, i32, i32]),
+        "orc_cache_free": (None, [p]),
+        "orc_cache_region": (p, [p, i32, i32, i32]),
+        "orc_cache_seq_len": (i32, [p, i32, i32]),
+        "orc_append_rope": (ctypes.c_int, [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, i32]),
+        "orc_attn_prefill": (ctypes.c_int, [p, i32, i32, i32, p, p, i32, i32, f32, p, i32]),
+        "orc_attn_decode": (ctypes.c_int, [p, i32, i32, p, p, p, i32, i32, f32, p, i32]),
+        "orc_max_threads": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def lib(path: str | None = None):
+    """Load (building first if needed) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Oracle:
+    """numpy-facing wrapper over one oracle library (the default one or a given path)."""
+
+    def __init__(self, path: str | None = None):
+        self.L = lib(path)
+
+    def max_threads(self) -> int:
+        return int(self.L.orc_max_threads())
+
+    def rope_inv_freq(self, hd, base, scale=1.0):
+        out = np.zeros(max(hd // 2, 1), np.float32)
+        st = self.L.orc_rope_inv_freq(hd, base, scale, _ptr(out))
+        if st:
+            raise ValueError(f"orc_rope_inv_freq status {st}")
+        return out[: hd // 2]
+
+    def rope_cos_sin(self, hd, base, scale, p):
+        cs = np.zeros(hd // 2, np.float32)
+        sn = np.zeros(hd // 2, np.float32)
+        st = self.L.orc_rope_cos_sin(hd, base, scale, p, _ptr(cs), _ptr(sn))
+        if st:
+            raise ValueError(f"orc_rope_cos_sin status {st}")
+        return cs, sn
+
+    def rope(self, x, pos, base, scale=1.0, style=ROPE_NEOX):
+        """x: [nt][nh][hd]; returns a rotated copy."""
+        x = _f32(x).copy()
+        pos = _i32(pos)
+        nt, nh, hd = x.shape
+        st = self.L.orc_rope(_ptr(x), nt, nh, hd, _ptr(pos), base, scale, style)
+        if st:
+            raise ValueError(f"orc_rope status {st}")
+        return x
+
+
+class OracleCache:
+    """The oracle's KV cache: zeroed regions [n_seq][n_layer][capacity][n_head_kv*hd_kv]."""
+
+    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, oracle: Oracle | None = None):
+        self.o = oracle or Oracle()
+        self.L = self.o.L
+        self.n_seq, self.n_layer = n_seq, n_layer
+        self.n_head_kv, self.hd_kv, self.capacity = n_head_kv, hd_kv, capacity
+        self.nkt = n_head_kv * hd_kv
+        self.h = self.L.orc_cache_new(n_seq, n_layer, n_head_kv, hd_kv, capacity)
+        if not self.h:
+            raise ValueError("orc_cache_new rejected the geometry")
+
+    def close(self):
+        if self.h:
+            self.L.orc_cache_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def region(self, which, seq, layer) -> np.ndarray:
+        """Live numpy view of one region ([capacity][nkt]); which=0 for K, 1 for V."""
+        ptr = self.L.orc_cache_region(self.h, which, seq, layer)
+        if not ptr:
+            raise IndexError("bad seq/layer")
+        buf = (ctypes.c_float * (self.capacity * self.nkt)).from_address(ptr)
+        return np.frombuffer(buf, dtype=np.float32).reshape(self.capacity, self.nkt)
+
+    def k(self, seq, layer):
+        return self.region(0, seq, layer)
+
+    def v(self, seq, layer):
+        return self.region(1, seq, layer)
+
+    def seq_len(self, seq, layer) -> int:
+        return int(self.L.orc_cache_seq_len(self.h, seq, layer))
+
+    def append_rope(self, layer, seq_ids, pos, q, n_head, hd, k, v, base, scale=1.0,
+                    style=ROPE_NEOX):
+        """Returns (status, rotated q copy or None)."""
+        seq_ids, pos = _i32(seq_ids), _i32(pos)
+        nt = int(pos.shape[0])
+        qq = None if q is None else _f32(q).copy()
+        k, v = _f32(k), _f32(v)
+        st = self.L.orc_append_rope(self.h, layer, nt, _ptr(seq_ids), _ptr(pos), _ptr(qq),
+                                    n_head, hd, _ptr(k), _ptr(v), base, scale, style)
+        return st, qq
+
+    def attn_prefill(self, seq, layer, pos, q, n_head, hd, scale, nthreads=0):
+        pos = _i32(pos)
+        nt = int(pos.shape[0])
+        q = _f32(q)
+        out = np.zeros((nt, n_head, self.hd_kv), np.float32)
+        st = self.L.orc_attn_prefill(self.h, seq, layer, nt, _ptr(pos), _ptr(q), n_head, hd,
+                                     scale, _ptr(out), nthreads)
+        return st, out
+
+    def attn_decode(self, layer, seq_ids, pos, q, n_head, hd, scale, nthreads=0):
+        seq_ids, pos = _i32(seq_ids), _i32(pos)
+        n = int(pos.shape[0])
+        q = _f32(q)
+        out = np.zeros((n, n_head, self.hd_kv), np.float32)
+        st = self.L.orc_attn_decode(self.h, layer, n, _ptr(seq_ids), _ptr(pos), _ptr(q), n_head,
+                                    hd, scale, _ptr(out), nthreads)
+        return st, out

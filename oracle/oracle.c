@@ -1,0 +1,418 @@
+/*
+ * oracle.c -- plain, slow CPU statement of causal grouped-query attention over a
+ * per-layer KV cache.
+ *
+ * THIS IS TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg load it.  It shares no code,
+ * header, table or constant with the HIP library: every step below is written out
+ * from the pages it cites.
+ *
+ * Sources (titles of the pages; sections named inline):
+ *   [MINFER-11] "11 · Attention, vec ops, and the KV cache"
+ *   [ZEROCOPY]  "IV.2: Zero-copy KV cache"
+ *   [MINFER-13] "13 · The decode loop and graph reuse"
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared -lm.
+ * No FMA contraction anywhere: every product and sum below is rounded to f32 on its
+ * own, as the scalar code on the pages does.
+ *
+ * Precision follows the pages where they fix it: scores, exponentials, normalisation
+ * and the weighted V sum are f32; the softmax denominator is summed in f64
+ * ([MINFER-11] §3.2.5, the softmax routine's f64 accumulator).  RoPE frequencies and
+ * cos/sin are the correctly rounded f32 values of the exact expressions (evaluated in
+ * long double and rounded once), because the pages' f32 powf/sin_cos depend on the libm
+ * that runs them.
+ *
+ * Pins: every function here is checked by tests against closed forms, the pages'
+ * worked examples, arbitrary-precision values and an f64 brute force; no function is
+ * "parity unpinned".
+ */
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Status values.  They use the same numbers as the library's public status enum so a
+ * test can compare error behaviour call by call (a format that must agree). */
+enum {
+    ORC_OK = 0,
+    ORC_E_ARG = 1,
+    ORC_E_GEOMETRY = 2,
+    ORC_E_RANGE = 3,
+    ORC_E_DUP = 4,
+    ORC_E_NOMEM = 5
+};
+
+/* RoPE pair layouts ([MINFER-11] §3.2.2, the two layout styles). */
+enum { ORC_ROPE_NEOX = 0, ORC_ROPE_INTERLEAVED = 1, ORC_ROPE_NONE = 2 };
+
+#define ORC_MAX_HEAD_DIM 256        /* the pages' fixed 128-entry frequency table */
+#define ORC_MAX_POSITION (1 << 24)  /* positions travel as exact integers in f32 */
+
+/* ------------------------------------------------------------------------------ */
+/* RoPE ([MINFER-11] §2.3 "RoPE: position without position embeddings",            */
+/*       §3.2.2 "RoPE -- the node arm and cpu_rope")                                */
+/* ------------------------------------------------------------------------------ */
+
+/* Angular speed of subspace i: freq_scale / base^(2i/hd), rounded once to f32. */
+int orc_rope_inv_freq(int32_t hd, float freq_base, float freq_scale, float *inv)
+{
+    if (hd <= 0 || (hd & 1) || hd > ORC_MAX_HEAD_DIM || !inv) return ORC_E_ARG;
+    for (int32_t i = 0; i < hd / 2; i++) {
+        long double expo = (long double)(2 * i) / (long double)hd;
+        long double speed = (long double)freq_scale / powl((long double)freq_base, expo);
+        inv[i] = (float)speed;
+    }
+    return ORC_OK;
+}
+
+/* cos and sin of the angle position x speed.  The angle itself is an f32 product, as
+ * on the page; its cos and sin are correctly rounded to f32. */
+int orc_rope_cos_sin(int32_t hd, float freq_base, float freq_scale, int32_t p,
+                     float *cs, float *sn)
+{
+    float inv[ORC_MAX_HEAD_DIM / 2];
+    int st = orc_rope_inv_freq(hd, freq_base, freq_scale, inv);
+    if (st != ORC_OK) return st;
+    if (p < 0) return ORC_E_RANGE;
+    for (int32_t i = 0; i < hd / 2; i++) {
+        float theta = (float)p * inv[i];
+        cs[i] = (float)cosl((long double)theta);
+        sn[i] = (float)sinl((long double)theta);
+    }
+    return ORC_OK;
+}
+
+/* Rotate one head vector x[0..hd) in place at position p.
+ * NEOX pairs are (i, i + hd/2); interleaved pairs are (2i, 2i+1).  The rotation is
+ *   x0' = x0*cos - x1*sin,  x1' = x0*sin + x1*cos,
+ * each product and each sum rounded to f32 separately. */
+static void rotate_head(float *x, int32_t hd, const float *cs, const float *sn, int32_t style)
+{
+    int32_t half = hd / 2;
+    for (int32_t i = 0; i < half; i++) {
+        int32_t i0, i1;
+        if (style == ORC_ROPE_NEOX) { i0 = i; i1 = i + half; }
+        else { i0 = 2 * i; i1 = 2 * i + 1; }
+        float x0 = x[i0], x1 = x[i1];
+        float a = x0 * cs[i];
+        float b = x1 * sn[i];
+        float c = x0 * sn[i];
+        float d = x1 * cs[i];
+        x[i0] = a - b;
+        x[i1] = c + d;
+    }
+}
+
+/* Apply RoPE in place to x laid out [nt][nh][hd], token t at position pos[t]. */
+int orc_rope(float *x, int32_t nt, int32_t nh, int32_t hd, const int32_t *pos,
+             float freq_base, float freq_scale, int32_t style)
+{
+    if (style == ORC_ROPE_NONE) return ORC_OK;
+    if (style != ORC_ROPE_NEOX && style != ORC_ROPE_INTERLEAVED) return ORC_E_ARG;
+    if (nt < 0 || nh <= 0 || (nt > 0 && (!x || !pos))) return ORC_E_ARG;
+    float cs[ORC_MAX_HEAD_DIM / 2], sn[ORC_MAX_HEAD_DIM / 2];
+    for (int32_t t = 0; t < nt; t++) {
+        int st = orc_rope_cos_sin(hd, freq_base, freq_scale, pos[t], cs, sn);
+        if (st != ORC_OK) return st;
+        for (int32_t h = 0; h < nh; h++)
+            rotate_head(x + ((size_t)t * nh + h) * hd, hd, cs, sn, style);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* The KV cache: persistent per-layer K and V regions, row p at offset p * row     */
+/* width ([MINFER-11] §2.2 "Why the KV cache exists", §3.2.3 "The KV store / load  */
+/* pair"; [ZEROCOPY] "The cache appends in place").  Regions are sized once and    */
+/* start zeroed, so rows never written read as zeros.                              */
+/* ------------------------------------------------------------------------------ */
+
+typedef struct orc_cache {
+    int32_t n_seq, n_layer, n_head_kv, hd_kv, capacity;
+    size_t region;      /* floats per (seq, layer) region: capacity * n_head_kv * hd_kv */
+    float *k, *v;       /* [n_seq][n_layer][capacity][n_head_kv * hd_kv] */
+    int32_t *hw;        /* high-water mark per (seq, layer): max written position + 1 */
+} orc_cache;
+
+orc_cache *orc_cache_new(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
+                         int32_t capacity)
+{
+    if (n_seq <= 0 || n_layer <= 0 || n_head_kv <= 0 || hd_kv <= 0 || (hd_kv & 1) ||
+        hd_kv > ORC_MAX_HEAD_DIM || capacity <= 0 || capacity > ORC_MAX_POSITION)
+        return NULL;
+    orc_cache *c = (orc_cache *)calloc(1, sizeof(orc_cache));
+    if (!c) return NULL;
+    c->n_seq = n_seq; c->n_layer = n_layer; c->n_head_kv = n_head_kv;
+    c->hd_kv = hd_kv; c->capacity = capacity;
+    c->region = (size_t)capacity * (size_t)n_head_kv * (size_t)hd_kv;
+    size_t total = (size_t)n_seq * (size_t)n_layer * c->region;
+    c->k = (float *)calloc(total, sizeof(float));
+    c->v = (float *)calloc(total, sizeof(float));
+    c->hw = (int32_t *)calloc((size_t)n_seq * n_layer, sizeof(int32_t));
+    if (!c->k || !c->v || !c->hw) {
+        free(c->k); free(c->v); free(c->hw); free(c);
+        return NULL;
+    }
+    return c;
+}
+
+void orc_cache_free(orc_cache *c)
+{
+    if (!c) return;
+    free(c->k); free(c->v); free(c->hw); free(c);
+}
+
+/* which = 0 for K, 1 for V.  Returns the [capacity][n_head_kv * hd_kv] region. */
+float *orc_cache_region(orc_cache *c, int32_t which, int32_t seq, int32_t layer)
+{
+    if (!c || seq < 0 || seq >= c->n_seq || layer < 0 || layer >= c->n_layer) return NULL;
+    float *base = which ? c->v : c->k;
+    return base + ((size_t)seq * c->n_layer + layer) * c->region;
+}
+
+int32_t orc_cache_seq_len(const orc_cache *c, int32_t seq, int32_t layer)
+{
+    if (!c || seq < 0 || seq >= c->n_seq || layer < 0 || layer >= c->n_layer) return -1;
+    return c->hw[(size_t)seq * c->n_layer + layer];
+}
+
+static int cmp_i64(const void *a, const void *b)
+{
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Store this step's K/V rows at the positions the caller passes, after rotating q
+ * (optional, in place) and k.  Everything is checked before anything is written:
+ * a position outside the region is an error, never a clamp ([MINFER-11] §3.2.3 and
+ * §3.4 "Pitfalls & invariants"); two rows aimed at the same (sequence, position) in
+ * one call are refused because their order would be ambiguous.
+ * q: [nt][n_head][hd] (may be NULL); k, v: [nt][n_head_kv][hd_kv]. */
+int orc_append_rope(orc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                    const int32_t *pos, float *q, int32_t n_head, int32_t hd,
+                    const float *k, const float *v, float freq_base, float freq_scale,
+                    int32_t style)
+{
+    if (!c || layer < 0 || layer >= c->n_layer || nt < 0) return ORC_E_ARG;
+    if (nt == 0) return ORC_OK;
+    if (!seq_ids || !pos || !k || !v) return ORC_E_ARG;
+    if (style != ORC_ROPE_NEOX && style != ORC_ROPE_INTERLEAVED && style != ORC_ROPE_NONE)
+        return ORC_E_ARG;
+    if (style != ORC_ROPE_NONE &&
+        (!(freq_base > 0.0f) || !isfinite(freq_base) || !(freq_scale > 0.0f) ||
+         !isfinite(freq_scale)))
+        return ORC_E_ARG;
+    if (q) {
+        if (n_head <= 0 || n_head % c->n_head_kv != 0) return ORC_E_ARG;
+        if (hd <= 0 || (hd & 1) || hd > ORC_MAX_HEAD_DIM) return ORC_E_ARG;
+        if (hd < c->hd_kv) return ORC_E_GEOMETRY;
+    }
+    for (int32_t t = 0; t < nt; t++)
+        if (seq_ids[t] < 0 || seq_ids[t] >= c->n_seq) return ORC_E_ARG;
+    for (int32_t t = 0; t < nt; t++)
+        if (pos[t] < 0 || pos[t] >= c->capacity) return ORC_E_RANGE;
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)nt);
+    if (!keys) return ORC_E_NOMEM;
+    for (int32_t t = 0; t < nt; t++) keys[t] = ((int64_t)seq_ids[t] << 32) | (int64_t)pos[t];
+    qsort(keys, (size_t)nt, sizeof(int64_t), cmp_i64);
+    int dup = 0;
+    for (int32_t t = 1; t < nt; t++) if (keys[t] == keys[t - 1]) dup = 1;
+    free(keys);
+    if (dup) return ORC_E_DUP;
+
+    /* Checks passed: rotate q, then write every row. */
+    if (q) {
+        int st = orc_rope(q, nt, n_head, hd, pos, freq_base, freq_scale, style);
+        if (st != ORC_OK) return st;
+    }
+    const int32_t nkt = c->n_head_kv * c->hd_kv;
+    float *row = (float *)malloc(sizeof(float) * (size_t)nkt);
+    if (!row) return ORC_E_NOMEM;
+    for (int32_t t = 0; t < nt; t++) {
+        memcpy(row, k + (size_t)t * nkt, sizeof(float) * (size_t)nkt);
+        int st = orc_rope(row, 1, c->n_head_kv, c->hd_kv, &pos[t], freq_base, freq_scale, style);
+        if (st != ORC_OK) { free(row); return st; }
+        float *kd = orc_cache_region(c, 0, seq_ids[t], layer) + (size_t)pos[t] * nkt;
+        float *vd = orc_cache_region(c, 1, seq_ids[t], layer) + (size_t)pos[t] * nkt;
+        memcpy(kd, row, sizeof(float) * (size_t)nkt);
+        memcpy(vd, v + (size_t)t * nkt, sizeof(float) * (size_t)nkt);
+        int32_t *hw = &c->hw[(size_t)seq_ids[t] * c->n_layer + layer];
+        if (pos[t] + 1 > *hw) *hw = pos[t] + 1;
+    }
+    free(row);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Attention ([MINFER-11] §2.1 "What attention computes", §2.4 GQA, §3.2.4 "GQA    */
+/* attention", §3.2.5 softmax).                                                     */
+/* ------------------------------------------------------------------------------ */
+
+/* Sequential f32 dot product, one rounding per product and per sum. */
+static float dot_f32(int32_t n, const float *a, const float *b)
+{
+    float s = 0.0f;
+    for (int32_t i = 0; i < n; i++) s += a[i] * b[i];
+    return s;
+}
+
+/* One query row against rows [0, vl) of one kv head's slice of the regions.
+ *   score_j = (q . k_j) * scale                 (f32)
+ *   e_j     = exp(score_j - max_j score_j)      (f32)
+ *   sum     = sum_j e_j                          (f64)
+ *   w_j     = e_j * (f32)(1 / sum)               (f32)
+ *   out     = sum_j w_j * v_j, in j order        (f32)
+ * Rows at or beyond vl are the masked tail: their weight is exp(-inf) = 0 exactly and
+ * their zero contribution is not formed. */
+static void attend_row(const float *qrow, const float *kreg, const float *vreg, int32_t nkt,
+                       int32_t hk, int32_t hd_kv, int32_t vl, float scale, float *scr,
+                       float *out)
+{
+    float mx = -INFINITY;
+    for (int32_t j = 0; j < vl; j++) {
+        const float *kr = kreg + (size_t)j * nkt + (size_t)hk * hd_kv;
+        float s = dot_f32(hd_kv, qrow, kr) * scale;
+        scr[j] = s;
+        if (s > mx) mx = s;
+    }
+    double sum = 0.0;
+    for (int32_t j = 0; j < vl; j++) {
+        float e = expf(scr[j] - mx);
+        scr[j] = e;
+        sum += (double)e;
+    }
+    float inv = (float)(1.0 / sum);
+    for (int32_t j = 0; j < vl; j++) scr[j] *= inv;
+    for (int32_t d = 0; d < hd_kv; d++) out[d] = 0.0f;
+    for (int32_t j = 0; j < vl; j++) {
+        const float *vr = vreg + (size_t)j * nkt + (size_t)hk * hd_kv;
+        float w = scr[j];
+        for (int32_t d = 0; d < hd_kv; d++) out[d] += w * vr[d];
+    }
+}
+
+static int check_heads(const orc_cache *c, int32_t n_head, int32_t hd)
+{
+    if (n_head <= 0 || n_head % c->n_head_kv != 0) return ORC_E_ARG;
+    if (hd <= 0 || (hd & 1) || hd > ORC_MAX_HEAD_DIM) return ORC_E_ARG;
+    if (hd < c->hd_kv) return ORC_E_GEOMETRY;
+    return ORC_OK;
+}
+
+/* Work unit: one (token, query head) row.  Units never reduce against each other and
+ * each owns its scratch, so the result is the same at any thread count. */
+static int attend_units(const float *const *kregs, const float *const *vregs,
+                        const int32_t *pos, int32_t nt, const float *q, int32_t n_head,
+                        int32_t hd, int32_t n_head_kv, int32_t hd_kv, int32_t max_vl,
+                        float scale, float *out, int32_t nthreads)
+{
+    const int32_t gqa = n_head / n_head_kv;
+    const int32_t nkt = n_head_kv * hd_kv;
+    const int64_t units = (int64_t)nt * n_head;
+    int failed = 0;
+#ifdef _OPENMP
+    int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nth)
+#endif
+    {
+        float *scr = (float *)malloc(sizeof(float) * (size_t)(max_vl > 0 ? max_vl : 1));
+        if (!scr) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t u = 0; u < units; u++) {
+                int32_t t = (int32_t)(u / n_head), h = (int32_t)(u % n_head);
+                int32_t hk = h / gqa;
+                int32_t vl = pos[t] + 1;
+                attend_row(q + ((size_t)t * n_head + h) * hd, kregs[t], vregs[t], nkt, hk,
+                           hd_kv, vl, scale, scr, out + ((size_t)t * n_head + h) * hd_kv);
+            }
+            free(scr);
+        }
+    }
+    (void)nthreads;
+    return failed ? ORC_E_NOMEM : ORC_OK;
+}
+
+/* nt query tokens of one sequence.  Token t sees rows [0, pos[t]] of the layer's
+ * regions: the causal mask is the window length, not a matrix.
+ * q: [nt][n_head][hd] (rotated); out: [nt][n_head][hd_kv]. */
+int orc_attn_prefill(const orc_cache *c, int32_t seq, int32_t layer, int32_t nt,
+                     const int32_t *pos, const float *q, int32_t n_head, int32_t hd,
+                     float scale, float *out, int32_t nthreads)
+{
+    if (!c || seq < 0 || seq >= c->n_seq || layer < 0 || layer >= c->n_layer || nt < 0)
+        return ORC_E_ARG;
+    if (nt == 0) return ORC_OK;
+    if (!pos || !q || !out || !isfinite(scale)) return ORC_E_ARG;
+    int st = check_heads(c, n_head, hd);
+    if (st != ORC_OK) return st;
+    int32_t max_vl = 0;
+    for (int32_t t = 0; t < nt; t++) {
+        if (pos[t] < 0 || pos[t] >= c->capacity) return ORC_E_RANGE;
+        if (pos[t] + 1 > max_vl) max_vl = pos[t] + 1;
+    }
+    const float **kr = (const float **)malloc(sizeof(float *) * (size_t)nt);
+    const float **vr = (const float **)malloc(sizeof(float *) * (size_t)nt);
+    if (!kr || !vr) { free(kr); free(vr); return ORC_E_NOMEM; }
+    const float *kreg = orc_cache_region((orc_cache *)c, 0, seq, layer);
+    const float *vreg = orc_cache_region((orc_cache *)c, 1, seq, layer);
+    for (int32_t t = 0; t < nt; t++) { kr[t] = kreg; vr[t] = vreg; }
+    st = attend_units(kr, vr, pos, nt, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl, scale,
+                      out, nthreads);
+    free(kr); free(vr);
+    return st;
+}
+
+/* One query token per batch entry b, at pos[b] of sequence seq_ids[b].  Entries only
+ * read the cache, so two entries may name the same sequence.
+ * q: [n_seq][n_head][hd]; out: [n_seq][n_head][hd_kv]. */
+int orc_attn_decode(const orc_cache *c, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
+                    const int32_t *pos, const float *q, int32_t n_head, int32_t hd,
+                    float scale, float *out, int32_t nthreads)
+{
+    if (!c || layer < 0 || layer >= c->n_layer || n_seq < 0) return ORC_E_ARG;
+    if (n_seq == 0) return ORC_OK;
+    if (!seq_ids || !pos || !q || !out || !isfinite(scale)) return ORC_E_ARG;
+    int st = check_heads(c, n_head, hd);
+    if (st != ORC_OK) return st;
+    for (int32_t b = 0; b < n_seq; b++)
+        if (seq_ids[b] < 0 || seq_ids[b] >= c->n_seq) return ORC_E_ARG;
+    int32_t max_vl = 0;
+    for (int32_t b = 0; b < n_seq; b++) {
+        if (pos[b] < 0 || pos[b] >= c->capacity) return ORC_E_RANGE;
+        if (pos[b] + 1 > max_vl) max_vl = pos[b] + 1;
+    }
+    const float **kr = (const float **)malloc(sizeof(float *) * (size_t)n_seq);
+    const float **vr = (const float **)malloc(sizeof(float *) * (size_t)n_seq);
+    if (!kr || !vr) { free(kr); free(vr); return ORC_E_NOMEM; }
+    for (int32_t b = 0; b < n_seq; b++) {
+        kr[b] = orc_cache_region((orc_cache *)c, 0, seq_ids[b], layer);
+        vr[b] = orc_cache_region((orc_cache *)c, 1, seq_ids[b], layer);
+    }
+    st = attend_units(kr, vr, pos, n_seq, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl, scale,
+                      out, nthreads);
+    free(kr); free(vr);
+    return st;
+}
+
+/* Threads the attention calls use when nthreads is 0. */
+int32_t orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,419 @@
+"""Pins that tie the oracle to something other than itself.
+
+Each pin takes an `oracle.Oracle` (the real one, or a deliberately broken copy built by
+the mutant test) and raises AssertionError if the oracle disagrees with what the pages
+and the mathematics fix: the pages' worked examples (tests/golden/), closed forms,
+arbitrary-precision values (mpmath), invariants the pages state, and an f64 brute force
+on tiny shapes.
+
+Sources: "11 · Attention, vec ops, and the KV cache" (§2.1 attention, §2.3 RoPE, §2.4
+GQA, §3.2.2 RoPE, §3.2.3 KV store, §3.2.4 attention, §3.2.5 softmax, §3.4 invariants)
+and "IV.2: Zero-copy KV cache" (append in place, no copy of existing rows).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+
+from oracle import (E_ARG, E_DUP, E_GEOMETRY, E_RANGE, OK, ROPE_INTERLEAVED, ROPE_NEOX,
+                    ROPE_NONE, Oracle, OracleCache)
+from tests import bruteforce as bf
+from tests.workloads import custom, custom_positions
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rn32(x: mpmath.mpf) -> np.float32:
+    """Round an arbitrary-precision value to the nearest f32 (ties to even)."""
+    with mpmath.workprec(24):
+        y = +x
+    return np.float32(float(y))
+
+
+def f32bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------------------------
+# RoPE
+# ------------------------------------------------------------------------------------
+
+def pin_inv_freq_correctly_rounded(o: Oracle):
+    """Every frequency equals freq_scale / base^(2i/hd) computed to 60 digits, then
+    rounded once to f32 (the reading of the pages' powf that no libm changes)."""
+    mpmath.mp.dps = 60
+    for hd in (4, 16, 64, 128, 256):
+        for base in (1.0e4, 1.0e6, 5.0e5):
+            for fs in (1.0, 0.25):
+                got = o.rope_inv_freq(hd, base, fs)
+                want = [rn32(mpmath.mpf(float(np.float32(fs))) /
+                             mpmath.power(mpmath.mpf(float(np.float32(base))),
+                                          mpmath.mpf(2 * i) / hd)) for i in range(hd // 2)]
+                assert np.array_equal(f32bits(got), f32bits(want)), (hd, base, fs)
+
+
+def pin_rope_worked_example(o: Oracle):
+    """§3.2.2 worked example: hd = 4, base = 1e4, pos = 2.  Pair 0 turns by 2 rad;
+    pair 1's speed is 1e4^(-1/2) = 0.01 by the formula (the page prints 0.1)."""
+    g = golden("rope_hd4_base1e4_pos2.json")["what_the_page_states"]
+    hd, base, p = g["hd"], g["freq_base"], g["pos"]
+    inv = o.rope_inv_freq(hd, base, 1.0)
+    assert inv[0] == np.float32(1.0)
+    assert inv[1] == np.float32(0.01)
+    cs, sn = o.rope_cos_sin(hd, base, 1.0, p)
+    assert np.float32(p) * inv[0] == np.float32(g["pair0_angle_rad"])
+    mpmath.mp.dps = 40
+    assert cs[0] == rn32(mpmath.cos(2)) and sn[0] == rn32(mpmath.sin(2))
+    th1 = mpmath.mpf(float(np.float32(2.0) * np.float32(0.01)))
+    assert cs[1] == rn32(mpmath.cos(th1)) and sn[1] == rn32(mpmath.sin(th1))
+    # Closed-form rotation of basis vectors (NEOX pairs (0,2), (1,3)).
+    e0 = np.array([[[1.0, 0.0, 0.0, 0.0]]], np.float32)
+    # (Values compared with ==, so a zero's sign does not matter; nonzero entries are
+    # exact because one factor of every product is 0 or 1.)
+    r = o.rope(e0, [p], base, 1.0, ROPE_NEOX)[0, 0]
+    assert np.array_equal(r, np.array([cs[0], 0.0, sn[0], 0.0], np.float32))
+    e3 = np.array([[[0.0, 0.0, 0.0, 1.0]]], np.float32)
+    r = o.rope(e3, [p], base, 1.0, ROPE_NEOX)[0, 0]
+    assert np.array_equal(r, np.array([0.0, -sn[1], 0.0, cs[1]], np.float32))
+    # Interleaved pairs (0,1), (2,3).
+    r = o.rope(e0, [p], base, 1.0, ROPE_INTERLEAVED)[0, 0]
+    assert np.array_equal(r, np.array([cs[0], sn[0], 0.0, 0.0], np.float32))
+
+
+def pin_cos_sin_correctly_rounded(o: Oracle):
+    """cos/sin of the f32 angle, correctly rounded: sampled against mpmath at the
+    long-context positions and both ends of the frequency range."""
+    mpmath.mp.dps = 40
+    rng = np.random.default_rng(11)
+    for hd in (16, 64, 128):
+        inv = o.rope_inv_freq(hd, 1.0e6, 1.0)
+        ps = np.concatenate([[0, 1, 2, 511, 32767, 40959], rng.integers(0, 40960, 6)])
+        for p in ps:
+            cs, sn = o.rope_cos_sin(hd, 1.0e6, 1.0, int(p))
+            for i in (0, 1, hd // 4, hd // 2 - 1):
+                th = mpmath.mpf(float(np.float32(p) * inv[i]))
+                assert cs[i] == rn32(mpmath.cos(th)), (hd, p, i)
+                assert sn[i] == rn32(mpmath.sin(th)), (hd, p, i)
+
+
+def pin_rope_pos0_identity(o: Oracle):
+    """Position 0 turns every pair by 0 rad: RoPE is the identity, bit for bit, on
+    N(0,1) data (which never holds a signed zero)."""
+    x = custom(1, (3, 4, 64))
+    for style in (ROPE_NEOX, ROPE_INTERLEAVED):
+        r = o.rope(x, [0, 0, 0], 1.0e6, 1.0, style)
+        assert np.array_equal(f32bits(r), f32bits(x))
+
+
+def pin_rope_brute_force(o: Oracle):
+    """Explicit f64 rotation matrices (their own pair lists and angles) agree with the
+    oracle within a few f32 ulps, for both layouts and a spread of positions."""
+    for style in (ROPE_NEOX, ROPE_INTERLEAVED):
+        for hd in (4, 16, 64):
+            x = custom(2 + hd, (5, 3, hd))
+            pos = [0, 1, 7, 300, 4095]
+            got = o.rope(x, pos, 1.0e4, 1.0, style).astype(np.float64)
+            want = bf.rope_bf(x, pos, 1.0e4, 1.0, style)
+            err = np.abs(got - want)
+            bound = 4 * np.finfo(np.float32).eps * (np.abs(x).max() + 1e-30)
+            assert err.max() <= bound, (style, hd, err.max())
+
+
+def pin_rope_norm_and_relative_position(o: Oracle):
+    """Rotation keeps each vector's norm, and <R(m)q, R(n)k> depends only on m - n."""
+    q = custom(3, (1, 1, 64))
+    k = custom(4, (1, 1, 64))
+    for style in (ROPE_NEOX, ROPE_INTERLEAVED):
+        r = o.rope(q, [1234], 1.0e4, 1.0, style)
+        n0, n1 = np.linalg.norm(q.astype(np.float64)), np.linalg.norm(r.astype(np.float64))
+        assert abs(n0 - n1) <= 1e-6 * n0
+        scale = np.linalg.norm(q) * np.linalg.norm(k)
+        for (m, n, d) in ((5, 2, 3), (10, 10, 7), (3, 9, 20)):
+            a = float(np.dot(o.rope(q, [m], 1.0e4, 1.0, style).ravel().astype(np.float64),
+                             o.rope(k, [n], 1.0e4, 1.0, style).ravel().astype(np.float64)))
+            b = float(np.dot(o.rope(q, [m + d], 1.0e4, 1.0, style).ravel().astype(np.float64),
+                             o.rope(k, [n + d], 1.0e4, 1.0, style).ravel().astype(np.float64)))
+            assert abs(a - b) <= 1e-5 * scale, (style, m, n, d, a, b)
+
+
+# ------------------------------------------------------------------------------------
+# Append (KV store)
+# ------------------------------------------------------------------------------------
+
+def pin_append_rows_land_in_place(o: Oracle):
+    """A store writes row t at offset pos[t] * row width of its (seq, layer) region and
+    nothing else; regions never move; the high-water mark is max(pos) + 1."""
+    c = OracleCache(2, 2, 2, 16, 20, o)
+    nkt = 32
+    k0 = c.k(1, 1).ctypes.data
+    k = custom(5, (3, 2, 16))
+    v = custom(6, (3, 2, 16))
+    st, _ = c.append_rope(1, [1, 1, 0], [4, 9, 2], None, 0, 0, k, v, 1.0e6, 1.0, ROPE_NONE)
+    assert st == OK
+    assert c.k(1, 1).ctypes.data == k0
+    K, V = c.k(1, 1), c.v(1, 1)
+    assert np.array_equal(f32bits(K[4]), f32bits(k[0].ravel()))
+    assert np.array_equal(f32bits(K[9]), f32bits(k[1].ravel()))
+    assert np.array_equal(f32bits(V[9]), f32bits(v[1].ravel()))
+    assert np.array_equal(f32bits(c.k(0, 1)[2]), f32bits(k[2].ravel()))
+    others = [r for r in range(20) if r not in (4, 9)]
+    assert not K[others].any() and not V[others].any()
+    assert not c.k(0, 0).any() and not c.k(1, 0).any()
+    assert c.seq_len(1, 1) == 10 and c.seq_len(0, 1) == 3 and c.seq_len(1, 0) == 0
+    assert K.shape == (20, nkt)
+    c.close()
+
+
+def pin_append_rotates_k_not_v(o: Oracle):
+    """The stored K row is k rotated at its position with the kv head dim's own
+    frequencies; the stored V row is v unchanged; q comes back rotated with hd's."""
+    c = OracleCache(1, 1, 2, 16, 8, o)
+    q = custom(7, (2, 4, 32))       # hd = 32 > hd_kv = 16
+    k = custom(8, (2, 2, 16))
+    v = custom(9, (2, 2, 16))
+    st, qr = c.append_rope(0, [0, 0], [3, 5], q, 4, 32, k, v, 1.0e4, 1.0, ROPE_NEOX)
+    assert st == OK
+    want_k = bf.rope_bf(k, [3, 5], 1.0e4, 1.0, bf.NEOX)
+    want_q = bf.rope_bf(q, [3, 5], 1.0e4, 1.0, bf.NEOX)
+    assert np.abs(c.k(0, 0)[[3, 5]].reshape(2, 2, 16) - want_k).max() < 1e-5
+    assert np.abs(qr - want_q).max() < 1e-5
+    assert np.array_equal(f32bits(c.v(0, 0)[[3, 5]]), f32bits(v.reshape(2, 32)))
+
+
+def pin_append_errors_write_nothing(o: Oracle):
+    """Position out of range -> error, never a clamp; duplicate (seq, pos) -> error;
+    bad sequence -> error; hd < hd_kv -> geometry error.  No error writes anything."""
+    c = OracleCache(2, 1, 2, 16, 10, o)
+    k = custom(10, (2, 2, 16))
+    v = custom(11, (2, 2, 16))
+    q = custom(12, (2, 4, 16))
+    cases = [
+        (dict(seq=[0, 0], pos=[3, 10]), E_RANGE),
+        (dict(seq=[0, 0], pos=[-1, 3]), E_RANGE),
+        (dict(seq=[0, 0], pos=[4, 4]), E_DUP),
+        (dict(seq=[0, 2], pos=[4, 5]), E_ARG),
+        (dict(seq=[0, 1], pos=[4, 4], hd=8), E_GEOMETRY),
+        (dict(seq=[0, 1], pos=[4, 4], hd=15), E_ARG),
+        (dict(seq=[0, 1], pos=[4, 4], n_head=3, q=custom(13, (2, 3, 16))), E_ARG),
+    ]
+    for kw, want in cases:
+        qq = kw.get("q", q)
+        hd = kw.get("hd", 16)
+        if hd != 16:
+            qq = custom(14, (2, 4, hd))
+        st, _ = c.append_rope(0, kw["seq"], kw["pos"], qq, kw.get("n_head", 4), hd, k, v,
+                              1.0e6, 1.0, ROPE_NEOX)
+        assert st == want, (kw, st, want)
+        assert not c.k(0, 0).any() and not c.k(1, 0).any() and not c.v(0, 0).any()
+        assert c.seq_len(0, 0) == 0 and c.seq_len(1, 0) == 0
+    # Distinct sequences may share a position.
+    st, _ = c.append_rope(0, [0, 1], [4, 4], q, 4, 16, k, v, 1.0e6, 1.0, ROPE_NEOX)
+    assert st == OK
+    c.close()
+
+
+# ------------------------------------------------------------------------------------
+# Attention
+# ------------------------------------------------------------------------------------
+
+def _cache_with_rows(o, K, V, n_head_kv, hd_kv, capacity):
+    c = OracleCache(1, 1, n_head_kv, hd_kv, capacity, o)
+    rows = len(K)
+    st, _ = c.append_rope(0, [0] * rows, list(range(rows)), None, 0, 0,
+                          np.asarray(K, np.float32).reshape(rows, n_head_kv, hd_kv),
+                          np.asarray(V, np.float32).reshape(rows, n_head_kv, hd_kv),
+                          1.0e6, 1.0, ROPE_NONE)
+    assert st == OK
+    return c
+
+
+def pin_attn_worked_example_1(o: Oracle):
+    """§3.2.4 first example: q = [1,1,0,0] at pos 1 blends v0 and v1 equally:
+    out = [2, 3, 0, 0] exactly; the third (masked) slot adds nothing."""
+    g = golden("attn_example1.json")
+    i = g["inputs"]
+    c = _cache_with_rows(o, i["k_rows"], i["v_rows"], 1, 4, i["capacity"])
+    st, out = c.attn_prefill(0, 0, [i["pos"]], np.array([[i["q"]]], np.float32), 1, 4,
+                             i["scale"])
+    assert st == OK
+    assert np.array_equal(out[0, 0], np.array(g["page_values"]["out"], np.float32))
+    c.close()
+
+
+def pin_attn_worked_example_2(o: Oracle):
+    """§3.2.4 variation: q = [1,0,0,0] scores [0.5, 0]; weights are the closed form
+    [1/(1+e^-0.5), 1/(1+e^0.5)] (the page's [0.73, 0.27] is softmax([1, 0]))."""
+    g = golden("attn_example2.json")
+    i = g["inputs"]
+    c = _cache_with_rows(o, i["k_rows"], i["v_rows"], 1, 4, i["capacity"])
+    st, out = c.attn_prefill(0, 0, [i["pos"]], np.array([[i["q"]]], np.float32), 1, 4,
+                             i["scale"])
+    assert st == OK
+    w0 = 1.0 / (1.0 + math.exp(-0.5))
+    want = [w0 * 1 + (1 - w0) * 3, w0 * 2 + (1 - w0) * 4, 0.0, 0.0]
+    assert np.abs(out[0, 0] - want).max() <= 1e-6
+    # The page's printed weights are those of the unscaled scores.
+    assert abs(1.0 / (1.0 + math.exp(-1.0)) - 0.73) < 0.005
+    c.close()
+
+
+def pin_attn_worked_example_3(o: Oracle):
+    """§3.2.4 decode step: append k2/v2 at pos 2, then tokens at pos 0, 1, 2 see 1, 2, 3
+    rows.  Token 2's output is the closed form; token 0 returns v0 exactly."""
+    g = golden("attn_example3.json")
+    i = g["inputs"]
+    c = _cache_with_rows(o, i["k_rows"][:2], i["v_rows"][:2], 1, 4, i["capacity"])
+    a = i["append"]
+    st, _ = c.append_rope(0, [0], [a["pos"]], None, 0, 0, np.array([[a["k"]]], np.float32),
+                          np.array([[a["v"]]], np.float32), 1.0e6, 1.0, ROPE_NONE)
+    assert st == OK and c.seq_len(0, 0) == 3
+    e = math.exp(0.5)
+    w0, w1 = 1 / (1 + 2 * e), e / (1 + 2 * e)
+    want2 = [w0 * 1 + w1 * 3 + w1 * 5, w0 * 2 + w1 * 4, 0.0, 0.0]
+    st, out = c.attn_decode(0, [0], [i["pos2"]], np.array([[i["q2"]]], np.float32), 1, 4, 0.5)
+    assert st == OK
+    assert np.abs(out[0, 0] - want2).max() <= 1e-6
+    # Windows: token 0 sees only row 0 -> exactly v0, whatever its query.
+    q3 = np.array([[[0, 1, 1, 0]], [[0, 1, 1, 0]], [[0, 1, 1, 0]]], np.float32)
+    st, out = c.attn_prefill(0, 0, [0, 1, 2], q3, 1, 4, 0.5)
+    assert st == OK
+    assert np.array_equal(out[0, 0], np.array(i["v_rows"][0], np.float32))
+    assert np.abs(out[2, 0] - want2).max() <= 1e-6
+    c.close()
+
+
+def pin_attn_brute_force(o: Oracle):
+    """Random tiny shapes against the f64 mask-matrix brute force: GQA groups 1, 2, 3,
+    hd > hd_kv, non-contiguous and repeated positions, ragged windows."""
+    shapes = [
+        # nt, n_head, n_head_kv, hd, hd_kv, capacity
+        (5, 2, 2, 8, 8, 9),
+        (7, 4, 2, 16, 16, 13),
+        (6, 6, 2, 24, 16, 11),
+        (4, 3, 1, 10, 6, 40),
+    ]
+    for si, (nt, nh, nkv, hd, hdk, cap) in enumerate(shapes):
+        K = custom(100 + si, (cap, nkv * hdk))
+        V = custom(200 + si, (cap, nkv * hdk))
+        c = _cache_with_rows(o, K.reshape(cap, nkv, hdk), V.reshape(cap, nkv, hdk), nkv, hdk,
+                             cap)
+        q = custom(300 + si, (nt, nh, hd))
+        pos = custom_positions(400 + si, nt, 0, cap, unique=False)
+        scale = 0.37
+        st, out = c.attn_prefill(0, 0, pos, q, nh, hd, scale)
+        assert st == OK
+        want = bf.attention_bf(q, K, V, pos, nkv, scale)
+        err = np.abs(out - want)
+        assert err.max() <= 1e-6 + 1e-5 * np.abs(want).max(), (si, err.max())
+        st, outd = c.attn_decode(0, [0] * nt, pos, q, nh, hd, scale)
+        assert st == OK and np.array_equal(f32bits(outd), f32bits(out))
+        c.close()
+
+
+def pin_attn_invariants(o: Oracle):
+    """Weights sum to 1 (constant V rows come back unchanged); one cached row returns
+    its V exactly; equal scores give the mean of V; rows past pos[t] never matter."""
+    nkv, hdk, cap = 2, 16, 12
+    q = custom(20, (3, 4, 16))
+    K = custom(21, (cap, nkv, hdk))
+    # Constant V: any convex combination returns the constant.
+    Vc = np.full((cap, nkv, hdk), 0.75, np.float32)
+    c = _cache_with_rows(o, K, Vc, nkv, hdk, cap)
+    st, out = c.attn_prefill(0, 0, [2, 7, 11], q, 4, 16, 0.25)
+    assert st == OK and np.abs(out - 0.75).max() <= 1e-6
+    c.close()
+    # Single row: weight exactly 1.
+    V = custom(22, (cap, nkv, hdk))
+    c = _cache_with_rows(o, K, V, nkv, hdk, cap)
+    st, out = c.attn_prefill(0, 0, [0, 0, 0], q, 4, 16, 0.25)
+    assert st == OK
+    for h in range(4):
+        assert np.array_equal(f32bits(out[:, h]), f32bits(np.repeat(V[0:1, h // 2], 3, 0)))
+    # Causality: rewriting rows beyond every window changes nothing.
+    st, before = c.attn_prefill(0, 0, [2, 5, 6], q, 4, 16, 0.25)
+    k2 = custom(23, (5, nkv, hdk))
+    st2, _ = c.append_rope(0, [0] * 5, [7, 8, 9, 10, 11], None, 0, 0, k2, k2, 1.0e6, 1.0,
+                           ROPE_NONE)
+    st3, after = c.attn_prefill(0, 0, [2, 5, 6], q, 4, 16, 0.25)
+    assert st == st2 == st3 == OK and np.array_equal(f32bits(before), f32bits(after))
+    c.close()
+    # Equal scores (zero keys): the plain mean of the window's V rows.
+    c = _cache_with_rows(o, np.zeros_like(K), V, nkv, hdk, cap)
+    st, out = c.attn_prefill(0, 0, [4], q[:1], 4, 16, 0.25)
+    assert st == OK
+    assert np.abs(out[0, 0] - V[:5, 0].astype(np.float64).mean(0)).max() <= 1e-6
+    assert np.abs(out[0, 3] - V[:5, 1].astype(np.float64).mean(0)).max() <= 1e-6
+    c.close()
+
+
+def pin_attn_large_scores_stable(o: Oracle):
+    """Scores in the hundreds must not overflow: the max is subtracted before exp
+    (§3.2.5), so the result still matches the brute force and holds no NaN/inf."""
+    cap, nkv, hdk = 6, 1, 8
+    K = custom(30, (cap, nkv * hdk)) * 20
+    V = custom(31, (cap, nkv * hdk))
+    c = _cache_with_rows(o, K.reshape(cap, 1, 8), V.reshape(cap, 1, 8), 1, 8, cap)
+    q = custom(32, (2, 1, 8)) * 20
+    st, out = c.attn_prefill(0, 0, [3, 5], q, 1, 8, 1.0)
+    assert st == OK and np.isfinite(out).all()
+    want = bf.attention_bf(q, K, V, [3, 5], 1, 1.0)
+    assert np.abs(out - want).max() <= 1e-5
+    c.close()
+
+
+def pin_attn_thread_invariance(o: Oracle):
+    """Heads never reduce against each other: 1 thread and many give the same bits."""
+    cap, nkv, hdk = 64, 2, 16
+    K = custom(40, (cap, nkv, hdk))
+    V = custom(41, (cap, nkv, hdk))
+    c = _cache_with_rows(o, K, V, nkv, hdk, cap)
+    q = custom(42, (9, 6, 16))
+    pos = custom_positions(43, 9, 0, cap)
+    st1, a = c.attn_prefill(0, 0, pos, q, 6, 16, 0.25, nthreads=1)
+    st4, b = c.attn_prefill(0, 0, pos, q, 6, 16, 0.25, nthreads=4)
+    assert st1 == st4 == OK and np.array_equal(f32bits(a), f32bits(b))
+    c.close()
+
+
+def pin_attn_errors(o: Oracle):
+    """Attention rejects hd < hd_kv, a position beyond the region, a bad sequence and a
+    head count the kv heads do not divide."""
+    c = OracleCache(2, 1, 2, 16, 10, o)
+    q = custom(50, (1, 4, 16))
+    assert c.attn_prefill(0, 0, [3], custom(51, (1, 4, 8)), 4, 8, 0.25)[0] == E_GEOMETRY
+    assert c.attn_prefill(0, 0, [10], q, 4, 16, 0.25)[0] == E_RANGE
+    assert c.attn_prefill(2, 0, [3], q, 4, 16, 0.25)[0] == E_ARG
+    assert c.attn_prefill(0, 0, [3], custom(52, (1, 3, 16)), 3, 16, 0.25)[0] == E_ARG
+    assert c.attn_decode(0, [0, 5], [1, 2], custom(53, (2, 4, 16)), 4, 16, 0.25)[0] == E_ARG
+    assert c.attn_decode(0, [0, 1], [1, 10], custom(53, (2, 4, 16)), 4, 16, 0.25)[0] == E_RANGE
+    c.close()
+
+
+ALL_PINS = [
+    pin_inv_freq_correctly_rounded,
+    pin_rope_worked_example,
+    pin_cos_sin_correctly_rounded,
+    pin_rope_pos0_identity,
+    pin_rope_brute_force,
+    pin_rope_norm_and_relative_position,
+    pin_append_rows_land_in_place,
+    pin_append_rotates_k_not_v,
+    pin_append_errors_write_nothing,
+    pin_attn_worked_example_1,
+    pin_attn_worked_example_2,
+    pin_attn_worked_example_3,
+    pin_attn_brute_force,
+    pin_attn_invariants,
+    pin_attn_large_scores_stable,
+    pin_attn_thread_invariance,
+    pin_attn_errors,
+]

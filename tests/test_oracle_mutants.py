@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that the pins
+catch every one: a pin set that a dropped term, a flipped sign, a wrong index or a
+transposed operand can slip past is not a pin set.
+
+Each mutant is oracle.c with one textual substitution, built with the oracle's own
+flags into a temporary directory.  The real oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle as oracle_pkg
+from oracle import Oracle
+from tests.oracle_pins import ALL_PINS
+
+MUTANTS = {
+    # RoPE
+    "rotation_sign": ("x[i0] = a - b;", "x[i0] = a + b;"),
+    "rotation_swap_cos_sin": ("float a = x0 * cs[i];", "float a = x0 * sn[i];"),
+    "neox_pair_index": ("{ i0 = i; i1 = i + half; }", "{ i0 = i; i1 = hd - 1 - i; }"),
+    "freq_exponent_drops_2": ("(long double)(2 * i) / (long double)hd",
+                              "(long double)(i) / (long double)hd"),
+    "freq_scale_ignored": ("(long double)freq_scale / powl", "1.0L / powl"),
+    "angle_in_f64": ("cs[i] = (float)cosl((long double)theta);",
+                     "cs[i] = (float)cosl((long double)p * (long double)inv[i]);"),
+    # Store
+    "store_v_from_k": ("memcpy(vd, v + (size_t)t * nkt", "memcpy(vd, k + (size_t)t * nkt"),
+    "store_off_by_one_row": ("+ (size_t)pos[t] * nkt;\n        float *vd",
+                             "+ (size_t)(pos[t] > 0 ? pos[t] - 1 : 0) * nkt;\n        float *vd"),
+    "k_not_rotated": ("int st = orc_rope(row, 1,", "int st = 0 * orc_rope(row, 0,"),
+    "high_water_off": ("if (pos[t] + 1 > *hw) *hw = pos[t] + 1;", "if (pos[t] > *hw) *hw = pos[t];"),
+    "no_range_check": ("if (pos[t] < 0 || pos[t] >= c->capacity) return ORC_E_RANGE;\n    int64_t",
+                       "if (pos[t] < 0 || pos[t] > c->capacity) return ORC_E_RANGE;\n    int64_t"),
+    # Attention
+    "gqa_modulo": ("int32_t hk = h / gqa;", "int32_t hk = h % n_head_kv;"),
+    "window_drops_current_row": ("int32_t vl = pos[t] + 1;", "int32_t vl = pos[t] > 0 ? pos[t] : 1;"),
+    "no_scale": ("float s = dot_f32(hd_kv, qrow, kr) * scale;", "float s = dot_f32(hd_kv, qrow, kr);"),
+    "no_max_subtraction": ("float e = expf(scr[j] - mx);", "float e = expf(scr[j]);"),
+    "v_from_k_region": ("const float *vr = vreg + (size_t)j * nkt", "const float *vr = kreg + (size_t)j * nkt"),
+    "dot_over_hd_stride": ("(size_t)j * nkt + (size_t)hk * hd_kv;\n        float s",
+                           "(size_t)j * hd_kv + (size_t)hk * hd_kv;\n        float s"),
+    "no_normalisation": ("for (int32_t j = 0; j < vl; j++) scr[j] *= inv;", ""),
+}
+
+
+@pytest.fixture(scope="module")
+def src():
+    with open(oracle_pkg._SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, src, name):
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", *oracle_pkg.CFLAGS, str(path), "-o", str(lib), "-lm"], check=True)
+    o = Oracle(str(lib))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
