@@ -1,0 +1,205 @@
+/*
+ * kvc.h -- causal grouped-query attention over a per-layer KV cache, on MI355X (gfx950).
+ *
+ * One hot path, exposed as a C ABI of plain pointers and sizes:
+ *   kv_alloc        size the per-(sequence, layer) K and V regions once, zeroed
+ *   kv_append_rope  rotate q and k (RoPE) at positions given as data, write K/V rows
+ *                   in place at those positions
+ *   gqa_attn_prefill  nt query tokens of one sequence, token t attending rows [0, pos[t]]
+ *   gqa_attn_decode   one query token per sequence for a batch of sequences
+ * plus kv_free, kv_view, kv_seq_len and kv_last_error for ownership, inspection and
+ * error text.
+ *
+ * Sources (page titles; sections named per declaration):
+ *   [MINFER-11] "11 · Attention, vec ops, and the KV cache"
+ *   [ZEROCOPY]  "IV.2: Zero-copy KV cache"
+ *   [MINFER-13] "13 · The decode loop and graph reuse"
+ *
+ * Conventions for every call
+ *   - All tensors are f32.  "device" pointers are HIP device memory; "host" pointers are
+ *     ordinary host memory, read before the call returns (the caller may reuse them at
+ *     once).  Device buffers must stay valid until the work queued on `stream` is done.
+ *   - Device pointers must be 16-byte aligned and the tensors dense (row-major, no gaps).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only queues work;
+ *     nothing synchronises with the host except kv_alloc / kv_free.  Calls on one handle
+ *     must be issued from one host thread onto one stream (or be otherwise ordered):
+ *     the handle's staging and scratch memory is reused call after call.
+ *   - Store before attention: a row must be appended (on the same stream, earlier) before
+ *     an attention call that reads it ([MINFER-11] §3.4).  Rows never written read as 0.
+ *   - Every argument is checked on the host before any device work.  On any non-OK
+ *     status nothing is written: no cache row, no q element, no output element.
+ *     kv_last_error() then returns a message for the calling thread.
+ *   - nt == 0 / n_seq == 0 is an OK no-op (after the handle and layer are checked).
+ *
+ * Limits of this implementation: hd_kv (the KV head dim) must be one of 16, 32, 64, 128,
+ * 256; the query head dim hd must be even, <= 256 and >= hd_kv; positions < capacity
+ * <= 2^24.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvc_cache kvc_cache; /* opaque; owns the regions, tables and scratch */
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_E_ARG = 1,      /* bad pointer, size, index, style or unsupported head dim */
+    KVC_E_GEOMETRY = 2, /* hd < hd_kv: a query head shorter than its key ([MINFER-11] §1, §3.3) */
+    KVC_E_RANGE = 3,    /* a position < 0 or >= capacity: an error, never a clamp (§3.2.3) */
+    KVC_E_DUP = 4,      /* one append names the same (sequence, position) twice */
+    KVC_E_NOMEM = 5,    /* device or pinned host allocation failed */
+    KVC_E_HIP = 6       /* a HIP runtime call failed (message holds hipGetErrorString) */
+} kvc_status;
+
+/* Which elements form a rotating pair ([MINFER-11] §3.2.2, the layout styles). */
+typedef enum kvc_rope_style {
+    KVC_ROPE_NEOX = 0,        /* (i, i + hd/2): Qwen2/Qwen3 */
+    KVC_ROPE_INTERLEAVED = 1, /* (2i, 2i + 1): Llama */
+    KVC_ROPE_NONE = 2         /* no rotation: a plain store of k and v, q untouched */
+} kvc_rope_style;
+
+#define KVC_MAX_HEAD_DIM 256
+#define KVC_MAX_CAPACITY (1 << 24)
+
+/*
+ * kv_alloc -- create a cache of n_seq x n_layer persistent regions.
+ * [MINFER-11] §2.2 (each layer owns a K and a V region of n_kv_embd x n_ctx floats);
+ * [ZEROCOPY] "A Vec with capacity is already a preallocated buffer" (reserve once);
+ * [MINFER-13] §2.5 (the regions outlive every call that uses them).
+ *
+ *   out        host; receives the handle.
+ *   n_seq      independent sequences (>= 1).
+ *   n_layer    layers (>= 1).
+ *   n_head_kv  KV heads per row (>= 1).
+ *   hd_kv      KV head dim, one of 16, 32, 64, 128, 256.
+ *   capacity   rows per (sequence, layer) region, 1 .. 2^24.  Fixed for the handle's
+ *              life: the regions never grow, move or get copied.
+ *   stream     used for the zero fill; kv_alloc waits for it before returning.
+ *
+ * Layout in device memory: K[n_seq][n_layer][capacity][n_head_kv * hd_kv], V likewise;
+ * row p of a region holds position p, kv head hk at columns [hk*hd_kv, (hk+1)*hd_kv).
+ * All rows start as +0.0f.
+ * Errors: KVC_E_ARG (bad geometry or null out), KVC_E_NOMEM, KVC_E_HIP.  On error *out
+ * is set to NULL and nothing stays allocated.
+ */
+kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
+                    int32_t hd_kv, int32_t capacity, void *stream);
+
+/*
+ * kv_free -- wait for the device, then release every region, table and scratch buffer.
+ * Pointers from kv_view become invalid.  NULL is accepted (no-op).
+ */
+kvc_status kv_free(kvc_cache *c);
+
+/*
+ * kv_view -- borrow one (sequence, layer)'s regions without copying ([ZEROCOPY]
+ * "Reading without copying": a live reference into the cache's own storage).
+ *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] f32.
+ *         The pointers never change for the handle's life and stay owned by it.
+ * Errors: KVC_E_ARG for a NULL handle/pointer or seq/layer out of range.
+ */
+kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, float **k, float **v);
+
+/*
+ * kv_seq_len -- high-water mark of one (sequence, layer): 1 + the largest position ever
+ * appended there, 0 if none ([ZEROCOPY] the trait's seq_len).  Bookkeeping only: no
+ * kernel reads it; attention windows come from the positions passed to each call.
+ * Errors: KVC_E_ARG.
+ */
+kvc_status kv_seq_len(const kvc_cache *c, int32_t seq, int32_t layer, int32_t *len);
+
+/*
+ * kv_append_rope -- RoPE on q and k at the given positions, then write k and v rows in
+ * place.  [MINFER-11] §2.3 and §3.2.2 (RoPE: speed_i = freq_scale / freq_base^(2i/d),
+ * angle = position * speed_i, a 2-D rotation of each pair), §3.2.3 (the store: row t
+ * goes to offset pos[t] * row width of its layer's region; a position outside the region
+ * is an error); [ZEROCOPY] "The cache appends in place" (no reallocation, no copy of
+ * existing rows).
+ *
+ *   layer       layer whose regions receive the rows.
+ *   nt          tokens in this call.
+ *   seq_ids     host [nt]: sequence of token t (0 .. n_seq-1).
+ *   pos         host [nt]: position of token t (0 .. capacity-1).  (seq_ids[t], pos[t])
+ *               pairs must be distinct within one call.
+ *   q           device [nt][n_head][hd], rotated in place with head dim hd; may be NULL
+ *               (then n_head and hd are ignored).
+ *   n_head, hd  query heads (a multiple of n_head_kv) and query head dim (even,
+ *               hd_kv <= hd <= 256).
+ *   k, v        device [nt][n_head_kv][hd_kv].  k is rotated with head dim hd_kv and
+ *               written to K[seq_ids[t]][layer][pos[t]]; v is written unchanged to V.
+ *               The inputs k and v are not modified.
+ *   freq_base, freq_scale  RoPE base and speed scale (finite, > 0; ignored for NONE).
+ *   style       pair layout.
+ *
+ * Rounding: each speed and each cos/sin is the correctly rounded f32 of its exact value;
+ * the angle is the f32 product f32(pos) * speed; each product and sum of the rotation is
+ * rounded to f32 on its own (no fused multiply-add).  So rotated rows are bit-for-bit
+ * reproducible on any machine.
+ * Also raises the (seq, layer) high-water marks.
+ * Errors: KVC_E_ARG, KVC_E_GEOMETRY (q given and hd < hd_kv), KVC_E_RANGE, KVC_E_DUP,
+ * KVC_E_NOMEM, KVC_E_HIP.
+ */
+kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                          const int32_t *pos, float *q, int32_t n_head, int32_t hd,
+                          const float *k, const float *v, float freq_base, float freq_scale,
+                          kvc_rope_style style, void *stream);
+
+/*
+ * gqa_attn_prefill -- causal GQA attention for nt query tokens of one sequence.
+ * [MINFER-11] §2.1 (score = q.k * scale over s <= t, softmax, weighted sum of v),
+ * §2.4 (query head h reads kv head h / (n_head / n_head_kv)), §3.2.4 (the window of
+ * token t is rows [0, pos[t]]: the mask is a length, not a matrix), §2.5 (online softmax
+ * over tiles on a GPU).
+ *
+ *   seq, layer  the region pair read.
+ *   nt          query tokens.
+ *   pos         host [nt]: position of each query token (any order, repeats allowed).
+ *   q           device [nt][n_head][hd], already rotated; the dot uses q[t][h][0:hd_kv].
+ *   n_head, hd  as in kv_append_rope.
+ *   scale       multiplies every dot product (the model's 1/sqrt(hd); finite).
+ *   out         device [nt][n_head][hd_kv], overwritten.
+ *
+ * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE (a position >= capacity), KVC_E_NOMEM,
+ * KVC_E_HIP.
+ */
+kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int32_t nt,
+                            const int32_t *pos, const float *q, int32_t n_head, int32_t hd,
+                            float scale, float *out, void *stream);
+
+/*
+ * gqa_attn_decode -- one query token per batch entry: entry b attends rows [0, pos[b]] of
+ * sequence seq_ids[b].  Same mathematics as gqa_attn_prefill ([MINFER-11] §2.1, §2.4,
+ * §3.2.4); long windows are split across workgroups and merged by log-sum-exp
+ * ([MINFER-11] §2.5: split the KV axis across blocks, then reduce).
+ *
+ *   layer       the layer read.
+ *   n_seq       batch entries.
+ *   seq_ids     host [n_seq]: sequence of each entry (entries only read, so repeats are
+ *               allowed).
+ *   pos         host [n_seq]: position of each entry's query token.
+ *   q           device [n_seq][n_head][hd], already rotated.
+ *   n_head, hd, scale  as in gqa_attn_prefill.
+ *   out         device [n_seq][n_head][hd_kv], overwritten.
+ *
+ * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE, KVC_E_NOMEM, KVC_E_HIP.
+ */
+kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                           const int32_t *seq_ids, const int32_t *pos, const float *q,
+                           int32_t n_head, int32_t hd, float scale, float *out, void *stream);
+
+/*
+ * kv_last_error -- text of the calling thread's last non-OK status ("" if none).  The
+ * string is owned by the library and valid until the thread's next call.
+ */
+const char *kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

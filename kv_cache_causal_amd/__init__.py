@@ -1,0 +1,210 @@
+"""Python binding of libkvc.so: causal GQA attention over a per-layer KV cache on MI355X.
+
+Argument marshalling only.  Every step of the path (RoPE tables, RoPE + append,
+split-K decode, MFMA prefill) runs in the library's gfx950 kernels; this module turns
+torch device tensors into pointers, numpy/list host arrays into int32 buffers, picks the
+current torch stream, and raises KvcError on a non-OK status.  There is no fallback: if
+the library is not built, importing works but every call raises.
+
+The functions carry the C names of include/kvc.h and take the same arguments, minus the
+sizes the tensors already carry.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libkvc.so")
+
+OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM, E_HIP = range(7)
+ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
+STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANGE",
+                4: "KVC_E_DUP", 5: "KVC_E_NOMEM", 6: "KVC_E_HIP"}
+
+# Every symbol include/kvc.h declares.
+EXPORTS = ("kv_alloc", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
+           "gqa_attn_prefill", "gqa_attn_decode", "kv_last_error")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libkvc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(python -m kv_cache_causal_amd._build)")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7 (same soname as
+    # the system one libkvc.so was linked against).  Loading torch first makes libkvc.so
+    # bind to the runtime that owns torch's device memory and streams.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(path)
+    i32, f32, p = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    sig = {
+        "kv_alloc": [ctypes.POINTER(p), i32, i32, i32, i32, i32, p],
+        "kv_free": [p],
+        "kv_view": [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(p)],
+        "kv_seq_len": [p, i32, i32, ctypes.POINTER(i32)],
+        "kv_append_rope": [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, ctypes.c_int, p],
+        "gqa_attn_prefill": [p, i32, i32, i32, p, p, i32, i32, f32, p, p],
+        "gqa_attn_decode": [p, i32, i32, p, p, p, i32, i32, f32, p, p],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.kv_last_error.argtypes = []
+    L.kv_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def kv_last_error() -> str:
+    return lib().kv_last_error().decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise KvcError(st, kv_last_error())
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    """Device pointer of a dense f32 torch CUDA tensor (or None / a raw int pointer)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not (t.is_cuda and t.dtype.is_floating_point and t.element_size() == 4):
+        raise TypeError(f"{name} must be an f32 tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _host_i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    return a, a.ctypes.data
+
+
+class Cache:
+    """Owning wrapper of a kvc_cache handle (kv_free on close / garbage collection)."""
+
+    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None):
+        self.n_seq, self.n_layer = n_seq, n_layer
+        self.n_head_kv, self.hd_kv, self.capacity = n_head_kv, hd_kv, capacity
+        self.nkt = n_head_kv * hd_kv
+        h = ctypes.c_void_p()
+        _check(lib().kv_alloc(ctypes.byref(h), n_seq, n_layer, n_head_kv, hd_kv, capacity,
+                              _stream(stream)))
+        self.handle = h.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            _check(lib().kv_free(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def kv_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None) -> Cache:
+    return Cache(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream)
+
+
+def kv_free(c: Cache):
+    c.close()
+
+
+def kv_view(c: Cache, seq: int, layer: int):
+    """(k_ptr, v_ptr): device addresses of the [capacity][n_head_kv*hd_kv] regions."""
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().kv_view(c.handle, seq, layer, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def kv_seq_len(c: Cache, seq: int, layer: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib().kv_seq_len(c.handle, seq, layer, ctypes.byref(n)))
+    return n.value
+
+
+def kv_append_rope(c: Cache, layer, seq_ids, pos, q, n_head, hd, k, v, freq_base,
+                   freq_scale=1.0, style=ROPE_NEOX, stream=None):
+    """q: [nt][n_head][hd] f32 CUDA tensor or None (rotated in place); k, v:
+    [nt][n_head_kv][hd_kv].  seq_ids, pos: host int arrays of length nt."""
+    s_arr, s_ptr = _host_i32(seq_ids)
+    p_arr, p_ptr = _host_i32(pos)
+    if s_arr.size != p_arr.size:
+        raise ValueError("seq_ids and pos differ in length")
+    _check(lib().kv_append_rope(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
+                                n_head, hd, _dev(k, "k"), _dev(v, "v"), freq_base, freq_scale,
+                                style, _stream(stream)))
+
+
+def gqa_attn_prefill(c: Cache, seq, layer, pos, q, n_head, hd, scale, out, stream=None):
+    p_arr, p_ptr = _host_i32(pos)
+    _check(lib().gqa_attn_prefill(c.handle, seq, layer, int(p_arr.size), p_ptr, _dev(q, "q"),
+                                  n_head, hd, scale, _dev(out, "out"), _stream(stream)))
+
+
+def gqa_attn_decode(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out, stream=None):
+    s_arr, s_ptr = _host_i32(seq_ids)
+    p_arr, p_ptr = _host_i32(pos)
+    if s_arr.size != p_arr.size:
+        raise ValueError("seq_ids and pos differ in length")
+    _check(lib().gqa_attn_decode(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
+                                 n_head, hd, scale, _dev(out, "out"), _stream(stream)))
+
+
+_hip = None
+
+
+def kv_read(c: Cache, seq: int, layer: int, stream=None):
+    """Copies (device to device, on `stream`) of one (seq, layer)'s K and V regions as
+    [capacity][n_head_kv * hd_kv] torch tensors.  For inspection and tests."""
+    global _hip
+    import torch
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded (by soname)
+        _hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_void_p]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    kp, vp = kv_view(c, seq, layer)
+    out = []
+    for src in (kp, vp):
+        t = torch.empty((c.capacity, c.nkt), dtype=torch.float32, device="cuda")
+        e = _hip.hipMemcpyAsync(t.data_ptr(), src, c.capacity * c.nkt * 4, 3, _stream(stream))
+        if e != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed: {e}")
+        out.append(t)
+    return out[0], out[1]

@@ -1,0 +1,57 @@
+// Host-only shim over validate.cpp, built with g++ into libkvc_hostcheck.so.  It lets the
+// CPU test suite drive every argument check of the library without HIP or a GPU; the
+// library itself calls the same functions from kvc_api.cpp.
+#include <cstring>
+#include <string>
+
+#include "validate.hpp"
+
+namespace {
+thread_local std::string g_msg;
+
+kvc::Geometry geom(const int32_t *g5)
+{
+    kvc::Geometry g;
+    g.n_seq = g5[0];
+    g.n_layer = g5[1];
+    g.n_head_kv = g5[2];
+    g.hd_kv = g5[3];
+    g.capacity = g5[4];
+    return g;
+}
+}  // namespace
+
+extern "C" {
+
+const char *hc_last_message(void) { return g_msg.c_str(); }
+
+int hc_check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
+                   int32_t capacity)
+{
+    return kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, g_msg);
+}
+
+int hc_check_append(const int32_t *g5, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                    const int32_t *pos, const void *q, int32_t n_head, int32_t hd, const void *k,
+                    const void *v, float freq_base, float freq_scale, int32_t style)
+{
+    return kvc::check_append(geom(g5), layer, nt, seq_ids, pos, q, n_head, hd, k, v, freq_base,
+                             freq_scale, style, g_msg);
+}
+
+int hc_check_prefill(const int32_t *g5, int32_t seq, int32_t layer, int32_t nt,
+                     const int32_t *pos, const void *q, int32_t n_head, int32_t hd, float scale,
+                     const void *out)
+{
+    return kvc::check_prefill(geom(g5), seq, layer, nt, pos, q, n_head, hd, scale, out, g_msg);
+}
+
+int hc_check_decode(const int32_t *g5, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
+                    const int32_t *pos, const void *q, int32_t n_head, int32_t hd, float scale,
+                    const void *out)
+{
+    return kvc::check_decode(geom(g5), layer, n_seq, seq_ids, pos, q, n_head, hd, scale, out,
+                             g_msg);
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// K4: causal GQA prefill attention on the fp32 matrix cores (MFMA).
+//
+// "11 · Attention, vec ops, and the KV cache":
+//   §2.1   out_t = sum_{s <= t} softmax(q_t . k_s * scale) v_s.
+//   §2.4   query head h reads kv head h / (n_head / n_head_kv).
+//   §3.2.4 token t's window is rows [0, pos[t]] of the layer's regions; positions are data
+//          (any order, any gaps), so the mask is computed per (query, key) from pos.
+//   §2.5   on a GPU the (query, key) matrix is tiled and the softmax runs online.
+//
+// Prefill is a dense contraction (C5: >700 flop per byte), so both products run on
+// v_mfma_f32_16x16x4_f32, full fp32 in and out.  Design:
+//   * Workgroup = 4 wave64s = 64 query rows of one kv head: GB heads of the kv group x TQ
+//     tokens (GB * TQ = 64), so one K/V tile in LDS serves all of them.  Each wave owns 16
+//     query rows (one head, 16 tokens).
+//   * The transposed products keep every per-query quantity in one lane column:
+//       S^T[key][q]  = K[key][:] . Q[q][:]       (A = K tile from LDS, B = Q in registers)
+//       O^T[d][q]   += V^T[d][key] P^T[key][q]   (A = V tile from LDS, B = P in registers)
+//     With lane l = 16 * g + c, the S^T accumulator of a 16-key block holds keys 4g..4g+3
+//     of query c -- exactly the B operand the O^T product needs for its 4 k-steps, so P
+//     never leaves registers.  The head-dim contraction of S^T is permuted so lane group
+//     g owns dims [g*hd/4, (g+1)*hd/4): Q and K fragments are contiguous (b128 reads).
+//   * Online softmax per query column: the row max is a max over 16 registers and two
+//     cross-group shuffles; the rescale factor is per lane; the row sum stays per lane
+//     group until the end.
+//   * Causality from data: a block scans key tiles up to the max position of its tokens;
+//     a wave skips tiles beyond its own max; the per-element mask (key > pos) is a select.
+//   * Heavy query tiles (late positions) are launched first to shorten the tail.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int HD>
+struct PrefillCfg {
+    static constexpr int KT = HD >= 256 ? 32 : 64;  // keys per tile
+    static constexpr int KB = KT / 16;              // 16-key blocks per tile
+    static constexpr int DQ = HD / 4;               // dims per lane group
+    static constexpr int STR = HD + 4;              // LDS row stride (floats)
+};
+
+template <int HD>
+__global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t GB, int32_t TQ,
+                                                      int32_t n_qtiles, int32_t n_hsub)
+{
+    using C = PrefillCfg<HD>;
+    constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, STR = C::STR;
+    __shared__ float Ks[KT * STR];
+    __shared__ float Vs[KT * STR];
+    __shared__ int s_kmax;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int qc = lane & 15;   // query column of this lane
+    const int grp = lane >> 4;  // lane group: key rows 4grp..4grp+3 of each 16-key block
+
+    const int qtile = n_qtiles - 1 - (int)blockIdx.x;
+    const int hk = (int)blockIdx.y / n_hsub;
+    const int hs = (int)blockIdx.y - hk * n_hsub;
+    const int G = p.n_head / p.n_head_kv;
+    const int wpt = TQ / 16;                 // waves per head
+    const int g = hs * GB + wave / wpt;      // head within the kv group
+    const bool head_ok = g < G;
+    const int h = hk * G + (head_ok ? g : 0);
+    const int t = qtile * TQ + (wave % wpt) * 16 + qc;
+    const bool tok_ok = t < p.nt;
+    const int pq = tok_ok ? p.pos[t] : 0;
+
+    // Largest position among this block's tokens.
+    if (tid == 0) s_kmax = 0;
+    __syncthreads();
+    if (tid < TQ) {
+        const int tt = qtile * TQ + tid;
+        if (tt < p.nt) atomicMax(&s_kmax, p.pos[tt]);
+    }
+    // Largest position among this wave's 16 tokens (reduce over the 16 query columns).
+    int wmax = pq;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) wmax = max(wmax, __shfl_xor(wmax, off));
+
+    // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h).
+    float qf[DQ];
+    {
+        const float *qrow = p.q + ((int64_t)(tok_ok ? t : 0) * p.n_head + h) * p.hd + grp * DQ;
+#pragma unroll
+        for (int s = 0; s < DQ; s++) qf[s] = qrow[s];
+    }
+
+    floatx4 oacc[HD / 16];
+#pragma unroll
+    for (int db = 0; db < HD / 16; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY, l = 0.0f;
+
+    __syncthreads();
+    const int ntiles = s_kmax / KT + 1;
+    const int nkt = p.n_head_kv * HD;
+    const float *Kh = p.kc + hk * HD;
+    const float *Vh = p.vc + hk * HD;
+
+    for (int kt = 0; kt < ntiles; kt++) {
+        const int key0 = kt * KT;
+        // Stage the tile's K and V rows of kv head hk; rows past the region read as 0.
+        for (int idx = tid; idx < KT * (HD / 4); idx += 256) {
+            const int r = idx / (HD / 4);
+            const int c4 = idx - r * (HD / 4);
+            const int row = key0 + r;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (row < p.capacity) {
+                kv = *reinterpret_cast<const float4 *>(Kh + (int64_t)row * nkt + c4 * 4);
+                vv = *reinterpret_cast<const float4 *>(Vh + (int64_t)row * nkt + c4 * 4);
+            }
+            *reinterpret_cast<float4 *>(&Ks[r * STR + c4 * 4]) = kv;
+            *reinterpret_cast<float4 *>(&Vs[r * STR + c4 * 4]) = vv;
+        }
+        __syncthreads();
+
+        if (head_ok && key0 <= wmax) {
+            // S^T = K Q^T for KB blocks of 16 keys; independent accumulators interleaved.
+            floatx4 sacc[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++) sacc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < DQ; s += 4) {
+                float4 kf[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++)
+                    kf[kb] = *reinterpret_cast<const float4 *>(&Ks[(kb * 16 + qc) * STR + grp * DQ + s]);
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].x, qf[s + 0], sacc[kb]);
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].y, qf[s + 1], sacc[kb]);
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].z, qf[s + 2], sacc[kb]);
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].w, qf[s + 3], sacc[kb]);
+            }
+            // Scale to base-2 units and mask keys beyond this query's position.
+            float sv[KB][4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int key = key0 + kb * 16 + grp * 4 + r;
+                    const float x = key <= pq ? sacc[kb][r] * p.qscale : -INFINITY;
+                    sv[kb][r] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            // Key 0 is in tile 0 and every window holds it, so mn is finite from tile 0 on.
+            const float mn = fmaxf(m, tmax);
+            const float alpha = fast_exp2(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < HD / 16; db++) oacc[db] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float pr = fast_exp2(sv[kb][r] - mn);
+                    sv[kb][r] = pr;
+                    l += pr;
+                }
+            m = mn;
+            // O^T += V^T P^T: k-step (kb, r) uses key kb*16 + 4*grp + r for lane group grp.
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * STR + qc];
+#pragma unroll
+                    for (int db = 0; db < HD / 16; db++)
+                        oacc[db] = mfma4(vrow[db * 16], sv[kb][r], oacc[db]);
+                }
+        }
+        __syncthreads();
+    }
+
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (head_ok && tok_ok) {
+        const float inv = 1.0f / l;
+        float *orow = p.out + ((int64_t)t * p.n_head + h) * HD + grp * 4;
+#pragma unroll
+        for (int db = 0; db < HD / 16; db++) {
+            const floatx4 o = oacc[db] * inv;
+            *reinterpret_cast<float4 *>(orow + db * 16) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+template <int HD>
+hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
+{
+    const int G = p.n_head / p.n_head_kv;
+    // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
+    int GB = 1;
+    while (GB * 2 <= G && GB * 2 <= 4) GB *= 2;
+    const int TQ = 64 / GB;
+    const int n_hsub = (G + GB - 1) / GB;
+    const int n_qtiles = (p.nt + TQ - 1) / TQ;
+    const dim3 grid((unsigned)n_qtiles, (unsigned)(p.n_head_kv * n_hsub)), block(256);
+    prefill_kernel<HD><<<grid, block, 0, s>>>(p, GB, TQ, n_qtiles, n_hsub);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
+{
+    if (p.nt <= 0) return hipSuccess;
+    switch (p.hd_kv) {
+    case 16: return launch_hd<16>(p, s);
+    case 32: return launch_hd<32>(p, s);
+    case 64: return launch_hd<64>(p, s);
+    case 128: return launch_hd<128>(p, s);
+    case 256: return launch_hd<256>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvc

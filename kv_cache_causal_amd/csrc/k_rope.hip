@@ -1,0 +1,138 @@
+// RoPE cos/sin table and K1: rotate q and k at positions given as data, store K/V rows.
+//
+// "11 · Attention, vec ops, and the KV cache":
+//   §2.3  RoPE: subspace i turns at speed freq_scale / base^(2i/hd); the angle is
+//         position x speed; each pair rotates as a 2-D vector.
+//   §3.2.2 the pair layouts: NEOX (i, i + hd/2) and interleaved (2i, 2i + 1).
+//   §3.2.3 the store: row t of this step goes to offset pos[t] x row width of its layer's
+//         region, a plain copy of the (rotated) k row and the v row.
+// "IV.2: Zero-copy KV cache": the append writes one row in place, no reallocation and no
+// copy of the rows already there.
+//
+// Reproducibility: the table holds, for every position p < capacity and pair i, the f32
+// nearest to cos/sin of the f32 angle f32(p) * speed_i, with speed_i the f32 nearest to
+// the exact expression.  Both are evaluated in f64 and rounded once to f32 (an f64
+// result sits within an f64 ulp or so of the exact value, far inside an f32 half-ulp
+// except at near-ties).  The rotation below is compiled with FMA contraction off, so each
+// product and each sum is rounded on its own and the result is the same bits as any
+// correctly rounded IEEE evaluation of the same formula.
+#include <hip/hip_runtime.h>
+
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
+
+__global__ void __launch_bounds__(256) rope_table_kernel(float2 *tab, int32_t rows, int32_t hd,
+                                                         float freq_base, float freq_scale)
+{
+    const int32_t half = hd >> 1;
+    const int64_t n = (int64_t)rows * half;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t p = (int32_t)(idx / half);
+        const int32_t i = (int32_t)(idx - (int64_t)p * half);
+        const double expo = (double)(2 * i) / (double)hd;
+        const float speed = (float)((double)freq_scale / pow((double)freq_base, expo));
+        const float theta = __fmul_rn((float)p, speed);
+        tab[idx] = make_float2((float)cos((double)theta), (float)sin((double)theta));
+    }
+}
+
+// Rotate one pair.  Contraction is off for this function: four rounded products, one
+// rounded difference and one rounded sum.
+__device__ __forceinline__ void rotate_pair(float x0, float x1, float2 cs_sn, float &y0,
+                                            float &y1)
+{
+#pragma clang fp contract(off)
+    const float a = x0 * cs_sn.x;
+    const float b = x1 * cs_sn.y;
+    const float c = x0 * cs_sn.y;
+    const float d = x1 * cs_sn.x;
+    y0 = a - b;
+    y1 = c + d;
+}
+
+// Rotate nh heads of width w (even) from src into dst (dst may equal src), using the
+// table row `tab` (w/2 entries).  Threads of the block stride over the nh * w/2 pairs,
+// so consecutive threads touch consecutive elements of a head.
+template <int STYLE>
+__device__ __forceinline__ void rotate_heads(const float *src, float *dst, int32_t nh, int32_t w,
+                                             const float2 *tab)
+{
+    const int32_t half = w >> 1;
+    const int32_t npairs = nh * half;
+    for (int32_t idx = threadIdx.x; idx < npairs; idx += blockDim.x) {
+        const int32_t h = idx / half;
+        const int32_t i = idx - h * half;
+        const int32_t i0 = STYLE == kNeox ? i : 2 * i;
+        const int32_t i1 = STYLE == kNeox ? i + half : 2 * i + 1;
+        const float *x = src + (int64_t)h * w;
+        float *y = dst + (int64_t)h * w;
+        float y0, y1;
+        rotate_pair(x[i0], x[i1], tab[i], y0, y1);
+        y[i0] = y0;
+        y[i1] = y1;
+    }
+}
+
+// One workgroup per token.  Reads: q row (if any), k row, v row, one table row per head
+// dim.  Writes: q row in place, one K row and one V row of the cache.
+template <int STYLE>
+__global__ void __launch_bounds__(256) append_kernel(AppendParams p)
+{
+    const int32_t t = blockIdx.x;
+    const int32_t pos = p.pos[t];
+    const int32_t seq = p.seq[t];
+    const int32_t nkt = p.n_head_kv * p.hd_kv;
+    const int64_t row = ((int64_t)seq * p.n_layer + p.layer) * p.region + (int64_t)pos * nkt;
+    const float *ksrc = p.k + (int64_t)t * nkt;
+    const float *vsrc = p.v + (int64_t)t * nkt;
+    float *kdst = p.kc + row;
+    float *vdst = p.vc + row;
+
+    if (STYLE != kNone) {
+        if (p.q) {
+            float *qt = p.q + (int64_t)t * p.n_head * p.hd;
+            rotate_heads<STYLE>(qt, qt, p.n_head, p.hd, p.tab_q + (int64_t)pos * (p.hd >> 1));
+        }
+        rotate_heads<STYLE>(ksrc, kdst, p.n_head_kv, p.hd_kv,
+                            p.tab_k + (int64_t)pos * (p.hd_kv >> 1));
+    } else {
+        const float4 *ks4 = reinterpret_cast<const float4 *>(ksrc);
+        float4 *kd4 = reinterpret_cast<float4 *>(kdst);
+        for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) kd4[i] = ks4[i];
+    }
+    // hd_kv is a multiple of 16, so rows are whole float4s and 16-byte aligned.
+    const float4 *vs4 = reinterpret_cast<const float4 *>(vsrc);
+    float4 *vd4 = reinterpret_cast<float4 *>(vdst);
+    for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) vd4[i] = vs4[i];
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
+                             float freq_scale, hipStream_t s)
+{
+    const int64_t n = (int64_t)rows * (hd >> 1);
+    const int64_t want = (n + 255) / 256;
+    const unsigned grid = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
+    rope_table_kernel<<<grid, 256, 0, s>>>(tab, rows, hd, freq_base, freq_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams &p, hipStream_t s)
+{
+    if (p.nt <= 0) return hipSuccess;
+    const dim3 grid((unsigned)p.nt), block(256);
+    switch (p.style) {
+    case kNeox: append_kernel<kNeox><<<grid, block, 0, s>>>(p); break;
+    case kInterleaved: append_kernel<kInterleaved><<<grid, block, 0, s>>>(p); break;
+    default: append_kernel<kNone><<<grid, block, 0, s>>>(p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,453 @@
+// The C ABI of kvc.h: handle, host validation, position staging, RoPE tables, launches.
+//
+// Per call: every argument is checked on the host (validate.cpp) before anything is
+// queued; host-side integer arrays (positions, sequence ids, chunk offsets) are copied
+// into a pinned staging ring and sent to the device with one async copy on the caller's
+// stream; then the kernels are queued on the same stream.  Nothing here waits for the
+// device except kv_alloc (zero fill) and kv_free.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_internal.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+kvc_status fail(kvc_status st, const std::string &msg)
+{
+    g_err = msg;
+    return st;
+}
+
+kvc_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(KVC_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define KVC_HIP(call)                                             \
+    do {                                                          \
+        hipError_t e_ = (call);                                   \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);         \
+    } while (0)
+
+struct RopeTable {
+    int32_t hd;
+    float base, fscale;
+    float2 *dev;
+};
+
+// Pinned host ring + device ring for the small integer arrays each call sends along.
+// A slot is reused only after the event recorded behind the kernels that read it has
+// completed, so the host never waits unless it runs a full ring ahead of the device.
+struct Staging {
+    int32_t *host = nullptr;
+    int32_t *dev = nullptr;
+    size_t cap = 0;   // ints
+    size_t head = 0;
+    uint64_t lap = 0;
+    struct Use {
+        size_t off, n;
+        uint64_t lap;
+        hipEvent_t ev;
+    };
+    std::deque<Use> inflight;
+    std::vector<hipEvent_t> pool;
+};
+
+}  // namespace
+
+struct kvc_cache {
+    kvc::Geometry g;
+    int device = 0;
+    float *K = nullptr, *V = nullptr;
+    int64_t region = 0;  // floats per (seq, layer) region
+    std::vector<int32_t> hw;
+    mutable Staging st;
+    mutable std::vector<RopeTable> tables;
+    mutable float *part = nullptr;  // split-K partials
+    mutable size_t part_cap = 0;    // floats
+};
+
+namespace {
+
+void staging_release(Staging &st)
+{
+    for (auto &u : st.inflight) {
+        hipEventSynchronize(u.ev);
+        hipEventDestroy(u.ev);
+    }
+    st.inflight.clear();
+    for (auto ev : st.pool) hipEventDestroy(ev);
+    st.pool.clear();
+    if (st.host) hipHostFree(st.host);
+    if (st.dev) hipFree(st.dev);
+    st.host = nullptr;
+    st.dev = nullptr;
+    st.cap = st.head = 0;
+}
+
+kvc_status staging_alloc(Staging &st, size_t ints)
+{
+    KVC_HIP(hipHostMalloc(reinterpret_cast<void **>(&st.host), ints * sizeof(int32_t),
+                          hipHostMallocDefault));
+    KVC_HIP(hipMalloc(reinterpret_cast<void **>(&st.dev), ints * sizeof(int32_t)));
+    st.cap = ints;
+    st.head = 0;
+    return KVC_OK;
+}
+
+// Copy `n` host ints into the ring and queue their upload on `s`.  Returns the device
+// address through *dev.  The caller must call staging_commit after queueing the kernels
+// that read it.
+kvc_status staging_push(Staging &st, const std::vector<int32_t> &data, hipStream_t s,
+                        const int32_t **dev)
+{
+    const size_t n = (data.size() + 63) & ~size_t(63);  // keep slots 256-byte aligned
+    if (n > st.cap) {
+        size_t cap = st.cap ? st.cap : 65536;
+        while (cap < n) cap *= 2;
+        staging_release(st);
+        kvc_status r = staging_alloc(st, cap);
+        if (r != KVC_OK) return r;
+    }
+    if (st.head + n > st.cap) {
+        st.head = 0;
+        st.lap++;
+    }
+    const size_t a = st.head, e = a + n;
+    while (!st.inflight.empty()) {
+        Staging::Use &u = st.inflight.front();
+        const bool stale = u.lap + 1 < st.lap;
+        const bool overlaps = u.lap < st.lap && u.off < e;
+        if (!stale && !overlaps) break;
+        KVC_HIP(hipEventSynchronize(u.ev));
+        st.pool.push_back(u.ev);
+        st.inflight.pop_front();
+    }
+    std::memcpy(st.host + a, data.data(), data.size() * sizeof(int32_t));
+    KVC_HIP(hipMemcpyAsync(st.dev + a, st.host + a, data.size() * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s));
+    st.head = e;
+    *dev = st.dev + a;
+    st.inflight.push_back(Staging::Use{a, n, st.lap, nullptr});
+    return KVC_OK;
+}
+
+kvc_status staging_commit(Staging &st, hipStream_t s)
+{
+    hipEvent_t ev;
+    if (!st.pool.empty()) {
+        ev = st.pool.back();
+        st.pool.pop_back();
+    } else {
+        KVC_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    }
+    KVC_HIP(hipEventRecord(ev, s));
+    st.inflight.back().ev = ev;
+    return KVC_OK;
+}
+
+// Drop the slot pushed last when its kernels could not be queued.
+void staging_abort(Staging &st)
+{
+    if (!st.inflight.empty() && st.inflight.back().ev == nullptr) st.inflight.pop_back();
+}
+
+kvc_status get_table(const kvc_cache *c, int32_t hd, float base, float fscale, hipStream_t s,
+                     const float2 **out)
+{
+    for (const RopeTable &t : c->tables) {
+        if (t.hd == hd && t.base == base && t.fscale == fscale) {
+            *out = t.dev;
+            return KVC_OK;
+        }
+    }
+    RopeTable t{hd, base, fscale, nullptr};
+    const size_t bytes = (size_t)c->g.capacity * (size_t)(hd / 2) * sizeof(float2);
+    if (hipMalloc(reinterpret_cast<void **>(&t.dev), bytes) != hipSuccess)
+        return fail(KVC_E_NOMEM, "RoPE table allocation failed");
+    hipError_t e = kvc::launch_rope_table(t.dev, c->g.capacity, hd, base, fscale, s);
+    if (e != hipSuccess) {
+        hipFree(t.dev);
+        return hip_fail(e, "rope table kernel");
+    }
+    c->tables.push_back(t);
+    *out = t.dev;
+    return KVC_OK;
+}
+
+float log2e_times(float scale) { return (float)((double)scale * 1.4426950408889634074); }
+
+int32_t env_split_rows()
+{
+    static const int32_t v = [] {
+        const char *e = std::getenv("KVC_SPLIT_ROWS");
+        return e ? std::max(0, std::atoi(e)) : 0;
+    }();
+    return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kv_last_error(void) { return g_err.c_str(); }
+
+kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
+                    int32_t hd_kv, int32_t capacity, void *stream)
+{
+    if (!out) return fail(KVC_E_ARG, "out is NULL");
+    *out = nullptr;
+    std::string msg;
+    kvc_status st = kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, msg);
+    if (st != KVC_OK) return fail(st, msg);
+
+    kvc_cache *c = new (std::nothrow) kvc_cache();
+    if (!c) return fail(KVC_E_NOMEM, "handle allocation failed");
+    c->g = kvc::Geometry{n_seq, n_layer, n_head_kv, hd_kv, capacity};
+    c->region = (int64_t)capacity * n_head_kv * hd_kv;
+    c->hw.assign((size_t)n_seq * n_layer, 0);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region * sizeof(float);
+
+    auto cleanup = [&](kvc_status code, const std::string &m) {
+        if (c->K) hipFree(c->K);
+        if (c->V) hipFree(c->V);
+        staging_release(c->st);
+        delete c;
+        return fail(code, m);
+    };
+    hipError_t e = hipGetDevice(&c->device);
+    if (e != hipSuccess) return cleanup(KVC_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (hipMalloc(reinterpret_cast<void **>(&c->K), bytes) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&c->V), bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return cleanup(KVC_E_NOMEM, "KV region allocation of 2 x " + std::to_string(bytes) +
+                                        " bytes failed");
+    }
+    if ((e = hipMemsetAsync(c->K, 0, bytes, s)) != hipSuccess ||
+        (e = hipMemsetAsync(c->V, 0, bytes, s)) != hipSuccess)
+        return cleanup(KVC_E_HIP, std::string("zero fill: ") + hipGetErrorString(e));
+    if (staging_alloc(c->st, 65536) != KVC_OK) return cleanup(KVC_E_NOMEM, "staging allocation failed");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess)
+        return cleanup(KVC_E_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    *out = c;
+    return KVC_OK;
+}
+
+kvc_status kv_free(kvc_cache *c)
+{
+    if (!c) return KVC_OK;
+    hipError_t e = hipDeviceSynchronize();
+    staging_release(c->st);
+    for (RopeTable &t : c->tables) hipFree(t.dev);
+    if (c->part) hipFree(c->part);
+    hipFree(c->K);
+    hipFree(c->V);
+    delete c;
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    return KVC_OK;
+}
+
+kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, float **k, float **v)
+{
+    if (!c || !k || !v) return fail(KVC_E_ARG, "NULL handle or output pointer");
+    if (seq < 0 || seq >= c->g.n_seq || layer < 0 || layer >= c->g.n_layer)
+        return fail(KVC_E_ARG, "seq/layer out of range");
+    const int64_t off = ((int64_t)seq * c->g.n_layer + layer) * c->region;
+    *k = c->K + off;
+    *v = c->V + off;
+    return KVC_OK;
+}
+
+kvc_status kv_seq_len(const kvc_cache *c, int32_t seq, int32_t layer, int32_t *len)
+{
+    if (!c || !len) return fail(KVC_E_ARG, "NULL handle or output pointer");
+    if (seq < 0 || seq >= c->g.n_seq || layer < 0 || layer >= c->g.n_layer)
+        return fail(KVC_E_ARG, "seq/layer out of range");
+    *len = c->hw[(size_t)seq * c->g.n_layer + layer];
+    return KVC_OK;
+}
+
+kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                          const int32_t *pos, float *q, int32_t n_head, int32_t hd,
+                          const float *k, const float *v, float freq_base, float freq_scale,
+                          kvc_rope_style style, void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_append(c->g, layer, nt, seq_ids, pos, q, n_head, hd, k, v,
+                                      freq_base, freq_scale, (int32_t)style, msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (nt == 0) return KVC_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    const float2 *tab_q = nullptr, *tab_k = nullptr;
+    if (style != KVC_ROPE_NONE) {
+        if ((st = get_table(c, c->g.hd_kv, freq_base, freq_scale, s, &tab_k)) != KVC_OK) return st;
+        if (q && (st = get_table(c, hd, freq_base, freq_scale, s, &tab_q)) != KVC_OK) return st;
+    }
+    std::vector<int32_t> ints((size_t)nt * 2);
+    std::memcpy(ints.data(), pos, sizeof(int32_t) * nt);
+    std::memcpy(ints.data() + nt, seq_ids, sizeof(int32_t) * nt);
+    const int32_t *dev = nullptr;
+    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+
+    kvc::AppendParams p{};
+    p.q = style == KVC_ROPE_NONE ? nullptr : q;
+    p.k = k;
+    p.v = v;
+    p.kc = c->K;
+    p.vc = c->V;
+    p.pos = dev;
+    p.seq = dev + nt;
+    p.tab_q = tab_q;
+    p.tab_k = tab_k;
+    p.region = c->region;
+    p.nt = nt;
+    p.n_head = n_head;
+    p.hd = hd;
+    p.n_head_kv = c->g.n_head_kv;
+    p.hd_kv = c->g.hd_kv;
+    p.n_layer = c->g.n_layer;
+    p.layer = layer;
+    p.style = (int32_t)style;
+    hipError_t e = kvc::launch_append(p, s);
+    if (e != hipSuccess) {
+        staging_abort(c->st);
+        return hip_fail(e, "append kernel");
+    }
+    if ((st = staging_commit(c->st, s)) != KVC_OK) return st;
+    for (int32_t t = 0; t < nt; t++) {
+        int32_t &w = c->hw[(size_t)seq_ids[t] * c->g.n_layer + layer];
+        w = std::max(w, pos[t] + 1);
+    }
+    return KVC_OK;
+}
+
+kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int32_t nt,
+                            const int32_t *pos, const float *q, int32_t n_head, int32_t hd,
+                            float scale, float *out, void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_prefill(c->g, seq, layer, nt, pos, q, n_head, hd, scale, out, msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (nt == 0) return KVC_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    std::vector<int32_t> ints(pos, pos + nt);
+    const int32_t *dev = nullptr;
+    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+    const int64_t off = ((int64_t)seq * c->g.n_layer + layer) * c->region;
+    kvc::PrefillParams p{};
+    p.q = q;
+    p.out = out;
+    p.kc = c->K + off;
+    p.vc = c->V + off;
+    p.pos = dev;
+    p.nt = nt;
+    p.n_head = n_head;
+    p.hd = hd;
+    p.n_head_kv = c->g.n_head_kv;
+    p.hd_kv = c->g.hd_kv;
+    p.capacity = c->g.capacity;
+    p.qscale = log2e_times(scale);
+    hipError_t e = kvc::launch_prefill(p, s);
+    if (e != hipSuccess) {
+        staging_abort(c->st);
+        return hip_fail(e, "prefill kernel");
+    }
+    return staging_commit(c->st, s);
+}
+
+kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                           const int32_t *seq_ids, const int32_t *pos, const float *q,
+                           int32_t n_head, int32_t hd, float scale, float *out, void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_decode(c->g, layer, n_seq, seq_ids, pos, q, n_head, hd, scale,
+                                      out, msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (n_seq == 0) return KVC_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    // Chunk size: aim for ~1024 workgroups over all kv heads (4 per CU), in whole block
+    // iterations; KVC_SPLIT_ROWS overrides the size (tuning only, never the result's
+    // meaning).
+    const int32_t br = kvc::decode_block_rows(c->g.hd_kv);
+    int64_t total_rows = 0;
+    for (int32_t b = 0; b < n_seq; b++) total_rows += (int64_t)pos[b] + 1;
+    int64_t rows = env_split_rows();
+    if (rows <= 0) {
+        const int64_t target = std::max<int64_t>(1, 1024 / c->g.n_head_kv);
+        rows = (total_rows + target - 1) / target;
+    }
+    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
+    std::vector<int32_t> ints((size_t)n_seq * 3 + 1);
+    int32_t *pp = ints.data(), *sp = pp + n_seq, *cb = sp + n_seq;
+    int64_t chunks = 0;
+    for (int32_t b = 0; b < n_seq; b++) {
+        pp[b] = pos[b];
+        sp[b] = seq_ids[b];
+        cb[b] = (int32_t)chunks;
+        chunks += ((int64_t)pos[b] + 1 + rows - 1) / rows;
+    }
+    cb[n_seq] = (int32_t)chunks;
+    if (chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
+
+    const size_t need = (size_t)chunks * n_head * (c->g.hd_kv + 4);
+    if (need > c->part_cap) {
+        if (c->part) {
+            KVC_HIP(hipStreamSynchronize(s));
+            hipFree(c->part);
+            c->part = nullptr;
+            c->part_cap = 0;
+        }
+        const size_t cap = std::max(need, c->part_cap * 2);
+        if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
+            return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
+        c->part_cap = cap;
+    }
+    const int32_t *dev = nullptr;
+    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+    kvc::DecodeParams p{};
+    p.q = q;
+    p.out = out;
+    p.part = c->part;
+    p.kc = c->K;
+    p.vc = c->V;
+    p.pos = dev;
+    p.seq = dev + n_seq;
+    p.cbase = dev + 2 * n_seq;
+    p.region = c->region;
+    p.n = n_seq;
+    p.n_head = n_head;
+    p.hd = hd;
+    p.n_head_kv = c->g.n_head_kv;
+    p.hd_kv = c->g.hd_kv;
+    p.n_layer = c->g.n_layer;
+    p.layer = layer;
+    p.rows_per_chunk = (int32_t)rows;
+    p.total_chunks = (int32_t)chunks;
+    p.qscale = log2e_times(scale);
+    hipError_t e = kvc::launch_decode(p, s);
+    if (e != hipSuccess) {
+        staging_abort(c->st);
+        return hip_fail(e, "decode kernels");
+    }
+    return staging_commit(c->st, s);
+}
+
+}  // extern "C"

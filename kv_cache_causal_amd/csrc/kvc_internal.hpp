@@ -1,0 +1,63 @@
+// Launch interface between the C ABI (kvc_api.cpp) and the gfx950 kernels.
+// Each launcher checks nothing itself: kvc_api.cpp validates every argument first and
+// hands over device pointers that the kernels' index arithmetic stays inside.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kvc {
+
+// Cache layout: K[n_seq][n_layer][capacity][n_head_kv * hd_kv] (V likewise); `region`
+// is capacity * n_head_kv * hd_kv floats.
+
+// ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------
+hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
+                             float freq_scale, hipStream_t s);
+
+// ---- K1: RoPE(q, k) + in-place K/V row store ------------------------------------------
+struct AppendParams {
+    float *q;               // [nt][n_head][hd] or nullptr
+    const float *k, *v;     // [nt][n_head_kv][hd_kv]
+    float *kc, *vc;         // cache bases
+    const int32_t *pos;     // device [nt]
+    const int32_t *seq;     // device [nt]
+    const float2 *tab_q;    // [capacity][hd/2] (nullptr if q is nullptr or style NONE)
+    const float2 *tab_k;    // [capacity][hd_kv/2] (nullptr for style NONE)
+    int64_t region;
+    int32_t nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style;
+};
+hipError_t launch_append(const AppendParams &p, hipStream_t s);
+
+// ---- K2 + K3: split-K decode and log-sum-exp combine -----------------------------------
+struct DecodeParams {
+    const float *q;          // [n][n_head][hd]
+    float *out;              // [n][n_head][hd_kv]
+    float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
+    const float *kc, *vc;    // cache bases
+    const int32_t *pos;      // device [n]
+    const int32_t *seq;      // device [n]
+    const int32_t *cbase;    // device [n + 1]: first chunk of entry b; cbase[n] = total
+    int64_t region;
+    int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer;
+    int32_t rows_per_chunk, total_chunks;
+    float qscale;            // scale * log2(e): scores are kept in base-2 units
+};
+// Rows per block iteration of the split-K kernel for a kv head dim (chunks should be a
+// multiple of it).
+int32_t decode_block_rows(int32_t hd_kv);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
+
+// ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
+struct PrefillParams {
+    const float *q;          // [nt][n_head][hd]
+    float *out;              // [nt][n_head][hd_kv]
+    const float *kc, *vc;    // this (seq, layer)'s K and V regions
+    const int32_t *pos;      // device [nt]
+    int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity;
+    float qscale;            // scale * log2(e)
+};
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
+
+}  // namespace kvc

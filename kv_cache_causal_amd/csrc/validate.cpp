@@ -1,0 +1,197 @@
+// Host-side argument checks (see validate.hpp).
+#include "validate.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+namespace kvc {
+namespace {
+
+std::string s(long long x) { return std::to_string(x); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The query-head checks shared by every call that takes q.
+kvc_status check_heads(const Geometry &g, int32_t n_head, int32_t hd, std::string &msg)
+{
+    if (n_head <= 0 || n_head % g.n_head_kv != 0) {
+        msg = "n_head " + s(n_head) + " is not a positive multiple of n_head_kv " + s(g.n_head_kv);
+        return KVC_E_ARG;
+    }
+    if (hd <= 0 || (hd & 1) || hd > KVC_MAX_HEAD_DIM) {
+        msg = "query head dim " + s(hd) + " must be even and in [2, " + s(KVC_MAX_HEAD_DIM) + "]";
+        return KVC_E_ARG;
+    }
+    if (hd < g.hd_kv) {
+        msg = "query head dim " + s(hd) + " < kv head dim " + s(g.hd_kv) +
+              ": a query head shorter than its key cannot be dotted against it";
+        return KVC_E_GEOMETRY;
+    }
+    return KVC_OK;
+}
+
+kvc_status check_positions(const Geometry &g, int32_t n, const int32_t *pos, std::string &msg)
+{
+    for (int32_t t = 0; t < n; t++) {
+        if (pos[t] < 0 || pos[t] >= g.capacity) {
+            msg = "position " + s(pos[t]) + " (entry " + s(t) + ") outside [0, capacity " +
+                  s(g.capacity) + ")";
+            return KVC_E_RANGE;
+        }
+    }
+    return KVC_OK;
+}
+
+kvc_status check_seq_ids(const Geometry &g, int32_t n, const int32_t *seq_ids, std::string &msg)
+{
+    for (int32_t t = 0; t < n; t++) {
+        if (seq_ids[t] < 0 || seq_ids[t] >= g.n_seq) {
+            msg = "sequence id " + s(seq_ids[t]) + " (entry " + s(t) + ") outside [0, " +
+                  s(g.n_seq) + ")";
+            return KVC_E_ARG;
+        }
+    }
+    return KVC_OK;
+}
+
+}  // namespace
+
+bool supported_kv_head_dim(int32_t hd_kv)
+{
+    return hd_kv == 16 || hd_kv == 32 || hd_kv == 64 || hd_kv == 128 || hd_kv == 256;
+}
+
+kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
+                       int32_t capacity, std::string &msg)
+{
+    if (n_seq <= 0 || n_layer <= 0 || n_head_kv <= 0) {
+        msg = "n_seq, n_layer and n_head_kv must be >= 1";
+        return KVC_E_ARG;
+    }
+    if (!supported_kv_head_dim(hd_kv)) {
+        msg = "kv head dim " + s(hd_kv) + " unsupported (16, 32, 64, 128 or 256)";
+        return KVC_E_ARG;
+    }
+    if (capacity <= 0 || capacity > KVC_MAX_CAPACITY) {
+        msg = "capacity " + s(capacity) + " outside [1, 2^24]";
+        return KVC_E_ARG;
+    }
+    // Row width and region sizes must fit the 64-bit offsets the kernels use.
+    const double bytes = 4.0 * n_seq * n_layer * (double)capacity * n_head_kv * hd_kv;
+    if (bytes > 9.0e15) {
+        msg = "cache of " + std::to_string(bytes) + " bytes is not addressable";
+        return KVC_E_ARG;
+    }
+    return KVC_OK;
+}
+
+kvc_status check_append(const Geometry &g, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                        const int32_t *pos, const void *q, int32_t n_head, int32_t hd,
+                        const void *k, const void *v, float freq_base, float freq_scale,
+                        int32_t style, std::string &msg)
+{
+    if (layer < 0 || layer >= g.n_layer) {
+        msg = "layer " + s(layer) + " outside [0, " + s(g.n_layer) + ")";
+        return KVC_E_ARG;
+    }
+    if (nt < 0) {
+        msg = "nt < 0";
+        return KVC_E_ARG;
+    }
+    if (nt == 0) return KVC_OK;
+    if (!seq_ids || !pos || !k || !v) {
+        msg = "seq_ids, pos, k and v must be non-NULL";
+        return KVC_E_ARG;
+    }
+    if (!aligned16(k) || !aligned16(v) || (q && !aligned16(q))) {
+        msg = "device tensors must be 16-byte aligned";
+        return KVC_E_ARG;
+    }
+    if (style != KVC_ROPE_NEOX && style != KVC_ROPE_INTERLEAVED && style != KVC_ROPE_NONE) {
+        msg = "unknown rope style " + s(style);
+        return KVC_E_ARG;
+    }
+    if (style != KVC_ROPE_NONE &&
+        (!(freq_base > 0.0f) || !std::isfinite(freq_base) || !(freq_scale > 0.0f) ||
+         !std::isfinite(freq_scale))) {
+        msg = "freq_base and freq_scale must be finite and > 0";
+        return KVC_E_ARG;
+    }
+    if (q) {
+        kvc_status st = check_heads(g, n_head, hd, msg);
+        if (st != KVC_OK) return st;
+    }
+    kvc_status st = check_seq_ids(g, nt, seq_ids, msg);
+    if (st != KVC_OK) return st;
+    st = check_positions(g, nt, pos, msg);
+    if (st != KVC_OK) return st;
+    // Two rows aimed at one (sequence, position) would race on the device.
+    std::vector<int64_t> keys((size_t)nt);
+    for (int32_t t = 0; t < nt; t++) keys[t] = ((int64_t)seq_ids[t] << 32) | (int64_t)pos[t];
+    std::sort(keys.begin(), keys.end());
+    for (size_t i = 1; i < keys.size(); i++) {
+        if (keys[i] == keys[i - 1]) {
+            msg = "sequence " + s(keys[i] >> 32) + " position " + s(keys[i] & 0xffffffff) +
+                  " appears twice in one append";
+            return KVC_E_DUP;
+        }
+    }
+    return KVC_OK;
+}
+
+kvc_status check_prefill(const Geometry &g, int32_t seq, int32_t layer, int32_t nt,
+                         const int32_t *pos, const void *q, int32_t n_head, int32_t hd,
+                         float scale, const void *out, std::string &msg)
+{
+    if (seq < 0 || seq >= g.n_seq || layer < 0 || layer >= g.n_layer) {
+        msg = "seq " + s(seq) + " / layer " + s(layer) + " out of range";
+        return KVC_E_ARG;
+    }
+    if (nt < 0) {
+        msg = "nt < 0";
+        return KVC_E_ARG;
+    }
+    if (nt == 0) return KVC_OK;
+    if (!pos || !q || !out || !std::isfinite(scale)) {
+        msg = "pos, q and out must be non-NULL and scale finite";
+        return KVC_E_ARG;
+    }
+    if (!aligned16(q) || !aligned16(out)) {
+        msg = "device tensors must be 16-byte aligned";
+        return KVC_E_ARG;
+    }
+    kvc_status st = check_heads(g, n_head, hd, msg);
+    if (st != KVC_OK) return st;
+    return check_positions(g, nt, pos, msg);
+}
+
+kvc_status check_decode(const Geometry &g, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
+                        const int32_t *pos, const void *q, int32_t n_head, int32_t hd,
+                        float scale, const void *out, std::string &msg)
+{
+    if (layer < 0 || layer >= g.n_layer) {
+        msg = "layer " + s(layer) + " outside [0, " + s(g.n_layer) + ")";
+        return KVC_E_ARG;
+    }
+    if (n_seq < 0) {
+        msg = "n_seq < 0";
+        return KVC_E_ARG;
+    }
+    if (n_seq == 0) return KVC_OK;
+    if (!seq_ids || !pos || !q || !out || !std::isfinite(scale)) {
+        msg = "seq_ids, pos, q and out must be non-NULL and scale finite";
+        return KVC_E_ARG;
+    }
+    if (!aligned16(q) || !aligned16(out)) {
+        msg = "device tensors must be 16-byte aligned";
+        return KVC_E_ARG;
+    }
+    kvc_status st = check_heads(g, n_head, hd, msg);
+    if (st != KVC_OK) return st;
+    st = check_seq_ids(g, n_seq, seq_ids, msg);
+    if (st != KVC_OK) return st;
+    return check_positions(g, n_seq, pos, msg);
+}
+
+}  // namespace kvc

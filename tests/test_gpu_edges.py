@@ -1,0 +1,179 @@
+"""GPU edge cases through the C ABI: every supported kv head dim, GQA group sizes that
+leave idle waves or need several passes, hd > hd_kv, single-row windows, positions out of
+order / repeated / at the end of the region, ragged tiles, the three RoPE styles, errors
+that must leave the cache untouched, and the no-copy/no-move contract."""
+import numpy as np
+import pytest
+
+import kv_cache_causal_amd as kvc
+from tests.gpu_util import Pair, assert_bitwise, assert_close, compare_cache, dev, host, say
+from tests.workloads import custom, custom_positions
+
+pytestmark = pytest.mark.gpu
+
+
+def build(seed, n_seq, n_head, n_head_kv, hd, hd_kv, capacity, rows, style=0, base=1e6):
+    """A cache pair with rows [0, rows) of sequence 0 (and 1 if present) written."""
+    p = Pair(n_seq, 1, n_head_kv, hd_kv, capacity)
+    for s in range(n_seq):
+        k = custom(seed * 10 + s, (rows, n_head_kv, hd_kv))
+        v = custom(seed * 10 + 5 + s, (rows, n_head_kv, hd_kv))
+        p.append(0, [s] * rows, np.arange(rows), None, n_head, hd, k, v, base, 1.0, style)
+    return p
+
+
+HEADS = [
+    # n_head, n_head_kv, hd, hd_kv
+    (2, 2, 16, 16),
+    (4, 1, 32, 32),
+    (6, 2, 64, 64),     # G = 3: one idle wave / lane of heads
+    (14, 2, 64, 64),    # G = 7
+    (16, 8, 128, 128),  # G = 2
+    (16, 1, 128, 128),  # G = 16: two decode passes, four prefill head subsets
+    (8, 4, 256, 256),
+    (4, 2, 48, 32),     # hd > hd_kv
+    (4, 2, 160, 128),   # hd > hd_kv, not a multiple of 4 only in the tail
+]
+
+
+@pytest.mark.parametrize("nh,nkv,hd,hdk", HEADS, ids=[f"h{a}kv{b}d{c}dk{d}" for a, b, c, d in HEADS])
+def test_decode_and_prefill_shapes(nh, nkv, hd, hdk):
+    say(f"shape n_head={nh} n_head_kv={nkv} hd={hd} hd_kv={hdk}")
+    cap, rows = 300, 300
+    p = build(1, 2, nh, nkv, hd, hdk, cap, rows)
+    # Decode: two sequences, long and short windows, one at the last row.
+    q = custom(2, (3, nh, hd))
+    seqs, pos = [0, 1, 0], [299, 0, 137]
+    got, want = p.decode(0, seqs, pos, dev(q), q, nh, hd, 0.31)
+    assert_close(got, want, "decode")
+    # A one-row window returns that V row exactly.
+    for h in range(nh):
+        assert_bitwise(got[1, h], p.o.v(1, 0)[0, (h // (nh // nkv)) * hdk:][:hdk], "pos 0 = v0")
+    # Prefill: 77 tokens (ragged tile), positions out of order with repeats.
+    nt = 77
+    q = custom(3, (nt, nh, hd))
+    pos = custom_positions(4, nt, 0, rows, unique=False)
+    got, want = p.prefill(0, 0, pos, dev(q), q, nh, hd, 0.29)
+    assert_close(got, want, "prefill")
+    p.close()
+
+
+@pytest.mark.parametrize("style", [0, 1, 2], ids=["neox", "interleaved", "none"])
+def test_rope_styles_and_hd_gt_hd_kv(style):
+    say(f"rope style {style}")
+    p = Pair(2, 3, 2, 32, 64)
+    nt = 40
+    q = custom(10, (nt, 4, 48))
+    k = custom(11, (nt, 2, 32))
+    v = custom(12, (nt, 2, 32))
+    seqs = np.array([0, 1] * (nt // 2), np.int32)
+    pos = np.concatenate([custom_positions(13, nt // 2, 0, 64), custom_positions(14, nt // 2, 0, 64)])
+    pos = pos.reshape(2, -1).T.reshape(-1)   # interleave the two sequences' positions
+    qd, qo = p.append(1, seqs, pos, q, 4, 48, k, v, 5e5, 0.5, style)
+    for s in range(2):
+        for layer in range(3):
+            compare_cache(p.g, p.o, s, layer, f"style {style}")
+    p.close()
+
+
+def test_positions_to_the_last_row_and_tiles_past_capacity():
+    say("capacity 100 (not a tile multiple), tokens at 98/99")
+    p = build(20, 1, 4, 2, 64, 64, 100, 100)
+    q = custom(21, (5, 4, 64))
+    pos = [99, 98, 0, 64, 63]
+    got, want = p.prefill(0, 0, pos, dev(q), q, 4, 64, 0.125)
+    assert_close(got, want, "prefill at the region's end")
+    got, want = p.decode(0, [0] * 5, pos, dev(q), q, 4, 64, 0.125)
+    assert_close(got, want, "decode at the region's end")
+    p.close()
+
+
+def test_unwritten_rows_read_as_zero():
+    """Rows inside a window that were never appended hold +0.0 and take part as zeros."""
+    say("unwritten rows")
+    p = Pair(1, 1, 2, 64, 256)
+    k = custom(30, (10, 2, 64))
+    p.append(0, [0] * 10, np.arange(0, 200, 20), None, 4, 64, k, k, 1e6, 1.0, 0)
+    q = custom(31, (3, 4, 64))
+    got, want = p.decode(0, [0, 0, 0], [199, 250, 5], dev(q), q, 4, 64, 0.125)
+    assert_close(got, want, "decode over gaps")
+    got, want = p.prefill(0, 0, [199, 250, 5], dev(q), q, 4, 64, 0.125)
+    assert_close(got, want, "prefill over gaps")
+    compare_cache(p.g, p.o, 0, 0, "gappy cache")
+    p.close()
+
+
+def test_errors_leave_everything_untouched():
+    say("error paths")
+    p = build(40, 2, 4, 2, 64, 64, 50, 20)
+    k = custom(41, (2, 2, 64))
+    q = custom(42, (2, 4, 64))
+    qd = dev(q)
+    kp0 = kvc.kv_view(p.g, 1, 0)
+    cases = [
+        (dict(seq=[0, 1], pos=[5, 50]), kvc.E_RANGE),
+        (dict(seq=[1, 1], pos=[7, 7]), kvc.E_DUP),
+        (dict(seq=[0, 2], pos=[1, 2]), kvc.E_ARG),
+        (dict(seq=[0, 1], pos=[1, 2], hd=32), kvc.E_GEOMETRY),
+    ]
+    for kw, code in cases:
+        hd = kw.get("hd", 64)
+        qq = qd if hd == 64 else dev(custom(43, (2, 4, hd)))
+        with pytest.raises(kvc.KvcError) as ei:
+            kvc.kv_append_rope(p.g, 0, kw["seq"], kw["pos"], qq, 4, hd, dev(k), dev(k), 1e6)
+        assert ei.value.status == code, (kw, ei.value)
+    assert_bitwise(host(qd), q, "q untouched by failed appends")
+    for s in range(2):
+        compare_cache(p.g, p.o, s, 0, "after failed appends")
+    import torch
+    out = torch.full((1, 4, 64), 7.0, device="cuda")
+    with pytest.raises(kvc.KvcError) as ei:
+        kvc.gqa_attn_decode(p.g, 0, [0], [50], qd[:1], 4, 64, 0.125, out)
+    assert ei.value.status == kvc.E_RANGE
+    with pytest.raises(kvc.KvcError) as ei:
+        kvc.gqa_attn_prefill(p.g, 0, 0, [3], dev(custom(44, (1, 4, 32))), 4, 32, 0.125, out)
+    assert ei.value.status == kvc.E_GEOMETRY
+    assert (host(out) == 7.0).all()
+    # Regions never move; a later good append still works.
+    assert kvc.kv_view(p.g, 1, 0) == kp0
+    p.append(0, [1], [49], q[:1], 4, 64, k[:1], k[:1])
+    compare_cache(p.g, p.o, 1, 0, "after recovery")
+    assert kvc.kv_view(p.g, 1, 0) == kp0
+    p.close()
+
+
+def test_empty_calls_are_noops():
+    say("nt = 0")
+    p = Pair(1, 1, 2, 16, 8)
+    kvc.kv_append_rope(p.g, 0, [], [], None, 0, 0, None, None, 1e6)
+    kvc.gqa_attn_prefill(p.g, 0, 0, [], None, 2, 16, 0.25, None)
+    kvc.gqa_attn_decode(p.g, 0, [], [], None, 2, 16, 0.25, None)
+    assert kvc.kv_seq_len(p.g, 0, 0) == 0
+    compare_cache(p.g, p.o, 0, 0, "untouched")
+    p.close()
+
+
+def test_overwrite_below_high_water_and_isolation():
+    """Rewriting an earlier position (a rollback) replaces exactly that row; other
+    sequences and layers never change."""
+    say("overwrite + isolation")
+    p = Pair(3, 2, 2, 32, 40)
+    for s in range(3):
+        k = custom(50 + s, (30, 2, 32))
+        p.append(1, [s] * 30, np.arange(30), None, 0, 0, k, k)
+    k = custom(60, (3, 2, 32))
+    p.append(1, [1, 1, 1], [3, 29, 10], custom(61, (3, 4, 32)), 4, 32, k, k)
+    for s in range(3):
+        for layer in range(2):
+            compare_cache(p.g, p.o, s, layer, "overwrite")
+    p.close()
+
+
+def test_long_window_many_chunks_matches_single_chunk_shape():
+    """A window split into many chunks (K3 merge) and a short one-chunk window."""
+    say("split-K long window")
+    p = build(70, 1, 16, 8, 128, 128, 9000, 9000)
+    q = custom(71, (2, 16, 128))
+    got, want = p.decode(0, [0, 0], [8999, 40], dev(q), q, 16, 128, 0.0883883461356163)
+    assert_close(got, want, "split-K")
+    p.close()

@@ -1,0 +1,137 @@
+"""GPU parity on the five workloads, at full size, through the C ABI.
+
+Each test drives the HIP library and the oracle with the same seeded inputs
+(tests/workloads.py) and compares: caches, rotated q and high-water marks bit for bit,
+attention outputs within the allclose bar of tests/gpu_util.py.  Where the oracle would
+take minutes (the 4,096-token prefill of the batch workload), it computes a sample of
+query rows one by one; the GPU computes all of them in the benchmark's launch
+configuration.
+"""
+import numpy as np
+import pytest
+
+from tests import workloads as W
+from tests.gpu_util import Pair, assert_close, compare_cache, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def fill(pair, w, seq, layer, n_rows, chunk=4096):
+    """Pre-fill rows [0, n_rows) of (seq, layer) on both sides (store only, q = None)."""
+    for ci, r0 in enumerate(range(0, n_rows, chunk)):
+        r1 = min(n_rows, r0 + chunk)
+        k, v = W.fill_rows(w, seq, layer, ci, r1 - r0)
+        k = k.reshape(r1 - r0, w.n_head_kv, w.hd_kv)
+        v = v.reshape(r1 - r0, w.n_head_kv, w.hd_kv)
+        pair.append(layer, [seq] * (r1 - r0), np.arange(r0, r1), None, 0, 0, k, v, w.base,
+                    w.freq_scale, w.style)
+
+
+def test_c1_tiny():
+    w = W.C1
+    say(f"C1 {w.name}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    nt = w.extra["prefill"]
+    pos = np.arange(nt, dtype=np.int32)
+    q, k, v = W.prefill_qkv(w, nt, 0)
+    qd, qo = p.append(0, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+    compare_cache(p.g, p.o, 0, 0, "C1 prefill")
+    got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale)
+    assert_close(got, want, "C1 prefill out")
+    for step in range(w.extra["decode_steps"]):
+        ps = [nt + step]
+        q, k, v = W.decode_qkv(w, 1, step, 0)
+        qd, qo = p.append(0, [0], ps, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+        got, want = p.decode(0, [0], ps, qd, qo, w.n_head, w.hd, w.scale)
+        assert_close(got, want, f"C1 decode step {step}")
+    compare_cache(p.g, p.o, 0, 0, "C1 after decode")
+    p.close()
+
+
+def test_c2_qwen25_layer():
+    w = W.C2
+    say(f"C2 {w.name}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    n_past = w.extra["n_past"]
+    fill(p, w, 0, 0, n_past)
+    q, k, v = W.decode_qkv(w, 1, 0, 0)
+    qd, qo = p.append(0, [0], [n_past], q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+    compare_cache(p.g, p.o, 0, 0, "C2")
+    got, want = p.decode(0, [0], [n_past], qd, qo, w.n_head, w.hd, w.scale)
+    assert_close(got, want, "C2 decode")
+    p.close()
+
+
+def test_c3_qwen3_stack():
+    w = W.C3
+    say(f"C3 {w.name}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    nt = w.extra["prefill"]
+    pos = np.arange(nt, dtype=np.int32)
+    worst = 0.0
+    for layer in range(w.n_layer):
+        q, k, v = W.prefill_qkv(w, nt, layer)
+        qd, qo = p.append(layer, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale,
+                          w.style)
+        got, want = p.prefill(0, layer, pos, qd, qo, w.n_head, w.hd, w.scale)
+        assert_close(got, want, f"C3 prefill layer {layer}")
+    for step in range(w.extra["decode_steps"]):
+        ps = [nt + step]
+        for layer in range(w.n_layer):
+            q, k, v = W.decode_qkv(w, 1, step, layer)
+            qd, qo = p.append(layer, [0], ps, q, w.n_head, w.hd, k, v, w.base, w.freq_scale,
+                              w.style)
+            got, want = p.decode(layer, [0], ps, qd, qo, w.n_head, w.hd, w.scale)
+            from tests.gpu_util import ATOL, RTOL
+            err = np.abs(got.astype(np.float64) - want)
+            assert (err <= ATOL + RTOL * np.abs(want)).all(), (step, layer, err.max())
+            worst = max(worst, float(err.max()))
+    say(f"  C3 decode 64 steps x 28 layers: max-abs {worst:.3e}")
+    for layer in range(w.n_layer):
+        compare_cache(p.g, p.o, 0, layer, "C3")
+    p.close()
+
+
+def test_c4_long_context():
+    w = W.C4
+    say(f"C4 {w.name}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    n_past = w.extra["n_past"]
+    fill(p, w, 0, 0, n_past, w.extra["fill_chunk"])
+    q, k, v = W.decode_qkv(w, 1, 0, 0)
+    qd, qo = p.append(0, [0], [n_past], q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+    compare_cache(p.g, p.o, 0, 0, "C4")
+    got, want = p.decode(0, [0], [n_past], qd, qo, w.n_head, w.hd, w.scale)
+    assert_close(got, want, "C4 decode")
+    p.close()
+
+
+def test_c5_batch():
+    w = W.C5
+    say(f"C5 {w.name}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    n_past = W.c5_n_past(w)
+    say(f"  n_past {n_past.tolist()}")
+    for s in range(w.n_seq):
+        fill(p, w, s, 0, int(n_past[s]), w.extra["fill_chunk"])
+    # Continuation prefill of 4096 tokens on sequence 0.
+    nt = w.extra["prefill"]
+    pos = np.arange(n_past[0], n_past[0] + nt, dtype=np.int32)
+    q, k, v = W.prefill_qkv(w, nt, 0, 0)
+    qd, qo = p.append(0, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, nt - 33, nt - 1],
+                                       rng.integers(0, nt, 56)]))
+    got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale, sample=sample)
+    assert_close(got, want, f"C5 prefill ({len(sample)} sampled tokens)")
+    # One decode step for all 32 sequences.
+    lens = n_past.copy()
+    lens[0] += nt
+    q, k, v = W.decode_qkv(w, w.n_seq, 0, 0)
+    seqs = np.arange(w.n_seq, dtype=np.int32)
+    qd, qo = p.append(0, seqs, lens, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+    got, want = p.decode(0, seqs, lens, qd, qo, w.n_head, w.hd, w.scale)
+    assert_close(got, want, "C5 batched decode")
+    for s in range(w.n_seq):
+        compare_cache(p.g, p.o, s, 0, "C5")
+    p.close()
