@@ -1,0 +1,232 @@
+"""Benchmark of the whole hot path on one MI355X.
+
+A step is one pass of every stage over the batch workload (Qwen3-0.6B-shaped, 32
+sequences with ragged cached lengths drawn uniformly from [128, 8192]):
+  1. kv_append_rope  RoPE + in-place append of a 4,096-token continuation on sequence 0
+  2. gqa_attn_prefill causal attention of those 4,096 tokens (fp32 MFMA)
+  3. kv_append_rope  RoPE + append of one token for each of the 32 sequences
+  4. gqa_attn_decode split-K decode attention for the 32 sequences (+ combine)
+Inputs are resident in HBM before the timed region; the timed region is K steps,
+bracketed by device synchronisation.  HIP events on the library's stream time each
+stage.
+
+Reported:
+  value          decode attention KV GB/s: algorithmic K+V bytes of the 32 windows
+                 (sum_b (pos_b + 1) * 2 * n_head_kv * hd_kv * 4) / decode-attention time
+  prefill_tflops algorithmic prefill FLOPs (4 * n_head * hd_kv * sum_t (pos_t + 1)) /
+                 prefill-attention time
+  roofline       the dominant kernel (prefill, MFMA-bound) against the fp32 matrix peak;
+  roofline_decode the decode kernels against HBM bandwidth
+  cpu_baseline   the plain C oracle on the host cores, on a bounded sample
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn KV GB/s (% HBM peak) and prefill attn TFLOP/s, Qwen3-0.6B shape"
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_causal_amd as kvc
+    from tests import workloads as W
+
+    w = W.C5
+    nt = w.extra["prefill"]
+    n_past = W.c5_n_past(w)
+    pre_pos = np.arange(n_past[0], n_past[0] + nt, dtype=np.int32)
+    lens = n_past.copy()
+    lens[0] += nt
+    seqs = np.arange(w.n_seq, dtype=np.int32)
+    kv_bytes = int((lens.astype(np.int64) + 1).sum()) * 2 * w.n_head_kv * w.hd_kv * 4
+    pre_flops = 4 * w.n_head * w.hd_kv * int((pre_pos.astype(np.int64) + 1).sum())
+
+    torch.cuda.init()
+    kvc.lib()
+    dev = torch.device("cuda:0")
+    log(f"bench: workload {w.name}; filling {int(n_past.sum())} cached rows")
+    t0 = time.time()
+    cache = kvc.kv_alloc(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    orc_cache = None
+    if not args.no_cpu_baseline:
+        from oracle import OracleCache
+        orc_cache = OracleCache(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    chunk = w.extra["fill_chunk"]
+    for s in range(w.n_seq):
+        for ci, r0 in enumerate(range(0, int(n_past[s]), chunk)):
+            r1 = min(int(n_past[s]), r0 + chunk)
+            k, v = W.fill_rows(w, s, 0, ci, r1 - r0)
+            k = k.reshape(r1 - r0, w.n_head_kv, w.hd_kv)
+            v = v.reshape(r1 - r0, w.n_head_kv, w.hd_kv)
+            rows = np.arange(r0, r1, dtype=np.int32)
+            kvc.kv_append_rope(cache, 0, np.full(r1 - r0, s, np.int32), rows, None, 0, 0,
+                               torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                               w.base, w.freq_scale, w.style)
+            if orc_cache is not None:
+                orc_cache.append_rope(0, np.full(r1 - r0, s, np.int32), rows, None, 0, 0, k, v,
+                                      w.base, w.freq_scale, w.style)
+    qp, kp, vp = (torch.from_numpy(a).to(dev) for a in W.prefill_qkv(w, nt, 0, 0))
+    qd, kd, vd = (torch.from_numpy(a).to(dev) for a in W.decode_qkv(w, w.n_seq, 0, 0))
+    out_pre = torch.empty((nt, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
+    out_dec = torch.empty((w.n_seq, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"bench: setup {time.time() - t0:.1f}s; n_past[0] {n_past[0]}, "
+        f"prefill {pre_flops / 1e9:.1f} GFLOP, decode {kv_bytes / 1e9:.3f} GB KV")
+
+    nsteps = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nsteps)]
+
+    def step(i):
+        e = ev[i]
+        e[0].record()
+        kvc.kv_append_rope(cache, 0, np.zeros(nt, np.int32), pre_pos, qp, w.n_head, w.hd, kp, vp,
+                           w.base, w.freq_scale, w.style)
+        e[1].record()
+        kvc.gqa_attn_prefill(cache, 0, 0, pre_pos, qp, w.n_head, w.hd, w.scale, out_pre)
+        e[2].record()
+        kvc.kv_append_rope(cache, 0, seqs, lens, qd, w.n_head, w.hd, kd, vd, w.base,
+                           w.freq_scale, w.style)
+        e[3].record()
+        kvc.gqa_attn_decode(cache, 0, seqs, lens, qd, w.n_head, w.hd, w.scale, out_dec)
+        e[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done; timing {args.steps}")
+    t_start = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    timed = ev[args.warmup:]
+    ms = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in timed])  # noqa: E731
+    t_app_pre, t_pre, t_app_dec, t_dec = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    t_step = ms(0, 4)
+    ms_per_step = wall * 1e3 / args.steps
+    dec_gbs = kv_bytes / (t_dec.mean() * 1e-3) / 1e9
+    pre_tflops = pre_flops / (t_pre.mean() * 1e-3) / 1e12
+    app_bytes = nt * (2 * w.n_head * w.hd + 4 * w.n_head_kv * w.hd_kv) * 4
+    log(f"bench: step {ms_per_step:.3f} ms (events {t_step.mean():.3f}); append+rope(4096) "
+        f"{t_app_pre.mean() * 1e3:.1f} us, prefill {t_pre.mean():.3f} ms, append(32) "
+        f"{t_app_dec.mean() * 1e3:.1f} us, decode {t_dec.mean() * 1e3:.1f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v and cache rows)",
+        "config": {
+            "workload": "qwen3-0.6b-batch: 32 sequences, 16 q heads / 8 kv heads, head dim 128, "
+                        "ragged n_past U[128,8192]; 4096-token continuation prefill on seq 0 + "
+                        "one decode step for all 32",
+            "n_seq": int(w.n_seq), "n_head": w.n_head, "n_head_kv": w.n_head_kv,
+            "hd": w.hd, "hd_kv": w.hd_kv, "capacity": w.capacity,
+            "n_past_seq0": int(n_past[0]), "prefill_tokens": nt,
+            "decode_window_rows": int((lens.astype(np.int64) + 1).sum()),
+        },
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "prefill_tflops": round(pre_tflops, 3),
+        "prefill_mfma_frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+        "stage_us": {
+            "append_rope_4096": round(float(t_app_pre.mean()) * 1e3, 2),
+            "prefill_attn": round(float(t_pre.mean()) * 1e3, 2),
+            "append_rope_32": round(float(t_app_dec.mean()) * 1e3, 2),
+            "decode_attn": round(float(t_dec.mean()) * 1e3, 2),
+        },
+        "append_gbs": round(app_bytes / (t_app_pre.mean() * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "prefill_kernel<128> (gqa_attn_prefill)",
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 3),
+            "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": pre_flops,
+            "avg_launch_us": round(float(t_pre.mean()) * 1e3, 2),
+        },
+        "roofline_decode": {
+            "kernel": "decode_split_kernel<128,2> + decode_combine_kernel<128> (gqa_attn_decode)",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(float(t_dec.mean()) * 1e3, 2),
+        },
+    }
+
+    if orc_cache is not None:
+        result["cpu_baseline"] = cpu_baseline(orc_cache, w, seqs, lens, kv_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(orc_cache, w, seqs, lens, kv_bytes, seconds):
+    """The oracle, as it stands, on the host cores: the full 32-sequence decode attention
+    (same windows as the GPU step), repeated until `seconds` of wall time have passed."""
+    from tests import workloads as W
+    q, _, _ = W.decode_qkv(w, w.n_seq, 0, 0)
+    threads = orc_cache.o.max_threads()
+    log(f"bench: oracle baseline on {threads} threads (about {seconds:.0f}s)")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        st, _ = orc_cache.attn_decode(0, seqs, lens, q, w.n_head, w.hd, w.scale)
+        assert st == 0
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(kv_bytes * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"decode attention of all 32 sequences ({kv_bytes / 1e9:.3f} GB of K/V per "
+                  f"pass), {reps} passes in {el:.1f}s; the 4096-token prefill is not sampled",
+    }
+
+
+if __name__ == "__main__":
+    main()
