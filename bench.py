@@ -51,6 +51,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy before timing, so that "
+                         "HBM counters (FETCH_SIZE / WRITE_SIZE) can be calibrated against "
+                         "a kernel of known traffic in the same profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -103,6 +107,14 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: setup {time.time() - t0:.1f}s; n_past[0] {n_past[0]}, "
         f"prefill {pre_flops / 1e9:.1f} GFLOP, decode {kv_bytes / 1e9:.3f} GB KV")
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copy probe: 1 GiB read + 1 GiB written by one copy kernel")
+        del src, dst
 
     nsteps = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nsteps)]

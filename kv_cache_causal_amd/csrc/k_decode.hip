@@ -1,4 +1,4 @@
-// K2 + K3: decode attention over long KV windows, split along the KV axis.
+// K2 + K3: decode attention over long KV windows, split along the KV axis, then merged.
 //
 // "11 · Attention, vec ops, and the KV cache":
 //   §2.1   out = sum_s softmax_s(q . k_s * scale) v_s over the window s in [0, pos].
@@ -11,19 +11,28 @@
 // used G = n_head / n_head_kv times, so it is bound by HBM bandwidth (G/2 flop per byte).
 // Design for gfx950:
 //   * Workgroup = one (batch entry, kv head, chunk of rows); 4 wave64s.  Chunks are sized
-//     on the host so the grid holds ~4 workgroups per CU.
-//   * A row slice (hd_kv floats of one kv head) is read by a group of LPR = hd_kv/8 lanes,
-//     each lane holding 8 dims as two float4 loads; one load instruction across the wave
-//     covers 64/LPR rows, whole 128-byte lines.
+//     on the host so the grid fills the chip several times over; the workgroups of one
+//     chunk's kv heads are adjacent in dispatch order (DRAM page locality).
+//   * A row slice (hd_kv floats of one kv head) is read by a group of LPR lanes, each
+//     holding 8 dims as two float4 loads (4 dims for groups of 3+ heads, to save
+//     registers); one load instruction across the wave
+//     covers 64/LPR rows, whole 128-byte lines.  Two register sets of 4 rows per lane
+//     group alternate, so one set's loads are in flight while the other is reduced.
 //   * The query vectors of every head of the kv group (up to 8 per pass) stay in
 //     registers, so each K/V element loaded from HBM is used for all of them in-register:
 //     the group's sharing costs no LDS traffic.
-//   * Dot products reduce over the LPR lanes of a row with xor shuffles; each lane group
-//     keeps its own running max / sum / accumulator (online softmax, base-2 exponent),
-//     and the 64/LPR groups of a wave and the 4 waves of the block are merged once at the
-//     end (shuffles, then LDS).  The merged (m, l, acc) of the chunk goes to a partial.
-//   * K3 merges the partials of each (entry, head) by log-sum-exp: out = sum_c 2^(m_c-M)
-//     acc_c / sum_c 2^(m_c-M) l_c.
+//   * Dot products reduce over the LPR lanes of a row with DPP row operations (no LDS);
+//     each lane group keeps its own running max / sum / accumulator (online softmax,
+//     base-2 exponent), and the lane groups of a wave and the 4 waves of the block are
+//     merged once at the end (shuffles, then LDS).
+//   * A window that fits one chunk is finished in place.  Otherwise each chunk writes its
+//     (m, l, acc) partial and K3 merges them by log-sum-exp:
+//     out = sum_c 2^(m_c-M) acc_c / sum_c 2^(m_c-M) l_c.  The merge is a separate kernel
+//     on purpose: a device-scope fence inside K2 (to let the last chunk merge) compiles
+//     on gfx950 to a full write-back and invalidate of the XCD's L2, which measured far
+//     slower than one extra launch.
+//   * The batch's positions, sequence ids and chunk offsets travel in the kernel
+//     arguments (up to 64 entries per launch), so a decode needs no host-to-device copy.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -34,10 +43,35 @@ namespace kvc {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kDimsPerLane = 8;   // two float4 per lane per row
-constexpr int kUnroll = 4;        // rows per lane group per iteration (loads in flight)
+constexpr int kUnroll = 4;        // rows per lane group per step (two steps in flight)
+
+// Dims of a row slice each lane holds: 8 (two float4) for kv groups of up to 2 query
+// heads, 4 (one float4) for larger groups, whose per-head registers would otherwise
+// crowd out the load buffers.
+template <int GP>
+constexpr int dims_per_lane() { return GP <= 2 ? 8 : 4; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of W lanes; every lane of a group gets the same bits (each step
+// adds a pair in both orders, which IEEE addition makes identical).
+template <int W>
+__device__ __forceinline__ float group_sum(float x)
+{
+    if constexpr (W >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (W >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (W >= 8) x += dpp<0x141>(x);  // row_half_mirror: i <-> 7 - i
+    if constexpr (W >= 16) x += dpp<0x140>(x); // row_mirror: i <-> 15 - i
+    if constexpr (W >= 32) x += __shfl_xor(x, 16);
+    if constexpr (W >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
 
 // Merge (m2, l2) into (m, l) in base-2 units; returns the scale factors for acc.
 __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2, float &a,
@@ -54,6 +88,7 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
 template <int HD, int GP>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
 {
+    constexpr int kDimsPerLane = dims_per_lane<GP>();
     constexpr int LPR = HD / kDimsPerLane;   // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave per unrolled step
     constexpr int NF4 = kDimsPerLane / 4;
@@ -63,17 +98,21 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const int wave = threadIdx.x >> 6;
     const int li = lane % LPR;
     const int rg = lane / LPR;
-    const int hk = blockIdx.y;
-    const int cg = blockIdx.x;
+    // Linear grid, kv head fastest: the n_head_kv workgroups of one chunk are dispatched
+    // together and read the slices of the same rows at about the same time, so each row
+    // (n_head_kv * hd_kv floats, contiguous) is fetched while its DRAM page is open.
+    const int hk = blockIdx.x % p.n_head_kv;
+    const int cg = blockIdx.x / p.n_head_kv;
     const int G = p.n_head / p.n_head_kv;
 
-    // Batch entry owning this chunk: cbase[b] <= cg < cbase[b + 1].
+    // Batch entry owning this chunk: cbase[b] <= cg < cbase[b + 1] (kernel arguments).
     int lo = 0, hi = p.n;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (p.cbase[mid] <= cg) lo = mid; else hi = mid;
     }
     const int b = lo;
+    const int nchunks = p.cbase[b + 1] - p.cbase[b];
     const int vl = p.pos[b] + 1;
     const int r0 = (cg - p.cbase[b]) * p.rows_per_chunk;
     const int r1 = min(r0 + p.rows_per_chunk, vl);
@@ -106,25 +145,34 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         for (int d = 0; d < kDimsPerLane; d++) acc[g][d] = 0.0f;
     }
 
+    // Rows are consumed in steps of BR per workgroup; two register sets alternate so the
+    // loads of step i+1 are in flight while step i is reduced.
     constexpr int BR = kWaves * RPW * kUnroll;
-    for (int rb = r0; rb < r1; rb += BR) {
-        float4 kf[kUnroll][NF4], vf[kUnroll][NF4];
-        bool valid[kUnroll];
+    const int nsteps = (r1 - r0 + BR - 1) / BR;
+    float4 kA[kUnroll][NF4], vA[kUnroll][NF4], kB[kUnroll][NF4], vB[kUnroll][NF4];
+
+    auto load = [&](float4 (&kf)[kUnroll][NF4], float4 (&vf)[kUnroll][NF4], int step) {
+        const int rb = r0 + step * BR;
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            const int row = rb + (u * kWaves + wave) * RPW + rg;
-            valid[u] = row < r1;
-            const float *kr = K + (int64_t)(valid[u] ? row : r0) * nkt + li * 4;
-            const float *vr = V + (int64_t)(valid[u] ? row : r0) * nkt + li * 4;
+            int row = rb + (u * kWaves + wave) * RPW + rg;
+            row = row < r1 ? row : r0;  // rows past the chunk re-read row r0 and are masked
+            const float *kr = K + (int64_t)row * nkt + li * 4;
+            const float *vr = V + (int64_t)row * nkt + li * 4;
 #pragma unroll
             for (int c = 0; c < NF4; c++) {
                 kf[u][c] = *reinterpret_cast<const float4 *>(kr + c * 4 * LPR);
                 vf[u][c] = *reinterpret_cast<const float4 *>(vr + c * 4 * LPR);
             }
         }
+    };
+    auto consume = [&](const float4 (&kf)[kUnroll][NF4], const float4 (&vf)[kUnroll][NF4],
+                       int step) {
+        const int rb = r0 + step * BR;
         float sc[kUnroll][GP];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
+            const bool valid = rb + (u * kWaves + wave) * RPW + rg < r1;
 #pragma unroll
             for (int g = 0; g < GP; g++) {
                 float s = 0.0f;
@@ -135,9 +183,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
                     s += qf[g][c * 4 + 2] * kf[u][c].z;
                     s += qf[g][c * 4 + 3] * kf[u][c].w;
                 }
-#pragma unroll
-                for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
-                sc[u][g] = valid[u] ? s : -INFINITY;
+                s = group_sum<LPR>(s);
+                sc[u][g] = valid ? s : -INFINITY;
             }
         }
 #pragma unroll
@@ -165,6 +212,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             }
             m[g] = mn;
         }
+    };
+
+    load(kA, vA, 0);
+    for (int st = 0; st < nsteps; st += 2) {
+        if (st + 1 < nsteps) load(kB, vB, st + 1);
+        consume(kA, vA, st);
+        if (st + 1 >= nsteps) break;
+        if (st + 2 < nsteps) load(kA, vA, st + 2);
+        consume(kB, vB, st + 1);
     }
 
     // Merge the row groups of the wave (lanes that share li).
@@ -184,7 +240,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         }
     }
 
-    // Merge the waves through LDS and write the chunk's partial.
+    // Merge the waves through LDS.
     __shared__ float sm[kWaves][GP][HD + 2];
     if (rg == 0) {
 #pragma unroll
@@ -200,10 +256,12 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < GP * HD; idx += blockDim.x) {
+
+    const int ngp = min(GP, G - g0);   // heads of this pass that exist
+    float *out_b = p.out + (int64_t)b * p.n_head * HD;
+    for (int idx = threadIdx.x; idx < ngp * HD; idx += blockDim.x) {
         const int g = idx / HD;
         const int d = idx - g * HD;
-        if (g0 + g >= G) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm[w][g][0]);
@@ -216,33 +274,91 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             A += f * sm[w][g][2 + d];
         }
         const int h = hk * G + g0 + g;
-        float *rec = p.part + ((int64_t)cg * p.n_head + h) * (HD + 4);
-        if (d == 0) {
-            rec[0] = M;
-            rec[1] = L;
+        if (nchunks == 1) {
+            out_b[(int64_t)h * HD + d] = A / L;
+        } else {
+            float *rec = p.part + ((int64_t)cg * p.n_head + h) * (HD + 4);
+            if (d == 0) {
+                rec[0] = M;
+                rec[1] = L;
+            }
+            rec[4 + d] = A;
         }
-        rec[4 + d] = A;
     }
 }
 
-// One workgroup per (batch entry, query head); thread d owns output dim d.
+// K3: one workgroup per (batch entry, query head) with more than one chunk.  Pass 1
+// finds M = max_c m_c and L = sum_c 2^(m_c - M) l_c with the chunks spread over the
+// threads; pass 2 gives each thread one output dim and a slice of the chunks (loads of
+// different chunks are independent, so they overlap), then sums the slices in LDS.
 template <int HD>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
 {
+    constexpr int SLICES = 256 / HD;   // chunk slices per output dim
+    __shared__ float red[256];
+    __shared__ float s_M, s_L;
     const int b = blockIdx.x;
     const int h = blockIdx.y;
     const int c0 = p.cbase[b], c1 = p.cbase[b + 1];
-    for (int d = threadIdx.x; d < HD; d += blockDim.x) {
-        float M = -INFINITY;
-        for (int c = c0; c < c1; c++) M = fmaxf(M, p.part[((int64_t)c * p.n_head + h) * (HD + 4)]);
-        float L = 0.0f, A = 0.0f;
-        for (int c = c0; c < c1; c++) {
-            const float *rec = p.part + ((int64_t)c * p.n_head + h) * (HD + 4);
-            const float f = fast_exp2(rec[0] - M);
-            L += f * rec[1];
-            A += f * rec[4 + d];
+    if (c1 - c0 <= 1) return;  // finished in place by the split kernel
+    const int tid = threadIdx.x;
+    const float *base = p.part + (int64_t)h * (HD + 4);
+    const int64_t cstride = (int64_t)p.n_head * (HD + 4);
+
+    float mx = -INFINITY;
+    for (int c = c0 + tid; c < c1; c += 256) mx = fmaxf(mx, base[(int64_t)c * cstride]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
+    }
+    if (tid == 0) s_M = red[0];
+    __syncthreads();
+    const float M = s_M;
+    float ls = 0.0f;
+    for (int c = c0 + tid; c < c1; c += 256) {
+        const float *rec = base + (int64_t)c * cstride;
+        ls += fast_exp2(rec[0] - M) * rec[1];
+    }
+    red[tid] = ls;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) s_L = red[0];
+    __syncthreads();
+    const float L = s_L;
+    __syncthreads();
+
+    // Eight independent chunks per trip keep eight loads in flight per thread.
+    const int d = tid % HD;
+    const int slice = tid / HD;
+    float a = 0.0f;
+    int c = c0 + slice;
+    for (; c + 7 * SLICES < c1; c += 8 * SLICES) {
+        float mm[8], vv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float *rec = base + (int64_t)(c + j * SLICES) * cstride;
+            mm[j] = rec[0];
+            vv[j] = rec[4 + d];
         }
-        p.out[((int64_t)b * p.n_head + h) * HD + d] = A / L;
+#pragma unroll
+        for (int j = 0; j < 8; j++) a += fast_exp2(mm[j] - M) * vv[j];
+    }
+    for (; c < c1; c += SLICES) {
+        const float *rec = base + (int64_t)c * cstride;
+        a += fast_exp2(rec[0] - M) * rec[4 + d];
+    }
+    red[tid] = a;
+    __syncthreads();
+    if (tid < HD) {
+        float t = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < SLICES; sl++) t += red[sl * HD + tid];
+        p.out[((int64_t)b * p.n_head + h) * HD + tid] = t / L;
     }
 }
 
@@ -250,7 +366,7 @@ template <int HD>
 hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 {
     const int G = p.n_head / p.n_head_kv;
-    const dim3 grid((unsigned)p.total_chunks, (unsigned)p.n_head_kv), block(256);
+    const dim3 grid((unsigned)p.total_chunks * (unsigned)p.n_head_kv), block(256);
     for (int g0 = 0; g0 < G; g0 += 8) {
         const int left = G - g0;
         if (left >= 5) decode_split_kernel<HD, 8><<<grid, block, 0, s>>>(p, g0);
@@ -258,8 +374,10 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
         else if (left == 2) decode_split_kernel<HD, 2><<<grid, block, 0, s>>>(p, g0);
         else decode_split_kernel<HD, 1><<<grid, block, 0, s>>>(p, g0);
     }
-    const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head), cblock(HD < 64 ? 64 : HD);
-    decode_combine_kernel<HD><<<cgrid, cblock, 0, s>>>(p);
+    if (p.total_chunks > p.n) {  // some entry spans several chunks
+        const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head);
+        decode_combine_kernel<HD><<<cgrid, 256, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
@@ -267,7 +385,8 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 
 int32_t decode_block_rows(int32_t hd_kv)
 {
-    const int lpr = hd_kv / kDimsPerLane;
+    // The larger of the two lane layouts' step sizes (both are powers of two).
+    const int lpr = hd_kv / 8;
     return kWaves * (64 / lpr) * kUnroll;
 }
 

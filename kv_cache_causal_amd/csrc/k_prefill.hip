@@ -49,17 +49,34 @@ struct PrefillCfg {
     static constexpr int KB = KT / 16;              // 16-key blocks per tile
     static constexpr int DQ = HD / 4;               // dims per lane group
     static constexpr int STR = HD + 4;              // LDS row stride (floats)
+    static constexpr int NDB = HD / 16;             // 16-dim output blocks
+    static constexpr int VEC = NDB >= 4 ? 4 : NDB;  // output blocks fed by one V read
+    static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
 };
 
 template <int HD>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t GB, int32_t TQ,
-                                                      int32_t n_qtiles, int32_t n_hsub)
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_t GB, int32_t TQ,
+                                                      int32_t n_qtiles, int32_t n_hsub,
+                                                      int32_t nblocks)
 {
     using C = PrefillCfg<HD>;
-    constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, STR = C::STR;
+    constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, STR = C::STR, NDB = C::NDB, VEC = C::VEC;
+    constexpr int LD = C::LD;
+    static_assert(LD * 256 * 4 == KT * HD, "tile split");
     __shared__ float Ks[KT * STR];
     __shared__ float Vs[KT * STR];
     __shared__ int s_kmax;
+
+    // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
+    // takes logical block (b % 8) * (nblocks / 8) + b / 8.  Each XCD then owns a
+    // contiguous range of logical blocks -- one kv head's query tiles when the counts
+    // divide -- and its L2 serves those tiles' shared K/V rows.  Within a range, heavy
+    // (late-position) query tiles come first.
+    const int per_xcd = (nblocks + 7) / 8;
+    const int logical = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (logical >= nblocks) return;
+    const int hgroup = logical / n_qtiles;
+    const int qtile = n_qtiles - 1 - (logical - hgroup * n_qtiles);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -67,9 +84,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
     const int qc = lane & 15;   // query column of this lane
     const int grp = lane >> 4;  // lane group: key rows 4grp..4grp+3 of each 16-key block
 
-    const int qtile = n_qtiles - 1 - (int)blockIdx.x;
-    const int hk = (int)blockIdx.y / n_hsub;
-    const int hs = (int)blockIdx.y - hk * n_hsub;
+    const int hk = hgroup / n_hsub;
+    const int hs = hgroup - hk * n_hsub;
     const int G = p.n_head / p.n_head_kv;
     const int wpt = TQ / 16;                 // waves per head
     const int g = hs * GB + wave / wpt;      // head within the kv group
@@ -86,10 +102,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
         const int tt = qtile * TQ + tid;
         if (tt < p.nt) atomicMax(&s_kmax, p.pos[tt]);
     }
-    // Largest position among this wave's 16 tokens (reduce over the 16 query columns).
-    int wmax = pq;
+    // Smallest and largest position among this wave's 16 tokens (invalid columns do not
+    // count towards the minimum).
+    int wmax = pq, wmin = tok_ok ? pq : 0x7fffffff;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) wmax = max(wmax, __shfl_xor(wmax, off));
+    for (int off = 1; off < 16; off <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, off));
+        wmin = min(wmin, __shfl_xor(wmin, off));
+    }
 
     // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h).
     float qf[DQ];
@@ -99,9 +119,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
         for (int s = 0; s < DQ; s++) qf[s] = qrow[s];
     }
 
-    floatx4 oacc[HD / 16];
+    floatx4 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < HD / 16; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int db = 0; db < NDB; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f;
 
     __syncthreads();
@@ -110,22 +130,39 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
     const float *Kh = p.kc + hk * HD;
     const float *Vh = p.vc + hk * HD;
 
-    for (int kt = 0; kt < ntiles; kt++) {
-        const int key0 = kt * KT;
-        // Stage the tile's K and V rows of kv head hk; rows past the region read as 0.
-        for (int idx = tid; idx < KT * (HD / 4); idx += 256) {
+    // Tile staging: thread tid moves float4 #(tid + 256 j) of the tile, j < LD; rows past
+    // the region read as 0.  The next tile's loads are issued before this tile's MFMAs.
+    float4 kreg[LD], vreg[LD];
+    auto fetch = [&](int key0) {
+#pragma unroll
+        for (int j = 0; j < LD; j++) {
+            const int idx = tid + 256 * j;
             const int r = idx / (HD / 4);
             const int c4 = idx - r * (HD / 4);
             const int row = key0 + r;
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            kreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            vreg[j] = kreg[j];
             if (row < p.capacity) {
-                kv = *reinterpret_cast<const float4 *>(Kh + (int64_t)row * nkt + c4 * 4);
-                vv = *reinterpret_cast<const float4 *>(Vh + (int64_t)row * nkt + c4 * 4);
+                kreg[j] = *reinterpret_cast<const float4 *>(Kh + (int64_t)row * nkt + c4 * 4);
+                vreg[j] = *reinterpret_cast<const float4 *>(Vh + (int64_t)row * nkt + c4 * 4);
             }
-            *reinterpret_cast<float4 *>(&Ks[r * STR + c4 * 4]) = kv;
-            *reinterpret_cast<float4 *>(&Vs[r * STR + c4 * 4]) = vv;
+        }
+    };
+    fetch(0);
+
+    for (int kt = 0; kt < ntiles; kt++) {
+        const int key0 = kt * KT;
+        __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+        for (int j = 0; j < LD; j++) {
+            const int idx = tid + 256 * j;
+            const int r = idx / (HD / 4);
+            const int c4 = idx - r * (HD / 4);
+            *reinterpret_cast<float4 *>(&Ks[r * STR + c4 * 4]) = kreg[j];
+            *reinterpret_cast<float4 *>(&Vs[r * STR + c4 * 4]) = vreg[j];
         }
         __syncthreads();
+        if (kt + 1 < ntiles) fetch(key0 + KT);
 
         if (head_ok && key0 <= wmax) {
             // S^T = K Q^T for KB blocks of 16 keys; independent accumulators interleaved.
@@ -147,18 +184,28 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].w, qf[s + 3], sacc[kb]);
             }
-            // Scale to base-2 units and mask keys beyond this query's position.
+            // Scale to base-2 units; mask keys beyond this query's position (only tiles
+            // that reach past the wave's smallest position need the compare).
             float sv[KB][4];
             float tmax = -INFINITY;
+            if (key0 + KT - 1 <= wmin) {
 #pragma unroll
-            for (int kb = 0; kb < KB; kb++)
+                for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int key = key0 + kb * 16 + grp * 4 + r;
-                    const float x = key <= pq ? sacc[kb][r] * p.qscale : -INFINITY;
-                    sv[kb][r] = x;
-                    tmax = fmaxf(tmax, x);
-                }
+                    for (int r = 0; r < 4; r++) {
+                        sv[kb][r] = sacc[kb][r] * p.qscale;
+                        tmax = fmaxf(tmax, sv[kb][r]);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int key = key0 + kb * 16 + grp * 4 + r;
+                        sv[kb][r] = key <= pq ? sacc[kb][r] * p.qscale : -INFINITY;
+                        tmax = fmaxf(tmax, sv[kb][r]);
+                    }
+            }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             // Key 0 is in tile 0 and every window holds it, so mn is finite from tile 0 on.
@@ -166,7 +213,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
             const float alpha = fast_exp2(m - mn);
             l *= alpha;
 #pragma unroll
-            for (int db = 0; db < HD / 16; db++) oacc[db] *= alpha;
+            for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -176,30 +223,57 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p, int32_t G
                     l += pr;
                 }
             m = mn;
-            // O^T += V^T P^T: k-step (kb, r) uses key kb*16 + 4*grp + r for lane group grp.
+            // O^T += V^T P^T.  k-step (kb, r) uses key kb*16 + 4*grp + r for lane group grp.
+            // Output block db = VEC*j + e takes, for A row i, dim 16*VEC*j + VEC*i + e, so
+            // one VEC-wide LDS read (dims 16*VEC*j + VEC*qc ...) feeds VEC blocks.
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * STR + qc];
+                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * STR + VEC * qc];
 #pragma unroll
-                    for (int db = 0; db < HD / 16; db++)
-                        oacc[db] = mfma4(vrow[db * 16], sv[kb][r], oacc[db]);
+                    for (int j = 0; j < NDB / VEC; j++) {
+                        float vv[VEC];
+                        if constexpr (VEC == 4) {
+                            const float4 v4 = *reinterpret_cast<const float4 *>(vrow + 16 * VEC * j);
+                            vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
+                        } else if constexpr (VEC == 2) {
+                            const float2 v2 = *reinterpret_cast<const float2 *>(vrow + 16 * VEC * j);
+                            vv[0] = v2.x; vv[1] = v2.y;
+                        } else {
+                            vv[0] = vrow[16 * VEC * j];
+                        }
+#pragma unroll
+                        for (int e = 0; e < VEC; e++)
+                            oacc[VEC * j + e] = mfma4(vv[e], sv[kb][r], oacc[VEC * j + e]);
+                    }
                 }
         }
-        __syncthreads();
     }
 
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (head_ok && tok_ok) {
+        // Block VEC*j + e, register r' holds dim 16*VEC*j + VEC*(4*grp + r') + e: for each
+        // (j, r') the VEC dims e = 0..VEC-1 are contiguous.
         const float inv = 1.0f / l;
-        float *orow = p.out + ((int64_t)t * p.n_head + h) * HD + grp * 4;
+        float *orow = p.out + ((int64_t)t * p.n_head + h) * HD;
 #pragma unroll
-        for (int db = 0; db < HD / 16; db++) {
-            const floatx4 o = oacc[db] * inv;
-            *reinterpret_cast<float4 *>(orow + db * 16) = make_float4(o[0], o[1], o[2], o[3]);
-        }
+        for (int j = 0; j < NDB / VEC; j++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                float *dst = orow + 16 * VEC * j + VEC * (4 * grp + rr);
+                if constexpr (VEC == 4) {
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(oacc[4 * j][rr] * inv, oacc[4 * j + 1][rr] * inv,
+                                    oacc[4 * j + 2][rr] * inv, oacc[4 * j + 3][rr] * inv);
+                } else if constexpr (VEC == 2) {
+                    *reinterpret_cast<float2 *>(dst) =
+                        make_float2(oacc[2 * j][rr] * inv, oacc[2 * j + 1][rr] * inv);
+                } else {
+                    dst[0] = oacc[j][rr] * inv;
+                }
+            }
     }
 }
 
@@ -213,8 +287,10 @@ hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
     const int TQ = 64 / GB;
     const int n_hsub = (G + GB - 1) / GB;
     const int n_qtiles = (p.nt + TQ - 1) / TQ;
-    const dim3 grid((unsigned)n_qtiles, (unsigned)(p.n_head_kv * n_hsub)), block(256);
-    prefill_kernel<HD><<<grid, block, 0, s>>>(p, GB, TQ, n_qtiles, n_hsub);
+    const int nblocks = n_qtiles * p.n_head_kv * n_hsub;
+    const int launched = (nblocks + 7) / 8 * 8;
+    prefill_kernel<HD><<<dim3((unsigned)launched), dim3(256), 0, s>>>(p, GB, TQ, n_qtiles, n_hsub,
+                                                                      nblocks);
     return hipGetLastError();
 }
 

@@ -84,8 +84,8 @@ template <int STYLE>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
 {
     const int32_t t = blockIdx.x;
-    const int32_t pos = p.pos[t];
-    const int32_t seq = p.seq[t];
+    const int32_t pos = p.pos ? p.pos[t] : p.ipos[t];
+    const int32_t seq = p.seq ? p.seq[t] : p.iseq[t];
     const int32_t nkt = p.n_head_kv * p.hd_kv;
     const int64_t row = ((int64_t)seq * p.n_layer + p.layer) * p.region + (int64_t)pos * nkt;
     const float *ksrc = p.k + (int64_t)t * nkt;

@@ -188,13 +188,11 @@ kvc_status get_table(const kvc_cache *c, int32_t hd, float base, float fscale, h
 
 float log2e_times(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
+// Optional override of the decode chunk size (rows), read at each call; 0 = automatic.
 int32_t env_split_rows()
 {
-    static const int32_t v = [] {
-        const char *e = std::getenv("KVC_SPLIT_ROWS");
-        return e ? std::max(0, std::atoi(e)) : 0;
-    }();
-    return v;
+    const char *e = std::getenv("KVC_SPLIT_ROWS");
+    return e ? std::max(0, std::atoi(e)) : 0;
 }
 
 }  // namespace
@@ -297,20 +295,26 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
         if ((st = get_table(c, c->g.hd_kv, freq_base, freq_scale, s, &tab_k)) != KVC_OK) return st;
         if (q && (st = get_table(c, hd, freq_base, freq_scale, s, &tab_q)) != KVC_OK) return st;
     }
-    std::vector<int32_t> ints((size_t)nt * 2);
-    std::memcpy(ints.data(), pos, sizeof(int32_t) * nt);
-    std::memcpy(ints.data() + nt, seq_ids, sizeof(int32_t) * nt);
-    const int32_t *dev = nullptr;
-    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
-
     kvc::AppendParams p{};
+    const bool inline_args = nt <= kvc::kInlineTokens;
+    const int32_t *dev = nullptr;
+    if (inline_args) {
+        std::memcpy(p.ipos, pos, sizeof(int32_t) * nt);
+        std::memcpy(p.iseq, seq_ids, sizeof(int32_t) * nt);
+    } else {
+        std::vector<int32_t> ints((size_t)nt * 2);
+        std::memcpy(ints.data(), pos, sizeof(int32_t) * nt);
+        std::memcpy(ints.data() + nt, seq_ids, sizeof(int32_t) * nt);
+        if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+    }
+
     p.q = style == KVC_ROPE_NONE ? nullptr : q;
     p.k = k;
     p.v = v;
     p.kc = c->K;
     p.vc = c->V;
-    p.pos = dev;
-    p.seq = dev + nt;
+    p.pos = inline_args ? nullptr : dev;
+    p.seq = inline_args ? nullptr : dev + nt;
     p.tab_q = tab_q;
     p.tab_k = tab_k;
     p.region = c->region;
@@ -324,10 +328,10 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
     p.style = (int32_t)style;
     hipError_t e = kvc::launch_append(p, s);
     if (e != hipSuccess) {
-        staging_abort(c->st);
+        if (!inline_args) staging_abort(c->st);
         return hip_fail(e, "append kernel");
     }
-    if ((st = staging_commit(c->st, s)) != KVC_OK) return st;
+    if (!inline_args && (st = staging_commit(c->st, s)) != KVC_OK) return st;
     for (int32_t t = 0; t < nt; t++) {
         int32_t &w = c->hw[(size_t)seq_ids[t] * c->g.n_layer + layer];
         w = std::max(w, pos[t] + 1);
@@ -383,31 +387,31 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
     if (n_seq == 0) return KVC_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    // Chunk size: aim for ~1024 workgroups over all kv heads (4 per CU), in whole block
-    // iterations; KVC_SPLIT_ROWS overrides the size (tuning only, never the result's
-    // meaning).
+    // Chunk size.  Small windows are launch-bound: one chunk per entry, no combine pass.
+    // Large ones: ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the
+    // per-chunk overheads (query load, merges, partial record, combine) stay small next
+    // to the stream.  KVC_SPLIT_ROWS overrides the size (tuning only, never the result).
     const int32_t br = kvc::decode_block_rows(c->g.hd_kv);
-    int64_t total_rows = 0;
-    for (int32_t b = 0; b < n_seq; b++) total_rows += (int64_t)pos[b] + 1;
-    int64_t rows = env_split_rows();
-    if (rows <= 0) {
-        const int64_t target = std::max<int64_t>(1, 1024 / c->g.n_head_kv);
-        rows = (total_rows + target - 1) / target;
-    }
-    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
-    std::vector<int32_t> ints((size_t)n_seq * 3 + 1);
-    int32_t *pp = ints.data(), *sp = pp + n_seq, *cb = sp + n_seq;
-    int64_t chunks = 0;
+    int64_t total_rows = 0, max_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) {
-        pp[b] = pos[b];
-        sp[b] = seq_ids[b];
-        cb[b] = (int32_t)chunks;
-        chunks += ((int64_t)pos[b] + 1 + rows - 1) / rows;
+        total_rows += (int64_t)pos[b] + 1;
+        max_rows = std::max<int64_t>(max_rows, (int64_t)pos[b] + 1);
     }
-    cb[n_seq] = (int32_t)chunks;
-    if (chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
+    const int64_t work = total_rows * c->g.n_head_kv;
+    int64_t rows = env_split_rows();
+    if (rows <= 0) rows = work <= 131072 ? max_rows : std::max<int64_t>(512, work / 2048);
+    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
 
-    const size_t need = (size_t)chunks * n_head * (c->g.hd_kv + 4);
+    // Launches of up to kInlineEntries entries; the partials buffer fits the largest.
+    const int32_t E = kvc::kInlineEntries;
+    int64_t max_chunks = 0;
+    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
+        int64_t ch = 0;
+        for (int32_t b = b0; b < std::min(n_seq, b0 + E); b++) ch += ((int64_t)pos[b] + rows) / rows;
+        max_chunks = std::max(max_chunks, ch);
+    }
+    if (max_chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
+    const size_t need = (size_t)max_chunks * n_head * (c->g.hd_kv + 4);
     if (need > c->part_cap) {
         if (c->part) {
             KVC_HIP(hipStreamSynchronize(s));
@@ -420,34 +424,38 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
             return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
         c->part_cap = cap;
     }
-    const int32_t *dev = nullptr;
-    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
-    kvc::DecodeParams p{};
-    p.q = q;
-    p.out = out;
-    p.part = c->part;
-    p.kc = c->K;
-    p.vc = c->V;
-    p.pos = dev;
-    p.seq = dev + n_seq;
-    p.cbase = dev + 2 * n_seq;
-    p.region = c->region;
-    p.n = n_seq;
-    p.n_head = n_head;
-    p.hd = hd;
-    p.n_head_kv = c->g.n_head_kv;
-    p.hd_kv = c->g.hd_kv;
-    p.n_layer = c->g.n_layer;
-    p.layer = layer;
-    p.rows_per_chunk = (int32_t)rows;
-    p.total_chunks = (int32_t)chunks;
-    p.qscale = log2e_times(scale);
-    hipError_t e = kvc::launch_decode(p, s);
-    if (e != hipSuccess) {
-        staging_abort(c->st);
-        return hip_fail(e, "decode kernels");
+
+    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
+        const int32_t n = std::min(E, n_seq - b0);
+        kvc::DecodeParams p{};
+        p.q = q + (int64_t)b0 * n_head * hd;
+        p.out = out + (int64_t)b0 * n_head * c->g.hd_kv;
+        p.part = c->part;
+        p.kc = c->K;
+        p.vc = c->V;
+        p.region = c->region;
+        p.n = n;
+        p.n_head = n_head;
+        p.hd = hd;
+        p.n_head_kv = c->g.n_head_kv;
+        p.hd_kv = c->g.hd_kv;
+        p.n_layer = c->g.n_layer;
+        p.layer = layer;
+        p.rows_per_chunk = (int32_t)rows;
+        p.qscale = log2e_times(scale);
+        int32_t chunks = 0;
+        for (int32_t i = 0; i < n; i++) {
+            p.pos[i] = pos[b0 + i];
+            p.seq[i] = seq_ids[b0 + i];
+            p.cbase[i] = chunks;
+            chunks += (int32_t)(((int64_t)pos[b0 + i] + rows) / rows);
+        }
+        p.cbase[n] = chunks;
+        p.total_chunks = chunks;
+        hipError_t e = kvc::launch_decode(p, s);
+        if (e != hipSuccess) return hip_fail(e, "decode kernels");
     }
-    return staging_commit(c->st, s);
+    return KVC_OK;
 }
 
 }  // extern "C"

@@ -17,32 +17,39 @@ hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_b
                              float freq_scale, hipStream_t s);
 
 // ---- K1: RoPE(q, k) + in-place K/V row store ------------------------------------------
+// Up to kInlineTokens positions / sequence ids ride in the kernel arguments (no upload);
+// longer appends pass them through device memory (pos/seq non-null).
+constexpr int kInlineTokens = 64;
 struct AppendParams {
     float *q;               // [nt][n_head][hd] or nullptr
     const float *k, *v;     // [nt][n_head_kv][hd_kv]
     float *kc, *vc;         // cache bases
-    const int32_t *pos;     // device [nt]
-    const int32_t *seq;     // device [nt]
+    const int32_t *pos;     // device [nt], or nullptr: use ipos
+    const int32_t *seq;     // device [nt], or nullptr: use iseq
     const float2 *tab_q;    // [capacity][hd/2] (nullptr if q is nullptr or style NONE)
     const float2 *tab_k;    // [capacity][hd_kv/2] (nullptr for style NONE)
     int64_t region;
     int32_t nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style;
+    int32_t ipos[kInlineTokens], iseq[kInlineTokens];
 };
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 
 // ---- K2 + K3: split-K decode and log-sum-exp combine -----------------------------------
+// One launch covers up to kInlineEntries batch entries, whose positions, sequence ids
+// and chunk offsets ride in the kernel arguments.
+constexpr int kInlineEntries = 64;
 struct DecodeParams {
-    const float *q;          // [n][n_head][hd]
+    const float *q;          // [n][n_head][hd] (this launch's entries)
     float *out;              // [n][n_head][hd_kv]
     float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
     const float *kc, *vc;    // cache bases
-    const int32_t *pos;      // device [n]
-    const int32_t *seq;      // device [n]
-    const int32_t *cbase;    // device [n + 1]: first chunk of entry b; cbase[n] = total
     int64_t region;
     int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer;
     int32_t rows_per_chunk, total_chunks;
     float qscale;            // scale * log2(e): scores are kept in base-2 units
+    int32_t pos[kInlineEntries];
+    int32_t seq[kInlineEntries];
+    int32_t cbase[kInlineEntries + 1];  // first chunk of entry b; cbase[n] = total_chunks
 };
 // Rows per block iteration of the split-K kernel for a kv head dim (chunks should be a
 // multiple of it).
