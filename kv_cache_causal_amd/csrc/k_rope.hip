@@ -78,9 +78,53 @@ __device__ __forceinline__ void rotate_heads(const float *src, float *dst, int32
     }
 }
 
-// One workgroup per token.  Reads: q row (if any), k row, v row, one table row per head
-// dim.  Writes: q row in place, one K row and one V row of the cache.
+// Vector form of rotate_heads for widths where every access is a whole, aligned float4:
+// a NEOX thread rotates 4 consecutive pairs (i..i+3 with i+half..i+half+3), an
+// interleaved thread 2 consecutive pairs (4 consecutive elements).  Same arithmetic.
 template <int STYLE>
+__device__ __forceinline__ void rotate_heads_vec(const float *src, float *dst, int32_t nh,
+                                                 int32_t w, const float2 *tab)
+{
+    const int32_t half = w >> 1;
+    const int32_t per_head = w >> 2;  // float4 units per head
+    const int32_t nq = nh * (STYLE == kNeox ? per_head / 2 : per_head);
+    for (int32_t idx = threadIdx.x; idx < nq; idx += blockDim.x) {
+        if constexpr (STYLE == kNeox) {
+            const int32_t h = idx / (per_head / 2);
+            const int32_t i = (idx - h * (per_head / 2)) * 4;
+            const float *x = src + (int64_t)h * w;
+            float *y = dst + (int64_t)h * w;
+            const float4 a = *reinterpret_cast<const float4 *>(x + i);
+            const float4 b = *reinterpret_cast<const float4 *>(x + half + i);
+            const float4 t0 = *reinterpret_cast<const float4 *>(tab + i);
+            const float4 t1 = *reinterpret_cast<const float4 *>(tab + i + 2);
+            float4 ya, yb;
+            rotate_pair(a.x, b.x, make_float2(t0.x, t0.y), ya.x, yb.x);
+            rotate_pair(a.y, b.y, make_float2(t0.z, t0.w), ya.y, yb.y);
+            rotate_pair(a.z, b.z, make_float2(t1.x, t1.y), ya.z, yb.z);
+            rotate_pair(a.w, b.w, make_float2(t1.z, t1.w), ya.w, yb.w);
+            *reinterpret_cast<float4 *>(y + i) = ya;
+            *reinterpret_cast<float4 *>(y + half + i) = yb;
+        } else {
+            const int32_t h = idx / per_head;
+            const int32_t e = (idx - h * per_head) * 4;
+            const float *x = src + (int64_t)h * w;
+            float *y = dst + (int64_t)h * w;
+            const float4 a = *reinterpret_cast<const float4 *>(x + e);
+            const float4 t = *reinterpret_cast<const float4 *>(tab + e / 2);
+            float4 ya;
+            rotate_pair(a.x, a.y, make_float2(t.x, t.y), ya.x, ya.y);
+            rotate_pair(a.z, a.w, make_float2(t.z, t.w), ya.z, ya.w);
+            *reinterpret_cast<float4 *>(y + e) = ya;
+        }
+    }
+}
+
+// One workgroup per token.  Reads: q row (if any), k row, v row, one table row per head
+// dim.  Writes: q row in place, one K row and one V row of the cache.  QVEC selects the
+// float4 form for q (hd a multiple of 8 for NEOX, of 4 for interleaved); k always
+// qualifies (hd_kv is a multiple of 16).
+template <int STYLE, bool QVEC>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
 {
     const int32_t t = blockIdx.x;
@@ -96,10 +140,12 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
     if (STYLE != kNone) {
         if (p.q) {
             float *qt = p.q + (int64_t)t * p.n_head * p.hd;
-            rotate_heads<STYLE>(qt, qt, p.n_head, p.hd, p.tab_q + (int64_t)pos * (p.hd >> 1));
+            const float2 *tq = p.tab_q + (int64_t)pos * (p.hd >> 1);
+            if constexpr (QVEC) rotate_heads_vec<STYLE>(qt, qt, p.n_head, p.hd, tq);
+            else rotate_heads<STYLE>(qt, qt, p.n_head, p.hd, tq);
         }
-        rotate_heads<STYLE>(ksrc, kdst, p.n_head_kv, p.hd_kv,
-                            p.tab_k + (int64_t)pos * (p.hd_kv >> 1));
+        rotate_heads_vec<STYLE>(ksrc, kdst, p.n_head_kv, p.hd_kv,
+                                p.tab_k + (int64_t)pos * (p.hd_kv >> 1));
     } else {
         const float4 *ks4 = reinterpret_cast<const float4 *>(ksrc);
         float4 *kd4 = reinterpret_cast<float4 *>(kdst);
@@ -128,9 +174,15 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
     if (p.nt <= 0) return hipSuccess;
     const dim3 grid((unsigned)p.nt), block(256);
     switch (p.style) {
-    case kNeox: append_kernel<kNeox><<<grid, block, 0, s>>>(p); break;
-    case kInterleaved: append_kernel<kInterleaved><<<grid, block, 0, s>>>(p); break;
-    default: append_kernel<kNone><<<grid, block, 0, s>>>(p); break;
+    case kNeox:
+        if (p.hd % 8 == 0) append_kernel<kNeox, true><<<grid, block, 0, s>>>(p);
+        else append_kernel<kNeox, false><<<grid, block, 0, s>>>(p);
+        break;
+    case kInterleaved:
+        if (p.hd % 4 == 0) append_kernel<kInterleaved, true><<<grid, block, 0, s>>>(p);
+        else append_kernel<kInterleaved, false><<<grid, block, 0, s>>>(p);
+        break;
+    default: append_kernel<kNone, false><<<grid, block, 0, s>>>(p); break;
     }
     return hipGetLastError();
 }

@@ -1,10 +1,10 @@
 // The C ABI of kvc.h: handle, host validation, position staging, RoPE tables, launches.
 //
 // Per call: every argument is checked on the host (validate.cpp) before anything is
-// queued; host-side integer arrays (positions, sequence ids, chunk offsets) are copied
-// into a pinned staging ring and sent to the device with one async copy on the caller's
-// stream; then the kernels are queued on the same stream.  Nothing here waits for the
-// device except kv_alloc (zero fill) and kv_free.
+// queued.  Host-side integer arrays (positions, sequence ids, chunk offsets) ride in the
+// kernel arguments when short, or in a pinned staging ring the kernels read in place
+// when long; then the kernels are queued on the caller's stream.  Nothing here waits
+// for the device except kv_alloc (zero fill) and kv_free.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -46,12 +46,14 @@ struct RopeTable {
     float2 *dev;
 };
 
-// Pinned host ring + device ring for the small integer arrays each call sends along.
-// A slot is reused only after the event recorded behind the kernels that read it has
-// completed, so the host never waits unless it runs a full ring ahead of the device.
+// Pinned, coherent host ring for the integer arrays a call sends along when they do not
+// fit the kernel arguments (positions and sequence ids of long appends and prefills).
+// The kernels read a slot in place through its device-visible address: no copy is
+// queued.  A slot is reused only after the event recorded behind the kernels that read
+// it has completed, so the host never waits unless it runs a full ring ahead.
 struct Staging {
     int32_t *host = nullptr;
-    int32_t *dev = nullptr;
+    int32_t *dev = nullptr;   // device view of `host`
     size_t cap = 0;   // ints
     size_t head = 0;
     uint64_t lap = 0;
@@ -90,7 +92,6 @@ void staging_release(Staging &st)
     for (auto ev : st.pool) hipEventDestroy(ev);
     st.pool.clear();
     if (st.host) hipHostFree(st.host);
-    if (st.dev) hipFree(st.dev);
     st.host = nullptr;
     st.dev = nullptr;
     st.cap = st.head = 0;
@@ -99,18 +100,16 @@ void staging_release(Staging &st)
 kvc_status staging_alloc(Staging &st, size_t ints)
 {
     KVC_HIP(hipHostMalloc(reinterpret_cast<void **>(&st.host), ints * sizeof(int32_t),
-                          hipHostMallocDefault));
-    KVC_HIP(hipMalloc(reinterpret_cast<void **>(&st.dev), ints * sizeof(int32_t)));
+                          hipHostMallocMapped | hipHostMallocCoherent));
+    KVC_HIP(hipHostGetDevicePointer(reinterpret_cast<void **>(&st.dev), st.host, 0));
     st.cap = ints;
     st.head = 0;
     return KVC_OK;
 }
 
-// Copy `n` host ints into the ring and queue their upload on `s`.  Returns the device
-// address through *dev.  The caller must call staging_commit after queueing the kernels
-// that read it.
-kvc_status staging_push(Staging &st, const std::vector<int32_t> &data, hipStream_t s,
-                        const int32_t **dev)
+// Copy `n` host ints into the ring.  Returns the device-visible address through *dev.
+// The caller must call staging_commit after queueing the kernels that read it.
+kvc_status staging_push(Staging &st, const std::vector<int32_t> &data, const int32_t **dev)
 {
     const size_t n = (data.size() + 63) & ~size_t(63);  // keep slots 256-byte aligned
     if (n > st.cap) {
@@ -135,8 +134,6 @@ kvc_status staging_push(Staging &st, const std::vector<int32_t> &data, hipStream
         st.inflight.pop_front();
     }
     std::memcpy(st.host + a, data.data(), data.size() * sizeof(int32_t));
-    KVC_HIP(hipMemcpyAsync(st.dev + a, st.host + a, data.size() * sizeof(int32_t),
-                           hipMemcpyHostToDevice, s));
     st.head = e;
     *dev = st.dev + a;
     st.inflight.push_back(Staging::Use{a, n, st.lap, nullptr});
@@ -305,7 +302,7 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
         std::vector<int32_t> ints((size_t)nt * 2);
         std::memcpy(ints.data(), pos, sizeof(int32_t) * nt);
         std::memcpy(ints.data() + nt, seq_ids, sizeof(int32_t) * nt);
-        if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+        if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
     }
 
     p.q = style == KVC_ROPE_NONE ? nullptr : q;
@@ -352,7 +349,7 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
 
     std::vector<int32_t> ints(pos, pos + nt);
     const int32_t *dev = nullptr;
-    if ((st = staging_push(c->st, ints, s, &dev)) != KVC_OK) return st;
+    if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
     const int64_t off = ((int64_t)seq * c->g.n_layer + layer) * c->region;
     kvc::PrefillParams p{};
     p.q = q;

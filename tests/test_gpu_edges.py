@@ -177,3 +177,21 @@ def test_long_window_many_chunks_matches_single_chunk_shape():
     got, want = p.decode(0, [0, 0], [8999, 40], dev(q), q, 16, 128, 0.0883883461356163)
     assert_close(got, want, "split-K")
     p.close()
+
+
+@pytest.mark.parametrize("style,hd", [(0, 20), (1, 18), (0, 40), (1, 36)],
+                         ids=["neox20", "inter18", "neox40", "inter36"])
+def test_rope_query_widths_scalar_and_vector_paths(style, hd):
+    """Query head dims that rule out (20, 18) or allow (40, 36) whole-float4 access."""
+    say(f"rope q width {hd} style {style}")
+    p = Pair(1, 1, 2, 16, 96)
+    nt = 70  # more than the 64 that travel in kernel arguments: positions go via memory
+    q = custom(80 + hd, (nt, 4, hd))
+    k = custom(81, (nt, 2, 16))
+    v = custom(82, (nt, 2, 16))
+    pos = custom_positions(83, nt, 0, 96)
+    qd, qo = p.append(0, [0] * nt, pos, q, 4, hd, k, v, 1e4, 1.0, style)
+    compare_cache(p.g, p.o, 0, 0, f"width {hd}")
+    got, want = p.prefill(0, 0, pos, qd, qo, 4, hd, 0.2)
+    assert_close(got, want, f"prefill width {hd}")
+    p.close()
