@@ -111,12 +111,13 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         wmin = min(wmin, __shfl_xor(wmin, off));
     }
 
-    // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h).
+    // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h), pre-multiplied by
+    // scale * log2(e) so the S^T accumulators are already in base-2 units.
     float qf[DQ];
     {
         const float *qrow = p.q + ((int64_t)(tok_ok ? t : 0) * p.n_head + h) * p.hd + grp * DQ;
 #pragma unroll
-        for (int s = 0; s < DQ; s++) qf[s] = qrow[s];
+        for (int s = 0; s < DQ; s++) qf[s] = qrow[s] * p.qscale;
     }
 
     floatx4 oacc[NDB];
@@ -130,22 +131,27 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     const float *Kh = p.kc + hk * HD;
     const float *Vh = p.vc + hk * HD;
 
-    // Tile staging: thread tid moves float4 #(tid + 256 j) of the tile, j < LD; rows past
-    // the region read as 0.  The next tile's loads are issued before this tile's MFMAs.
-    float4 kreg[LD], vreg[LD];
+    // Tile staging: thread tid moves float4 #(tid + 256 j) of the tile, j < LD, i.e. row
+    // tid / (HD/4) + j * RSTEP, column (tid % (HD/4)) * 4.  Addresses are a uniform tile
+    // base plus a per-thread 32-bit byte offset.  Regions are padded to a whole number of
+    // 64-row tiles (zero rows past the capacity, beyond every position and so masked), so
+    // every tile load is inside the region.  The next tile's loads are issued before this
+    // tile's MFMAs.
+    constexpr int RSTEP = 256 / (HD / 4);      // rows between a thread's float4s
+    const int trow = tid / (HD / 4);
+    const int tcol = (tid % (HD / 4)) * 4;
+    const uint32_t toff = (uint32_t)(trow * nkt + tcol) * 4u;
+    const int64_t jstride = (int64_t)RSTEP * nkt * 4;  // bytes between a thread's float4s
+    // Native 4-float vectors: with float4 structs the compiler turns these unconditional
+    // copies into an aggregate copy and keeps the arrays in scratch memory.
+    floatx4 kreg[LD], vreg[LD];
     auto fetch = [&](int key0) {
+        const char *kb0 = reinterpret_cast<const char *>(Kh + (int64_t)key0 * nkt);
+        const char *vb0 = reinterpret_cast<const char *>(Vh + (int64_t)key0 * nkt);
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            const int idx = tid + 256 * j;
-            const int r = idx / (HD / 4);
-            const int c4 = idx - r * (HD / 4);
-            const int row = key0 + r;
-            kreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            vreg[j] = kreg[j];
-            if (row < p.capacity) {
-                kreg[j] = *reinterpret_cast<const float4 *>(Kh + (int64_t)row * nkt + c4 * 4);
-                vreg[j] = *reinterpret_cast<const float4 *>(Vh + (int64_t)row * nkt + c4 * 4);
-            }
+            kreg[j] = *reinterpret_cast<const floatx4 *>(kb0 + j * jstride + toff);
+            vreg[j] = *reinterpret_cast<const floatx4 *>(vb0 + j * jstride + toff);
         }
     };
     fetch(0);
@@ -155,11 +161,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            const int idx = tid + 256 * j;
-            const int r = idx / (HD / 4);
-            const int c4 = idx - r * (HD / 4);
-            *reinterpret_cast<float4 *>(&Ks[r * STR + c4 * 4]) = kreg[j];
-            *reinterpret_cast<float4 *>(&Vs[r * STR + c4 * 4]) = vreg[j];
+            *reinterpret_cast<floatx4 *>(&Ks[(trow + j * RSTEP) * STR + tcol]) = kreg[j];
+            *reinterpret_cast<floatx4 *>(&Vs[(trow + j * RSTEP) * STR + tcol]) = vreg[j];
         }
         __syncthreads();
         if (kt + 1 < ntiles) fetch(key0 + KT);
@@ -184,8 +187,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].w, qf[s + 3], sacc[kb]);
             }
-            // Scale to base-2 units; mask keys beyond this query's position (only tiles
-            // that reach past the wave's smallest position need the compare).
+            // Mask keys beyond this query's position (only tiles that reach past the
+            // wave's smallest position need the compare).
             float sv[KB][4];
             float tmax = -INFINITY;
             if (key0 + KT - 1 <= wmin) {
@@ -193,7 +196,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                 for (int kb = 0; kb < KB; kb++)
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        sv[kb][r] = sacc[kb][r] * p.qscale;
+                        sv[kb][r] = sacc[kb][r];
                         tmax = fmaxf(tmax, sv[kb][r]);
                     }
             } else {
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
                         const int key = key0 + kb * 16 + grp * 4 + r;
-                        sv[kb][r] = key <= pq ? sacc[kb][r] * p.qscale : -INFINITY;
+                        sv[kb][r] = key <= pq ? sacc[kb][r] : -INFINITY;
                         tmax = fmaxf(tmax, sv[kb][r]);
                     }
             }
@@ -210,10 +213,14 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             // Key 0 is in tile 0 and every window holds it, so mn is finite from tile 0 on.
             const float mn = fmaxf(m, tmax);
-            const float alpha = fast_exp2(m - mn);
-            l *= alpha;
+            // The running max moves rarely after the first tiles: rescale only when some
+            // lane's did (alpha = 1 exactly otherwise).
+            if (__any(mn != m)) {
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
+                for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll

@@ -210,7 +210,9 @@ kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_h
     kvc_cache *c = new (std::nothrow) kvc_cache();
     if (!c) return fail(KVC_E_NOMEM, "handle allocation failed");
     c->g = kvc::Geometry{n_seq, n_layer, n_head_kv, hd_kv, capacity};
-    c->region = (int64_t)capacity * n_head_kv * hd_kv;
+    const int64_t rows = ((int64_t)capacity + kvc::kRegionRowAlign - 1) / kvc::kRegionRowAlign *
+                         kvc::kRegionRowAlign;
+    c->region = rows * n_head_kv * hd_kv;
     c->hw.assign((size_t)n_seq * n_layer, 0);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region * sizeof(float);

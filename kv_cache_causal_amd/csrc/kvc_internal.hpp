@@ -9,8 +9,11 @@
 
 namespace kvc {
 
-// Cache layout: K[n_seq][n_layer][capacity][n_head_kv * hd_kv] (V likewise); `region`
-// is capacity * n_head_kv * hd_kv floats.
+// Cache layout: K[n_seq][n_layer][rows][n_head_kv * hd_kv] (V likewise) with
+// rows = capacity rounded up to a multiple of kRegionRowAlign; `region` is
+// rows * n_head_kv * hd_kv floats.  Rows at or past the capacity stay zero and are never
+// inside a window; they let the prefill kernel load whole key tiles unconditionally.
+constexpr int kRegionRowAlign = 64;
 
 // ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------
 hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
