@@ -48,7 +48,11 @@ struct PrefillCfg {
     static constexpr int KT = HD >= 256 ? 32 : 64;  // keys per tile
     static constexpr int KB = KT / 16;              // 16-key blocks per tile
     static constexpr int DQ = HD / 4;               // dims per lane group
-    static constexpr int STR = HD + 4;              // LDS row stride (floats)
+    // LDS row strides (floats), measured with a bank-conflict probe on gfx950: the
+    // K-fragment reads (16 rows, one column) cost the least with 4 floats of padding,
+    // the V-fragment reads (contiguous row pieces) are conflict-free unpadded.
+    static constexpr int KSTR = HD + 4;
+    static constexpr int VSTR = HD;
     static constexpr int NDB = HD / 16;             // 16-dim output blocks
     static constexpr int VEC = NDB >= 4 ? 4 : NDB;  // output blocks fed by one V read
     static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
@@ -60,11 +64,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                                                       int32_t nblocks)
 {
     using C = PrefillCfg<HD>;
-    constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, STR = C::STR, NDB = C::NDB, VEC = C::VEC;
+    constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, NDB = C::NDB, VEC = C::VEC;
+    constexpr int KSTR = C::KSTR, VSTR = C::VSTR;
     constexpr int LD = C::LD;
     static_assert(LD * 256 * 4 == KT * HD, "tile split");
-    __shared__ float Ks[KT * STR];
-    __shared__ float Vs[KT * STR];
+    __shared__ float Ks[KT * KSTR];
+    __shared__ float Vs[KT * VSTR];
     __shared__ int s_kmax;
 
     // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
@@ -161,8 +166,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            *reinterpret_cast<floatx4 *>(&Ks[(trow + j * RSTEP) * STR + tcol]) = kreg[j];
-            *reinterpret_cast<floatx4 *>(&Vs[(trow + j * RSTEP) * STR + tcol]) = vreg[j];
+            *reinterpret_cast<floatx4 *>(&Ks[(trow + j * RSTEP) * KSTR + tcol]) = kreg[j];
+            *reinterpret_cast<floatx4 *>(&Vs[(trow + j * RSTEP) * VSTR + tcol]) = vreg[j];
         }
         __syncthreads();
         if (kt + 1 < ntiles) fetch(key0 + KT);
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                 float4 kf[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++)
-                    kf[kb] = *reinterpret_cast<const float4 *>(&Ks[(kb * 16 + qc) * STR + grp * DQ + s]);
+                    kf[kb] = *reinterpret_cast<const float4 *>(&Ks[(kb * 16 + qc) * KSTR + grp * DQ + s]);
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].x, qf[s + 0], sacc[kb]);
 #pragma unroll
@@ -237,7 +242,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * STR + VEC * qc];
+                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * VSTR + VEC * qc];
 #pragma unroll
                     for (int j = 0; j < NDB / VEC; j++) {
                         float vv[VEC];
