@@ -16,7 +16,9 @@ Reported:
   prefill_tflops algorithmic prefill FLOPs (4 * n_head * hd_kv * sum_t (pos_t + 1)) /
                  prefill-attention time
   roofline       the dominant kernel (prefill, MFMA-bound) against the fp32 matrix peak;
-  roofline_decode the decode kernels against HBM bandwidth
+  roofline_decode the decode kernels against HBM bandwidth; `traffic` in both is HBM bytes
+                 per launch from copy-calibrated FETCH_SIZE + WRITE_SIZE counters recorded in
+                 profiles/ (null once the kernel sources differ from the profiled ones)
   cpu_baseline   the plain C oracle on the host cores, on a bounded sample
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
@@ -193,7 +195,7 @@ def main():
             "peak": FP32_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill"),
             "flops_per_launch": pre_flops,
             "avg_launch_us": round(float(t_pre.mean()) * 1e3, 2),
         },
@@ -204,7 +206,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode"),
             "bytes_per_launch": kv_bytes,
             "avg_launch_us": round(float(t_dec.mean()) * 1e3, 2),
         },
@@ -213,6 +215,23 @@ def main():
     if orc_cache is not None:
         result["cpu_baseline"] = cpu_baseline(orc_cache, w, seqs, lens, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) recorded in
+    profiles/ for this workload, or None when the kernel sources changed since the
+    counters were taken (the record keeps their sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3-0.6b-batch.json")
+    try:
+        rec = json.load(open(path))
+        for f, h in rec["source_sha256"].items():
+            src = os.path.join(ROOT, "kv_cache_causal_amd", "csrc", f)
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != h:
+                return None
+        return int(rec[kernel]["fetch_bytes"] + rec[kernel]["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(orc_cache, w, seqs, lens, kv_bytes, seconds):

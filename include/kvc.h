@@ -81,9 +81,10 @@ typedef enum kvc_rope_style {
  *              life: the regions never grow, move or get copied.
  *   stream     used for the zero fill; kv_alloc waits for it before returning.
  *
- * Layout in device memory: K[n_seq][n_layer][capacity][n_head_kv * hd_kv], V likewise;
- * row p of a region holds position p, kv head hk at columns [hk*hd_kv, (hk+1)*hd_kv).
- * All rows start as +0.0f.
+ * Layout in device memory: K[n_seq][n_layer][rows][n_head_kv * hd_kv], V likewise, with
+ * rows = capacity rounded up to a multiple of 64 (the extra rows stay zero and are never
+ * inside a window); row p of a region holds position p, kv head hk at columns
+ * [hk*hd_kv, (hk+1)*hd_kv).  All rows start as +0.0f.
  * Errors: KVC_E_ARG (bad geometry or null out), KVC_E_NOMEM, KVC_E_HIP.  On error *out
  * is set to NULL and nothing stays allocated.
  */
@@ -99,8 +100,9 @@ kvc_status kv_free(kvc_cache *c);
 /*
  * kv_view -- borrow one (sequence, layer)'s regions without copying ([ZEROCOPY]
  * "Reading without copying": a live reference into the cache's own storage).
- *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] f32.
- *         The pointers never change for the handle's life and stay owned by it.
+ *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] f32 (the
+ *         region's first capacity rows).  The pointers never change for the handle's
+ *         life and stay owned by it.
  * Errors: KVC_E_ARG for a NULL handle/pointer or seq/layer out of range.
  */
 kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, float **k, float **v);
