@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM = 0, 1, 2, 3, 4, 5
 ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
+KV_F32, KV_F16 = 0, 1
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
           "-std=c11", "-Wall", "-Wextra"]
@@ -45,6 +46,9 @@ def _bind(lib):
         "orc_rope_cos_sin": (ctypes.c_int, [i32, f32, f32, i32, p, p]),
         "orc_rope": (ctypes.c_int, [p, i32, i32, i32, p, f32, f32, i32]),
         "orc_cache_new": (p, [i32, i32, i32, i32, i32]),
+        "orc_cache_new_typed": (p, [i32, i32, i32, i32, i32, i32]),
+        "orc_f32_to_f16": (ctypes.c_uint16, [f32]),
+        "orc_f16_to_f32": (f32, [ctypes.c_uint16]),
         "orc_cache_free": (None, [p]),
         "orc_cache_region": (p, [p, i32, i32, i32]),
         "orc_cache_seq_len": (i32, [p, i32, i32]),
@@ -109,6 +113,15 @@ class Oracle:
             raise ValueError(f"orc_rope_cos_sin status {st}")
         return cs, sn
 
+    def f32_to_f16(self, x):
+        """Element-wise binary16 bit patterns (uint16) of f32 values."""
+        x = np.asarray(x, np.float32).ravel()
+        return np.array([self.L.orc_f32_to_f16(float(v)) for v in x], np.uint16)
+
+    def f16_to_f32(self, h):
+        h = np.asarray(h, np.uint16).ravel()
+        return np.array([self.L.orc_f16_to_f32(int(v)) for v in h], np.float32)
+
     def rope(self, x, pos, base, scale=1.0, style=ROPE_NEOX):
         """x: [nt][nh][hd]; returns a rotated copy."""
         x = _f32(x).copy()
@@ -121,15 +134,18 @@ class Oracle:
 
 
 class OracleCache:
-    """The oracle's KV cache: zeroed regions [n_seq][n_layer][capacity][n_head_kv*hd_kv]."""
+    """The oracle's KV cache: zeroed regions [n_seq][n_layer][capacity][n_head_kv*hd_kv] of
+    f32 values (dtype KV_F32) or binary16 bit patterns (KV_F16)."""
 
-    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, oracle: Oracle | None = None):
+    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, oracle: Oracle | None = None,
+                 dtype: int = KV_F32):
         self.o = oracle or Oracle()
         self.L = self.o.L
         self.n_seq, self.n_layer = n_seq, n_layer
         self.n_head_kv, self.hd_kv, self.capacity = n_head_kv, hd_kv, capacity
         self.nkt = n_head_kv * hd_kv
-        self.h = self.L.orc_cache_new(n_seq, n_layer, n_head_kv, hd_kv, capacity)
+        self.dtype = dtype
+        self.h = self.L.orc_cache_new_typed(n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype)
         if not self.h:
             raise ValueError("orc_cache_new rejected the geometry")
 
@@ -145,11 +161,16 @@ class OracleCache:
             pass
 
     def region(self, which, seq, layer) -> np.ndarray:
-        """Live numpy view of one region ([capacity][nkt]); which=0 for K, 1 for V."""
+        """Live numpy view of one region ([capacity][nkt]); which=0 for K, 1 for V.
+        float32 for an f32 cache, uint16 (binary16 bits) for an f16 cache."""
         ptr = self.L.orc_cache_region(self.h, which, seq, layer)
         if not ptr:
             raise IndexError("bad seq/layer")
-        buf = (ctypes.c_float * (self.capacity * self.nkt)).from_address(ptr)
+        n = self.capacity * self.nkt
+        if self.dtype == KV_F16:
+            buf = (ctypes.c_uint16 * n).from_address(ptr)
+            return np.frombuffer(buf, dtype=np.uint16).reshape(self.capacity, self.nkt)
+        buf = (ctypes.c_float * n).from_address(ptr)
         return np.frombuffer(buf, dtype=np.float32).reshape(self.capacity, self.nkt)
 
     def k(self, seq, layer):

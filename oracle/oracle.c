@@ -23,9 +23,13 @@
  * long double and rounded once), because the pages' f32 powf/sin_cos depend on the libm
  * that runs them.
  *
+ * Regions hold f32, or IEEE binary16 for the half-precision cache ([MINFER-11] §2.5):
+ * the store rounds each f32 value to binary16 (nearest, ties to even) and attention
+ * widens it back to f32 exactly before the same f32 arithmetic.
+ *
  * Pins: every function here is checked by tests against closed forms, the pages'
- * worked examples, arbitrary-precision values and an f64 brute force; no function is
- * "parity unpinned".
+ * worked examples, arbitrary-precision values, numpy's binary16 conversion and an f64
+ * brute force; no function is "parity unpinned".
  */
 #include <float.h>
 #include <math.h>
@@ -133,27 +137,88 @@ int orc_rope(float *x, int32_t nt, int32_t nh, int32_t hd, const int32_t *pos,
 /* start zeroed, so rows never written read as zeros.                              */
 /* ------------------------------------------------------------------------------ */
 
+/* Storage formats of the regions.  F16 is the half-precision cache of [MINFER-11] §2.5
+ * ("Storage") and §3.3: the store rounds each value to IEEE binary16, attention widens
+ * it back to f32 and computes in f32. */
+enum { ORC_KV_F32 = 0, ORC_KV_F16 = 1 };
+
+/* IEEE-754 binary32 -> binary16, round to nearest, ties to even; overflow gives inf,
+ * tiny values become subnormals or signed zero; NaN stays a (quiet) NaN. */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, sizeof x);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const uint32_t exp = (x >> 23) & 0xffu;
+    uint32_t man = x & 0x7fffffu;
+    if (exp == 0xffu) return (uint16_t)(sign | (man ? 0x7e00u : 0x7c00u));
+    const int32_t e = (int32_t)exp - 127 + 15;        /* binary16 biased exponent */
+    if (e >= 31) return (uint16_t)(sign | 0x7c00u);     /* beyond the largest finite */
+    if (e <= 0) {                                       /* subnormal or zero result */
+        if (e < -10) return (uint16_t)sign;             /* below half the smallest subnormal */
+        man |= 0x800000u;                               /* make the leading 1 explicit */
+        const int32_t shift = 14 - e;                   /* value = man * 2^-24 after shift */
+        uint32_t h = man >> shift;
+        const uint32_t rem = man & ((1u << shift) - 1u);
+        const uint32_t half = 1u << (shift - 1);
+        if (rem > half || (rem == half && (h & 1u))) h++;
+        return (uint16_t)(sign | h);                    /* a carry lands on the smallest normal */
+    }
+    uint32_t h = sign | ((uint32_t)e << 10) | (man >> 13);
+    const uint32_t rem = man & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h++; /* a carry may reach inf: correct */
+    return (uint16_t)h;
+}
+
+/* IEEE-754 binary16 -> binary32 (exact). */
+float orc_f16_to_f32(uint16_t h)
+{
+    const uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    uint32_t exp = ((uint32_t)h >> 10) & 0x1fu;
+    uint32_t man = (uint32_t)h & 0x3ffu;
+    uint32_t x;
+    if (exp == 0) {
+        if (man == 0) {
+            x = sign;
+        } else {                                        /* subnormal: normalise */
+            int32_t shifts = 0;
+            while (!(man & 0x400u)) { man <<= 1; shifts++; }
+            man &= 0x3ffu;
+            x = sign | ((uint32_t)(127 - 14 - shifts) << 23) | (man << 13);
+        }
+    } else if (exp == 31) {
+        x = sign | 0x7f800000u | (man << 13);
+    } else {
+        x = sign | ((exp - 15 + 127) << 23) | (man << 13);
+    }
+    float f;
+    memcpy(&f, &x, sizeof f);
+    return f;
+}
+
 typedef struct orc_cache {
-    int32_t n_seq, n_layer, n_head_kv, hd_kv, capacity;
-    size_t region;      /* floats per (seq, layer) region: capacity * n_head_kv * hd_kv */
-    float *k, *v;       /* [n_seq][n_layer][capacity][n_head_kv * hd_kv] */
+    int32_t n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype;
+    size_t region;      /* elements per (seq, layer) region: capacity * n_head_kv * hd_kv */
+    void *k, *v;        /* [n_seq][n_layer][capacity][n_head_kv * hd_kv], f32 or f16 bits */
     int32_t *hw;        /* high-water mark per (seq, layer): max written position + 1 */
 } orc_cache;
 
-orc_cache *orc_cache_new(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
-                         int32_t capacity)
+orc_cache *orc_cache_new_typed(int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
+                               int32_t hd_kv, int32_t capacity, int32_t dtype)
 {
     if (n_seq <= 0 || n_layer <= 0 || n_head_kv <= 0 || hd_kv <= 0 || (hd_kv & 1) ||
-        hd_kv > ORC_MAX_HEAD_DIM || capacity <= 0 || capacity > ORC_MAX_POSITION)
+        hd_kv > ORC_MAX_HEAD_DIM || capacity <= 0 || capacity > ORC_MAX_POSITION ||
+        (dtype != ORC_KV_F32 && dtype != ORC_KV_F16))
         return NULL;
     orc_cache *c = (orc_cache *)calloc(1, sizeof(orc_cache));
     if (!c) return NULL;
     c->n_seq = n_seq; c->n_layer = n_layer; c->n_head_kv = n_head_kv;
-    c->hd_kv = hd_kv; c->capacity = capacity;
+    c->hd_kv = hd_kv; c->capacity = capacity; c->dtype = dtype;
     c->region = (size_t)capacity * (size_t)n_head_kv * (size_t)hd_kv;
-    size_t total = (size_t)n_seq * (size_t)n_layer * c->region;
-    c->k = (float *)calloc(total, sizeof(float));
-    c->v = (float *)calloc(total, sizeof(float));
+    const size_t total = (size_t)n_seq * (size_t)n_layer * c->region;
+    const size_t esz = dtype == ORC_KV_F16 ? sizeof(uint16_t) : sizeof(float);
+    c->k = calloc(total, esz);   /* all-zero bits are +0.0 in both formats */
+    c->v = calloc(total, esz);
     c->hw = (int32_t *)calloc((size_t)n_seq * n_layer, sizeof(int32_t));
     if (!c->k || !c->v || !c->hw) {
         free(c->k); free(c->v); free(c->hw); free(c);
@@ -162,18 +227,41 @@ orc_cache *orc_cache_new(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int3
     return c;
 }
 
+orc_cache *orc_cache_new(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
+                         int32_t capacity)
+{
+    return orc_cache_new_typed(n_seq, n_layer, n_head_kv, hd_kv, capacity, ORC_KV_F32);
+}
+
 void orc_cache_free(orc_cache *c)
 {
     if (!c) return;
     free(c->k); free(c->v); free(c->hw); free(c);
 }
 
-/* which = 0 for K, 1 for V.  Returns the [capacity][n_head_kv * hd_kv] region. */
-float *orc_cache_region(orc_cache *c, int32_t which, int32_t seq, int32_t layer)
+static size_t elem_size(const orc_cache *c)
+{
+    return c->dtype == ORC_KV_F16 ? sizeof(uint16_t) : sizeof(float);
+}
+
+/* which = 0 for K, 1 for V.  Returns the [capacity][n_head_kv * hd_kv] region (f32
+ * values, or binary16 bit patterns for an f16 cache). */
+void *orc_cache_region(orc_cache *c, int32_t which, int32_t seq, int32_t layer)
 {
     if (!c || seq < 0 || seq >= c->n_seq || layer < 0 || layer >= c->n_layer) return NULL;
-    float *base = which ? c->v : c->k;
-    return base + ((size_t)seq * c->n_layer + layer) * c->region;
+    char *base = (char *)(which ? c->v : c->k);
+    return base + ((size_t)seq * c->n_layer + layer) * c->region * elem_size(c);
+}
+
+/* Write n f32 values into a region at element offset off, in the cache's format. */
+static void store_values(orc_cache *c, void *region, size_t off, const float *src, int32_t n)
+{
+    if (c->dtype == ORC_KV_F16) {
+        uint16_t *d = (uint16_t *)region + off;
+        for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[i]);
+    } else {
+        memcpy((float *)region + off, src, sizeof(float) * (size_t)n);
+    }
 }
 
 int32_t orc_cache_seq_len(const orc_cache *c, int32_t seq, int32_t layer)
@@ -238,10 +326,9 @@ int orc_append_rope(orc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_
         memcpy(row, k + (size_t)t * nkt, sizeof(float) * (size_t)nkt);
         int st = orc_rope(row, 1, c->n_head_kv, c->hd_kv, &pos[t], freq_base, freq_scale, style);
         if (st != ORC_OK) { free(row); return st; }
-        float *kd = orc_cache_region(c, 0, seq_ids[t], layer) + (size_t)pos[t] * nkt;
-        float *vd = orc_cache_region(c, 1, seq_ids[t], layer) + (size_t)pos[t] * nkt;
-        memcpy(kd, row, sizeof(float) * (size_t)nkt);
-        memcpy(vd, v + (size_t)t * nkt, sizeof(float) * (size_t)nkt);
+        const size_t off = (size_t)pos[t] * nkt;
+        store_values(c, orc_cache_region(c, 0, seq_ids[t], layer), off, row, nkt);
+        store_values(c, orc_cache_region(c, 1, seq_ids[t], layer), off, v + (size_t)t * nkt, nkt);
         int32_t *hw = &c->hw[(size_t)seq_ids[t] * c->n_layer + layer];
         if (pos[t] + 1 > *hw) *hw = pos[t] + 1;
     }
@@ -262,6 +349,18 @@ static float dot_f32(int32_t n, const float *a, const float *b)
     return s;
 }
 
+/* Kv head hk of row j of a region as f32 values: the region itself for an f32 cache,
+ * the binary16 values widened into buf for an f16 cache. */
+static const float *head_row(const void *reg, int32_t dtype, size_t j, int32_t nkt, int32_t hk,
+                             int32_t hd_kv, float *buf)
+{
+    const size_t off = j * (size_t)nkt + (size_t)hk * hd_kv;
+    if (dtype == ORC_KV_F32) return (const float *)reg + off;
+    const uint16_t *h = (const uint16_t *)reg + off;
+    for (int32_t d = 0; d < hd_kv; d++) buf[d] = orc_f16_to_f32(h[d]);
+    return buf;
+}
+
 /* One query row against rows [0, vl) of one kv head's slice of the regions.
  *   score_j = (q . k_j) * scale                 (f32)
  *   e_j     = exp(score_j - max_j score_j)      (f32)
@@ -270,13 +369,13 @@ static float dot_f32(int32_t n, const float *a, const float *b)
  *   out     = sum_j w_j * v_j, in j order        (f32)
  * Rows at or beyond vl are the masked tail: their weight is exp(-inf) = 0 exactly and
  * their zero contribution is not formed. */
-static void attend_row(const float *qrow, const float *kreg, const float *vreg, int32_t nkt,
-                       int32_t hk, int32_t hd_kv, int32_t vl, float scale, float *scr,
-                       float *out)
+static void attend_row(const float *qrow, const void *kreg, const void *vreg, int32_t dtype,
+                       int32_t nkt, int32_t hk, int32_t hd_kv, int32_t vl, float scale,
+                       float *scr, float *rowbuf, float *out)
 {
     float mx = -INFINITY;
     for (int32_t j = 0; j < vl; j++) {
-        const float *kr = kreg + (size_t)j * nkt + (size_t)hk * hd_kv;
+        const float *kr = head_row(kreg, dtype, (size_t)j, nkt, hk, hd_kv, rowbuf);
         float s = dot_f32(hd_kv, qrow, kr) * scale;
         scr[j] = s;
         if (s > mx) mx = s;
@@ -291,7 +390,7 @@ static void attend_row(const float *qrow, const float *kreg, const float *vreg, 
     for (int32_t j = 0; j < vl; j++) scr[j] *= inv;
     for (int32_t d = 0; d < hd_kv; d++) out[d] = 0.0f;
     for (int32_t j = 0; j < vl; j++) {
-        const float *vr = vreg + (size_t)j * nkt + (size_t)hk * hd_kv;
+        const float *vr = head_row(vreg, dtype, (size_t)j, nkt, hk, hd_kv, rowbuf);
         float w = scr[j];
         for (int32_t d = 0; d < hd_kv; d++) out[d] += w * vr[d];
     }
@@ -307,7 +406,7 @@ static int check_heads(const orc_cache *c, int32_t n_head, int32_t hd)
 
 /* Work unit: one (token, query head) row.  Units never reduce against each other and
  * each owns its scratch, so the result is the same at any thread count. */
-static int attend_units(const float *const *kregs, const float *const *vregs,
+static int attend_units(const void *const *kregs, const void *const *vregs, int32_t dtype,
                         const int32_t *pos, int32_t nt, const float *q, int32_t n_head,
                         int32_t hd, int32_t n_head_kv, int32_t hd_kv, int32_t max_vl,
                         float scale, float *out, int32_t nthreads)
@@ -322,7 +421,8 @@ static int attend_units(const float *const *kregs, const float *const *vregs,
 #endif
     {
         float *scr = (float *)malloc(sizeof(float) * (size_t)(max_vl > 0 ? max_vl : 1));
-        if (!scr) {
+        float *rowbuf = (float *)malloc(sizeof(float) * (size_t)hd_kv);
+        if (!scr || !rowbuf) {
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
@@ -335,11 +435,13 @@ static int attend_units(const float *const *kregs, const float *const *vregs,
                 int32_t t = (int32_t)(u / n_head), h = (int32_t)(u % n_head);
                 int32_t hk = h / gqa;
                 int32_t vl = pos[t] + 1;
-                attend_row(q + ((size_t)t * n_head + h) * hd, kregs[t], vregs[t], nkt, hk,
-                           hd_kv, vl, scale, scr, out + ((size_t)t * n_head + h) * hd_kv);
+                attend_row(q + ((size_t)t * n_head + h) * hd, kregs[t], vregs[t], dtype, nkt,
+                           hk, hd_kv, vl, scale, scr, rowbuf,
+                           out + ((size_t)t * n_head + h) * hd_kv);
             }
-            free(scr);
         }
+        free(scr);
+        free(rowbuf);
     }
     (void)nthreads;
     return failed ? ORC_E_NOMEM : ORC_OK;
@@ -363,14 +465,14 @@ int orc_attn_prefill(const orc_cache *c, int32_t seq, int32_t layer, int32_t nt,
         if (pos[t] < 0 || pos[t] >= c->capacity) return ORC_E_RANGE;
         if (pos[t] + 1 > max_vl) max_vl = pos[t] + 1;
     }
-    const float **kr = (const float **)malloc(sizeof(float *) * (size_t)nt);
-    const float **vr = (const float **)malloc(sizeof(float *) * (size_t)nt);
+    const void **kr = (const void **)malloc(sizeof(void *) * (size_t)nt);
+    const void **vr = (const void **)malloc(sizeof(void *) * (size_t)nt);
     if (!kr || !vr) { free(kr); free(vr); return ORC_E_NOMEM; }
-    const float *kreg = orc_cache_region((orc_cache *)c, 0, seq, layer);
-    const float *vreg = orc_cache_region((orc_cache *)c, 1, seq, layer);
+    const void *kreg = orc_cache_region((orc_cache *)c, 0, seq, layer);
+    const void *vreg = orc_cache_region((orc_cache *)c, 1, seq, layer);
     for (int32_t t = 0; t < nt; t++) { kr[t] = kreg; vr[t] = vreg; }
-    st = attend_units(kr, vr, pos, nt, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl, scale,
-                      out, nthreads);
+    st = attend_units(kr, vr, c->dtype, pos, nt, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl,
+                      scale, out, nthreads);
     free(kr); free(vr);
     return st;
 }
@@ -394,15 +496,15 @@ int orc_attn_decode(const orc_cache *c, int32_t layer, int32_t n_seq, const int3
         if (pos[b] < 0 || pos[b] >= c->capacity) return ORC_E_RANGE;
         if (pos[b] + 1 > max_vl) max_vl = pos[b] + 1;
     }
-    const float **kr = (const float **)malloc(sizeof(float *) * (size_t)n_seq);
-    const float **vr = (const float **)malloc(sizeof(float *) * (size_t)n_seq);
+    const void **kr = (const void **)malloc(sizeof(void *) * (size_t)n_seq);
+    const void **vr = (const void **)malloc(sizeof(void *) * (size_t)n_seq);
     if (!kr || !vr) { free(kr); free(vr); return ORC_E_NOMEM; }
     for (int32_t b = 0; b < n_seq; b++) {
         kr[b] = orc_cache_region((orc_cache *)c, 0, seq_ids[b], layer);
         vr[b] = orc_cache_region((orc_cache *)c, 1, seq_ids[b], layer);
     }
-    st = attend_units(kr, vr, pos, n_seq, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl, scale,
-                      out, nthreads);
+    st = attend_units(kr, vr, c->dtype, pos, n_seq, q, n_head, hd, c->n_head_kv, c->hd_kv,
+                      max_vl, scale, out, nthreads);
     free(kr); free(vr);
     return st;
 }

@@ -19,8 +19,8 @@ import os
 import mpmath
 import numpy as np
 
-from oracle import (E_ARG, E_DUP, E_GEOMETRY, E_RANGE, OK, ROPE_INTERLEAVED, ROPE_NEOX,
-                    ROPE_NONE, Oracle, OracleCache)
+from oracle import (E_ARG, E_DUP, E_GEOMETRY, E_RANGE, KV_F16, OK, ROPE_INTERLEAVED,
+                    ROPE_NEOX, ROPE_NONE, Oracle, OracleCache)
 from tests import bruteforce as bf
 from tests.workloads import custom, custom_positions
 
@@ -398,6 +398,75 @@ def pin_attn_errors(o: Oracle):
     c.close()
 
 
+# ------------------------------------------------------------------------------------
+# Half-precision cache ("11 · Attention, vec ops, and the KV cache" §2.5 and §3.3: the GPU
+# backends may keep K/V in f16 to halve the bytes; arithmetic stays f32)
+# ------------------------------------------------------------------------------------
+
+def f16_edge_values():
+    """f32 values at every kind of binary16 rounding boundary."""
+    h = np.arange(0, 0x7c00, dtype=np.uint32)              # every finite positive half
+    lo = h[:-1].astype(np.uint16).view(np.float16).astype(np.float64)
+    hi = h[1:].astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = ((lo + hi) / 2)                                 # exact ties (representable in f32)
+    sel = np.linspace(0, len(mids) - 1, 4000).astype(int)
+    vals = np.concatenate([mids[sel], np.nextafter(mids[sel], 0), np.nextafter(mids[sel], 1),
+                           [0.0, 65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+                            1.5 * 2.0 ** -24, 2.0 ** -26, 2.0 ** -14, 1e-30, 3.1e-5, 6.1e-5]])
+    vals = vals.astype(np.float32)
+    return np.concatenate([vals, -vals, [np.inf, -np.inf]]).astype(np.float32)
+
+
+def pin_f16_round_to_nearest_even(o: Oracle):
+    """f32 -> binary16 equals IEEE round-to-nearest-even (numpy's float16 conversion) on
+    every tie and its neighbours, overflow, subnormals, zeros and a wide random sample."""
+    x = np.concatenate([f16_edge_values(),
+                        (np.random.default_rng(3).standard_normal(6000) *
+                         np.repeat([1e-7, 1e-4, 1.0, 1e3, 3e4, 7e4], 1000)).astype(np.float32)])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = o.f32_to_f16(x)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def pin_f16_widening_exact(o: Oracle):
+    """binary16 -> f32 is exact for all 63,488 finite patterns (and keeps inf)."""
+    h = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (h & 0x7c00) != 0x7c00
+    hs = np.concatenate([h[finite], np.array([0x7c00, 0xfc00], np.uint16)])
+    want = hs.view(np.float16).astype(np.float32)
+    got = o.f16_to_f32(hs)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def pin_f16_cache_store_and_attention(o: Oracle):
+    """An f16 cache stores binary16(rot(k)) and binary16(v) (rot pinned above), and its
+    attention equals the f64 brute force over the widened rows."""
+    cap, nkv, hdk = 24, 2, 16
+    k = custom(60, (cap, nkv, hdk)) * 3
+    v = custom(61, (cap, nkv, hdk))
+    c32 = OracleCache(1, 1, nkv, hdk, cap, o)
+    c16 = OracleCache(1, 1, nkv, hdk, cap, o, dtype=KV_F16)
+    for c in (c32, c16):
+        st, _ = c.append_rope(0, [0] * cap, np.arange(cap), None, 0, 0, k, v, 1e4, 1.0, ROPE_NEOX)
+        assert st == OK
+    assert np.array_equal(c16.k(0, 0), c32.k(0, 0).astype(np.float16).view(np.uint16))
+    assert np.array_equal(c16.v(0, 0), v.reshape(cap, -1).astype(np.float16).view(np.uint16))
+    K = c16.k(0, 0).view(np.float16).astype(np.float64)
+    V = c16.v(0, 0).view(np.float16).astype(np.float64)
+    q = custom(62, (6, 4, 16))
+    pos = [0, 5, 9, 17, 23, 23]
+    st, out = c16.attn_prefill(0, 0, pos, q, 4, 16, 0.3)
+    assert st == OK
+    want = bf.attention_bf(q, K, V, pos, nkv, 0.3)
+    assert np.abs(out - want).max() <= 1e-6 + 1e-5 * np.abs(want).max()
+    st, outd = c16.attn_decode(0, [0] * 6, pos, q, 4, 16, 0.3)
+    assert st == OK and np.array_equal(outd.view(np.uint32), out.view(np.uint32))
+    c32.close()
+    c16.close()
+
+
 ALL_PINS = [
     pin_inv_freq_correctly_rounded,
     pin_rope_worked_example,
@@ -416,4 +485,7 @@ ALL_PINS = [
     pin_attn_large_scores_stable,
     pin_attn_thread_invariance,
     pin_attn_errors,
+    pin_f16_round_to_nearest_even,
+    pin_f16_widening_exact,
+    pin_f16_cache_store_and_attention,
 ]

@@ -25,9 +25,9 @@ MUTANTS = {
     "angle_in_f64": ("cs[i] = (float)cosl((long double)theta);",
                      "cs[i] = (float)cosl((long double)p * (long double)inv[i]);"),
     # Store
-    "store_v_from_k": ("memcpy(vd, v + (size_t)t * nkt", "memcpy(vd, k + (size_t)t * nkt"),
-    "store_off_by_one_row": ("+ (size_t)pos[t] * nkt;\n        float *vd",
-                             "+ (size_t)(pos[t] > 0 ? pos[t] - 1 : 0) * nkt;\n        float *vd"),
+    "store_v_from_k": ("off, v + (size_t)t * nkt, nkt);", "off, k + (size_t)t * nkt, nkt);"),
+    "store_off_by_one_row": ("const size_t off = (size_t)pos[t] * nkt;",
+                             "const size_t off = (size_t)(pos[t] > 0 ? pos[t] - 1 : 0) * nkt;"),
     "k_not_rotated": ("int st = orc_rope(row, 1,", "int st = 0 * orc_rope(row, 0,"),
     "high_water_off": ("if (pos[t] + 1 > *hw) *hw = pos[t] + 1;", "if (pos[t] > *hw) *hw = pos[t];"),
     "no_range_check": ("if (pos[t] < 0 || pos[t] >= c->capacity) return ORC_E_RANGE;\n    int64_t",
@@ -37,10 +37,18 @@ MUTANTS = {
     "window_drops_current_row": ("int32_t vl = pos[t] + 1;", "int32_t vl = pos[t] > 0 ? pos[t] : 1;"),
     "no_scale": ("float s = dot_f32(hd_kv, qrow, kr) * scale;", "float s = dot_f32(hd_kv, qrow, kr);"),
     "no_max_subtraction": ("float e = expf(scr[j] - mx);", "float e = expf(scr[j]);"),
-    "v_from_k_region": ("const float *vr = vreg + (size_t)j * nkt", "const float *vr = kreg + (size_t)j * nkt"),
-    "dot_over_hd_stride": ("(size_t)j * nkt + (size_t)hk * hd_kv;\n        float s",
-                           "(size_t)j * hd_kv + (size_t)hk * hd_kv;\n        float s"),
+    "v_from_k_region": ("const float *vr = head_row(vreg,", "const float *vr = head_row(kreg,"),
+    "row_stride": ("const size_t off = j * (size_t)nkt + (size_t)hk * hd_kv;",
+                   "const size_t off = j * (size_t)hd_kv + (size_t)hk * hd_kv;"),
     "no_normalisation": ("for (int32_t j = 0; j < vl; j++) scr[j] *= inv;", ""),
+    # Half-precision cache
+    "f16_truncates": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h++;", ""),
+    "f16_ties_away": ("(rem == 0x1000u && (h & 1u))", "(rem == 0x1000u)"),
+    "f16_subnormal_shift": ("const int32_t shift = 14 - e;", "const int32_t shift = 13 - e;"),
+    "f16_widen_bias": ("x = sign | ((exp - 15 + 127) << 23) | (man << 13);",
+                       "x = sign | ((exp - 16 + 127) << 23) | (man << 13);"),
+    "f16_store_skipped": ("for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[i]);",
+                          "for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[0]);"),
 }
 
 
