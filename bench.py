@@ -21,7 +21,7 @@ Reported:
                  profiles/ (null once the kernel sources differ from the profiled ones)
   cpu_baseline   the plain C oracle on the host cores, on a bounded sample
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--kv f16]
 """
 from __future__ import annotations
 
@@ -53,6 +53,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--kv", choices=["f32", "f16"], default="f32",
+                    help="region format: f32, or binary16 (half the bytes; arithmetic in f32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before timing, so that "
                          "HBM counters (FETCH_SIZE / WRITE_SIZE) can be calibrated against "
@@ -75,7 +77,8 @@ def main():
     lens = n_past.copy()
     lens[0] += nt
     seqs = np.arange(w.n_seq, dtype=np.int32)
-    kv_bytes = int((lens.astype(np.int64) + 1).sum()) * 2 * w.n_head_kv * w.hd_kv * 4
+    esize = 2 if args.kv == "f16" else 4
+    kv_bytes = int((lens.astype(np.int64) + 1).sum()) * 2 * w.n_head_kv * w.hd_kv * esize
     pre_flops = 4 * w.n_head * w.hd_kv * int((pre_pos.astype(np.int64) + 1).sum())
 
     torch.cuda.init()
@@ -83,11 +86,13 @@ def main():
     dev = torch.device("cuda:0")
     log(f"bench: workload {w.name}; filling {int(n_past.sum())} cached rows")
     t0 = time.time()
-    cache = kvc.kv_alloc(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    kv_dtype = kvc.KV_F16 if args.kv == "f16" else kvc.KV_F32
+    cache = kvc.kv_alloc(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv_dtype)
     orc_cache = None
     if not args.no_cpu_baseline:
         from oracle import OracleCache
-        orc_cache = OracleCache(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+        orc_cache = OracleCache(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity,
+                                dtype=kv_dtype)
     chunk = w.extra["fill_chunk"]
     for s in range(w.n_seq):
         for ci, r0 in enumerate(range(0, int(n_past[s]), chunk)):
@@ -151,7 +156,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     dec_gbs = kv_bytes / (t_dec.mean() * 1e-3) / 1e9
     pre_tflops = pre_flops / (t_pre.mean() * 1e-3) / 1e12
-    app_bytes = nt * (2 * w.n_head * w.hd + 4 * w.n_head_kv * w.hd_kv) * 4
+    app_bytes = nt * (2 * w.n_head * w.hd + 2 * w.n_head_kv * w.hd_kv) * 4 + \
+        nt * 2 * w.n_head_kv * w.hd_kv * esize
     log(f"bench: step {ms_per_step:.3f} ms (events {t_step.mean():.3f}); append+rope(4096) "
         f"{t_app_pre.mean() * 1e3:.1f} us, prefill {t_pre.mean():.3f} ms, append(32) "
         f"{t_app_dec.mean() * 1e3:.1f} us, decode {t_dec.mean() * 1e3:.1f} us")
@@ -167,12 +173,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # arithmetic; the region format is config.kv_dtype
         "data": "synthetic (seeded N(0,1) q/k/v and cache rows)",
         "config": {
             "workload": "qwen3-0.6b-batch: 32 sequences, 16 q heads / 8 kv heads, head dim 128, "
                         "ragged n_past U[128,8192]; 4096-token continuation prefill on seq 0 + "
                         "one decode step for all 32",
+            "kv_dtype": args.kv,
             "n_seq": int(w.n_seq), "n_head": w.n_head, "n_head_kv": w.n_head_kv,
             "hd": w.hd, "hd_kv": w.hd_kv, "capacity": w.capacity,
             "n_past_seq0": int(n_past[0]), "prefill_tokens": nt,
@@ -195,7 +202,7 @@ def main():
             "peak": FP32_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("prefill"),
+            "traffic": measured_traffic("prefill") if args.kv == "f32" else None,
             "flops_per_launch": pre_flops,
             "avg_launch_us": round(float(t_pre.mean()) * 1e3, 2),
         },
@@ -206,7 +213,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode"),
+            "traffic": measured_traffic("decode") if args.kv == "f32" else None,
             "bytes_per_launch": kv_bytes,
             "avg_launch_us": round(float(t_dec.mean()) * 1e3, 2),
         },

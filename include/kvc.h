@@ -7,8 +7,8 @@
  *                   in place at those positions
  *   gqa_attn_prefill  nt query tokens of one sequence, token t attending rows [0, pos[t]]
  *   gqa_attn_decode   one query token per sequence for a batch of sequences
- * plus kv_free, kv_view, kv_seq_len and kv_last_error for ownership, inspection and
- * error text.
+ * plus kv_alloc_typed (half-precision regions), kv_free, kv_view, kv_seq_len and
+ * kv_last_error for storage format, ownership, inspection and error text.
  *
  * Sources (page titles; sections named per declaration):
  *   [MINFER-11] "11 · Attention, vec ops, and the KV cache"
@@ -16,7 +16,8 @@
  *   [MINFER-13] "13 · The decode loop and graph reuse"
  *
  * Conventions for every call
- *   - All tensors are f32.  "device" pointers are HIP device memory; "host" pointers are
+ *   - q, k, v and out are f32 (the cache regions are f32 or binary16, see kvc_kv_dtype).
+ *     "device" pointers are HIP device memory; "host" pointers are
  *     ordinary host memory, read before the call returns (the caller may reuse them at
  *     once).  Device buffers must stay valid until the work queued on `stream` is done.
  *   - Device pointers must be 16-byte aligned and the tensors dense (row-major, no gaps).
@@ -63,6 +64,15 @@ typedef enum kvc_rope_style {
     KVC_ROPE_NONE = 2         /* no rotation: a plain store of k and v, q untouched */
 } kvc_rope_style;
 
+/* Element format of the K and V regions.  F16 is the half-precision cache
+ * ([MINFER-11] §2.5 "Storage" and §3.3): the store rounds each rotated k value and each
+ * v value to IEEE binary16 (nearest, ties to even); attention widens them back to f32
+ * and computes in f32.  It halves the bytes decode attention reads. */
+typedef enum kvc_kv_dtype {
+    KVC_KV_F32 = 0,
+    KVC_KV_F16 = 1
+} kvc_kv_dtype;
+
 #define KVC_MAX_HEAD_DIM 256
 #define KVC_MAX_CAPACITY (1 << 24)
 
@@ -92,6 +102,15 @@ kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_h
                     int32_t hd_kv, int32_t capacity, void *stream);
 
 /*
+ * kv_alloc_typed -- kv_alloc with an explicit region element format (kv_alloc is
+ * kv_alloc_typed with KVC_KV_F32).  With KVC_KV_F16 every region element is 2 bytes;
+ * everything else (layout, calls, errors) is as for kv_alloc.
+ * Errors: as kv_alloc, plus KVC_E_ARG for an unknown format.
+ */
+kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
+                          int32_t hd_kv, int32_t capacity, kvc_kv_dtype dtype, void *stream);
+
+/*
  * kv_free -- wait for the device, then release every region, table and scratch buffer.
  * Pointers from kv_view become invalid.  NULL is accepted (no-op).
  */
@@ -100,12 +119,12 @@ kvc_status kv_free(kvc_cache *c);
 /*
  * kv_view -- borrow one (sequence, layer)'s regions without copying ([ZEROCOPY]
  * "Reading without copying": a live reference into the cache's own storage).
- *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] f32 (the
- *         region's first capacity rows).  The pointers never change for the handle's
- *         life and stay owned by it.
+ *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] elements
+ *         (f32, or binary16 for a KVC_KV_F16 cache; the region's first capacity rows).
+ *         The pointers never change for the handle's life and stay owned by it.
  * Errors: KVC_E_ARG for a NULL handle/pointer or seq/layer out of range.
  */
-kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, float **k, float **v);
+kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, void **k, void **v);
 
 /*
  * kv_seq_len -- high-water mark of one (sequence, layer): 1 + the largest position ever

@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkvc.so")
 
 OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM, E_HIP = range(7)
 ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
+KV_F32, KV_F16 = 0, 1
 STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANGE",
                 4: "KVC_E_DUP", 5: "KVC_E_NOMEM", 6: "KVC_E_HIP"}
 
 # Every symbol include/kvc.h declares.
-EXPORTS = ("kv_alloc", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
+EXPORTS = ("kv_alloc", "kv_alloc_typed", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
            "gqa_attn_prefill", "gqa_attn_decode", "kv_last_error")
 
 
@@ -55,6 +56,7 @@ def lib(path: str = LIB_PATH):
     i32, f32, p = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     sig = {
         "kv_alloc": [ctypes.POINTER(p), i32, i32, i32, i32, i32, p],
+        "kv_alloc_typed": [ctypes.POINTER(p), i32, i32, i32, i32, i32, ctypes.c_int, p],
         "kv_free": [p],
         "kv_view": [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(p)],
         "kv_seq_len": [p, i32, i32, ctypes.POINTER(i32)],
@@ -108,15 +110,22 @@ def _host_i32(a):
 
 
 class Cache:
-    """Owning wrapper of a kvc_cache handle (kv_free on close / garbage collection)."""
+    """Owning wrapper of a kvc_cache handle (kv_free on close / garbage collection).
+    dtype KV_F32 (kv_alloc) or KV_F16 (binary16 regions, kv_alloc_typed)."""
 
-    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None):
+    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None, dtype=KV_F32):
         self.n_seq, self.n_layer = n_seq, n_layer
         self.n_head_kv, self.hd_kv, self.capacity = n_head_kv, hd_kv, capacity
         self.nkt = n_head_kv * hd_kv
+        self.dtype = dtype
         h = ctypes.c_void_p()
-        _check(lib().kv_alloc(ctypes.byref(h), n_seq, n_layer, n_head_kv, hd_kv, capacity,
-                              _stream(stream)))
+        if dtype == KV_F32:
+            st = lib().kv_alloc(ctypes.byref(h), n_seq, n_layer, n_head_kv, hd_kv, capacity,
+                                _stream(stream))
+        else:
+            st = lib().kv_alloc_typed(ctypes.byref(h), n_seq, n_layer, n_head_kv, hd_kv,
+                                      capacity, dtype, _stream(stream))
+        _check(st)
         self.handle = h.value
 
     def close(self):
@@ -137,8 +146,8 @@ class Cache:
         self.close()
 
 
-def kv_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None) -> Cache:
-    return Cache(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream)
+def kv_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None, dtype=KV_F32) -> Cache:
+    return Cache(n_seq, n_layer, n_head_kv, hd_kv, capacity, stream, dtype)
 
 
 def kv_free(c: Cache):
@@ -191,7 +200,8 @@ _hip = None
 
 def kv_read(c: Cache, seq: int, layer: int, stream=None):
     """Copies (device to device, on `stream`) of one (seq, layer)'s K and V regions as
-    [capacity][n_head_kv * hd_kv] torch tensors.  For inspection and tests."""
+    [capacity][n_head_kv * hd_kv] torch tensors (float32, or float16 for a binary16
+    cache).  For inspection and tests."""
     global _hip
     import torch
     if _hip is None:
@@ -202,8 +212,10 @@ def kv_read(c: Cache, seq: int, layer: int, stream=None):
     kp, vp = kv_view(c, seq, layer)
     out = []
     for src in (kp, vp):
-        t = torch.empty((c.capacity, c.nkt), dtype=torch.float32, device="cuda")
-        e = _hip.hipMemcpyAsync(t.data_ptr(), src, c.capacity * c.nkt * 4, 3, _stream(stream))
+        dt = torch.float16 if c.dtype == KV_F16 else torch.float32
+        t = torch.empty((c.capacity, c.nkt), dtype=dt, device="cuda")
+        e = _hip.hipMemcpyAsync(t.data_ptr(), src, c.capacity * c.nkt * t.element_size(), 3,
+                                _stream(stream))
         if e != 0:
             raise RuntimeError(f"hipMemcpyAsync failed: {e}")
         out.append(t)

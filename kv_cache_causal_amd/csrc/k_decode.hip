@@ -13,9 +13,10 @@
 //   * Workgroup = one (batch entry, kv head, chunk of rows); 4 wave64s.  Chunks are sized
 //     on the host so the grid fills the chip several times over; the workgroups of one
 //     chunk's kv heads are adjacent in dispatch order (DRAM page locality).
-//   * A row slice (hd_kv floats of one kv head) is read by a group of LPR lanes, each
-//     holding 8 dims as two float4 loads (4 dims for groups of 3+ heads, to save
-//     registers); one load instruction across the wave
+//   * A row slice (hd_kv values of one kv head) is read by a group of LPR lanes, each
+//     holding 8 dims (4 for groups of 3+ heads, to save registers): two float4 loads for
+//     an f32 cache, one 16-byte load of packed halves for a binary16 cache (widened to
+//     f32 as they are used); one load instruction across the wave
 //     covers 64/LPR rows, whole 128-byte lines.  Two register sets of 4 rows per lane
 //     group alternate, so one set's loads are in flight while the other is reduced.
 //   * The query vectors of every head of the kv group (up to 8 per pass) stay in
@@ -73,6 +74,62 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// How a lane group reads its DPL dims of a row slice (LPR lanes per row).  Raw is what
+// one row occupies in registers until it is used (binary16 stays packed); dim(li, i) is
+// the head dim of the lane's i-th value, so q is loaded in the same order.
+//   f32, 8 dims: two float4 at li*4 and 4*LPR + li*4 (each load instruction covers whole
+//                lines of several rows);  f32, 4 dims: one float4 at li*4;
+//   f16, 8 dims: one 16-byte load of 8 halves at li*8;  f16, 4 dims: 4 halves at li*4.
+template <typename KVT, int DPL, int LPR>
+struct RowIO;
+template <int LPR>
+struct RowIO<float, 8, LPR> {
+    struct Raw { floatx4 a, b; };
+    static __device__ __forceinline__ Raw load(const float *row, int li)
+    {
+        Raw r;
+        r.a = *reinterpret_cast<const floatx4 *>(row + li * 4);
+        r.b = *reinterpret_cast<const floatx4 *>(row + 4 * LPR + li * 4);
+        return r;
+    }
+    static __device__ __forceinline__ float get(const Raw &r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
+    static __device__ __forceinline__ int dim(int li, int i) { return (i / 4) * 4 * LPR + li * 4 + (i % 4); }
+};
+template <int LPR>
+struct RowIO<float, 4, LPR> {
+    typedef floatx4 Raw;
+    static __device__ __forceinline__ Raw load(const float *row, int li)
+    {
+        return *reinterpret_cast<const floatx4 *>(row + li * 4);
+    }
+    static __device__ __forceinline__ float get(const Raw &r, int i) { return r[i]; }
+    static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
+};
+template <int LPR>
+struct RowIO<_Float16, 8, LPR> {
+    typedef half8_t Raw;
+    static __device__ __forceinline__ Raw load(const _Float16 *row, int li)
+    {
+        return *reinterpret_cast<const half8_t *>(row + li * 8);
+    }
+    static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
+    static __device__ __forceinline__ int dim(int li, int i) { return li * 8 + i; }
+};
+template <int LPR>
+struct RowIO<_Float16, 4, LPR> {
+    typedef half4_t Raw;
+    static __device__ __forceinline__ Raw load(const _Float16 *row, int li)
+    {
+        return *reinterpret_cast<const half4_t *>(row + li * 4);
+    }
+    static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
+    static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
+};
+
 // Merge (m2, l2) into (m, l) in base-2 units; returns the scale factors for acc.
 __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2, float &a,
                                           float &b)
@@ -85,13 +142,14 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
     m = mn;
 }
 
-template <int HD, int GP>
+template <int HD, int GP, typename KVT>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
 {
     constexpr int kDimsPerLane = dims_per_lane<GP>();
     constexpr int LPR = HD / kDimsPerLane;   // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave per unrolled step
-    constexpr int NF4 = kDimsPerLane / 4;
+    using IO = RowIO<KVT, kDimsPerLane, LPR>;
+    using Raw = typename IO::Raw;
     static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "head dim");
 
     const int lane = threadIdx.x & 63;
@@ -119,21 +177,17 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const int seq = p.seq[b];
     const int nkt = p.n_head_kv * HD;
     const int64_t region = ((int64_t)seq * p.n_layer + p.layer) * p.region;
-    const float *K = p.kc + region + hk * HD;
-    const float *V = p.vc + region + hk * HD;
+    const KVT *K = static_cast<const KVT *>(p.kc) + region + hk * HD;
+    const KVT *V = static_cast<const KVT *>(p.vc) + region + hk * HD;
 
-    // Lane dims: d(c, e) = c * 4 * LPR + li * 4 + e, so one float4 load across the LPR
-    // lanes of a row covers 16 * LPR contiguous bytes.
+    // The lane's query values in the order its row values arrive (IO::dim).
     float qf[GP][kDimsPerLane];
 #pragma unroll
     for (int g = 0; g < GP; g++) {
         const bool ok = g0 + g < G;
         const float *qrow = p.q + ((int64_t)b * p.n_head + (hk * G + (ok ? g0 + g : 0))) * p.hd;
 #pragma unroll
-        for (int c = 0; c < NF4; c++)
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                qf[g][c * 4 + e] = ok ? qrow[c * 4 * LPR + li * 4 + e] * p.qscale : 0.0f;
+        for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = ok ? qrow[IO::dim(li, i)] * p.qscale : 0.0f;
     }
 
     float m[GP], l[GP], acc[GP][kDimsPerLane];
@@ -149,25 +203,19 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     // loads of step i+1 are in flight while step i is reduced.
     constexpr int BR = kWaves * RPW * kUnroll;
     const int nsteps = (r1 - r0 + BR - 1) / BR;
-    float4 kA[kUnroll][NF4], vA[kUnroll][NF4], kB[kUnroll][NF4], vB[kUnroll][NF4];
+    Raw kA[kUnroll], vA[kUnroll], kB[kUnroll], vB[kUnroll];
 
-    auto load = [&](float4 (&kf)[kUnroll][NF4], float4 (&vf)[kUnroll][NF4], int step) {
+    auto load = [&](Raw (&kf)[kUnroll], Raw (&vf)[kUnroll], int step) {
         const int rb = r0 + step * BR;
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             int row = rb + (u * kWaves + wave) * RPW + rg;
             row = row < r1 ? row : r0;  // rows past the chunk re-read row r0 and are masked
-            const float *kr = K + (int64_t)row * nkt + li * 4;
-            const float *vr = V + (int64_t)row * nkt + li * 4;
-#pragma unroll
-            for (int c = 0; c < NF4; c++) {
-                kf[u][c] = *reinterpret_cast<const float4 *>(kr + c * 4 * LPR);
-                vf[u][c] = *reinterpret_cast<const float4 *>(vr + c * 4 * LPR);
-            }
+            kf[u] = IO::load(K + (int64_t)row * nkt, li);
+            vf[u] = IO::load(V + (int64_t)row * nkt, li);
         }
     };
-    auto consume = [&](const float4 (&kf)[kUnroll][NF4], const float4 (&vf)[kUnroll][NF4],
-                       int step) {
+    auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], int step) {
         const int rb = r0 + step * BR;
         float sc[kUnroll][GP];
 #pragma unroll
@@ -177,12 +225,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             for (int g = 0; g < GP; g++) {
                 float s = 0.0f;
 #pragma unroll
-                for (int c = 0; c < NF4; c++) {
-                    s += qf[g][c * 4 + 0] * kf[u][c].x;
-                    s += qf[g][c * 4 + 1] * kf[u][c].y;
-                    s += qf[g][c * 4 + 2] * kf[u][c].z;
-                    s += qf[g][c * 4 + 3] * kf[u][c].w;
-                }
+                for (int i = 0; i < kDimsPerLane; i++) s += qf[g][i] * IO::get(kf[u], i);
                 s = group_sum<LPR>(s);
                 sc[u][g] = valid ? s : -INFINITY;
             }
@@ -203,12 +246,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
                 const float pu = fast_exp2(sc[u][g] - ref);
                 l[g] += pu;
 #pragma unroll
-                for (int c = 0; c < NF4; c++) {
-                    acc[g][c * 4 + 0] += pu * vf[u][c].x;
-                    acc[g][c * 4 + 1] += pu * vf[u][c].y;
-                    acc[g][c * 4 + 2] += pu * vf[u][c].z;
-                    acc[g][c * 4 + 3] += pu * vf[u][c].w;
-                }
+                for (int i = 0; i < kDimsPerLane; i++) acc[g][i] += pu * IO::get(vf[u], i);
             }
             m[g] = mn;
         }
@@ -250,9 +288,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
                 sm[wave][g][1] = l[g];
             }
 #pragma unroll
-            for (int c = 0; c < NF4; c++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) sm[wave][g][2 + c * 4 * LPR + li * 4 + e] = acc[g][c * 4 + e];
+            for (int i = 0; i < kDimsPerLane; i++) sm[wave][g][2 + IO::dim(li, i)] = acc[g][i];
         }
     }
     __syncthreads();
@@ -362,18 +398,25 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
     }
 }
 
-template <int HD>
-hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
+template <int HD, typename KVT>
+void launch_split(const DecodeParams &p, hipStream_t s)
 {
     const int G = p.n_head / p.n_head_kv;
     const dim3 grid((unsigned)p.total_chunks * (unsigned)p.n_head_kv), block(256);
     for (int g0 = 0; g0 < G; g0 += 8) {
         const int left = G - g0;
-        if (left >= 5) decode_split_kernel<HD, 8><<<grid, block, 0, s>>>(p, g0);
-        else if (left >= 3) decode_split_kernel<HD, 4><<<grid, block, 0, s>>>(p, g0);
-        else if (left == 2) decode_split_kernel<HD, 2><<<grid, block, 0, s>>>(p, g0);
-        else decode_split_kernel<HD, 1><<<grid, block, 0, s>>>(p, g0);
+        if (left >= 5) decode_split_kernel<HD, 8, KVT><<<grid, block, 0, s>>>(p, g0);
+        else if (left >= 3) decode_split_kernel<HD, 4, KVT><<<grid, block, 0, s>>>(p, g0);
+        else if (left == 2) decode_split_kernel<HD, 2, KVT><<<grid, block, 0, s>>>(p, g0);
+        else decode_split_kernel<HD, 1, KVT><<<grid, block, 0, s>>>(p, g0);
     }
+}
+
+template <int HD>
+hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
+{
+    if (p.kv_f16) launch_split<HD, _Float16>(p, s);
+    else launch_split<HD, float>(p, s);
     if (p.total_chunks > p.n) {  // some entry spans several chunks
         const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head);
         decode_combine_kernel<HD><<<cgrid, 256, 0, s>>>(p);

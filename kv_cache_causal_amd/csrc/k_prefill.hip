@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "kvc_internal.hpp"
 
@@ -58,16 +59,48 @@ struct PrefillCfg {
     static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
 };
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// How the 256 threads stage one K or V tile (KT rows x HD values) from a region of KVT
+// elements into the f32 LDS tile: each thread moves NCH chunks of CH consecutive values
+// (one load each), widening binary16 to f32 on the way.
+template <int HD, typename KVT>
+struct TileIO;
 template <int HD>
+struct TileIO<HD, float> {
+    static constexpr int CH = 4;
+    typedef floatx4 Raw;
+    static __device__ __forceinline__ void put(float *lds, const Raw &r)
+    {
+        *reinterpret_cast<floatx4 *>(lds) = r;
+    }
+};
+template <int HD>
+struct TileIO<HD, _Float16> {
+    static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 8 ? 8 : 4;
+    typedef typename std::conditional<CH == 8, half8_t, half4_t>::type Raw;
+    static __device__ __forceinline__ void put(float *lds, const Raw &r)
+    {
+        *reinterpret_cast<floatx4 *>(lds) = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+        if constexpr (CH == 8)
+            *reinterpret_cast<floatx4 *>(lds + 4) =
+                floatx4{(float)r[4], (float)r[5], (float)r[6], (float)r[7]};
+    }
+};
+
+template <int HD, typename KVT>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_t GB, int32_t TQ,
                                                       int32_t n_qtiles, int32_t n_hsub,
                                                       int32_t nblocks)
 {
     using C = PrefillCfg<HD>;
+    using TIO = TileIO<HD, KVT>;
     constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, NDB = C::NDB, VEC = C::VEC;
     constexpr int KSTR = C::KSTR, VSTR = C::VSTR;
-    constexpr int LD = C::LD;
-    static_assert(LD * 256 * 4 == KT * HD, "tile split");
+    constexpr int CH = TIO::CH;
+    constexpr int LD = KT * HD / (256 * CH);   // chunks per thread per tile (K or V)
+    static_assert(LD * 256 * CH == KT * HD && LD >= 1, "tile split");
     __shared__ float Ks[KT * KSTR];
     __shared__ float Vs[KT * VSTR];
     __shared__ int s_kmax;
@@ -133,30 +166,30 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     __syncthreads();
     const int ntiles = s_kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
-    const float *Kh = p.kc + hk * HD;
-    const float *Vh = p.vc + hk * HD;
+    const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
+    const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
 
-    // Tile staging: thread tid moves float4 #(tid + 256 j) of the tile, j < LD, i.e. row
-    // tid / (HD/4) + j * RSTEP, column (tid % (HD/4)) * 4.  Addresses are a uniform tile
-    // base plus a per-thread 32-bit byte offset.  Regions are padded to a whole number of
-    // 64-row tiles (zero rows past the capacity, beyond every position and so masked), so
-    // every tile load is inside the region.  The next tile's loads are issued before this
-    // tile's MFMAs.
-    constexpr int RSTEP = 256 / (HD / 4);      // rows between a thread's float4s
-    const int trow = tid / (HD / 4);
-    const int tcol = (tid % (HD / 4)) * 4;
-    const uint32_t toff = (uint32_t)(trow * nkt + tcol) * 4u;
-    const int64_t jstride = (int64_t)RSTEP * nkt * 4;  // bytes between a thread's float4s
-    // Native 4-float vectors: with float4 structs the compiler turns these unconditional
+    // Tile staging: thread tid moves chunk #(tid + 256 j) of the tile, j < LD, i.e. row
+    // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
+    // uniform tile base plus a per-thread 32-bit byte offset.  Regions are padded to a
+    // whole number of 64-row tiles (zero rows past the capacity, beyond every position and
+    // so masked), so every tile load is inside the region.  The next tile's loads are
+    // issued before this tile's MFMAs.
+    constexpr int RSTEP = 256 * CH / HD;       // rows between a thread's chunks
+    const int trow = tid / (HD / CH);
+    const int tcol = (tid % (HD / CH)) * CH;
+    const uint32_t toff = (uint32_t)(trow * nkt + tcol) * (uint32_t)sizeof(KVT);
+    const int64_t jstride = (int64_t)RSTEP * nkt * (int64_t)sizeof(KVT);
+    // Native vector registers: with struct types the compiler turns these unconditional
     // copies into an aggregate copy and keeps the arrays in scratch memory.
-    floatx4 kreg[LD], vreg[LD];
+    typename TIO::Raw kreg[LD], vreg[LD];
     auto fetch = [&](int key0) {
         const char *kb0 = reinterpret_cast<const char *>(Kh + (int64_t)key0 * nkt);
         const char *vb0 = reinterpret_cast<const char *>(Vh + (int64_t)key0 * nkt);
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            kreg[j] = *reinterpret_cast<const floatx4 *>(kb0 + j * jstride + toff);
-            vreg[j] = *reinterpret_cast<const floatx4 *>(vb0 + j * jstride + toff);
+            kreg[j] = *reinterpret_cast<const typename TIO::Raw *>(kb0 + j * jstride + toff);
+            vreg[j] = *reinterpret_cast<const typename TIO::Raw *>(vb0 + j * jstride + toff);
         }
     };
     fetch(0);
@@ -166,8 +199,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            *reinterpret_cast<floatx4 *>(&Ks[(trow + j * RSTEP) * KSTR + tcol]) = kreg[j];
-            *reinterpret_cast<floatx4 *>(&Vs[(trow + j * RSTEP) * VSTR + tcol]) = vreg[j];
+            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
+            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
         }
         __syncthreads();
         if (kt + 1 < ntiles) fetch(key0 + KT);
@@ -289,8 +322,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     }
 }
 
-template <int HD>
-hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
+template <int HD, typename KVT>
+hipError_t launch_hd_t(const PrefillParams &p, hipStream_t s)
 {
     const int G = p.n_head / p.n_head_kv;
     // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
@@ -301,9 +334,15 @@ hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
     const int n_qtiles = (p.nt + TQ - 1) / TQ;
     const int nblocks = n_qtiles * p.n_head_kv * n_hsub;
     const int launched = (nblocks + 7) / 8 * 8;
-    prefill_kernel<HD><<<dim3((unsigned)launched), dim3(256), 0, s>>>(p, GB, TQ, n_qtiles, n_hsub,
-                                                                      nblocks);
+    prefill_kernel<HD, KVT><<<dim3((unsigned)launched), dim3(256), 0, s>>>(p, GB, TQ, n_qtiles,
+                                                                           n_hsub, nblocks);
     return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
+{
+    return p.kv_f16 ? launch_hd_t<HD, _Float16>(p, s) : launch_hd_t<HD, float>(p, s);
 }
 
 }  // namespace

@@ -25,6 +25,24 @@ namespace {
 
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+// Store 4 f32 values at dst: as they are for an f32 region, rounded to binary16 (nearest,
+// ties to even: v_cvt_f16_f32 in the default rounding mode) for a half region.
+__device__ __forceinline__ void store4(float *dst, float4 v)
+{
+    *reinterpret_cast<float4 *>(dst) = v;
+}
+__device__ __forceinline__ void store4(_Float16 *dst, float4 v)
+{
+    half4_t h;
+    h[0] = (_Float16)v.x;
+    h[1] = (_Float16)v.y;
+    h[2] = (_Float16)v.z;
+    h[3] = (_Float16)v.w;
+    *reinterpret_cast<half4_t *>(dst) = h;
+}
+
 __global__ void __launch_bounds__(256) rope_table_kernel(float2 *tab, int32_t rows, int32_t hd,
                                                          float freq_base, float freq_scale)
 {
@@ -81,8 +99,8 @@ __device__ __forceinline__ void rotate_heads(const float *src, float *dst, int32
 // Vector form of rotate_heads for widths where every access is a whole, aligned float4:
 // a NEOX thread rotates 4 consecutive pairs (i..i+3 with i+half..i+half+3), an
 // interleaved thread 2 consecutive pairs (4 consecutive elements).  Same arithmetic.
-template <int STYLE>
-__device__ __forceinline__ void rotate_heads_vec(const float *src, float *dst, int32_t nh,
+template <int STYLE, typename DT>
+__device__ __forceinline__ void rotate_heads_vec(const float *src, DT *dst, int32_t nh,
                                                  int32_t w, const float2 *tab)
 {
     const int32_t half = w >> 1;
@@ -93,7 +111,7 @@ __device__ __forceinline__ void rotate_heads_vec(const float *src, float *dst, i
             const int32_t h = idx / (per_head / 2);
             const int32_t i = (idx - h * (per_head / 2)) * 4;
             const float *x = src + (int64_t)h * w;
-            float *y = dst + (int64_t)h * w;
+            DT *y = dst + (int64_t)h * w;
             const float4 a = *reinterpret_cast<const float4 *>(x + i);
             const float4 b = *reinterpret_cast<const float4 *>(x + half + i);
             const float4 t0 = *reinterpret_cast<const float4 *>(tab + i);
@@ -103,28 +121,29 @@ __device__ __forceinline__ void rotate_heads_vec(const float *src, float *dst, i
             rotate_pair(a.y, b.y, make_float2(t0.z, t0.w), ya.y, yb.y);
             rotate_pair(a.z, b.z, make_float2(t1.x, t1.y), ya.z, yb.z);
             rotate_pair(a.w, b.w, make_float2(t1.z, t1.w), ya.w, yb.w);
-            *reinterpret_cast<float4 *>(y + i) = ya;
-            *reinterpret_cast<float4 *>(y + half + i) = yb;
+            store4(y + i, ya);
+            store4(y + half + i, yb);
         } else {
             const int32_t h = idx / per_head;
             const int32_t e = (idx - h * per_head) * 4;
             const float *x = src + (int64_t)h * w;
-            float *y = dst + (int64_t)h * w;
+            DT *y = dst + (int64_t)h * w;
             const float4 a = *reinterpret_cast<const float4 *>(x + e);
             const float4 t = *reinterpret_cast<const float4 *>(tab + e / 2);
             float4 ya;
             rotate_pair(a.x, a.y, make_float2(t.x, t.y), ya.x, ya.y);
             rotate_pair(a.z, a.w, make_float2(t.z, t.w), ya.z, ya.w);
-            *reinterpret_cast<float4 *>(y + e) = ya;
+            store4(y + e, ya);
         }
     }
 }
 
 // One workgroup per token.  Reads: q row (if any), k row, v row, one table row per head
-// dim.  Writes: q row in place, one K row and one V row of the cache.  QVEC selects the
-// float4 form for q (hd a multiple of 8 for NEOX, of 4 for interleaved); k always
-// qualifies (hd_kv is a multiple of 16).
-template <int STYLE, bool QVEC>
+// dim.  Writes: q row in place, one K row and one V row of the cache (elements of type
+// KVT: f32, or binary16 rounded from the f32 result).  QVEC selects the float4 form for q
+// (hd a multiple of 8 for NEOX, of 4 for interleaved); k always qualifies (hd_kv is a
+// multiple of 16).
+template <int STYLE, bool QVEC, typename KVT>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
 {
     const int32_t t = blockIdx.x;
@@ -134,8 +153,8 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
     const int64_t row = ((int64_t)seq * p.n_layer + p.layer) * p.region + (int64_t)pos * nkt;
     const float *ksrc = p.k + (int64_t)t * nkt;
     const float *vsrc = p.v + (int64_t)t * nkt;
-    float *kdst = p.kc + row;
-    float *vdst = p.vc + row;
+    KVT *kdst = static_cast<KVT *>(p.kc) + row;
+    KVT *vdst = static_cast<KVT *>(p.vc) + row;
 
     if (STYLE != kNone) {
         if (p.q) {
@@ -148,13 +167,11 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
                                 p.tab_k + (int64_t)pos * (p.hd_kv >> 1));
     } else {
         const float4 *ks4 = reinterpret_cast<const float4 *>(ksrc);
-        float4 *kd4 = reinterpret_cast<float4 *>(kdst);
-        for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) kd4[i] = ks4[i];
+        for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) store4(kdst + 4 * i, ks4[i]);
     }
-    // hd_kv is a multiple of 16, so rows are whole float4s and 16-byte aligned.
+    // hd_kv is a multiple of 16, so rows are whole float4s (half4s) and aligned.
     const float4 *vs4 = reinterpret_cast<const float4 *>(vsrc);
-    float4 *vd4 = reinterpret_cast<float4 *>(vdst);
-    for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) vd4[i] = vs4[i];
+    for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) store4(vdst + 4 * i, vs4[i]);
 }
 
 }  // namespace
@@ -169,21 +186,28 @@ hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_b
     return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendParams &p, hipStream_t s)
+template <typename KVT>
+void launch_append_t(const AppendParams &p, hipStream_t s)
 {
-    if (p.nt <= 0) return hipSuccess;
     const dim3 grid((unsigned)p.nt), block(256);
     switch (p.style) {
     case kNeox:
-        if (p.hd % 8 == 0) append_kernel<kNeox, true><<<grid, block, 0, s>>>(p);
-        else append_kernel<kNeox, false><<<grid, block, 0, s>>>(p);
+        if (p.hd % 8 == 0) append_kernel<kNeox, true, KVT><<<grid, block, 0, s>>>(p);
+        else append_kernel<kNeox, false, KVT><<<grid, block, 0, s>>>(p);
         break;
     case kInterleaved:
-        if (p.hd % 4 == 0) append_kernel<kInterleaved, true><<<grid, block, 0, s>>>(p);
-        else append_kernel<kInterleaved, false><<<grid, block, 0, s>>>(p);
+        if (p.hd % 4 == 0) append_kernel<kInterleaved, true, KVT><<<grid, block, 0, s>>>(p);
+        else append_kernel<kInterleaved, false, KVT><<<grid, block, 0, s>>>(p);
         break;
-    default: append_kernel<kNone, false><<<grid, block, 0, s>>>(p); break;
+    default: append_kernel<kNone, false, KVT><<<grid, block, 0, s>>>(p); break;
     }
+}
+
+hipError_t launch_append(const AppendParams &p, hipStream_t s)
+{
+    if (p.nt <= 0) return hipSuccess;
+    if (p.kv_f16) launch_append_t<_Float16>(p, s);
+    else launch_append_t<float>(p, s);
     return hipGetLastError();
 }
 

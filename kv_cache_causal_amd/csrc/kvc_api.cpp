@@ -71,8 +71,10 @@ struct Staging {
 struct kvc_cache {
     kvc::Geometry g;
     int device = 0;
-    float *K = nullptr, *V = nullptr;
-    int64_t region = 0;  // floats per (seq, layer) region
+    int32_t kv_f16 = 0;       // regions hold binary16 instead of f32
+    size_t esize = 4;         // bytes per region element
+    char *K = nullptr, *V = nullptr;
+    int64_t region = 0;       // elements per (seq, layer) region
     std::vector<int32_t> hw;
     mutable Staging st;
     mutable std::vector<RopeTable> tables;
@@ -201,21 +203,31 @@ const char *kv_last_error(void) { return g_err.c_str(); }
 kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
                     int32_t hd_kv, int32_t capacity, void *stream)
 {
+    return kv_alloc_typed(out, n_seq, n_layer, n_head_kv, hd_kv, capacity, KVC_KV_F32, stream);
+}
+
+kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
+                          int32_t hd_kv, int32_t capacity, kvc_kv_dtype dtype, void *stream)
+{
     if (!out) return fail(KVC_E_ARG, "out is NULL");
     *out = nullptr;
     std::string msg;
     kvc_status st = kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, msg);
     if (st != KVC_OK) return fail(st, msg);
+    if (dtype != KVC_KV_F32 && dtype != KVC_KV_F16)
+        return fail(KVC_E_ARG, "unknown region format " + std::to_string((int)dtype));
 
     kvc_cache *c = new (std::nothrow) kvc_cache();
     if (!c) return fail(KVC_E_NOMEM, "handle allocation failed");
     c->g = kvc::Geometry{n_seq, n_layer, n_head_kv, hd_kv, capacity};
+    c->kv_f16 = dtype == KVC_KV_F16;
+    c->esize = c->kv_f16 ? 2 : 4;
     const int64_t rows = ((int64_t)capacity + kvc::kRegionRowAlign - 1) / kvc::kRegionRowAlign *
                          kvc::kRegionRowAlign;
     c->region = rows * n_head_kv * hd_kv;
     c->hw.assign((size_t)n_seq * n_layer, 0);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region * sizeof(float);
+    const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region * c->esize;
 
     auto cleanup = [&](kvc_status code, const std::string &m) {
         if (c->K) hipFree(c->K);
@@ -256,12 +268,12 @@ kvc_status kv_free(kvc_cache *c)
     return KVC_OK;
 }
 
-kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, float **k, float **v)
+kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, void **k, void **v)
 {
     if (!c || !k || !v) return fail(KVC_E_ARG, "NULL handle or output pointer");
     if (seq < 0 || seq >= c->g.n_seq || layer < 0 || layer >= c->g.n_layer)
         return fail(KVC_E_ARG, "seq/layer out of range");
-    const int64_t off = ((int64_t)seq * c->g.n_layer + layer) * c->region;
+    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region * c->esize;
     *k = c->K + off;
     *v = c->V + off;
     return KVC_OK;
@@ -325,6 +337,7 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
     p.n_layer = c->g.n_layer;
     p.layer = layer;
     p.style = (int32_t)style;
+    p.kv_f16 = c->kv_f16;
     hipError_t e = kvc::launch_append(p, s);
     if (e != hipSuccess) {
         if (!inline_args) staging_abort(c->st);
@@ -352,12 +365,13 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     std::vector<int32_t> ints(pos, pos + nt);
     const int32_t *dev = nullptr;
     if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
-    const int64_t off = ((int64_t)seq * c->g.n_layer + layer) * c->region;
+    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region * c->esize;
     kvc::PrefillParams p{};
     p.q = q;
     p.out = out;
     p.kc = c->K + off;
     p.vc = c->V + off;
+    p.kv_f16 = c->kv_f16;
     p.pos = dev;
     p.nt = nt;
     p.n_head = n_head;
@@ -440,6 +454,7 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
         p.hd_kv = c->g.hd_kv;
         p.n_layer = c->g.n_layer;
         p.layer = layer;
+        p.kv_f16 = c->kv_f16;
         p.rows_per_chunk = (int32_t)rows;
         p.qscale = log2e_times(scale);
         int32_t chunks = 0;

@@ -11,8 +11,9 @@ namespace kvc {
 
 // Cache layout: K[n_seq][n_layer][rows][n_head_kv * hd_kv] (V likewise) with
 // rows = capacity rounded up to a multiple of kRegionRowAlign; `region` is
-// rows * n_head_kv * hd_kv floats.  Rows at or past the capacity stay zero and are never
-// inside a window; they let the prefill kernel load whole key tiles unconditionally.
+// rows * n_head_kv * hd_kv elements, f32 or binary16 (`kv_f16`).  Rows at or past the
+// capacity stay zero and are never inside a window; they let the prefill kernel load
+// whole key tiles unconditionally.
 constexpr int kRegionRowAlign = 64;
 
 // ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------
@@ -26,13 +27,14 @@ constexpr int kInlineTokens = 64;
 struct AppendParams {
     float *q;               // [nt][n_head][hd] or nullptr
     const float *k, *v;     // [nt][n_head_kv][hd_kv]
-    float *kc, *vc;         // cache bases
+    void *kc, *vc;          // cache bases (f32 or binary16 elements)
     const int32_t *pos;     // device [nt], or nullptr: use ipos
     const int32_t *seq;     // device [nt], or nullptr: use iseq
     const float2 *tab_q;    // [capacity][hd/2] (nullptr if q is nullptr or style NONE)
     const float2 *tab_k;    // [capacity][hd_kv/2] (nullptr for style NONE)
     int64_t region;
     int32_t nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style;
+    int32_t kv_f16;         // regions hold binary16 (rounded to nearest even on store)
     int32_t ipos[kInlineTokens], iseq[kInlineTokens];
 };
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
@@ -45,9 +47,9 @@ struct DecodeParams {
     const float *q;          // [n][n_head][hd] (this launch's entries)
     float *out;              // [n][n_head][hd_kv]
     float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
-    const float *kc, *vc;    // cache bases
+    const void *kc, *vc;     // cache bases (f32 or binary16 elements)
     int64_t region;
-    int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer;
+    int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer, kv_f16;
     int32_t rows_per_chunk, total_chunks;
     float qscale;            // scale * log2(e): scores are kept in base-2 units
     int32_t pos[kInlineEntries];
@@ -63,9 +65,9 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 struct PrefillParams {
     const float *q;          // [nt][n_head][hd]
     float *out;              // [nt][n_head][hd_kv]
-    const float *kc, *vc;    // this (seq, layer)'s K and V regions
+    const void *kc, *vc;     // this (seq, layer)'s K and V regions (f32 or binary16)
     const int32_t *pos;      // device [nt]
-    int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity;
+    int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity, kv_f16;
     float qscale;            // scale * log2(e)
 };
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);

@@ -31,6 +31,9 @@ def host(t):
 
 
 def bits(a):
+    a = np.asarray(a)
+    if a.dtype in (np.float16, np.uint16):
+        return np.ascontiguousarray(a).view(np.uint16)
     return np.ascontiguousarray(a, np.float32).view(np.uint32)
 
 
@@ -63,7 +66,7 @@ def assert_close(gpu, orc, what):
 def compare_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
     import kv_cache_causal_amd as kvc
     K, V = kvc.kv_read(lib_cache, seq, layer)
-    K, V = host(K), host(V)
+    K, V = host(K), host(V)   # float16 arrays for a binary16 cache: compared as bits
     ok, ov = orc_cache.k(seq, layer), orc_cache.v(seq, layer)
     if rows is not None:
         K, V, ok, ov = K[rows], V[rows], ok[rows], ov[rows]
@@ -76,12 +79,12 @@ def compare_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
 class Pair:
     """A library cache and an oracle cache of the same geometry, driven in lock step."""
 
-    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity):
+    def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype=0):
         import kv_cache_causal_amd as kvc
         from oracle import OracleCache
         self.kvc = kvc
-        self.g = kvc.kv_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity)
-        self.o = OracleCache(n_seq, n_layer, n_head_kv, hd_kv, capacity)
+        self.g = kvc.kv_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype=dtype)
+        self.o = OracleCache(n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype=dtype)
         self.n_head_kv, self.hd_kv = n_head_kv, hd_kv
 
     def close(self):

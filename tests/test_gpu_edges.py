@@ -12,9 +12,9 @@ from tests.workloads import custom, custom_positions
 pytestmark = pytest.mark.gpu
 
 
-def build(seed, n_seq, n_head, n_head_kv, hd, hd_kv, capacity, rows, style=0, base=1e6):
+def build(seed, n_seq, n_head, n_head_kv, hd, hd_kv, capacity, rows, style=0, base=1e6, kv=0):
     """A cache pair with rows [0, rows) of sequence 0 (and 1 if present) written."""
-    p = Pair(n_seq, 1, n_head_kv, hd_kv, capacity)
+    p = Pair(n_seq, 1, n_head_kv, hd_kv, capacity, dtype=kv)
     for s in range(n_seq):
         k = custom(seed * 10 + s, (rows, n_head_kv, hd_kv))
         v = custom(seed * 10 + 5 + s, (rows, n_head_kv, hd_kv))
@@ -36,19 +36,23 @@ HEADS = [
 ]
 
 
+@pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
 @pytest.mark.parametrize("nh,nkv,hd,hdk", HEADS, ids=[f"h{a}kv{b}d{c}dk{d}" for a, b, c, d in HEADS])
-def test_decode_and_prefill_shapes(nh, nkv, hd, hdk):
-    say(f"shape n_head={nh} n_head_kv={nkv} hd={hd} hd_kv={hdk}")
+def test_decode_and_prefill_shapes(nh, nkv, hd, hdk, kv):
+    say(f"shape n_head={nh} n_head_kv={nkv} hd={hd} hd_kv={hdk} kv={kv}")
     cap, rows = 300, 300
-    p = build(1, 2, nh, nkv, hd, hdk, cap, rows)
+    p = build(1, 2, nh, nkv, hd, hdk, cap, rows, kv=kv)
     # Decode: two sequences, long and short windows, one at the last row.
     q = custom(2, (3, nh, hd))
     seqs, pos = [0, 1, 0], [299, 0, 137]
     got, want = p.decode(0, seqs, pos, dev(q), q, nh, hd, 0.31)
     assert_close(got, want, "decode")
-    # A one-row window returns that V row exactly.
+    # A one-row window returns that V row exactly (widened from binary16 if stored so).
+    v0 = p.o.v(1, 0)[0]
+    if kv:
+        v0 = v0.view(np.float16).astype(np.float32)
     for h in range(nh):
-        assert_bitwise(got[1, h], p.o.v(1, 0)[0, (h // (nh // nkv)) * hdk:][:hdk], "pos 0 = v0")
+        assert_bitwise(got[1, h], v0[(h // (nh // nkv)) * hdk:][:hdk], "pos 0 = v0")
     # Prefill: 77 tokens (ragged tile), positions out of order with repeats.
     nt = 77
     q = custom(3, (nt, nh, hd))
@@ -58,10 +62,11 @@ def test_decode_and_prefill_shapes(nh, nkv, hd, hdk):
     p.close()
 
 
+@pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
 @pytest.mark.parametrize("style", [0, 1, 2], ids=["neox", "interleaved", "none"])
-def test_rope_styles_and_hd_gt_hd_kv(style):
-    say(f"rope style {style}")
-    p = Pair(2, 3, 2, 32, 64)
+def test_rope_styles_and_hd_gt_hd_kv(style, kv):
+    say(f"rope style {style} kv={kv}")
+    p = Pair(2, 3, 2, 32, 64, dtype=kv)
     nt = 40
     q = custom(10, (nt, 4, 48))
     k = custom(11, (nt, 2, 32))
@@ -194,4 +199,21 @@ def test_rope_query_widths_scalar_and_vector_paths(style, hd):
     compare_cache(p.g, p.o, 0, 0, f"width {hd}")
     got, want = p.prefill(0, 0, pos, qd, qo, 4, hd, 0.2)
     assert_close(got, want, f"prefill width {hd}")
+    p.close()
+
+
+@pytest.mark.parametrize("style", [0, 2], ids=["neox", "none"])
+def test_f16_store_rounding_edges(style):
+    """binary16 stores of values that round to subnormals, to zero, across ties, to the
+    largest finite half and to infinity: bit-identical to the oracle's rounding."""
+    say(f"f16 store edges style {style}")
+    p = Pair(1, 1, 2, 64, 128, dtype=1)
+    rng = np.random.default_rng(90)
+    scales = np.array([1e-9, 3e-8, 6e-8, 1e-6, 6.1e-5, 1.0, 2049.0, 65504.0, 65520.0, 1e5],
+                      np.float32)
+    k = (rng.standard_normal((100, 2, 64)) * scales[rng.integers(0, len(scales), (100, 2, 64))])
+    v = (rng.standard_normal((100, 2, 64)) * scales[rng.integers(0, len(scales), (100, 2, 64))])
+    k, v = k.astype(np.float32), v.astype(np.float32)
+    p.append(0, [0] * 100, np.arange(100), None, 4, 64, k, v, 1e6, 1.0, style)
+    compare_cache(p.g, p.o, 0, 0, "f16 edges")
     p.close()

@@ -15,6 +15,9 @@ from tests.gpu_util import Pair, assert_close, compare_cache, dev, say
 
 pytestmark = pytest.mark.gpu
 
+# Region formats: f32, and the binary16 cache (store rounds to half, attention widens).
+KV = pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
+
 
 def fill(pair, w, seq, layer, n_rows, chunk=4096):
     """Pre-fill rows [0, n_rows) of (seq, layer) on both sides (store only, q = None)."""
@@ -27,10 +30,11 @@ def fill(pair, w, seq, layer, n_rows, chunk=4096):
                     w.freq_scale, w.style)
 
 
-def test_c1_tiny():
+@KV
+def test_c1_tiny(kv):
     w = W.C1
-    say(f"C1 {w.name}")
-    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    say(f"C1 {w.name} kv={kv}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     nt = w.extra["prefill"]
     pos = np.arange(nt, dtype=np.int32)
     q, k, v = W.prefill_qkv(w, nt, 0)
@@ -48,10 +52,11 @@ def test_c1_tiny():
     p.close()
 
 
-def test_c2_qwen25_layer():
+@KV
+def test_c2_qwen25_layer(kv):
     w = W.C2
-    say(f"C2 {w.name}")
-    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    say(f"C2 {w.name} kv={kv}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     n_past = w.extra["n_past"]
     fill(p, w, 0, 0, n_past)
     q, k, v = W.decode_qkv(w, 1, 0, 0)
@@ -62,10 +67,11 @@ def test_c2_qwen25_layer():
     p.close()
 
 
-def test_c3_qwen3_stack():
+@KV
+def test_c3_qwen3_stack(kv):
     w = W.C3
-    say(f"C3 {w.name}")
-    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    say(f"C3 {w.name} kv={kv}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     nt = w.extra["prefill"]
     pos = np.arange(nt, dtype=np.int32)
     worst = 0.0
@@ -92,10 +98,11 @@ def test_c3_qwen3_stack():
     p.close()
 
 
-def test_c4_long_context():
+@KV
+def test_c4_long_context(kv):
     w = W.C4
-    say(f"C4 {w.name}")
-    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    say(f"C4 {w.name} kv={kv}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     n_past = w.extra["n_past"]
     fill(p, w, 0, 0, n_past, w.extra["fill_chunk"])
     q, k, v = W.decode_qkv(w, 1, 0, 0)
@@ -106,10 +113,11 @@ def test_c4_long_context():
     p.close()
 
 
-def test_c5_batch():
+@KV
+def test_c5_batch(kv):
     w = W.C5
-    say(f"C5 {w.name}")
-    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    say(f"C5 {w.name} kv={kv}")
+    p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     n_past = W.c5_n_past(w)
     say(f"  n_past {n_past.tolist()}")
     for s in range(w.n_seq):
