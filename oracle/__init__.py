@@ -22,7 +22,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM = 0, 1, 2, 3, 4, 5
 ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
-KV_F32, KV_F16 = 0, 1
+KV_F32, KV_F16, KV_Q8_0 = 0, 1, 2
+Q8_BLOCK, Q8_BLOCK_BYTES = 32, 34
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
           "-std=c11", "-Wall", "-Wextra"]
@@ -49,6 +50,8 @@ def _bind(lib):
         "orc_cache_new_typed": (p, [i32, i32, i32, i32, i32, i32]),
         "orc_f32_to_f16": (ctypes.c_uint16, [f32]),
         "orc_f16_to_f32": (f32, [ctypes.c_uint16]),
+        "orc_q8_quantize_row": (ctypes.c_int, [p, i32, p]),
+        "orc_q8_dequantize_row": (ctypes.c_int, [p, i32, p]),
         "orc_cache_free": (None, [p]),
         "orc_cache_region": (p, [p, i32, i32, i32]),
         "orc_cache_seq_len": (i32, [p, i32, i32]),
@@ -122,6 +125,24 @@ class Oracle:
         h = np.asarray(h, np.uint16).ravel()
         return np.array([self.L.orc_f16_to_f32(int(v)) for v in h], np.float32)
 
+    def q8_quantize(self, x):
+        """Q8_0 blocks of a 1-D array (length a multiple of 32), as raw bytes
+        [n/32][34]: binary16 scale (little-endian) then 32 int8 codes."""
+        x = _f32(x).ravel()
+        out = np.zeros((x.size // Q8_BLOCK, Q8_BLOCK_BYTES), np.uint8)
+        st = self.L.orc_q8_quantize_row(_ptr(x), x.size, _ptr(out))
+        if st:
+            raise ValueError(f"orc_q8_quantize_row status {st}")
+        return out
+
+    def q8_dequantize(self, blocks):
+        blocks = np.ascontiguousarray(blocks, np.uint8).reshape(-1, Q8_BLOCK_BYTES)
+        out = np.zeros(blocks.shape[0] * Q8_BLOCK, np.float32)
+        st = self.L.orc_q8_dequantize_row(_ptr(blocks), out.size, _ptr(out))
+        if st:
+            raise ValueError(f"orc_q8_dequantize_row status {st}")
+        return out
+
     def rope(self, x, pos, base, scale=1.0, style=ROPE_NEOX):
         """x: [nt][nh][hd]; returns a rotated copy."""
         x = _f32(x).copy()
@@ -131,6 +152,14 @@ class Oracle:
         if st:
             raise ValueError(f"orc_rope status {st}")
         return x
+
+
+def q8_split(blocks):
+    """Split Q8_0 blocks [..., 34] into (scales uint16 [...], codes int8 [..., 32])."""
+    b = np.ascontiguousarray(blocks, np.uint8)
+    scales = b[..., :2].copy().view(np.uint16)[..., 0]
+    codes = b[..., 2:].copy().view(np.int8)
+    return scales, codes
 
 
 class OracleCache:
@@ -161,12 +190,18 @@ class OracleCache:
             pass
 
     def region(self, which, seq, layer) -> np.ndarray:
-        """Live numpy view of one region ([capacity][nkt]); which=0 for K, 1 for V.
-        float32 for an f32 cache, uint16 (binary16 bits) for an f16 cache."""
+        """Live numpy view of one region; which=0 for K, 1 for V.  [capacity][nkt]
+        float32 for an f32 cache, uint16 (binary16 bits) for an f16 cache; for a Q8_0
+        cache [capacity][nkt/32][34] bytes (see q8_split)."""
         ptr = self.L.orc_cache_region(self.h, which, seq, layer)
         if not ptr:
             raise IndexError("bad seq/layer")
         n = self.capacity * self.nkt
+        if self.dtype == KV_Q8_0:
+            nb = n // Q8_BLOCK * Q8_BLOCK_BYTES
+            buf = (ctypes.c_uint8 * nb).from_address(ptr)
+            return np.frombuffer(buf, dtype=np.uint8).reshape(self.capacity, self.nkt // Q8_BLOCK,
+                                                              Q8_BLOCK_BYTES)
         if self.dtype == KV_F16:
             buf = (ctypes.c_uint16 * n).from_address(ptr)
             return np.frombuffer(buf, dtype=np.uint16).reshape(self.capacity, self.nkt)

@@ -25,7 +25,14 @@
  *
  * Regions hold f32, or IEEE binary16 for the half-precision cache ([MINFER-11] §2.5):
  * the store rounds each f32 value to binary16 (nearest, ties to even) and attention
- * widens it back to f32 exactly before the same f32 arithmetic.
+ * widens it back to f32 exactly before the same f32 arithmetic.  A third format packs
+ * each row as Q8_0 blocks ([MINFER-11] §2.5 "Storage" and the FAQ on cache formats:
+ * 34 bytes per 32 values, quantized by the store, dequantized by attention).  The pages
+ * give the block size but not its arithmetic; the reading taken here is the published
+ * Q8_0 block of the GGML family: scale d = max|x| / 127 in f32, stored as binary16;
+ * codes round(x * (1/d)) to nearest, halves away from zero, with 1/d the f32 reciprocal
+ * of the f32 scale (0 for an all-zero block); value = f32(binary16 d) * code, which is
+ * exact in f32.
  *
  * Pins: every function here is checked by tests against closed forms, the pages'
  * worked examples, arbitrary-precision values, numpy's binary16 conversion and an f64
@@ -140,7 +147,7 @@ int orc_rope(float *x, int32_t nt, int32_t nh, int32_t hd, const int32_t *pos,
 /* Storage formats of the regions.  F16 is the half-precision cache of [MINFER-11] §2.5
  * ("Storage") and §3.3: the store rounds each value to IEEE binary16, attention widens
  * it back to f32 and computes in f32. */
-enum { ORC_KV_F32 = 0, ORC_KV_F16 = 1 };
+enum { ORC_KV_F32 = 0, ORC_KV_F16 = 1, ORC_KV_Q8_0 = 2 };
 
 /* IEEE-754 binary32 -> binary16, round to nearest, ties to even; overflow gives inf,
  * tiny values become subnormals or signed zero; NaN stays a (quiet) NaN. */
@@ -196,10 +203,63 @@ float orc_f16_to_f32(uint16_t h)
     return f;
 }
 
+/* ------------------------------------------------------------------------------ */
+/* Q8_0 blocks (reading stated in the header).                                       */
+/* ------------------------------------------------------------------------------ */
+
+#define ORC_Q8_BLOCK 32
+
+/* One block: the binary16 scale, then the 32 signed 8-bit codes (34 bytes). */
+typedef struct {
+    uint16_t d;
+    int8_t qs[ORC_Q8_BLOCK];
+} orc_q8_block;
+
+_Static_assert(sizeof(orc_q8_block) == 34, "a Q8_0 block is 34 bytes");
+
+/* Quantize n values (n a multiple of 32) into n / 32 blocks.  Inputs must be finite:
+ * a non-finite value makes its block's codes unspecified (here 0). */
+int orc_q8_quantize_row(const float *x, int32_t n, void *out)
+{
+    if (!x || !out || n < 0 || n % ORC_Q8_BLOCK) return ORC_E_ARG;
+    orc_q8_block *b = (orc_q8_block *)out;
+    for (int32_t blk = 0; blk < n / ORC_Q8_BLOCK; blk++) {
+        const float *xb = x + (size_t)blk * ORC_Q8_BLOCK;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < ORC_Q8_BLOCK; i++) {
+            const float a = fabsf(xb[i]);
+            if (a > amax) amax = a;
+        }
+        const float d = amax / 127.0f;
+        const float id = d != 0.0f ? 1.0f / d : 0.0f;
+        b[blk].d = orc_f32_to_f16(d);
+        for (int32_t i = 0; i < ORC_Q8_BLOCK; i++) {
+            const float r = roundf(xb[i] * id);   /* halves away from zero */
+            b[blk].qs[i] = (r >= -127.0f && r <= 127.0f) ? (int8_t)r : 0;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantize n / 32 blocks into n values. */
+int orc_q8_dequantize_row(const void *in, int32_t n, float *out)
+{
+    if (!in || !out || n < 0 || n % ORC_Q8_BLOCK) return ORC_E_ARG;
+    const orc_q8_block *b = (const orc_q8_block *)in;
+    for (int32_t blk = 0; blk < n / ORC_Q8_BLOCK; blk++) {
+        const float d = orc_f16_to_f32(b[blk].d);
+        for (int32_t i = 0; i < ORC_Q8_BLOCK; i++)
+            out[(size_t)blk * ORC_Q8_BLOCK + i] = d * (float)b[blk].qs[i];
+    }
+    return ORC_OK;
+}
+
 typedef struct orc_cache {
     int32_t n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype;
-    size_t region;      /* elements per (seq, layer) region: capacity * n_head_kv * hd_kv */
-    void *k, *v;        /* [n_seq][n_layer][capacity][n_head_kv * hd_kv], f32 or f16 bits */
+    size_t region;      /* values per (seq, layer) region: capacity * n_head_kv * hd_kv */
+    size_t region_bytes;
+    void *k, *v;        /* [n_seq][n_layer][capacity][row]: a row is n_head_kv * hd_kv f32
+                           values, binary16 bit patterns, or Q8_0 blocks */
     int32_t *hw;        /* high-water mark per (seq, layer): max written position + 1 */
 } orc_cache;
 
@@ -208,17 +268,23 @@ orc_cache *orc_cache_new_typed(int32_t n_seq, int32_t n_layer, int32_t n_head_kv
 {
     if (n_seq <= 0 || n_layer <= 0 || n_head_kv <= 0 || hd_kv <= 0 || (hd_kv & 1) ||
         hd_kv > ORC_MAX_HEAD_DIM || capacity <= 0 || capacity > ORC_MAX_POSITION ||
-        (dtype != ORC_KV_F32 && dtype != ORC_KV_F16))
+        (dtype != ORC_KV_F32 && dtype != ORC_KV_F16 && dtype != ORC_KV_Q8_0))
         return NULL;
+    /* Q8_0 blocks run along the row; with hd_kv a multiple of 32 each block lies in one
+     * kv head, so a head's slice is whole blocks. */
+    if (dtype == ORC_KV_Q8_0 && hd_kv % ORC_Q8_BLOCK) return NULL;
     orc_cache *c = (orc_cache *)calloc(1, sizeof(orc_cache));
     if (!c) return NULL;
     c->n_seq = n_seq; c->n_layer = n_layer; c->n_head_kv = n_head_kv;
     c->hd_kv = hd_kv; c->capacity = capacity; c->dtype = dtype;
     c->region = (size_t)capacity * (size_t)n_head_kv * (size_t)hd_kv;
-    const size_t total = (size_t)n_seq * (size_t)n_layer * c->region;
-    const size_t esz = dtype == ORC_KV_F16 ? sizeof(uint16_t) : sizeof(float);
-    c->k = calloc(total, esz);   /* all-zero bits are +0.0 in both formats */
-    c->v = calloc(total, esz);
+    if (dtype == ORC_KV_Q8_0)
+        c->region_bytes = c->region / ORC_Q8_BLOCK * sizeof(orc_q8_block);
+    else
+        c->region_bytes = c->region * (dtype == ORC_KV_F16 ? sizeof(uint16_t) : sizeof(float));
+    const size_t total = (size_t)n_seq * (size_t)n_layer * c->region_bytes;
+    c->k = calloc(total, 1);   /* all-zero bytes are +0.0 in every format */
+    c->v = calloc(total, 1);
     c->hw = (int32_t *)calloc((size_t)n_seq * n_layer, sizeof(int32_t));
     if (!c->k || !c->v || !c->hw) {
         free(c->k); free(c->v); free(c->hw); free(c);
@@ -239,24 +305,22 @@ void orc_cache_free(orc_cache *c)
     free(c->k); free(c->v); free(c->hw); free(c);
 }
 
-static size_t elem_size(const orc_cache *c)
-{
-    return c->dtype == ORC_KV_F16 ? sizeof(uint16_t) : sizeof(float);
-}
-
-/* which = 0 for K, 1 for V.  Returns the [capacity][n_head_kv * hd_kv] region (f32
- * values, or binary16 bit patterns for an f16 cache). */
+/* which = 0 for K, 1 for V.  Returns the [capacity][row] region (f32 values, binary16
+ * bit patterns, or n_head_kv * hd_kv / 32 Q8_0 blocks per row). */
 void *orc_cache_region(orc_cache *c, int32_t which, int32_t seq, int32_t layer)
 {
     if (!c || seq < 0 || seq >= c->n_seq || layer < 0 || layer >= c->n_layer) return NULL;
     char *base = (char *)(which ? c->v : c->k);
-    return base + ((size_t)seq * c->n_layer + layer) * c->region * elem_size(c);
+    return base + ((size_t)seq * c->n_layer + layer) * c->region_bytes;
 }
 
-/* Write n f32 values into a region at element offset off, in the cache's format. */
+/* Write n f32 values into a region at value offset off (a row start), in the cache's
+ * format. */
 static void store_values(orc_cache *c, void *region, size_t off, const float *src, int32_t n)
 {
-    if (c->dtype == ORC_KV_F16) {
+    if (c->dtype == ORC_KV_Q8_0) {
+        orc_q8_quantize_row(src, n, (orc_q8_block *)region + off / ORC_Q8_BLOCK);
+    } else if (c->dtype == ORC_KV_F16) {
         uint16_t *d = (uint16_t *)region + off;
         for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[i]);
     } else {
@@ -350,12 +414,17 @@ static float dot_f32(int32_t n, const float *a, const float *b)
 }
 
 /* Kv head hk of row j of a region as f32 values: the region itself for an f32 cache,
- * the binary16 values widened into buf for an f16 cache. */
+ * the binary16 values widened into buf for an f16 cache, the head's Q8_0 blocks
+ * dequantized into buf for a Q8_0 cache. */
 static const float *head_row(const void *reg, int32_t dtype, size_t j, int32_t nkt, int32_t hk,
                              int32_t hd_kv, float *buf)
 {
     const size_t off = j * (size_t)nkt + (size_t)hk * hd_kv;
     if (dtype == ORC_KV_F32) return (const float *)reg + off;
+    if (dtype == ORC_KV_Q8_0) {
+        orc_q8_dequantize_row((const orc_q8_block *)reg + off / ORC_Q8_BLOCK, hd_kv, buf);
+        return buf;
+    }
     const uint16_t *h = (const uint16_t *)reg + off;
     for (int32_t d = 0; d < hd_kv; d++) buf[d] = orc_f16_to_f32(h[d]);
     return buf;

@@ -19,8 +19,8 @@ import os
 import mpmath
 import numpy as np
 
-from oracle import (E_ARG, E_DUP, E_GEOMETRY, E_RANGE, KV_F16, OK, ROPE_INTERLEAVED,
-                    ROPE_NEOX, ROPE_NONE, Oracle, OracleCache)
+from oracle import (E_ARG, E_DUP, E_GEOMETRY, E_RANGE, KV_F16, KV_Q8_0, OK, ROPE_INTERLEAVED,
+                    ROPE_NEOX, ROPE_NONE, Oracle, OracleCache, q8_split)
 from tests import bruteforce as bf
 from tests.workloads import custom, custom_positions
 
@@ -467,6 +467,110 @@ def pin_f16_cache_store_and_attention(o: Oracle):
     c16.close()
 
 
+# ------------------------------------------------------------------------------------
+# Q8_0 cache ("11 · Attention, vec ops, and the KV cache" §2.5 "Storage": 34 bytes per 32
+# values; the block arithmetic is the reading stated in tests/golden/q8_0_blocks.json)
+# ------------------------------------------------------------------------------------
+
+def pin_q8_worked_blocks(o: Oracle):
+    """Hand-derived blocks: unit and half scales, a scale that binary16 cannot hold (and
+    which separates the f32-reciprocal reading from a binary16-reciprocal one), a
+    subnormal scale, an all-zero block; ties go away from zero."""
+    g = golden("q8_0_blocks.json")
+    for blk in g["blocks"]:
+        x = np.array(blk["x"], np.float32)
+        scales, codes = q8_split(o.q8_quantize(x))
+        assert int(scales[0]) == blk["scale_bits"], (blk["name"], hex(int(scales[0])))
+        assert codes[0].tolist() == blk["codes"], (blk["name"], codes[0].tolist())
+        deq = o.q8_dequantize(o.q8_quantize(x))
+        for i, want in blk.get("dequantized", {}).items():
+            assert deq[int(i)] == np.float32(want), (blk["name"], i, deq[int(i)], want)
+        if blk["scale_bits"] in (0x3C00,):   # unit scale: values are the codes
+            assert np.array_equal(deq, np.array(blk["codes"], np.float32))
+
+
+def pin_q8_block_invariants(o: Oracle):
+    """On seeded blocks of many magnitudes: the largest-magnitude value gets code +-127
+    with its sign; codes stay in [-127, 127]; negating the block negates the codes and
+    keeps the scale; scaling by 2^k keeps the codes and moves the scale's exponent by k;
+    blocks of a row are quantized independently; the stored scale is the binary16
+    nearest to max|x| / 127 (checked in f64 against numpy's binary16); the dequantization
+    error is within d/2 plus the scale's own rounding."""
+    x = custom(70, (64, 32)) * np.float32(3)
+    x *= np.float32(2.0) ** np.repeat(np.arange(-6, 10, dtype=np.float32), 4)[:, None]
+    b = o.q8_quantize(x.ravel())
+    scales, codes = q8_split(b)
+    assert np.abs(codes.astype(np.int32)).max() <= 127
+    for r in range(x.shape[0]):
+        i = int(np.argmax(np.abs(x[r])))
+        assert codes[r, i] == (127 if x[r, i] > 0 else -127), (r, codes[r, i])
+        one_s, one_c = q8_split(o.q8_quantize(x[r]))
+        assert one_s[0] == scales[r] and np.array_equal(one_c[0], codes[r])
+        amax = np.abs(x[r].astype(np.float64)).max()
+        d16 = np.float64(scales[r:r + 1].view(np.float16)[0])
+        # d/2^11 bounds binary16 rounding of a normal scale; the exact quotient sits
+        # within an f32 rounding of the f32 d.
+        assert abs(d16 - amax / 127) <= (amax / 127) * (2.0 ** -11 + 2.0 ** -23), r
+        deq = o.q8_dequantize(b[r:r + 1]).astype(np.float64)
+        bound = (amax / 127) * (0.5 + 2.0 ** -16) + 127 * abs(d16 - amax / 127)
+        assert np.abs(deq - x[r]).max() <= bound, r
+    neg_s, neg_c = q8_split(o.q8_quantize(-x.ravel()))
+    assert np.array_equal(neg_s, scales) and np.array_equal(neg_c, -codes)
+    y = x[16:48]   # scales well inside the binary16 normal range
+    ys, yc = q8_split(o.q8_quantize(y.ravel()))
+    ys2, yc2 = q8_split(o.q8_quantize((y * np.float32(8)).ravel()))
+    assert np.array_equal(yc2, yc)
+    assert np.array_equal(ys2.view(np.float16).astype(np.float64),
+                          ys.view(np.float16).astype(np.float64) * 8)
+
+
+def pin_q8_cache_store_and_attention(o: Oracle):
+    """A Q8_0 cache stores the blocks of rot(k) and of v at each row (rot pinned above,
+    blocks pinned by the two pins before), and its attention is the f32 attention of
+    the dequantized rows (values built here from the stored bytes with numpy's
+    binary16), so it equals the f64 brute force within the f32 bar.  hd_kv must be a
+    multiple of 32."""
+    cap, nkv, hdk = 20, 2, 32
+    k = custom(63, (cap, nkv, hdk)) * 3
+    v = custom(64, (cap, nkv, hdk))
+    c32 = OracleCache(1, 1, nkv, hdk, cap, o)
+    cq = OracleCache(1, 1, nkv, hdk, cap, o, dtype=KV_Q8_0)
+    for c in (c32, cq):
+        st, _ = c.append_rope(0, [0] * cap, np.arange(cap), None, 0, 0, k, v, 1e4, 1.0, ROPE_NEOX)
+        assert st == OK
+    for which, src in ((0, c32.k(0, 0)), (1, v.reshape(cap, -1))):
+        reg = cq.region(which, 0, 0)
+        for r in range(cap):
+            assert np.array_equal(reg[r].ravel(), o.q8_quantize(src[r]).ravel()), (which, r)
+    deq = []
+    for which in (0, 1):
+        sc, cd = q8_split(cq.region(which, 0, 0))
+        deq.append((sc.view(np.float16).astype(np.float32)[..., None] *
+                    cd.astype(np.float32)).reshape(cap, nkv * hdk))
+    cd32 = OracleCache(1, 1, nkv, hdk, cap, o)
+    st, _ = cd32.append_rope(0, [0] * cap, np.arange(cap), None, 0, 0, deq[0], deq[1], 0, 0,
+                             ROPE_NONE)
+    assert st == OK
+    q = custom(65, (5, 4, 32))
+    pos = [0, 3, 11, 19, 19]
+    st, out = cq.attn_prefill(0, 0, pos, q, 4, 32, 0.2)
+    st2, want32 = cd32.attn_prefill(0, 0, pos, q, 4, 32, 0.2)
+    assert st == OK and st2 == OK
+    assert np.array_equal(out.view(np.uint32), want32.view(np.uint32))
+    want = bf.attention_bf(q, deq[0].astype(np.float64), deq[1].astype(np.float64), pos, nkv, 0.2)
+    assert np.abs(out - want).max() <= 1e-6 + 1e-5 * np.abs(want).max()
+    st, outd = cq.attn_decode(0, [0] * 5, pos, q, 4, 32, 0.2)
+    assert st == OK and np.array_equal(outd.view(np.uint32), out.view(np.uint32))
+    for c in (c32, cq, cd32):
+        c.close()
+    try:
+        OracleCache(1, 1, 2, 16, 8, o, dtype=KV_Q8_0)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a Q8_0 cache with hd_kv = 16 was accepted")
+
+
 ALL_PINS = [
     pin_inv_freq_correctly_rounded,
     pin_rope_worked_example,
@@ -488,4 +592,7 @@ ALL_PINS = [
     pin_f16_round_to_nearest_even,
     pin_f16_widening_exact,
     pin_f16_cache_store_and_attention,
+    pin_q8_worked_blocks,
+    pin_q8_block_invariants,
+    pin_q8_cache_store_and_attention,
 ]

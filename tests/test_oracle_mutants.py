@@ -49,6 +49,22 @@ MUTANTS = {
                        "x = sign | ((exp - 16 + 127) << 23) | (man << 13);"),
     "f16_store_skipped": ("for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[i]);",
                           "for (int32_t i = 0; i < n; i++) d[i] = orc_f32_to_f16(src[0]);"),
+    # Q8_0 cache
+    "q8_ties_to_even": ("const float r = roundf(xb[i] * id);", "const float r = rintf(xb[i] * id);"),
+    "q8_truncates": ("const float r = roundf(xb[i] * id);", "const float r = truncf(xb[i] * id);"),
+    "q8_divides_by_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
+    "q8_reciprocal_of_half_scale": (
+        "const float id = d != 0.0f ? 1.0f / d : 0.0f;",
+        "const float id = d != 0.0f ? 1.0f / orc_f16_to_f32(orc_f32_to_f16(d)) : 0.0f;"),
+    "q8_signed_max": ("const float a = fabsf(xb[i]);", "const float a = xb[i];"),
+    "q8_stores_amax": ("b[blk].d = orc_f32_to_f16(d);", "b[blk].d = orc_f32_to_f16(amax);"),
+    "q8_dequant_drops_scale": ("out[(size_t)blk * ORC_Q8_BLOCK + i] = d * (float)b[blk].qs[i];",
+                               "out[(size_t)blk * ORC_Q8_BLOCK + i] = (float)b[blk].qs[i];"),
+    "q8_head_offset_dropped": (
+        "orc_q8_dequantize_row((const orc_q8_block *)reg + off / ORC_Q8_BLOCK, hd_kv, buf);",
+        "orc_q8_dequantize_row((const orc_q8_block *)reg + j * (size_t)nkt / ORC_Q8_BLOCK, hd_kv, buf);"),
+    "q8_store_skipped": ("orc_q8_quantize_row(src, n, (orc_q8_block *)region + off / ORC_Q8_BLOCK);",
+                         "(void)src;"),
 }
 
 
