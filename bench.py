@@ -12,7 +12,8 @@ stage.
 
 Reported:
   value          decode attention KV GB/s: algorithmic K+V bytes of the 32 windows
-                 (sum_b (pos_b + 1) * 2 * n_head_kv * hd_kv * 4) / decode-attention time
+                 (sum_b (pos_b + 1) * 2 * n_head_kv * hd_kv * bytes per value: 4 for f32,
+                 2 for binary16, 34/32 for Q8_0) / decode-attention time
   prefill_tflops algorithmic prefill FLOPs (4 * n_head * hd_kv * sum_t (pos_t + 1)) /
                  prefill-attention time
   roofline       the dominant kernel (prefill, MFMA-bound) against the fp32 matrix peak;
@@ -21,7 +22,8 @@ Reported:
                  profiles/ (null once the kernel sources differ from the profiled ones)
   cpu_baseline   the plain C oracle on the host cores, on a bounded sample
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--kv f16]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+                       [--kv f32|f16|q8_0]
 """
 from __future__ import annotations
 
@@ -53,7 +55,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--kv", choices=["f32", "f16"], default="f32",
+    ap.add_argument("--kv", choices=["f32", "f16", "q8_0"], default="f32",
                     help="region format: f32, or binary16 (half the bytes; arithmetic in f32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before timing, so that "
@@ -77,8 +79,10 @@ def main():
     lens = n_past.copy()
     lens[0] += nt
     seqs = np.arange(w.n_seq, dtype=np.int32)
-    esize = 2 if args.kv == "f16" else 4
-    kv_bytes = int((lens.astype(np.int64) + 1).sum()) * 2 * w.n_head_kv * w.hd_kv * esize
+    # Bytes per cached value: f32 4, binary16 2, Q8_0 34/32 (a code plus its share of the
+    # block's 2-byte scale).
+    esize = {"f32": 4, "f16": 2, "q8_0": 34 / 32}[args.kv]
+    kv_bytes = int(int((lens.astype(np.int64) + 1).sum()) * 2 * w.n_head_kv * w.hd_kv * esize)
     pre_flops = 4 * w.n_head * w.hd_kv * int((pre_pos.astype(np.int64) + 1).sum())
 
     torch.cuda.init()
@@ -86,7 +90,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"bench: workload {w.name}; filling {int(n_past.sum())} cached rows")
     t0 = time.time()
-    kv_dtype = kvc.KV_F16 if args.kv == "f16" else kvc.KV_F32
+    kv_dtype = {"f32": kvc.KV_F32, "f16": kvc.KV_F16, "q8_0": kvc.KV_Q8_0}[args.kv]
     cache = kvc.kv_alloc(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv_dtype)
     orc_cache = None
     if not args.no_cpu_baseline:

@@ -7,7 +7,7 @@
  *                   in place at those positions
  *   gqa_attn_prefill  nt query tokens of one sequence, token t attending rows [0, pos[t]]
  *   gqa_attn_decode   one query token per sequence for a batch of sequences
- * plus kv_alloc_typed (half-precision regions), kv_free, kv_view, kv_seq_len and
+ * plus kv_alloc_typed (binary16 or Q8_0 regions), kv_free, kv_view, kv_seq_len and
  * kv_last_error for storage format, ownership, inspection and error text.
  *
  * Sources (page titles; sections named per declaration):
@@ -16,7 +16,8 @@
  *   [MINFER-13] "13 · The decode loop and graph reuse"
  *
  * Conventions for every call
- *   - q, k, v and out are f32 (the cache regions are f32 or binary16, see kvc_kv_dtype).
+ *   - q, k, v and out are f32 (the cache regions are f32, binary16 or Q8_0, see
+ *     kvc_kv_dtype).
  *     "device" pointers are HIP device memory; "host" pointers are
  *     ordinary host memory, read before the call returns (the caller may reuse them at
  *     once).  Device buffers must stay valid until the work queued on `stream` is done.
@@ -67,10 +68,20 @@ typedef enum kvc_rope_style {
 /* Element format of the K and V regions.  F16 is the half-precision cache
  * ([MINFER-11] §2.5 "Storage" and §3.3): the store rounds each rotated k value and each
  * v value to IEEE binary16 (nearest, ties to even); attention widens them back to f32
- * and computes in f32.  It halves the bytes decode attention reads. */
+ * and computes in f32.  It halves the bytes decode attention reads.
+ * Q8_0 is the packed cache of the same section and of the FAQ on cache formats: each
+ * row is cut into blocks of 32 values, 34 bytes each (3.76x fewer bytes than f32).  The
+ * pages fix the size, not the arithmetic; the library takes the published GGML Q8_0
+ * block: d = max|x| / 127 (f32 division), stored as binary16 (nearest, ties to even);
+ * code = round(x * r) to nearest with halves away from zero, r = 1/d as an f32
+ * division (r = 0 when d = 0); the value attention uses is f32(binary16 d) * code,
+ * exact in f32, and the arithmetic after it is f32 as for the other formats.  Needs
+ * hd_kv a multiple of 32 (each block inside one kv head).  Inputs to the store must be
+ * finite; values beyond 127 * 65504 in magnitude overflow the scale. */
 typedef enum kvc_kv_dtype {
     KVC_KV_F32 = 0,
-    KVC_KV_F16 = 1
+    KVC_KV_F16 = 1,
+    KVC_KV_Q8_0 = 2
 } kvc_kv_dtype;
 
 #define KVC_MAX_HEAD_DIM 256
@@ -104,8 +115,14 @@ kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_h
 /*
  * kv_alloc_typed -- kv_alloc with an explicit region element format (kv_alloc is
  * kv_alloc_typed with KVC_KV_F32).  With KVC_KV_F16 every region element is 2 bytes;
- * everything else (layout, calls, errors) is as for kv_alloc.
- * Errors: as kv_alloc, plus KVC_E_ARG for an unknown format.
+ * everything else (layout, calls, errors) is as for kv_alloc.  With KVC_KV_Q8_0 a
+ * region is rows * nkt int8 codes laid out [rows][nkt] (nkt = n_head_kv * hd_kv, the
+ * code of value i of row p at byte p * nkt + i), followed directly by rows * nkt / 32
+ * binary16 scales laid out [rows][nkt / 32] (scale of block i / 32 of row p): the same
+ * 34 bytes per 32 values as the interleaved block, as two planes so that every row of
+ * codes and of scales is aligned for vector loads.  Zero bytes decode to +0.0.
+ * Errors: as kv_alloc, plus KVC_E_ARG for an unknown format and KVC_E_GEOMETRY for a
+ * Q8_0 cache whose hd_kv is not a multiple of 32.
  */
 kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
                           int32_t hd_kv, int32_t capacity, kvc_kv_dtype dtype, void *stream);
@@ -120,7 +137,10 @@ kvc_status kv_free(kvc_cache *c);
  * kv_view -- borrow one (sequence, layer)'s regions without copying ([ZEROCOPY]
  * "Reading without copying": a live reference into the cache's own storage).
  *   k, v  host; each receives a device pointer to [capacity][n_head_kv * hd_kv] elements
- *         (f32, or binary16 for a KVC_KV_F16 cache; the region's first capacity rows).
+ *         (f32, or binary16 for a KVC_KV_F16 cache; the region's first capacity rows),
+ *         or to the start of a KVC_KV_Q8_0 region (codes, then scales at byte
+ *         rows * n_head_kv * hd_kv, rows = capacity rounded up to 64; see
+ *         kv_alloc_typed).
  *         The pointers never change for the handle's life and stay owned by it.
  * Errors: KVC_E_ARG for a NULL handle/pointer or seq/layer out of range.
  */

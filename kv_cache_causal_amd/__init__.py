@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkvc.so")
 
 OK, E_ARG, E_GEOMETRY, E_RANGE, E_DUP, E_NOMEM, E_HIP = range(7)
 ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE = 0, 1, 2
-KV_F32, KV_F16 = 0, 1
+KV_F32, KV_F16, KV_Q8_0 = 0, 1, 2
+REGION_ROW_ALIGN = 64   # region rows = capacity rounded up to this
 STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANGE",
                 4: "KVC_E_DUP", 5: "KVC_E_NOMEM", 6: "KVC_E_HIP"}
 
@@ -111,7 +112,8 @@ def _host_i32(a):
 
 class Cache:
     """Owning wrapper of a kvc_cache handle (kv_free on close / garbage collection).
-    dtype KV_F32 (kv_alloc) or KV_F16 (binary16 regions, kv_alloc_typed)."""
+    dtype KV_F32 (kv_alloc), KV_F16 (binary16 regions) or KV_Q8_0 (Q8_0 blocks), the
+    last two through kv_alloc_typed."""
 
     def __init__(self, n_seq, n_layer, n_head_kv, hd_kv, capacity, stream=None, dtype=KV_F32):
         self.n_seq, self.n_layer = n_seq, n_layer
@@ -201,7 +203,9 @@ _hip = None
 def kv_read(c: Cache, seq: int, layer: int, stream=None):
     """Copies (device to device, on `stream`) of one (seq, layer)'s K and V regions as
     [capacity][n_head_kv * hd_kv] torch tensors (float32, or float16 for a binary16
-    cache).  For inspection and tests."""
+    cache).  For a Q8_0 cache each of K and V is a pair (codes int8 [rows][nkt], scales
+    int16 holding binary16 bits [rows][nkt / 32]) over all rows = capacity rounded up
+    to 64.  For inspection and tests."""
     global _hip
     import torch
     if _hip is None:
@@ -211,6 +215,18 @@ def kv_read(c: Cache, seq: int, layer: int, stream=None):
         _hip.hipMemcpyAsync.restype = ctypes.c_int
     kp, vp = kv_view(c, seq, layer)
     out = []
+    if c.dtype == KV_Q8_0:
+        rows = -(-c.capacity // REGION_ROW_ALIGN) * REGION_ROW_ALIGN
+        nbytes = rows * c.nkt + rows * (c.nkt // 32) * 2
+        for src in (kp, vp):
+            t = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            e = _hip.hipMemcpyAsync(t.data_ptr(), src, nbytes, 3, _stream(stream))
+            if e != 0:
+                raise RuntimeError(f"hipMemcpyAsync failed: {e}")
+            codes = t[: rows * c.nkt].view(torch.int8).reshape(rows, c.nkt)
+            scales = t[rows * c.nkt:].view(torch.int16).reshape(rows, c.nkt // 32)
+            out.append((codes, scales))
+        return out[0], out[1]
     for src in (kp, vp):
         dt = torch.float16 if c.dtype == KV_F16 else torch.float32
         t = torch.empty((c.capacity, c.nkt), dtype=dt, device="cuda")

@@ -26,9 +26,9 @@ extern "C" {
 const char *hc_last_message(void) { return g_msg.c_str(); }
 
 int hc_check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
-                   int32_t capacity)
+                   int32_t capacity, int32_t dtype)
 {
-    return kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, g_msg);
+    return kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, dtype, g_msg);
 }
 
 int hc_check_append(const int32_t *g5, int32_t layer, int32_t nt, const int32_t *seq_ids,

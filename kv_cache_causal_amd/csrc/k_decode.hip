@@ -14,11 +14,16 @@
 //     on the host so the grid fills the chip several times over; the workgroups of one
 //     chunk's kv heads are adjacent in dispatch order (DRAM page locality).
 //   * A row slice (hd_kv values of one kv head) is read by a group of LPR lanes, each
-//     holding 8 dims (4 for groups of 3+ heads, to save registers): two float4 loads for
-//     an f32 cache, one 16-byte load of packed halves for a binary16 cache (widened to
-//     f32 as they are used); one load instruction across the wave
-//     covers 64/LPR rows, whole 128-byte lines.  Two register sets of 4 rows per lane
-//     group alternate, so one set's loads are in flight while the other is reduced.
+//     holding 32 bytes of it (16 for groups of 3+ heads, to save registers): two float4
+//     loads of an f32 cache, or two 16-byte loads of packed halves of a binary16 cache
+//     (widened to f32 as they are used); one load instruction across the wave covers
+//     64/LPR rows, whole 128-byte lines.  A Q8_0 cache gives each lane 16 codes (one
+//     16-byte load, all in one 32-value block) plus that block's binary16 scale; the
+//     codes are converted as they are used and the scale is applied once per lane and
+//     row: to the lane's partial dot product for K, to the softmax weight for V (each
+//     dequantized value is scale * code exactly, so only the rounding order differs
+//     from dequantize-then-multiply).  Two register sets of 4 rows per lane group
+//     alternate, so one set's loads are in flight while the other is reduced.
 //   * The query vectors of every head of the kv group (up to 8 per pass) stay in
 //     registers, so each K/V element loaded from HBM is used for all of them in-register:
 //     the group's sharing costs no LDS traffic.
@@ -46,11 +51,16 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;        // rows per lane group per step (two steps in flight)
 
-// Dims of a row slice each lane holds: 8 (two float4) for kv groups of up to 2 query
-// heads, 4 (one float4) for larger groups, whose per-head registers would otherwise
-// crowd out the load buffers.
-template <int GP>
-constexpr int dims_per_lane() { return GP <= 2 ? 8 : 4; }
+// Dims of a row slice each lane holds.  f32: 8 (two float4) for kv groups of up to 2
+// query heads, 4 (one float4) for larger groups, whose per-head registers would otherwise
+// crowd out the load buffers.  binary16 and Q8_0: 16 dims (32 or 16 bytes per lane) for
+// groups of up to 2, 8 for up to 4, 4 beyond.
+template <int GP, typename KVT>
+constexpr int dims_per_lane()
+{
+    if constexpr (sizeof(KVT) <= 2) return GP <= 2 ? 16 : (GP <= 4 ? 8 : 4);
+    return GP <= 2 ? 8 : 4;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -77,57 +87,149 @@ __device__ __forceinline__ float group_sum(float x)
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef int32_t intx2 __attribute__((ext_vector_type(2)));
+typedef int32_t intx4 __attribute__((ext_vector_type(4)));
+
+// Where one kv head's slices live in a region: row r's values start at element
+// r * nkt + hk * HD; a Q8_0 region's scales of row r start at byte scale_off +
+// 2 * (r * nkt + hk * HD) / 32.
+struct Slice {
+    const char *region;
+    int64_t scale_off;
+    int32_t nkt, hk;
+};
 
 // How a lane group reads its DPL dims of a row slice (LPR lanes per row).  Raw is what
-// one row occupies in registers until it is used (binary16 stays packed); dim(li, i) is
-// the head dim of the lane's i-th value, so q is loaded in the same order.
+// one row occupies in registers until it is used (binary16 and codes stay packed);
+// get(r, i) is the lane's i-th value (a code for Q8_0), scale(r) the factor that turns
+// codes into values (1 for the float formats); dim(li, i) is the head dim of the lane's
+// i-th value, so q is loaded in the same order.
 //   f32, 8 dims: two float4 at li*4 and 4*LPR + li*4 (each load instruction covers whole
 //                lines of several rows);  f32, 4 dims: one float4 at li*4;
-//   f16, 8 dims: one 16-byte load of 8 halves at li*8;  f16, 4 dims: 4 halves at li*4.
+//   f16, 16 dims: two 16-byte loads of 8 halves at li*8 and 8*LPR + li*8;
+//   f16, 8 dims: one 16-byte load at li*8;  f16, 4 dims: 4 halves at li*4;
+//   Q8_0, DPL dims: DPL codes at li*DPL (16, 8 or 4 bytes) and the scale of their block.
 template <typename KVT, int DPL, int LPR>
 struct RowIO;
+
+template <typename KVT>
+__device__ __forceinline__ const KVT *slice_row(const Slice &s, int64_t row, int hd)
+{
+    return reinterpret_cast<const KVT *>(s.region) + row * s.nkt + (int64_t)s.hk * hd;
+}
+
 template <int LPR>
 struct RowIO<float, 8, LPR> {
     struct Raw { floatx4 a, b; };
-    static __device__ __forceinline__ Raw load(const float *row, int li)
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
+        const float *p = slice_row<float>(s, row, 8 * LPR);
         Raw r;
-        r.a = *reinterpret_cast<const floatx4 *>(row + li * 4);
-        r.b = *reinterpret_cast<const floatx4 *>(row + 4 * LPR + li * 4);
+        r.a = *reinterpret_cast<const floatx4 *>(p + li * 4);
+        r.b = *reinterpret_cast<const floatx4 *>(p + 4 * LPR + li * 4);
         return r;
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
+    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return (i / 4) * 4 * LPR + li * 4 + (i % 4); }
 };
 template <int LPR>
 struct RowIO<float, 4, LPR> {
     typedef floatx4 Raw;
-    static __device__ __forceinline__ Raw load(const float *row, int li)
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return *reinterpret_cast<const floatx4 *>(row + li * 4);
+        return *reinterpret_cast<const floatx4 *>(slice_row<float>(s, row, 4 * LPR) + li * 4);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return r[i]; }
+    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
+};
+template <int LPR>
+struct RowIO<_Float16, 16, LPR> {
+    struct Raw { half8_t a, b; };
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
+    {
+        const _Float16 *p = slice_row<_Float16>(s, row, 16 * LPR);
+        Raw r;
+        r.a = *reinterpret_cast<const half8_t *>(p + li * 8);
+        r.b = *reinterpret_cast<const half8_t *>(p + 8 * LPR + li * 8);
+        return r;
+    }
+    static __device__ __forceinline__ float get(const Raw &r, int i)
+    {
+        return i < 8 ? (float)r.a[i] : (float)r.b[i - 8];
+    }
+    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
+    static __device__ __forceinline__ int dim(int li, int i) { return (i / 8) * 8 * LPR + li * 8 + (i % 8); }
 };
 template <int LPR>
 struct RowIO<_Float16, 8, LPR> {
     typedef half8_t Raw;
-    static __device__ __forceinline__ Raw load(const _Float16 *row, int li)
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return *reinterpret_cast<const half8_t *>(row + li * 8);
+        return *reinterpret_cast<const half8_t *>(slice_row<_Float16>(s, row, 8 * LPR) + li * 8);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
+    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 8 + i; }
 };
 template <int LPR>
 struct RowIO<_Float16, 4, LPR> {
     typedef half4_t Raw;
-    static __device__ __forceinline__ Raw load(const _Float16 *row, int li)
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return *reinterpret_cast<const half4_t *>(row + li * 4);
+        return *reinterpret_cast<const half4_t *>(slice_row<_Float16>(s, row, 4 * LPR) + li * 4);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
+    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
+};
+
+// Signed byte k of w as f32: one v_cvt_f32_i32 with an SDWA sign-extending byte select.
+// (Written out because the compiler, given byte vectors that pass through the
+// double-buffered register sets, unpacks every byte into its own register first.)
+__device__ __forceinline__ float code_to_f32(int32_t w, int k)
+{
+    float f;
+    switch (k) {
+    case 0: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f) : "v"(w)); break;
+    case 1: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(w)); break;
+    case 2: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(w)); break;
+    default: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(w)); break;
+    }
+    return f;
+}
+
+template <int DPL>
+struct CodeVec;
+template <> struct CodeVec<16> { typedef intx4 T; };
+template <> struct CodeVec<8> { typedef intx2 T; };
+template <> struct CodeVec<4> { typedef int32_t T; };
+
+template <int DPL, int LPR>
+struct RowIO<int8_t, DPL, LPR> {
+    static constexpr int HD = DPL * LPR;
+    typedef typename CodeVec<DPL>::T Codes;
+    struct Raw { Codes c; float d; };
+    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
+    {
+        const int64_t v0 = row * s.nkt + (int64_t)s.hk * HD + li * DPL;   // first value
+        Raw r;
+        r.c = *reinterpret_cast<const Codes *>(s.region + v0);
+        r.d = (float)*reinterpret_cast<const _Float16 *>(s.region + s.scale_off + 2 * (v0 / kQ8Block));
+        return r;
+    }
+    // Codes stay packed four to a register until used; a signed byte of a register
+    // converts in one instruction (sign-extending byte select on the operand).
+    static __device__ __forceinline__ float get(const Raw &r, int i)
+    {
+        int32_t w;
+        if constexpr (DPL == 4) w = r.c;
+        else w = r.c[i / 4];
+        return code_to_f32(w, i % 4);
+    }
+    static __device__ __forceinline__ float scale(const Raw &r) { return r.d; }
+    static __device__ __forceinline__ int dim(int li, int i) { return li * DPL + i; }
 };
 
 // Merge (m2, l2) into (m, l) in base-2 units; returns the scale factors for acc.
@@ -145,7 +247,7 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
 template <int HD, int GP, typename KVT>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
 {
-    constexpr int kDimsPerLane = dims_per_lane<GP>();
+    constexpr int kDimsPerLane = dims_per_lane<GP, KVT>();
     constexpr int LPR = HD / kDimsPerLane;   // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave per unrolled step
     using IO = RowIO<KVT, kDimsPerLane, LPR>;
@@ -176,9 +278,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const int r1 = min(r0 + p.rows_per_chunk, vl);
     const int seq = p.seq[b];
     const int nkt = p.n_head_kv * HD;
-    const int64_t region = ((int64_t)seq * p.n_layer + p.layer) * p.region;
-    const KVT *K = static_cast<const KVT *>(p.kc) + region + hk * HD;
-    const KVT *V = static_cast<const KVT *>(p.vc) + region + hk * HD;
+    const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
+    const Slice K{static_cast<const char *>(p.kc) + reg, p.scale_off, nkt, hk};
+    const Slice V{static_cast<const char *>(p.vc) + reg, p.scale_off, nkt, hk};
 
     // The lane's query values in the order its row values arrive (IO::dim).
     float qf[GP][kDimsPerLane];
@@ -211,8 +313,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         for (int u = 0; u < kUnroll; u++) {
             int row = rb + (u * kWaves + wave) * RPW + rg;
             row = row < r1 ? row : r0;  // rows past the chunk re-read row r0 and are masked
-            kf[u] = IO::load(K + (int64_t)row * nkt, li);
-            vf[u] = IO::load(V + (int64_t)row * nkt, li);
+            kf[u] = IO::load(K, row, li);
+            vf[u] = IO::load(V, row, li);
         }
     };
     auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], int step) {
@@ -226,7 +328,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
                 float s = 0.0f;
 #pragma unroll
                 for (int i = 0; i < kDimsPerLane; i++) s += qf[g][i] * IO::get(kf[u], i);
-                s = group_sum<LPR>(s);
+                s = group_sum<LPR>(s * IO::scale(kf[u]));
                 sc[u][g] = valid ? s : -INFINITY;
             }
         }
@@ -235,20 +337,26 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             float mt = sc[0][g];
 #pragma unroll
             for (int u = 1; u < kUnroll; u++) mt = fmaxf(mt, sc[u][g]);
+            // Rescale only when the running max grows (alpha = 0 on the first valid rows);
+            // after the first steps it rarely does, and an unchanged max would multiply by
+            // exactly 1.
             const float mn = fmaxf(m[g], mt);
-            const float ref = (mn == -INFINITY) ? 0.0f : mn;
-            const float alpha = fast_exp2(m[g] - ref);
-            l[g] *= alpha;
+            if (mn > m[g]) {
+                const float alpha = fast_exp2(m[g] - mn);
+                l[g] *= alpha;
 #pragma unroll
-            for (int d = 0; d < kDimsPerLane; d++) acc[g][d] *= alpha;
+                for (int d = 0; d < kDimsPerLane; d++) acc[g][d] *= alpha;
+                m[g] = mn;
+            }
+            const float ref = (m[g] == -INFINITY) ? 0.0f : m[g];
 #pragma unroll
             for (int u = 0; u < kUnroll; u++) {
                 const float pu = fast_exp2(sc[u][g] - ref);
                 l[g] += pu;
+                const float pv = pu * IO::scale(vf[u]);
 #pragma unroll
-                for (int i = 0; i < kDimsPerLane; i++) acc[g][i] += pu * IO::get(vf[u], i);
+                for (int i = 0; i < kDimsPerLane; i++) acc[g][i] += pv * IO::get(vf[u], i);
             }
-            m[g] = mn;
         }
     };
 
@@ -415,8 +523,11 @@ void launch_split(const DecodeParams &p, hipStream_t s)
 template <int HD>
 hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 {
-    if (p.kv_f16) launch_split<HD, _Float16>(p, s);
-    else launch_split<HD, float>(p, s);
+    if constexpr (HD % kQ8Block == 0) {
+        if (p.kv_fmt == kFmtQ8) launch_split<HD, int8_t>(p, s);
+    }
+    if (p.kv_fmt == kFmtF16) launch_split<HD, _Float16>(p, s);
+    else if (p.kv_fmt == kFmtF32) launch_split<HD, float>(p, s);
     if (p.total_chunks > p.n) {  // some entry spans several chunks
         const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head);
         decode_combine_kernel<HD><<<cgrid, 256, 0, s>>>(p);
@@ -426,10 +537,10 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 
 }  // namespace
 
-int32_t decode_block_rows(int32_t hd_kv)
+int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt)
 {
-    // The larger of the two lane layouts' step sizes (both are powers of two).
-    const int lpr = hd_kv / 8;
+    // The largest of the lane layouts' step sizes (all are powers of two).
+    const int lpr = hd_kv / (kv_fmt == kFmtF32 ? 8 : 16);
     return kWaves * (64 / lpr) * kUnroll;
 }
 

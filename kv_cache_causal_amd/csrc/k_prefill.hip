@@ -25,6 +25,8 @@
 //   * Causality from data: a block scans key tiles up to the max position of its tokens;
 //     a wave skips tiles beyond its own max; the per-element mask (key > pos) is a select.
 //   * Heavy query tiles (late positions) are launched first to shorten the tail.
+//   * Region formats: binary16 is widened and Q8_0 dequantized (scale * code, exact in
+//     f32) while a tile is copied into LDS, so the products always see f32 values.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -61,6 +63,21 @@ struct PrefillCfg {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef int32_t intx2 __attribute__((ext_vector_type(2)));
+typedef int32_t intx4 __attribute__((ext_vector_type(4)));
+
+// Signed byte k of w as f32 (one conversion with a sign-extending byte select).
+__device__ __forceinline__ float code_to_f32(int32_t w, int k)
+{
+    float f;
+    switch (k) {
+    case 0: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f) : "v"(w)); break;
+    case 1: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(w)); break;
+    case 2: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(w)); break;
+    default: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(w)); break;
+    }
+    return f;
+}
 
 // How the 256 threads stage one K or V tile (KT rows x HD values) from a region of KVT
 // elements into the f32 LDS tile: each thread moves NCH chunks of CH consecutive values
@@ -71,7 +88,7 @@ template <int HD>
 struct TileIO<HD, float> {
     static constexpr int CH = 4;
     typedef floatx4 Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r)
+    static __device__ __forceinline__ void put(float *lds, const Raw &r, float)
     {
         *reinterpret_cast<floatx4 *>(lds) = r;
     }
@@ -80,12 +97,27 @@ template <int HD>
 struct TileIO<HD, _Float16> {
     static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 8 ? 8 : 4;
     typedef typename std::conditional<CH == 8, half8_t, half4_t>::type Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r)
+    static __device__ __forceinline__ void put(float *lds, const Raw &r, float)
     {
         *reinterpret_cast<floatx4 *>(lds) = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
         if constexpr (CH == 8)
             *reinterpret_cast<floatx4 *>(lds + 4) =
                 floatx4{(float)r[4], (float)r[5], (float)r[6], (float)r[7]};
+    }
+};
+
+// Q8_0: CH codes (all inside one 32-value block) and that block's scale d.
+template <int HD>
+struct TileIO<HD, int8_t> {
+    static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 16 ? 16 : 8;
+    typedef typename std::conditional<CH == 16, intx4, intx2>::type Raw;
+    static __device__ __forceinline__ void put(float *lds, const Raw &r, float d)
+    {
+#pragma unroll
+        for (int w = 0; w < CH / 4; w++)
+            *reinterpret_cast<floatx4 *>(lds + 4 * w) =
+                floatx4{d * code_to_f32(r[w], 0), d * code_to_f32(r[w], 1),
+                        d * code_to_f32(r[w], 2), d * code_to_f32(r[w], 3)};
     }
 };
 
@@ -166,8 +198,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     __syncthreads();
     const int ntiles = s_kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
+    constexpr bool kQ8 = std::is_same<KVT, int8_t>::value;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
+    // Q8_0 scales of this head: row r's at byte scale_off + 2 * (r * nkt + hk * HD) / 32.
+    const char *Ksc = static_cast<const char *>(p.kc) + p.scale_off + 2 * (hk * HD / kQ8Block);
+    const char *Vsc = static_cast<const char *>(p.vc) + p.scale_off + 2 * (hk * HD / kQ8Block);
 
     // Tile staging: thread tid moves chunk #(tid + 256 j) of the tile, j < LD, i.e. row
     // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
@@ -183,6 +219,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     // Native vector registers: with struct types the compiler turns these unconditional
     // copies into an aggregate copy and keeps the arrays in scratch memory.
     typename TIO::Raw kreg[LD], vreg[LD];
+    float ksc[LD], vsc[LD];   // Q8_0 block scales (unused by the float formats)
+    const int nsb = nkt / kQ8Block;
+    const uint32_t soff = (uint32_t)(trow * nsb + tcol / kQ8Block) * 2u;
+    const int64_t sjstride = (int64_t)RSTEP * nsb * 2;
     auto fetch = [&](int key0) {
         const char *kb0 = reinterpret_cast<const char *>(Kh + (int64_t)key0 * nkt);
         const char *vb0 = reinterpret_cast<const char *>(Vh + (int64_t)key0 * nkt);
@@ -190,6 +230,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         for (int j = 0; j < LD; j++) {
             kreg[j] = *reinterpret_cast<const typename TIO::Raw *>(kb0 + j * jstride + toff);
             vreg[j] = *reinterpret_cast<const typename TIO::Raw *>(vb0 + j * jstride + toff);
+        }
+        if constexpr (kQ8) {
+            const char *ks0 = Ksc + (int64_t)key0 * nsb * 2;
+            const char *vs0 = Vsc + (int64_t)key0 * nsb * 2;
+#pragma unroll
+            for (int j = 0; j < LD; j++) {
+                ksc[j] = (float)*reinterpret_cast<const _Float16 *>(ks0 + j * sjstride + soff);
+                vsc[j] = (float)*reinterpret_cast<const _Float16 *>(vs0 + j * sjstride + soff);
+            }
         }
     };
     fetch(0);
@@ -199,8 +248,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
-            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
+            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j], ksc[j]);
+            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j], vsc[j]);
         }
         __syncthreads();
         if (kt + 1 < ntiles) fetch(key0 + KT);
@@ -342,7 +391,10 @@ hipError_t launch_hd_t(const PrefillParams &p, hipStream_t s)
 template <int HD>
 hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
 {
-    return p.kv_f16 ? launch_hd_t<HD, _Float16>(p, s) : launch_hd_t<HD, float>(p, s);
+    if constexpr (HD % kQ8Block == 0) {
+        if (p.kv_fmt == kFmtQ8) return launch_hd_t<HD, int8_t>(p, s);
+    }
+    return p.kv_fmt == kFmtF16 ? launch_hd_t<HD, _Float16>(p, s) : launch_hd_t<HD, float>(p, s);
 }
 
 }  // namespace

@@ -8,6 +8,9 @@
 //         region, a plain copy of the (rotated) k row and the v row.
 // "IV.2: Zero-copy KV cache": the append writes one row in place, no reallocation and no
 // copy of the rows already there.
+// Region formats ("11 · ..." §2.5 "Storage"): f32, binary16 (rounded to nearest even),
+// or Q8_0 blocks of 32 values (scale max|x| / 127 stored as binary16, codes rounded
+// half away from zero with the f32 reciprocal of the f32 scale: the GGML block).
 //
 // Reproducibility: the table holds, for every position p < capacity and pair i, the f32
 // nearest to cos/sin of the f32 angle f32(p) * speed_i, with speed_i the f32 nearest to
@@ -26,6 +29,12 @@ namespace {
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 
 // Store 4 f32 values at dst: as they are for an f32 region, rounded to binary16 (nearest,
 // ties to even: v_cvt_f16_f32 in the default rounding mode) for a half region.
@@ -143,6 +152,18 @@ __device__ __forceinline__ void rotate_heads_vec(const float *src, DT *dst, int3
 // KVT: f32, or binary16 rounded from the f32 result).  QVEC selects the float4 form for q
 // (hd a multiple of 8 for NEOX, of 4 for interleaved); k always qualifies (hd_kv is a
 // multiple of 16).
+// Rotate q of token t in place (f32, whatever the region format).
+template <int STYLE, bool QVEC>
+__device__ __forceinline__ void rotate_q(const AppendParams &p, int32_t t, int32_t pos)
+{
+    if (STYLE != kNone && p.q) {
+        float *qt = p.q + (int64_t)t * p.n_head * p.hd;
+        const float2 *tq = p.tab_q + (int64_t)pos * (p.hd >> 1);
+        if constexpr (QVEC) rotate_heads_vec<STYLE>(qt, qt, p.n_head, p.hd, tq);
+        else rotate_heads<STYLE>(qt, qt, p.n_head, p.hd, tq);
+    }
+}
+
 template <int STYLE, bool QVEC, typename KVT>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
 {
@@ -150,19 +171,14 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
     const int32_t pos = p.pos ? p.pos[t] : p.ipos[t];
     const int32_t seq = p.seq ? p.seq[t] : p.iseq[t];
     const int32_t nkt = p.n_head_kv * p.hd_kv;
-    const int64_t row = ((int64_t)seq * p.n_layer + p.layer) * p.region + (int64_t)pos * nkt;
+    const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
     const float *ksrc = p.k + (int64_t)t * nkt;
     const float *vsrc = p.v + (int64_t)t * nkt;
-    KVT *kdst = static_cast<KVT *>(p.kc) + row;
-    KVT *vdst = static_cast<KVT *>(p.vc) + row;
+    KVT *kdst = reinterpret_cast<KVT *>(static_cast<char *>(p.kc) + reg) + (int64_t)pos * nkt;
+    KVT *vdst = reinterpret_cast<KVT *>(static_cast<char *>(p.vc) + reg) + (int64_t)pos * nkt;
 
+    rotate_q<STYLE, QVEC>(p, t, pos);
     if (STYLE != kNone) {
-        if (p.q) {
-            float *qt = p.q + (int64_t)t * p.n_head * p.hd;
-            const float2 *tq = p.tab_q + (int64_t)pos * (p.hd >> 1);
-            if constexpr (QVEC) rotate_heads_vec<STYLE>(qt, qt, p.n_head, p.hd, tq);
-            else rotate_heads<STYLE>(qt, qt, p.n_head, p.hd, tq);
-        }
         rotate_heads_vec<STYLE>(ksrc, kdst, p.n_head_kv, p.hd_kv,
                                 p.tab_k + (int64_t)pos * (p.hd_kv >> 1));
     } else {
@@ -172,6 +188,95 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p)
     // hd_kv is a multiple of 16, so rows are whole float4s (half4s) and aligned.
     const float4 *vs4 = reinterpret_cast<const float4 *>(vsrc);
     for (int32_t i = threadIdx.x; i < (nkt >> 2); i += blockDim.x) store4(vdst + 4 * i, vs4[i]);
+}
+
+// Values e..e+3 (e a multiple of 4) of one head of width w after rotation, computed
+// with rotate_pair exactly as rotate_heads_vec computes them.  NEOX: all four lie in
+// one half (w / 2 is a multiple of 4), each the first or second output of its pair.
+template <int STYLE>
+__device__ __forceinline__ float4 rotated4(const float *x, int32_t e, int32_t w,
+                                           const float2 *tab)
+{
+    float4 y;
+    if constexpr (STYLE == kNeox) {
+        const int32_t half = w >> 1;
+        const bool lo = e < half;
+        const int32_t i = lo ? e : e - half;
+        const float4 a = *reinterpret_cast<const float4 *>(x + i);
+        const float4 b = *reinterpret_cast<const float4 *>(x + i + half);
+        const float4 t0 = *reinterpret_cast<const float4 *>(tab + i);
+        const float4 t1 = *reinterpret_cast<const float4 *>(tab + i + 2);
+        float4 y0, y1;
+        rotate_pair(a.x, b.x, make_float2(t0.x, t0.y), y0.x, y1.x);
+        rotate_pair(a.y, b.y, make_float2(t0.z, t0.w), y0.y, y1.y);
+        rotate_pair(a.z, b.z, make_float2(t1.x, t1.y), y0.z, y1.z);
+        rotate_pair(a.w, b.w, make_float2(t1.z, t1.w), y0.w, y1.w);
+        y = lo ? y0 : y1;
+    } else if constexpr (STYLE == kInterleaved) {
+        const float4 a = *reinterpret_cast<const float4 *>(x + e);
+        const float4 t = *reinterpret_cast<const float4 *>(tab + e / 2);
+        rotate_pair(a.x, a.y, make_float2(t.x, t.y), y.x, y.y);
+        rotate_pair(a.z, a.w, make_float2(t.z, t.w), y.z, y.w);
+    } else {
+        y = *reinterpret_cast<const float4 *>(x + e);
+    }
+    return y;
+}
+
+// Q8_0 store of values j..j+3 of a row, held by lane group member (idx % 8) of the 8
+// aligned lanes that together hold block j / 32: the block's max |x| is reduced across
+// the 8 lanes (DPP within each half-row), every lane derives the same scale and
+// reciprocal (IEEE f32 division), writes its 4 codes as one dword, and the group's
+// first lane writes the binary16 scale.
+__device__ __forceinline__ void q8_store4(float4 y, int8_t *codes, _Float16 *scales, int32_t j,
+                                          int32_t idx)
+{
+#pragma clang fp contract(off)
+    float a = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
+    a = fmaxf(a, dpp<0xB1>(a));   // lane ^ 1
+    a = fmaxf(a, dpp<0x4E>(a));   // lane ^ 2
+    a = fmaxf(a, dpp<0x141>(a));  // i <-> 7 - i within 8 lanes: the other quad
+    const float d = a / 127.0f;
+    const float r = d != 0.0f ? 1.0f / d : 0.0f;
+    const int32_t c0 = (int32_t)roundf(y.x * r), c1 = (int32_t)roundf(y.y * r);
+    const int32_t c2 = (int32_t)roundf(y.z * r), c3 = (int32_t)roundf(y.w * r);
+    const uint32_t packed = (uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8) |
+                            ((uint32_t)(c2 & 0xff) << 16) | ((uint32_t)(c3 & 0xff) << 24);
+    *reinterpret_cast<uint32_t *>(codes + j) = packed;
+    if ((idx & 7) == 0) scales[j / kQ8Block] = (_Float16)d;
+}
+
+// Q8_0 variant of append_kernel: the same rotation, then each row is quantized block by
+// block as it is stored.  Thread idx handles values 4 idx .. 4 idx + 3 of the row;
+// nkt / 4 is a multiple of 8 and so is the block size, so the 8 lanes of a block are
+// always active together.
+template <int STYLE, bool QVEC>
+__global__ void __launch_bounds__(256) append_q8_kernel(AppendParams p)
+{
+    const int32_t t = blockIdx.x;
+    const int32_t pos = p.pos ? p.pos[t] : p.ipos[t];
+    const int32_t seq = p.seq ? p.seq[t] : p.iseq[t];
+    const int32_t nkt = p.n_head_kv * p.hd_kv;
+    const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
+    const float *ksrc = p.k + (int64_t)t * nkt;
+    const float *vsrc = p.v + (int64_t)t * nkt;
+    char *kr = static_cast<char *>(p.kc) + reg;
+    char *vr = static_cast<char *>(p.vc) + reg;
+    int8_t *kcodes = reinterpret_cast<int8_t *>(kr) + (int64_t)pos * nkt;
+    int8_t *vcodes = reinterpret_cast<int8_t *>(vr) + (int64_t)pos * nkt;
+    _Float16 *kscales = reinterpret_cast<_Float16 *>(kr + p.scale_off) + (int64_t)pos * (nkt / kQ8Block);
+    _Float16 *vscales = reinterpret_cast<_Float16 *>(vr + p.scale_off) + (int64_t)pos * (nkt / kQ8Block);
+    const float2 *tk = STYLE == kNone ? nullptr : p.tab_k + (int64_t)pos * (p.hd_kv >> 1);
+
+    rotate_q<STYLE, QVEC>(p, t, pos);
+    for (int32_t idx = threadIdx.x; idx < (nkt >> 2); idx += blockDim.x) {
+        const int32_t j = idx * 4;
+        const int32_t h = j / p.hd_kv;
+        const int32_t e = j - h * p.hd_kv;
+        const float4 y = rotated4<STYLE>(ksrc + (int64_t)h * p.hd_kv, e, p.hd_kv, tk);
+        q8_store4(y, kcodes, kscales, j, idx);
+        q8_store4(*reinterpret_cast<const float4 *>(vsrc + j), vcodes, vscales, j, idx);
+    }
 }
 
 }  // namespace
@@ -203,10 +308,27 @@ void launch_append_t(const AppendParams &p, hipStream_t s)
     }
 }
 
+void launch_append_q8(const AppendParams &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.nt), block(256);
+    switch (p.style) {
+    case kNeox:
+        if (p.hd % 8 == 0) append_q8_kernel<kNeox, true><<<grid, block, 0, s>>>(p);
+        else append_q8_kernel<kNeox, false><<<grid, block, 0, s>>>(p);
+        break;
+    case kInterleaved:
+        if (p.hd % 4 == 0) append_q8_kernel<kInterleaved, true><<<grid, block, 0, s>>>(p);
+        else append_q8_kernel<kInterleaved, false><<<grid, block, 0, s>>>(p);
+        break;
+    default: append_q8_kernel<kNone, false><<<grid, block, 0, s>>>(p); break;
+    }
+}
+
 hipError_t launch_append(const AppendParams &p, hipStream_t s)
 {
     if (p.nt <= 0) return hipSuccess;
-    if (p.kv_f16) launch_append_t<_Float16>(p, s);
+    if (p.kv_fmt == kFmtQ8) launch_append_q8(p, s);
+    else if (p.kv_fmt == kFmtF16) launch_append_t<_Float16>(p, s);
     else launch_append_t<float>(p, s);
     return hipGetLastError();
 }

@@ -71,10 +71,10 @@ struct Staging {
 struct kvc_cache {
     kvc::Geometry g;
     int device = 0;
-    int32_t kv_f16 = 0;       // regions hold binary16 instead of f32
-    size_t esize = 4;         // bytes per region element
+    int32_t kv_fmt = kvc::kFmtF32;
     char *K = nullptr, *V = nullptr;
-    int64_t region = 0;       // elements per (seq, layer) region
+    int64_t region_bytes = 0;  // bytes per (seq, layer) region
+    int64_t scale_off = 0;     // Q8_0: byte offset of the block scales within a region
     std::vector<int32_t> hw;
     mutable Staging st;
     mutable std::vector<RopeTable> tables;
@@ -212,22 +212,26 @@ kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32
     if (!out) return fail(KVC_E_ARG, "out is NULL");
     *out = nullptr;
     std::string msg;
-    kvc_status st = kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, msg);
+    kvc_status st = kvc::check_alloc(n_seq, n_layer, n_head_kv, hd_kv, capacity, (int32_t)dtype,
+                                     msg);
     if (st != KVC_OK) return fail(st, msg);
-    if (dtype != KVC_KV_F32 && dtype != KVC_KV_F16)
-        return fail(KVC_E_ARG, "unknown region format " + std::to_string((int)dtype));
 
     kvc_cache *c = new (std::nothrow) kvc_cache();
     if (!c) return fail(KVC_E_NOMEM, "handle allocation failed");
     c->g = kvc::Geometry{n_seq, n_layer, n_head_kv, hd_kv, capacity};
-    c->kv_f16 = dtype == KVC_KV_F16;
-    c->esize = c->kv_f16 ? 2 : 4;
+    c->kv_fmt = (int32_t)dtype;
     const int64_t rows = ((int64_t)capacity + kvc::kRegionRowAlign - 1) / kvc::kRegionRowAlign *
                          kvc::kRegionRowAlign;
-    c->region = rows * n_head_kv * hd_kv;
+    const int64_t vals = rows * n_head_kv * hd_kv;
+    if (dtype == KVC_KV_Q8_0) {
+        c->scale_off = vals;                                    // int8 codes first
+        c->region_bytes = vals + vals / kvc::kQ8Block * 2;      // then binary16 scales
+    } else {
+        c->region_bytes = vals * (dtype == KVC_KV_F16 ? 2 : 4);
+    }
     c->hw.assign((size_t)n_seq * n_layer, 0);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region * c->esize;
+    const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region_bytes;
 
     auto cleanup = [&](kvc_status code, const std::string &m) {
         if (c->K) hipFree(c->K);
@@ -273,7 +277,7 @@ kvc_status kv_view(const kvc_cache *c, int32_t seq, int32_t layer, void **k, voi
     if (!c || !k || !v) return fail(KVC_E_ARG, "NULL handle or output pointer");
     if (seq < 0 || seq >= c->g.n_seq || layer < 0 || layer >= c->g.n_layer)
         return fail(KVC_E_ARG, "seq/layer out of range");
-    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region * c->esize;
+    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region_bytes;
     *k = c->K + off;
     *v = c->V + off;
     return KVC_OK;
@@ -328,7 +332,8 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
     p.seq = inline_args ? nullptr : dev + nt;
     p.tab_q = tab_q;
     p.tab_k = tab_k;
-    p.region = c->region;
+    p.region_bytes = c->region_bytes;
+    p.scale_off = c->scale_off;
     p.nt = nt;
     p.n_head = n_head;
     p.hd = hd;
@@ -337,7 +342,7 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
     p.n_layer = c->g.n_layer;
     p.layer = layer;
     p.style = (int32_t)style;
-    p.kv_f16 = c->kv_f16;
+    p.kv_fmt = c->kv_fmt;
     hipError_t e = kvc::launch_append(p, s);
     if (e != hipSuccess) {
         if (!inline_args) staging_abort(c->st);
@@ -365,13 +370,14 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     std::vector<int32_t> ints(pos, pos + nt);
     const int32_t *dev = nullptr;
     if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
-    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region * c->esize;
+    const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region_bytes;
     kvc::PrefillParams p{};
     p.q = q;
     p.out = out;
     p.kc = c->K + off;
     p.vc = c->V + off;
-    p.kv_f16 = c->kv_f16;
+    p.kv_fmt = c->kv_fmt;
+    p.scale_off = c->scale_off;
     p.pos = dev;
     p.nt = nt;
     p.n_head = n_head;
@@ -404,7 +410,7 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
     // Large ones: ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the
     // per-chunk overheads (query load, merges, partial record, combine) stay small next
     // to the stream.  KVC_SPLIT_ROWS overrides the size (tuning only, never the result).
-    const int32_t br = kvc::decode_block_rows(c->g.hd_kv);
+    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, c->kv_fmt);
     int64_t total_rows = 0, max_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) {
         total_rows += (int64_t)pos[b] + 1;
@@ -446,7 +452,8 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
         p.part = c->part;
         p.kc = c->K;
         p.vc = c->V;
-        p.region = c->region;
+        p.region_bytes = c->region_bytes;
+        p.scale_off = c->scale_off;
         p.n = n;
         p.n_head = n_head;
         p.hd = hd;
@@ -454,7 +461,7 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
         p.hd_kv = c->g.hd_kv;
         p.n_layer = c->g.n_layer;
         p.layer = layer;
-        p.kv_f16 = c->kv_f16;
+        p.kv_fmt = c->kv_fmt;
         p.rows_per_chunk = (int32_t)rows;
         p.qscale = log2e_times(scale);
         int32_t chunks = 0;

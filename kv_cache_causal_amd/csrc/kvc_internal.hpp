@@ -9,12 +9,18 @@
 
 namespace kvc {
 
-// Cache layout: K[n_seq][n_layer][rows][n_head_kv * hd_kv] (V likewise) with
-// rows = capacity rounded up to a multiple of kRegionRowAlign; `region` is
-// rows * n_head_kv * hd_kv elements, f32 or binary16 (`kv_f16`).  Rows at or past the
-// capacity stay zero and are never inside a window; they let the prefill kernel load
-// whole key tiles unconditionally.
+// Cache layout: one region per (seq, layer), K and V alike, `region_bytes` apart, each
+// holding rows = capacity rounded up to a multiple of kRegionRowAlign rows of
+// nkt = n_head_kv * hd_kv values:
+//   kFmtF32, kFmtF16: [rows][nkt] f32 or binary16 values;
+//   kFmtQ8:           [rows][nkt] int8 codes, then at byte `scale_off` (= rows * nkt)
+//                     [rows][nkt / 32] binary16 block scales (Q8_0: 32 values per
+//                     block, value = scale * code).
+// Rows at or past the capacity stay zero and are never inside a window; they let the
+// prefill kernel load whole key tiles unconditionally.
 constexpr int kRegionRowAlign = 64;
+enum KvFmt : int32_t { kFmtF32 = 0, kFmtF16 = 1, kFmtQ8 = 2 };
+constexpr int kQ8Block = 32;
 
 // ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------
 hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
@@ -27,14 +33,14 @@ constexpr int kInlineTokens = 64;
 struct AppendParams {
     float *q;               // [nt][n_head][hd] or nullptr
     const float *k, *v;     // [nt][n_head_kv][hd_kv]
-    void *kc, *vc;          // cache bases (f32 or binary16 elements)
+    void *kc, *vc;          // cache bases
     const int32_t *pos;     // device [nt], or nullptr: use ipos
     const int32_t *seq;     // device [nt], or nullptr: use iseq
     const float2 *tab_q;    // [capacity][hd/2] (nullptr if q is nullptr or style NONE)
     const float2 *tab_k;    // [capacity][hd_kv/2] (nullptr for style NONE)
-    int64_t region;
+    int64_t region_bytes, scale_off;
     int32_t nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style;
-    int32_t kv_f16;         // regions hold binary16 (rounded to nearest even on store)
+    int32_t kv_fmt;         // KvFmt: the store rounds to binary16 or quantizes to Q8_0
     int32_t ipos[kInlineTokens], iseq[kInlineTokens];
 };
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
@@ -47,9 +53,9 @@ struct DecodeParams {
     const float *q;          // [n][n_head][hd] (this launch's entries)
     float *out;              // [n][n_head][hd_kv]
     float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
-    const void *kc, *vc;     // cache bases (f32 or binary16 elements)
-    int64_t region;
-    int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer, kv_f16;
+    const void *kc, *vc;     // cache bases
+    int64_t region_bytes, scale_off;
+    int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer, kv_fmt;
     int32_t rows_per_chunk, total_chunks;
     float qscale;            // scale * log2(e): scores are kept in base-2 units
     int32_t pos[kInlineEntries];
@@ -58,16 +64,17 @@ struct DecodeParams {
 };
 // Rows per block iteration of the split-K kernel for a kv head dim (chunks should be a
 // multiple of it).
-int32_t decode_block_rows(int32_t hd_kv);
+int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
 struct PrefillParams {
     const float *q;          // [nt][n_head][hd]
     float *out;              // [nt][n_head][hd_kv]
-    const void *kc, *vc;     // this (seq, layer)'s K and V regions (f32 or binary16)
+    const void *kc, *vc;     // this (seq, layer)'s K and V regions
+    int64_t scale_off;       // Q8_0: byte offset of the scales in a region
     const int32_t *pos;      // device [nt]
-    int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity, kv_f16;
+    int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity, kv_fmt;
     float qscale;            // scale * log2(e)
 };
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);

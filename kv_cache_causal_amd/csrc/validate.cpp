@@ -63,7 +63,7 @@ bool supported_kv_head_dim(int32_t hd_kv)
 }
 
 kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
-                       int32_t capacity, std::string &msg)
+                       int32_t capacity, int32_t dtype, std::string &msg)
 {
     if (n_seq <= 0 || n_layer <= 0 || n_head_kv <= 0) {
         msg = "n_seq, n_layer and n_head_kv must be >= 1";
@@ -76,6 +76,15 @@ kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_
     if (capacity <= 0 || capacity > KVC_MAX_CAPACITY) {
         msg = "capacity " + s(capacity) + " outside [1, 2^24]";
         return KVC_E_ARG;
+    }
+    if (dtype != KVC_KV_F32 && dtype != KVC_KV_F16 && dtype != KVC_KV_Q8_0) {
+        msg = "unknown region format " + s(dtype);
+        return KVC_E_ARG;
+    }
+    // Q8_0 blocks of 32 run along a row; each must lie within one kv head.
+    if (dtype == KVC_KV_Q8_0 && hd_kv % 32 != 0) {
+        msg = "a Q8_0 cache needs hd_kv a multiple of 32, got " + s(hd_kv);
+        return KVC_E_GEOMETRY;
     }
     // Row width and region sizes must fit the 64-bit offsets the kernels use.
     const double bytes = 4.0 * n_seq * n_layer * (double)capacity * n_head_kv * hd_kv;

@@ -23,7 +23,7 @@ struct Geometry {
 bool supported_kv_head_dim(int32_t hd_kv);
 
 kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
-                       int32_t capacity, std::string &msg);
+                       int32_t capacity, int32_t dtype, std::string &msg);
 
 kvc_status check_append(const Geometry &g, int32_t layer, int32_t nt, const int32_t *seq_ids,
                         const int32_t *pos, const void *q, int32_t n_head, int32_t hd,

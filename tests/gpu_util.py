@@ -63,7 +63,44 @@ def assert_close(gpu, orc, what):
         f"{(rel[np.abs(orc) > 1e-3].max() if (np.abs(orc) > 1e-3).any() else 0.0):.3e}")
 
 
+def assert_equal(gpu, orc, what):
+    """Exact equality of integer arrays (codes, bit patterns)."""
+    gpu, orc = np.asarray(gpu), np.asarray(orc)
+    assert gpu.shape == orc.shape, (what, gpu.shape, orc.shape)
+    if not np.array_equal(gpu, orc):
+        bad = np.argwhere(gpu != orc)
+        idx = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements differ; first at {idx}: "
+                             f"gpu {gpu[idx]!r} oracle {orc[idx]!r}")
+
+
+def compare_q8_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
+    """Q8_0 regions: the library's code and scale planes against the oracle's 34-byte
+    blocks, bit for bit; the padding rows past the capacity must still be zero."""
+    import kv_cache_causal_amd as kvc
+    from oracle import q8_split
+    cap, nkt = orc_cache.capacity, orc_cache.nkt
+    sel = slice(None) if rows is None else rows
+    for name, (codes, scales), reg in zip("KV", kvc.kv_read(lib_cache, seq, layer),
+                                          (orc_cache.k(seq, layer), orc_cache.v(seq, layer))):
+        codes, scales = host(codes), host(scales).view(np.uint16)
+        osc, ocd = q8_split(reg)
+        assert_equal(codes[:cap][sel], ocd.reshape(cap, nkt)[sel], f"{what} {name} codes [{seq}][{layer}]")
+        assert_equal(scales[:cap][sel], osc[sel], f"{what} {name} scales [{seq}][{layer}]")
+        assert not codes[cap:].any() and not scales[cap:].any(), f"{what} {name}: padding rows written"
+
+
 def compare_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
+    import kv_cache_causal_amd as kvc
+    if lib_cache.dtype == kvc.KV_Q8_0:
+        compare_q8_cache(lib_cache, orc_cache, seq, layer, what, rows)
+    else:
+        compare_dense_cache(lib_cache, orc_cache, seq, layer, what, rows)
+    assert kvc.kv_seq_len(lib_cache, seq, layer) == orc_cache.seq_len(seq, layer), \
+        (what, seq, layer, kvc.kv_seq_len(lib_cache, seq, layer), orc_cache.seq_len(seq, layer))
+
+
+def compare_dense_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
     import kv_cache_causal_amd as kvc
     K, V = kvc.kv_read(lib_cache, seq, layer)
     K, V = host(K), host(V)   # float16 arrays for a binary16 cache: compared as bits
@@ -72,8 +109,6 @@ def compare_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
         K, V, ok, ov = K[rows], V[rows], ok[rows], ov[rows]
     assert_bitwise(K, ok, f"{what} K[{seq}][{layer}]")
     assert_bitwise(V, ov, f"{what} V[{seq}][{layer}]")
-    assert kvc.kv_seq_len(lib_cache, seq, layer) == orc_cache.seq_len(seq, layer), \
-        (what, seq, layer, kvc.kv_seq_len(lib_cache, seq, layer), orc_cache.seq_len(seq, layer))
 
 
 class Pair:

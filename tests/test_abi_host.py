@@ -59,6 +59,11 @@ def test_null_handle_is_rejected_without_device_work():
     out = ctypes.c_void_p()
     assert L.kv_alloc(ctypes.byref(out), 1, 1, 1, 24, 8, None) == kvc.E_ARG
     assert out.value is None and "unsupported" in kvc.kv_last_error()
+    # Region formats are checked before any device call too.
+    assert L.kv_alloc_typed(ctypes.byref(out), 1, 1, 2, 16, 8, kvc.KV_Q8_0, None) == kvc.E_GEOMETRY
+    assert out.value is None and "Q8_0" in kvc.kv_last_error()
+    assert L.kv_alloc_typed(ctypes.byref(out), 1, 1, 2, 32, 8, 3, None) == kvc.E_ARG
+    assert out.value is None and "format" in kvc.kv_last_error()
 
 
 # ---- validation parity with the oracle (library checks via the host-only shim) ----
@@ -69,7 +74,7 @@ def hc():
         pytest.skip("host-check shim not built")
     L = ctypes.CDLL(HOSTCHECK)
     p, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-    L.hc_check_alloc.argtypes = [i32] * 5
+    L.hc_check_alloc.argtypes = [i32] * 6
     L.hc_check_append.argtypes = [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, i32]
     L.hc_check_prefill.argtypes = [p, i32, i32, i32, p, p, i32, i32, f32, p]
     L.hc_check_decode.argtypes = [p, i32, i32, p, p, p, i32, i32, f32, p]
@@ -195,7 +200,21 @@ def test_decode_checks_match_oracle(hc, name, kw):
 
 
 def test_alloc_checks(hc):
-    assert hc.hc_check_alloc(1, 1, 8, 128, 40960) == kvc.OK
-    for bad in [(0, 1, 1, 16, 8), (1, 0, 1, 16, 8), (1, 1, 0, 16, 8), (1, 1, 1, 24, 8),
-                (1, 1, 1, 16, 0), (1, 1, 1, 16, (1 << 24) + 1)]:
-        assert hc.hc_check_alloc(*bad) == kvc.E_ARG, bad
+    for dt in (kvc.KV_F32, kvc.KV_F16, kvc.KV_Q8_0):
+        assert hc.hc_check_alloc(1, 1, 8, 128, 40960, dt) == kvc.OK
+        for bad in [(0, 1, 1, 32, 8), (1, 0, 1, 32, 8), (1, 1, 0, 32, 8), (1, 1, 1, 24, 8),
+                    (1, 1, 1, 32, 0), (1, 1, 1, 32, (1 << 24) + 1)]:
+            assert hc.hc_check_alloc(*bad, dt) == kvc.E_ARG, (bad, dt)
+    assert hc.hc_check_alloc(1, 1, 2, 16, 8, 3) == kvc.E_ARG
+    # The oracle accepts and refuses the same formats and geometries: Q8_0 blocks must
+    # lie inside one kv head (hd_kv a multiple of 32).
+    from oracle import Oracle
+    L = Oracle().L
+    for hdk in (16, 32, 64, 128, 256):
+        for dt in (kvc.KV_F32, kvc.KV_F16, kvc.KV_Q8_0):
+            lib_ok = hc.hc_check_alloc(1, 1, 2, hdk, 8, dt) == kvc.OK
+            h = L.orc_cache_new_typed(1, 1, 2, hdk, 8, dt)
+            assert lib_ok == bool(h), (hdk, dt)
+            if h:
+                L.orc_cache_free(h)
+    assert hc.hc_check_alloc(1, 1, 2, 16, 8, kvc.KV_Q8_0) == kvc.E_GEOMETRY

@@ -36,9 +36,26 @@ HEADS = [
 ]
 
 
-@pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
+FORMATS = pytest.mark.parametrize("kv", [0, 1, 2], ids=["f32", "f16", "q8_0"])
+
+
+def v_row(pair, kv, seq, row):
+    """Row `row` of the oracle's V region as f32 values (widened or dequantized)."""
+    v = pair.o.v(seq, 0)[row]
+    if kv == 1:
+        return v.view(np.float16).astype(np.float32)
+    if kv == 2:
+        from oracle import q8_split
+        sc, cd = q8_split(v)
+        return (sc.view(np.float16).astype(np.float32)[:, None] * cd.astype(np.float32)).ravel()
+    return v
+
+
+@FORMATS
 @pytest.mark.parametrize("nh,nkv,hd,hdk", HEADS, ids=[f"h{a}kv{b}d{c}dk{d}" for a, b, c, d in HEADS])
 def test_decode_and_prefill_shapes(nh, nkv, hd, hdk, kv):
+    if kv == 2 and hdk % 32:
+        pytest.skip("Q8_0 needs hd_kv a multiple of 32")
     say(f"shape n_head={nh} n_head_kv={nkv} hd={hd} hd_kv={hdk} kv={kv}")
     cap, rows = 300, 300
     p = build(1, 2, nh, nkv, hd, hdk, cap, rows, kv=kv)
@@ -47,10 +64,9 @@ def test_decode_and_prefill_shapes(nh, nkv, hd, hdk, kv):
     seqs, pos = [0, 1, 0], [299, 0, 137]
     got, want = p.decode(0, seqs, pos, dev(q), q, nh, hd, 0.31)
     assert_close(got, want, "decode")
-    # A one-row window returns that V row exactly (widened from binary16 if stored so).
-    v0 = p.o.v(1, 0)[0]
-    if kv:
-        v0 = v0.view(np.float16).astype(np.float32)
+    # A one-row window returns that V row exactly (widened from binary16 or dequantized
+    # from Q8_0 if stored so).
+    v0 = v_row(p, kv, 1, 0)
     for h in range(nh):
         assert_bitwise(got[1, h], v0[(h // (nh // nkv)) * hdk:][:hdk], "pos 0 = v0")
     # Prefill: 77 tokens (ragged tile), positions out of order with repeats.
@@ -62,7 +78,7 @@ def test_decode_and_prefill_shapes(nh, nkv, hd, hdk, kv):
     p.close()
 
 
-@pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
+@FORMATS
 @pytest.mark.parametrize("style", [0, 1, 2], ids=["neox", "interleaved", "none"])
 def test_rope_styles_and_hd_gt_hd_kv(style, kv):
     say(f"rope style {style} kv={kv}")
@@ -217,3 +233,39 @@ def test_f16_store_rounding_edges(style):
     p.append(0, [0] * 100, np.arange(100), None, 4, 64, k, v, 1e6, 1.0, style)
     compare_cache(p.g, p.o, 0, 0, "f16 edges")
     p.close()
+
+
+@pytest.mark.parametrize("style", [0, 1, 2], ids=["neox", "interleaved", "none"])
+def test_q8_store_edges(style):
+    """Q8_0 stores bit-identical to the oracle's blocks: the hand-derived blocks (ties
+    away from zero, a scale binary16 cannot hold, a subnormal scale, zero blocks) and
+    random blocks spanning tiny (zero or subnormal scale) to huge (infinite scale)
+    magnitudes; then attention over them."""
+    import json
+    import os
+    say(f"q8 store edges style {style}")
+    p = Pair(1, 1, 2, 64, 128, dtype=2)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "q8_0_blocks.json")) as f:
+        blocks = [np.array(b["x"], np.float32) for b in json.load(f)["blocks"]]
+    rng = np.random.default_rng(91)
+    mags = np.array([1e-12, 1e-9, 1e-7, 1e-5, 1e-3, 1.0, 300.0, 1e5, 1e7], np.float32)
+    k = rng.standard_normal((100, 4, 32)) * mags[rng.integers(0, len(mags), (100, 4, 1))]
+    v = rng.standard_normal((100, 4, 32)) * mags[rng.integers(0, len(mags), (100, 4, 1))]
+    k, v = k.astype(np.float32), v.astype(np.float32)
+    for i, b in enumerate(blocks):      # rows 0..4: the worked blocks, in both regions
+        k[i, :] = b
+        v[i, :] = b[::-1]
+    k, v = k.reshape(100, 2, 64), v.reshape(100, 2, 64)
+    p.append(0, [0] * 100, np.arange(100), None, 4, 64, k, v, 1e6, 1.0, style)
+    compare_cache(p.g, p.o, 0, 0, "q8 edges")
+    # Attention over the worked rows only (a 1e7 block's scale overflows to infinity).
+    q = custom(92, (3, 4, 64))
+    got, want = p.decode(0, [0, 0, 0], [0, 2, 4], dev(q), q, 4, 64, 0.125)
+    assert_close(got, want, "q8 decode over edge blocks")
+    p.close()
+
+
+def test_q8_geometry_is_checked():
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_alloc(1, 1, 2, 16, 64, dtype=kvc.KV_Q8_0)
+    assert e.value.status == kvc.E_GEOMETRY

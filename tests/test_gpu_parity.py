@@ -15,8 +15,9 @@ from tests.gpu_util import Pair, assert_close, compare_cache, dev, say
 
 pytestmark = pytest.mark.gpu
 
-# Region formats: f32, and the binary16 cache (store rounds to half, attention widens).
-KV = pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
+# Region formats: f32, the binary16 cache (store rounds to half, attention widens) and
+# the Q8_0 cache (store quantizes 32-value blocks, attention dequantizes).
+KV = pytest.mark.parametrize("kv", [0, 1, 2], ids=["f32", "f16", "q8_0"])
 
 
 def fill(pair, w, seq, layer, n_rows, chunk=4096):
@@ -33,6 +34,8 @@ def fill(pair, w, seq, layer, n_rows, chunk=4096):
 @KV
 def test_c1_tiny(kv):
     w = W.C1
+    if kv == 2:
+        pytest.skip("Q8_0 blocks need hd_kv a multiple of 32; this workload has hd_kv 16")
     say(f"C1 {w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     nt = w.extra["prefill"]
