@@ -58,6 +58,8 @@ def _bind(lib):
         "orc_append_rope": (ctypes.c_int, [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, i32]),
         "orc_attn_prefill": (ctypes.c_int, [p, i32, i32, i32, p, p, i32, i32, f32, p, i32]),
         "orc_attn_decode": (ctypes.c_int, [p, i32, i32, p, p, p, i32, i32, f32, p, i32]),
+        "orc_attn_decode_runs": (ctypes.c_int, [p, i32, i32, p, p, p, p, p, i32, i32, f32, p,
+                                                i32]),
         "orc_max_threads": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -162,6 +164,18 @@ def q8_split(blocks):
     return scales, codes
 
 
+def runs_csr(runs):
+    """Per-query lists of (start, len) runs -> (run_off [n+1], run_start, run_len) int32."""
+    off = np.zeros(len(runs) + 1, np.int32)
+    starts, lens = [], []
+    for b, rl in enumerate(runs):
+        for st, ln in rl:
+            starts.append(st)
+            lens.append(ln)
+        off[b + 1] = len(starts)
+    return off, np.array(starts, np.int32), np.array(lens, np.int32)
+
+
 class OracleCache:
     """The oracle's KV cache: zeroed regions [n_seq][n_layer][capacity][n_head_kv*hd_kv] of
     f32 values (dtype KV_F32) or binary16 bit patterns (KV_F16)."""
@@ -244,4 +258,18 @@ class OracleCache:
         out = np.zeros((n, n_head, self.hd_kv), np.float32)
         st = self.L.orc_attn_decode(self.h, layer, n, _ptr(seq_ids), _ptr(pos), _ptr(q), n_head,
                                     hd, scale, _ptr(out), nthreads)
+        return st, out
+
+    def attn_decode_runs(self, layer, seq_ids, runs, q, n_head, hd, scale, nthreads=0):
+        """runs: per query, a list of (start, len) cell runs (its explicit window)."""
+        seq_ids = _i32(seq_ids)
+        n = int(seq_ids.shape[0])
+        off, starts, lens = runs_csr(runs)
+        if starts.size == 0:   # keep valid pointers for the call
+            starts, lens = np.zeros(1, np.int32), np.zeros(1, np.int32)
+        q = _f32(q)
+        out = np.zeros((n, n_head, self.hd_kv), np.float32)
+        st = self.L.orc_attn_decode_runs(self.h, layer, n, _ptr(seq_ids), _ptr(off), _ptr(starts),
+                                         _ptr(lens), _ptr(q), n_head, hd, scale, _ptr(out),
+                                         nthreads)
         return st, out

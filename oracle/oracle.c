@@ -430,21 +430,23 @@ static const float *head_row(const void *reg, int32_t dtype, size_t j, int32_t n
     return buf;
 }
 
-/* One query row against rows [0, vl) of one kv head's slice of the regions.
+/* One query row against vl rows of one kv head's slice of the regions: rows [0, vl), or,
+ * when `cells` is given, rows cells[0 .. vl) in that order (an explicit window).
  *   score_j = (q . k_j) * scale                 (f32)
  *   e_j     = exp(score_j - max_j score_j)      (f32)
  *   sum     = sum_j e_j                          (f64)
  *   w_j     = e_j * (f32)(1 / sum)               (f32)
  *   out     = sum_j w_j * v_j, in j order        (f32)
- * Rows at or beyond vl are the masked tail: their weight is exp(-inf) = 0 exactly and
+ * Rows outside the window are the masked tail: their weight is exp(-inf) = 0 exactly and
  * their zero contribution is not formed. */
 static void attend_row(const float *qrow, const void *kreg, const void *vreg, int32_t dtype,
-                       int32_t nkt, int32_t hk, int32_t hd_kv, int32_t vl, float scale,
-                       float *scr, float *rowbuf, float *out)
+                       int32_t nkt, int32_t hk, int32_t hd_kv, const int32_t *cells, int32_t vl,
+                       float scale, float *scr, float *rowbuf, float *out)
 {
     float mx = -INFINITY;
     for (int32_t j = 0; j < vl; j++) {
-        const float *kr = head_row(kreg, dtype, (size_t)j, nkt, hk, hd_kv, rowbuf);
+        const size_t row = cells ? (size_t)cells[j] : (size_t)j;
+        const float *kr = head_row(kreg, dtype, row, nkt, hk, hd_kv, rowbuf);
         float s = dot_f32(hd_kv, qrow, kr) * scale;
         scr[j] = s;
         if (s > mx) mx = s;
@@ -459,7 +461,8 @@ static void attend_row(const float *qrow, const void *kreg, const void *vreg, in
     for (int32_t j = 0; j < vl; j++) scr[j] *= inv;
     for (int32_t d = 0; d < hd_kv; d++) out[d] = 0.0f;
     for (int32_t j = 0; j < vl; j++) {
-        const float *vr = head_row(vreg, dtype, (size_t)j, nkt, hk, hd_kv, rowbuf);
+        const size_t vrow = cells ? (size_t)cells[j] : (size_t)j;
+        const float *vr = head_row(vreg, dtype, vrow, nkt, hk, hd_kv, rowbuf);
         float w = scr[j];
         for (int32_t d = 0; d < hd_kv; d++) out[d] += w * vr[d];
     }
@@ -474,9 +477,11 @@ static int check_heads(const orc_cache *c, int32_t n_head, int32_t hd)
 }
 
 /* Work unit: one (token, query head) row.  Units never reduce against each other and
- * each owns its scratch, so the result is the same at any thread count. */
+ * each owns its scratch, so the result is the same at any thread count.  Token t's window
+ * is rows [0, pos[t]], or, when `cells` is given, the ncell[t] rows cells[t][..]. */
 static int attend_units(const void *const *kregs, const void *const *vregs, int32_t dtype,
-                        const int32_t *pos, int32_t nt, const float *q, int32_t n_head,
+                        const int32_t *pos, const int32_t *const *cells, const int32_t *ncell,
+                        int32_t nt, const float *q, int32_t n_head,
                         int32_t hd, int32_t n_head_kv, int32_t hd_kv, int32_t max_vl,
                         float scale, float *out, int32_t nthreads)
 {
@@ -503,9 +508,9 @@ static int attend_units(const void *const *kregs, const void *const *vregs, int3
             for (int64_t u = 0; u < units; u++) {
                 int32_t t = (int32_t)(u / n_head), h = (int32_t)(u % n_head);
                 int32_t hk = h / gqa;
-                int32_t vl = pos[t] + 1;
+                int32_t vl = cells ? ncell[t] : pos[t] + 1;
                 attend_row(q + ((size_t)t * n_head + h) * hd, kregs[t], vregs[t], dtype, nkt,
-                           hk, hd_kv, vl, scale, scr, rowbuf,
+                           hk, hd_kv, cells ? cells[t] : NULL, vl, scale, scr, rowbuf,
                            out + ((size_t)t * n_head + h) * hd_kv);
             }
         }
@@ -540,7 +545,7 @@ int orc_attn_prefill(const orc_cache *c, int32_t seq, int32_t layer, int32_t nt,
     const void *kreg = orc_cache_region((orc_cache *)c, 0, seq, layer);
     const void *vreg = orc_cache_region((orc_cache *)c, 1, seq, layer);
     for (int32_t t = 0; t < nt; t++) { kr[t] = kreg; vr[t] = vreg; }
-    st = attend_units(kr, vr, c->dtype, pos, nt, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl,
+    st = attend_units(kr, vr, c->dtype, pos, NULL, NULL, nt, q, n_head, hd, c->n_head_kv, c->hd_kv, max_vl,
                       scale, out, nthreads);
     free(kr); free(vr);
     return st;
@@ -572,9 +577,88 @@ int orc_attn_decode(const orc_cache *c, int32_t layer, int32_t n_seq, const int3
         kr[b] = orc_cache_region((orc_cache *)c, 0, seq_ids[b], layer);
         vr[b] = orc_cache_region((orc_cache *)c, 1, seq_ids[b], layer);
     }
-    st = attend_units(kr, vr, c->dtype, pos, n_seq, q, n_head, hd, c->n_head_kv, c->hd_kv,
+    st = attend_units(kr, vr, c->dtype, pos, NULL, NULL, n_seq, q, n_head, hd, c->n_head_kv, c->hd_kv,
                       max_vl, scale, out, nthreads);
     free(kr); free(vr);
+    return st;
+}
+
+static int cmp_run(const void *a, const void *b)
+{
+    const int32_t *x = (const int32_t *)a, *y = (const int32_t *)b;
+    return (x[0] > y[0]) - (x[0] < y[0]);
+}
+
+/* Decode over explicit windows ("13 · The decode loop and graph reuse" §2.2, Budget 3:
+ * the cells a query may read are an input -- a list of runs -- resolved by the caller,
+ * not a bound derived from positions; "Pitfalls" item 4: rows past a rolled-back cursor
+ * are never read because the window does not name them).
+ * Query b attends, in its (seq_ids[b], layer) regions, the cells of its runs
+ * r = run_off[b] .. run_off[b+1]-1, each run the rows [run_start[r], run_start[r] +
+ * run_len[r]), taken in the listed order.  Reading of the run list (the pages name it but
+ * do not define its encoding): every query has at least one run; every run is non-empty
+ * and inside the region; the runs of one query name each cell at most once (a repeated
+ * cell is refused, ORC_E_DUP, since it would count twice in the softmax).
+ * q: [n][n_head][hd]; out: [n][n_head][hd_kv]. */
+int orc_attn_decode_runs(const orc_cache *c, int32_t layer, int32_t n, const int32_t *seq_ids,
+                         const int32_t *run_off, const int32_t *run_start,
+                         const int32_t *run_len, const float *q, int32_t n_head, int32_t hd,
+                         float scale, float *out, int32_t nthreads)
+{
+    if (!c || layer < 0 || layer >= c->n_layer || n < 0) return ORC_E_ARG;
+    if (n == 0) return ORC_OK;
+    if (!seq_ids || !run_off || !run_start || !run_len || !q || !out || !isfinite(scale))
+        return ORC_E_ARG;
+    int st = check_heads(c, n_head, hd);
+    if (st != ORC_OK) return st;
+    for (int32_t b = 0; b < n; b++)
+        if (seq_ids[b] < 0 || seq_ids[b] >= c->n_seq) return ORC_E_ARG;
+    if (run_off[0] != 0) return ORC_E_ARG;
+    for (int32_t b = 0; b < n; b++)
+        if (run_off[b + 1] <= run_off[b]) return ORC_E_ARG;   /* at least one run each */
+    const int32_t nr = run_off[n];
+    for (int32_t r = 0; r < nr; r++)
+        if (run_len[r] <= 0) return ORC_E_ARG;
+    for (int32_t r = 0; r < nr; r++)
+        if (run_start[r] < 0 || (int64_t)run_start[r] + run_len[r] > c->capacity) return ORC_E_RANGE;
+    /* Overlap: sort each query's runs by start and compare neighbours. */
+    int32_t *tmp = (int32_t *)malloc(sizeof(int32_t) * 2 * (size_t)nr);
+    int32_t *ncell = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t **cells = (int32_t **)calloc((size_t)n, sizeof(int32_t *));
+    const void **kr = (const void **)malloc(sizeof(void *) * (size_t)n);
+    const void **vr = (const void **)malloc(sizeof(void *) * (size_t)n);
+    st = ORC_OK;
+    if (!tmp || !ncell || !cells || !kr || !vr) st = ORC_E_NOMEM;
+    for (int32_t b = 0; st == ORC_OK && b < n; b++) {
+        const int32_t r0 = run_off[b], r1 = run_off[b + 1];
+        for (int32_t r = r0; r < r1; r++) {
+            tmp[2 * r] = run_start[r];
+            tmp[2 * r + 1] = run_len[r];
+        }
+        qsort(tmp + 2 * r0, (size_t)(r1 - r0), 2 * sizeof(int32_t), cmp_run);
+        for (int32_t r = r0 + 1; r < r1; r++)
+            if ((int64_t)tmp[2 * (r - 1)] + tmp[2 * (r - 1) + 1] > tmp[2 * r]) st = ORC_E_DUP;
+    }
+    int32_t max_vl = 0;
+    for (int32_t b = 0; st == ORC_OK && b < n; b++) {
+        int64_t total = 0;
+        for (int32_t r = run_off[b]; r < run_off[b + 1]; r++) total += run_len[r];
+        ncell[b] = (int32_t)total;   /* <= capacity: the runs are disjoint cells of a region */
+        if (ncell[b] > max_vl) max_vl = ncell[b];
+        cells[b] = (int32_t *)malloc(sizeof(int32_t) * (size_t)ncell[b]);
+        if (!cells[b]) { st = ORC_E_NOMEM; break; }
+        int32_t j = 0;
+        for (int32_t r = run_off[b]; r < run_off[b + 1]; r++)
+            for (int32_t i = 0; i < run_len[r]; i++) cells[b][j++] = run_start[r] + i;
+        kr[b] = orc_cache_region((orc_cache *)c, 0, seq_ids[b], layer);
+        vr[b] = orc_cache_region((orc_cache *)c, 1, seq_ids[b], layer);
+    }
+    if (st == ORC_OK)
+        st = attend_units(kr, vr, c->dtype, NULL, (const int32_t *const *)cells, ncell, n, q,
+                          n_head, hd, c->n_head_kv, c->hd_kv, max_vl, scale, out, nthreads);
+    if (cells)
+        for (int32_t b = 0; b < n; b++) free(cells[b]);
+    free(cells); free(ncell); free(tmp); free(kr); free(vr);
     return st;
 }
 

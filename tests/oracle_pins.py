@@ -571,6 +571,118 @@ def pin_q8_cache_store_and_attention(o: Oracle):
         raise AssertionError("a Q8_0 cache with hd_kv = 16 was accepted")
 
 
+# ------------------------------------------------------------------------------------
+# Explicit windows ("13 · The decode loop and graph reuse" §2.2 Budget 3: a query's
+# allowed cells are an input, a list of runs; "Pitfalls" item 4: stale cells past a
+# rolled-back cursor are never read)
+# ------------------------------------------------------------------------------------
+
+def _runs_cache(o, seed, n_seq=2, cap=48, nkv=2, hdk=16):
+    c = OracleCache(n_seq, 1, nkv, hdk, cap, o)
+    for s in range(n_seq):
+        k = custom(seed + s, (cap, nkv, hdk)) * 2
+        v = custom(seed + 10 + s, (cap, nkv, hdk))
+        st, _ = c.append_rope(0, [s] * cap, np.arange(cap), None, 0, 0, k, v, 1e4, 1.0, ROPE_NEOX)
+        assert st == OK
+    return c
+
+
+def pin_runs_single_run_is_the_causal_window(o: Oracle):
+    """A window of one run [0, pos] (or of consecutive runs covering it in order) is the
+    position-derived window: bit-identical to the pinned decode."""
+    c = _runs_cache(o, 100)
+    q = custom(102, (5, 4, 16))
+    seqs, pos = [0, 1, 0, 1, 0], [0, 7, 31, 47, 20]
+    st, want = c.attn_decode(0, seqs, pos, q, 4, 16, 0.3)
+    assert st == OK
+    st, got = c.attn_decode_runs(0, seqs, [[(0, p + 1)] for p in pos], q, 4, 16, 0.3)
+    assert st == OK and np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    split = [[(0, 1)], [(0, 3), (3, 5)], [(0, 10), (10, 1), (11, 21)], [(0, 47), (47, 1)],
+             [(0, 20), (20, 1)]]
+    st, got = c.attn_decode_runs(0, seqs, split, q, 4, 16, 0.3)
+    assert st == OK and np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    c.close()
+
+
+def pin_runs_brute_force(o: Oracle):
+    """Scattered, out-of-order runs against an f64 brute force whose mask is built from
+    the runs (cell j is allowed iff some run holds it), GQA groups of 2."""
+    c = _runs_cache(o, 110)
+    q = custom(112, (4, 4, 16))
+    runs = [[(40, 8), (3, 5), (20, 1)], [(0, 48)], [(47, 1)], [(10, 10), (0, 2), (30, 6)]]
+    seqs = [1, 0, 0, 1]
+    st, got = c.attn_decode_runs(0, seqs, runs, q, 4, 16, 0.27)
+    assert st == OK
+    for b in range(4):
+        allowed = np.zeros(48, bool)
+        for s0, ln in runs[b]:
+            allowed[s0:s0 + ln] = True
+        K = c.k(seqs[b], 0).astype(np.float64)[allowed]
+        V = c.v(seqs[b], 0).astype(np.float64)[allowed]
+        want = bf.attention_bf(q[b:b + 1], K, V, [K.shape[0] - 1], 2, 0.27)
+        assert np.abs(got[b] - want[0]).max() <= 1e-6 + 1e-5 * np.abs(want).max(), b
+    # Run order changes only the summation order.
+    st, rev = c.attn_decode_runs(0, seqs, [r[::-1] for r in runs], q, 4, 16, 0.27)
+    assert st == OK and np.abs(rev - got).max() <= 1e-6
+    c.close()
+
+
+def pin_runs_stale_cells_and_shared_region(o: Oracle):
+    """Cells outside a window are never read (rewriting them changes nothing, bit for
+    bit), and rows stored at any cells of a region -- e.g. a second sequence's rows after
+    the first's -- attend exactly as the same rows at the start of a region of their own."""
+    c = _runs_cache(o, 120, n_seq=1)
+    q = custom(122, (2, 4, 16))
+    runs = [[(0, 20)], [(24, 10)]]
+    st, before = c.attn_decode_runs(0, [0, 0], runs, q, 4, 16, 0.3)
+    assert st == OK
+    junk = np.full((4, 2, 16), 1e30, np.float32)
+    st, _ = c.append_rope(0, [0] * 4, [20, 21, 22, 23], None, 0, 0, junk, junk, 0, 0, ROPE_NONE)
+    assert st == OK
+    st, after = c.attn_decode_runs(0, [0, 0], runs, q, 4, 16, 0.3)
+    assert st == OK and np.array_equal(after.view(np.uint32), before.view(np.uint32))
+    alone = OracleCache(1, 1, 2, 16, 10, o)
+    rows = c.k(0, 0)[24:34].reshape(10, 2, 16), c.v(0, 0)[24:34].reshape(10, 2, 16)
+    st, _ = alone.append_rope(0, [0] * 10, np.arange(10), None, 0, 0, rows[0], rows[1], 0, 0,
+                              ROPE_NONE)
+    assert st == OK
+    st, want = alone.attn_decode(0, [0], [9], q[1:], 4, 16, 0.3)
+    assert st == OK and np.array_equal(after[1:].view(np.uint32), want.view(np.uint32))
+    alone.close()
+    c.close()
+
+
+def pin_runs_errors(o: Oracle):
+    """Malformed windows are refused before anything is computed."""
+    c = _runs_cache(o, 130)
+    q = custom(131, (2, 4, 16))
+    L = c.L
+
+    def call(off, starts, lens, seqs=(0, 1)):
+        seqs = np.asarray(seqs, np.int32)
+        off, starts, lens = (np.asarray(a, np.int32) for a in (off, starts, lens))
+        out = np.zeros((len(seqs), 4, 16), np.float32)
+        return L.orc_attn_decode_runs(c.h, 0, len(seqs), seqs.ctypes.data, off.ctypes.data,
+                                      starts.ctypes.data, lens.ctypes.data,
+                                      np.ascontiguousarray(q[:len(seqs)]).ctypes.data, 4, 16,
+                                      0.3, out.ctypes.data, 0)
+
+    assert call([0, 1, 2], [0, 5], [3, 4]) == OK
+    assert call([0, 1, 3], [0, 5, 9], [3, 4, 1]) == OK          # adjacent runs
+    assert call([1, 2, 3], [0, 5, 0], [3, 4, 1]) == E_ARG       # offsets must start at 0
+    assert call([0, 1, 1], [0], [3]) == E_ARG                   # a query with no run
+    assert call([0, 1, 2], [0, 5], [3, 0]) == E_ARG             # empty run
+    assert call([0, 1, 2], [0, -1], [3, 2]) == E_RANGE          # before the region
+    # Past the capacity (48); on sequence 0, so that a broken check reads only memory of
+    # the next region.
+    assert call([0, 1, 2], [0, 40], [3, 9], seqs=(1, 0)) == E_RANGE
+    assert call([0, 1, 2], [0, 47], [3, 1]) == OK               # the last cell
+    assert call([0, 2, 3], [0, 2, 7], [3, 4, 1]) == E_DUP       # overlapping runs
+    assert call([0, 2, 3], [6, 6, 7], [1, 1, 1]) == E_DUP       # the same cell twice
+    assert call([0, 1, 2], [0, 5], [3, 4], seqs=(0, 2)) == E_ARG
+    c.close()
+
+
 ALL_PINS = [
     pin_inv_freq_correctly_rounded,
     pin_rope_worked_example,
@@ -595,4 +707,8 @@ ALL_PINS = [
     pin_q8_worked_blocks,
     pin_q8_block_invariants,
     pin_q8_cache_store_and_attention,
+    pin_runs_single_run_is_the_causal_window,
+    pin_runs_brute_force,
+    pin_runs_stale_cells_and_shared_region,
+    pin_runs_errors,
 ]

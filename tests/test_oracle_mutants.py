@@ -63,6 +63,15 @@ MUTANTS = {
     "q8_head_offset_dropped": (
         "orc_q8_dequantize_row((const orc_q8_block *)reg + off / ORC_Q8_BLOCK, hd_kv, buf);",
         "orc_q8_dequantize_row((const orc_q8_block *)reg + j * (size_t)nkt / ORC_Q8_BLOCK, hd_kv, buf);"),
+    # Explicit windows
+    "runs_start_ignored": ("for (int32_t i = 0; i < run_len[r]; i++) cells[b][j++] = run_start[r] + i;",
+                           "for (int32_t i = 0; i < run_len[r]; i++) cells[b][j++] = i;"),
+    "runs_v_window_ignored": ("const size_t vrow = cells ? (size_t)cells[j] : (size_t)j;",
+                              "const size_t vrow = (size_t)j;"),
+    "runs_overlap_allowed": ("if ((int64_t)tmp[2 * (r - 1)] + tmp[2 * (r - 1) + 1] > tmp[2 * r]) st = ORC_E_DUP;",
+                             "if ((int64_t)tmp[2 * (r - 1)] + tmp[2 * (r - 1) + 1] > tmp[2 * r] + 1) st = ORC_E_DUP;"),
+    "runs_range_off_by_one": ("(int64_t)run_start[r] + run_len[r] > c->capacity) return ORC_E_RANGE;",
+                              "(int64_t)run_start[r] + run_len[r] > c->capacity + 1) return ORC_E_RANGE;"),
     "q8_store_skipped": ("orc_q8_quantize_row(src, n, (orc_q8_block *)region + off / ORC_Q8_BLOCK);",
                          "(void)src;"),
 }
