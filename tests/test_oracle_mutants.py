@@ -34,7 +34,8 @@ MUTANTS = {
                        "if (pos[t] < 0 || pos[t] > c->capacity) return ORC_E_RANGE;\n    int64_t"),
     # Attention
     "gqa_modulo": ("int32_t hk = h / gqa;", "int32_t hk = h % n_head_kv;"),
-    "window_drops_current_row": ("int32_t vl = pos[t] + 1;", "int32_t vl = pos[t] > 0 ? pos[t] : 1;"),
+    "window_drops_current_row": ("int32_t vl = cells ? ncell[t] : pos[t] + 1;",
+                                 "int32_t vl = cells ? ncell[t] : (pos[t] > 0 ? pos[t] : 1);"),
     "no_scale": ("float s = dot_f32(hd_kv, qrow, kr) * scale;", "float s = dot_f32(hd_kv, qrow, kr);"),
     "no_max_subtraction": ("float e = expf(scr[j] - mx);", "float e = expf(scr[j]);"),
     "v_from_k_region": ("const float *vr = head_row(vreg,", "const float *vr = head_row(kreg,"),
