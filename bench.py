@@ -23,7 +23,7 @@ Reported:
   cpu_baseline   the plain C oracle on the host cores, on a bounded sample
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
-                       [--kv f32|f16|q8_0]
+                       [--kv f32|f16|q8_0] [--decode-runs]
 """
 from __future__ import annotations
 
@@ -57,6 +57,9 @@ def main():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--kv", choices=["f32", "f16", "q8_0"], default="f32",
                     help="region format: f32, or binary16 (half the bytes; arithmetic in f32)")
+    ap.add_argument("--decode-runs", action="store_true",
+                    help="stage 4 through gqa_attn_decode_runs: each sequence's window given "
+                         "as two explicit runs, its second half first")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before timing, so that "
                          "HBM counters (FETCH_SIZE / WRITE_SIZE) can be calibrated against "
@@ -130,6 +133,10 @@ def main():
     nsteps = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nsteps)]
 
+    # The same windows as explicit runs: [L/2, L) then [0, L/2) for window length L.
+    win_runs = [[(int(x + 1) // 2, int(x + 1) - int(x + 1) // 2), (0, int(x + 1) // 2)]
+                for x in lens]
+
     def step(i):
         e = ev[i]
         e[0].record()
@@ -141,7 +148,11 @@ def main():
         kvc.kv_append_rope(cache, 0, seqs, lens, qd, w.n_head, w.hd, kd, vd, w.base,
                            w.freq_scale, w.style)
         e[3].record()
-        kvc.gqa_attn_decode(cache, 0, seqs, lens, qd, w.n_head, w.hd, w.scale, out_dec)
+        if args.decode_runs:
+            kvc.gqa_attn_decode_runs(cache, 0, seqs, win_runs, qd, w.n_head, w.hd, w.scale,
+                                     out_dec)
+        else:
+            kvc.gqa_attn_decode(cache, 0, seqs, lens, qd, w.n_head, w.hd, w.scale, out_dec)
         e[4].record()
 
     for i in range(args.warmup):
@@ -184,6 +195,8 @@ def main():
                         "ragged n_past U[128,8192]; 4096-token continuation prefill on seq 0 + "
                         "one decode step for all 32",
             "kv_dtype": args.kv,
+            "decode_windows": "explicit runs, 2 per sequence" if args.decode_runs else
+                              "position-derived [0, pos]",
             "n_seq": int(w.n_seq), "n_head": w.n_head, "n_head_kv": w.n_head_kv,
             "hd": w.hd, "hd_kv": w.hd_kv, "capacity": w.capacity,
             "n_past_seq0": int(n_past[0]), "prefill_tokens": nt,
@@ -211,13 +224,15 @@ def main():
             "avg_launch_us": round(float(t_pre.mean()) * 1e3, 2),
         },
         "roofline_decode": {
-            "kernel": "decode_split_kernel<128,2> + decode_combine_kernel<128> (gqa_attn_decode)",
+            "kernel": "decode_split_kernel<128,2> + decode_combine_kernel<128> (" +
+                      ("gqa_attn_decode_runs)" if args.decode_runs else "gqa_attn_decode)"),
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode") if args.kv == "f32" else None,
+            "traffic": measured_traffic("decode") if args.kv == "f32" and not args.decode_runs
+            else None,
             "bytes_per_launch": kv_bytes,
             "avg_launch_us": round(float(t_dec.mean()) * 1e3, 2),
         },

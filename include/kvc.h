@@ -7,6 +7,7 @@
  *                   in place at those positions
  *   gqa_attn_prefill  nt query tokens of one sequence, token t attending rows [0, pos[t]]
  *   gqa_attn_decode   one query token per sequence for a batch of sequences
+ *   gqa_attn_decode_runs  the same over explicit windows (lists of row runs)
  * plus kv_alloc_typed (binary16 or Q8_0 regions), kv_free, kv_view, kv_seq_len and
  * kv_last_error for storage format, ownership, inspection and error text.
  *
@@ -232,6 +233,35 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
 kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
                            const int32_t *seq_ids, const int32_t *pos, const float *q,
                            int32_t n_head, int32_t hd, float scale, float *out, void *stream);
+
+/*
+ * gqa_attn_decode_runs -- gqa_attn_decode over explicit windows: entry b attends the
+ * rows its runs name instead of rows [0, pos[b]] ([MINFER-13] §2.2, Budget 3: the cells a
+ * query may read are an input resolved by the caller, a list of runs, not a bound derived
+ * from positions; §3.4 "Pitfalls & invariants" item 4: rows past a rolled-back cursor
+ * are never read because no window names them).  Windows say which rows take part; they do not move
+ * rows, so a caller that stores several sequences' rows in one region (at distinct
+ * positions) reads each sequence's rows with its own runs.
+ *
+ *   layer, n_seq, seq_ids  as in gqa_attn_decode.
+ *   run_off     host [n_seq + 1]: entry b's runs are r = run_off[b] .. run_off[b+1]-1;
+ *               run_off[0] = 0 and every entry has at least one run.
+ *   run_start   host [run_off[n_seq]]: first row of run r.
+ *   run_len     host [run_off[n_seq]]: rows in run r (>= 1); rows
+ *               [run_start[r], run_start[r] + run_len[r]) must lie in [0, capacity).
+ *               The runs of one entry may come in any order but must not share a row.
+ *   q, n_head, hd, scale, out  as in gqa_attn_decode.
+ * The result is attention over the union of the entry's runs; the order of the runs
+ * changes only the rounding (within the same tolerance as gqa_attn_decode).
+ * The chunk table is staged in pinned host memory that the kernels read in place.
+ * Errors: KVC_E_ARG (also for a malformed run list), KVC_E_GEOMETRY, KVC_E_RANGE (a run
+ * outside the region), KVC_E_DUP (two runs of one entry share a row), KVC_E_NOMEM,
+ * KVC_E_HIP.  On error nothing is queued.
+ */
+kvc_status gqa_attn_decode_runs(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                                const int32_t *seq_ids, const int32_t *run_off,
+                                const int32_t *run_start, const int32_t *run_len, const float *q,
+                                int32_t n_head, int32_t hd, float scale, float *out, void *stream);
 
 /*
  * kv_last_error -- text of the calling thread's last non-OK status ("" if none).  The

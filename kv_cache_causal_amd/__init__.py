@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANG
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kv_alloc", "kv_alloc_typed", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
-           "gqa_attn_prefill", "gqa_attn_decode", "kv_last_error")
+           "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_runs", "kv_last_error")
 
 
 class KvcError(RuntimeError):
@@ -64,6 +64,7 @@ def lib(path: str = LIB_PATH):
         "kv_append_rope": [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, ctypes.c_int, p],
         "gqa_attn_prefill": [p, i32, i32, i32, p, p, i32, i32, f32, p, p],
         "gqa_attn_decode": [p, i32, i32, p, p, p, i32, i32, f32, p, p],
+        "gqa_attn_decode_runs": [p, i32, i32, p, p, p, p, p, i32, i32, f32, p, p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -195,6 +196,27 @@ def gqa_attn_decode(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out, st
         raise ValueError("seq_ids and pos differ in length")
     _check(lib().gqa_attn_decode(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
                                  n_head, hd, scale, _dev(out, "out"), _stream(stream)))
+
+
+def gqa_attn_decode_runs(c: Cache, layer, seq_ids, runs, q, n_head, hd, scale, out,
+                         stream=None):
+    """runs: for each entry, a list of (start, len) row runs -- its explicit window."""
+    s_arr, s_ptr = _host_i32(seq_ids)
+    if s_arr.size != len(runs):
+        raise ValueError("seq_ids and runs differ in length")
+    off = [0]
+    starts, lens = [], []
+    for rl in runs:
+        for st, ln in rl:
+            starts.append(st)
+            lens.append(ln)
+        off.append(len(starts))
+    o_arr, o_ptr = _host_i32(off)
+    st_arr, st_ptr = _host_i32(starts if starts else [0])
+    ln_arr, ln_ptr = _host_i32(lens if lens else [0])
+    _check(lib().gqa_attn_decode_runs(c.handle, layer, int(s_arr.size), s_ptr, o_ptr, st_ptr,
+                                      ln_ptr, _dev(q, "q"), n_head, hd, scale, _dev(out, "out"),
+                                      _stream(stream)))
 
 
 _hip = None

@@ -54,4 +54,12 @@ int hc_check_decode(const int32_t *g5, int32_t layer, int32_t n_seq, const int32
                              g_msg);
 }
 
+int hc_check_decode_runs(const int32_t *g5, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
+                         const int32_t *run_off, const int32_t *run_start, const int32_t *run_len,
+                         const void *q, int32_t n_head, int32_t hd, float scale, const void *out)
+{
+    return kvc::check_decode_runs(geom(g5), layer, n_seq, seq_ids, run_off, run_start, run_len, q,
+                                  n_head, hd, scale, out, g_msg);
+}
+
 }  // extern "C"

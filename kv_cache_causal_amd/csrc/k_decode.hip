@@ -17,8 +17,8 @@
 //     holding 32 bytes of it (16 for groups of 3+ heads, to save registers): two float4
 //     loads of an f32 cache, or two 16-byte loads of packed halves of a binary16 cache
 //     (widened to f32 as they are used); one load instruction across the wave covers
-//     64/LPR rows, whole 128-byte lines.  A Q8_0 cache gives each lane 16 codes (one
-//     16-byte load, all in one 32-value block) plus that block's binary16 scale; the
+//     64/LPR rows, whole 128-byte lines.  A Q8_0 cache gives each lane 8 codes (one
+//     8-byte load, all in one 32-value block) plus that block's binary16 scale; the
 //     codes are converted as they are used and the scale is applied once per lane and
 //     row: to the lane's partial dot product for K, to the softmax weight for V (each
 //     dequantized value is scale * code exactly, so only the rounding order differs
@@ -39,6 +39,10 @@
 //     slower than one extra launch.
 //   * The batch's positions, sequence ids and chunk offsets travel in the kernel
 //     arguments (up to 64 entries per launch), so a decode needs no host-to-device copy.
+//   * Explicit windows ("13 · The decode loop and graph reuse" §2.2: a query's cells are
+//     an input, a list of runs): the host cuts every run into chunks of at most
+//     rows_per_chunk rows and passes the (first row, rows) table; the kernel and the
+//     merge are otherwise the same -- a chunk is a contiguous row range either way.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -53,12 +57,15 @@ constexpr int kUnroll = 4;        // rows per lane group per step (two steps in 
 
 // Dims of a row slice each lane holds.  f32: 8 (two float4) for kv groups of up to 2
 // query heads, 4 (one float4) for larger groups, whose per-head registers would otherwise
-// crowd out the load buffers.  binary16 and Q8_0: 16 dims (32 or 16 bytes per lane) for
-// groups of up to 2, 8 for up to 4, 4 beyond.
+// crowd out the load buffers.  binary16: 16 dims (32 bytes per lane) for groups of up to
+// 2, 8 for up to 4, 4 beyond.  Q8_0: 8 codes (8 bytes) for groups of up to 4, 4 beyond:
+// with 16 the code conversions held so many registers that only 2 waves fit per SIMD;
+// with 8, 3 fit and the batch workload's decode measured ~10% faster.
 template <int GP, typename KVT>
 constexpr int dims_per_lane()
 {
-    if constexpr (sizeof(KVT) <= 2) return GP <= 2 ? 16 : (GP <= 4 ? 8 : 4);
+    if constexpr (sizeof(KVT) == 1) return GP <= 4 ? 8 : 4;
+    if constexpr (sizeof(KVT) == 2) return GP <= 2 ? 16 : (GP <= 4 ? 8 : 4);
     return GP <= 2 ? 8 : 4;
 }
 
@@ -273,9 +280,14 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     }
     const int b = lo;
     const int nchunks = p.cbase[b + 1] - p.cbase[b];
-    const int vl = p.pos[b] + 1;
-    const int r0 = (cg - p.cbase[b]) * p.rows_per_chunk;
-    const int r1 = min(r0 + p.rows_per_chunk, vl);
+    int r0, r1;   // this chunk's rows [r0, r1), never empty
+    if (p.pieces) {
+        r0 = p.pieces[2 * cg];
+        r1 = r0 + p.pieces[2 * cg + 1];
+    } else {
+        r0 = (cg - p.cbase[b]) * p.rows_per_chunk;
+        r1 = min(r0 + p.rows_per_chunk, p.pos[b] + 1);
+    }
     const int seq = p.seq[b];
     const int nkt = p.n_head_kv * HD;
     const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
@@ -540,7 +552,7 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt)
 {
     // The largest of the lane layouts' step sizes (all are powers of two).
-    const int lpr = hd_kv / (kv_fmt == kFmtF32 ? 8 : 16);
+    const int lpr = hd_kv / (kv_fmt == kFmtF16 ? 16 : 8);
     return kWaves * (64 / lpr) * kUnroll;
 }
 

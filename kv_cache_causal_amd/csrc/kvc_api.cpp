@@ -194,6 +194,121 @@ int32_t env_split_rows()
     return e ? std::max(0, std::atoi(e)) : 0;
 }
 
+// Split-K decode of n_seq validated entries.  Entry b's window is rows [0, pos[b]]
+// (run_off == nullptr) or the union of its runs run_off[b] .. run_off[b+1]-1.
+kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
+                         const int32_t *pos, const int32_t *run_off, const int32_t *run_start,
+                         const int32_t *run_len, const float *q, int32_t n_head, int32_t hd,
+                         float scale, float *out, hipStream_t s)
+{
+    const bool runs = run_off != nullptr;
+    auto window_rows = [&](int32_t b) -> int64_t {
+        if (!runs) return (int64_t)pos[b] + 1;
+        int64_t t = 0;
+        for (int32_t r = run_off[b]; r < run_off[b + 1]; r++) t += run_len[r];
+        return t;
+    };
+    // Chunk size.  Small windows are launch-bound: one chunk per entry, no combine pass.
+    // Large ones: ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the
+    // per-chunk overheads (query load, merges, partial record, combine) stay small next
+    // to the stream.  KVC_SPLIT_ROWS overrides the size (tuning only, never the result).
+    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, c->kv_fmt);
+    int64_t total_rows = 0, max_rows = 0;
+    for (int32_t b = 0; b < n_seq; b++) {
+        total_rows += window_rows(b);
+        max_rows = std::max<int64_t>(max_rows, window_rows(b));
+    }
+    const int64_t work = total_rows * c->g.n_head_kv;
+    int64_t rows = env_split_rows();
+    if (rows <= 0) rows = work <= 131072 ? max_rows : std::max<int64_t>(512, work / 2048);
+    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
+    // Chunks of entry b: its window cut into pieces of at most `rows` rows (each run on
+    // its own for an explicit window).
+    auto chunks_of = [&](int32_t b) -> int64_t {
+        if (!runs) return ((int64_t)pos[b] + rows) / rows;
+        int64_t ch = 0;
+        for (int32_t r = run_off[b]; r < run_off[b + 1]; r++) ch += (run_len[r] + rows - 1) / rows;
+        return ch;
+    };
+
+    // Launches of up to kInlineEntries entries; the partials buffer fits the largest.
+    const int32_t E = kvc::kInlineEntries;
+    int64_t max_chunks = 0;
+    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
+        int64_t ch = 0;
+        for (int32_t b = b0; b < std::min(n_seq, b0 + E); b++) ch += chunks_of(b);
+        max_chunks = std::max(max_chunks, ch);
+    }
+    if (max_chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
+    const size_t need = (size_t)max_chunks * n_head * (c->g.hd_kv + 4);
+    if (need > c->part_cap) {
+        if (c->part) {
+            KVC_HIP(hipStreamSynchronize(s));
+            hipFree(c->part);
+            c->part = nullptr;
+            c->part_cap = 0;
+        }
+        const size_t cap = std::max(need, c->part_cap * 2);
+        if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
+            return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
+        c->part_cap = cap;
+    }
+
+    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
+        const int32_t n = std::min(E, n_seq - b0);
+        kvc::DecodeParams p{};
+        p.q = q + (int64_t)b0 * n_head * hd;
+        p.out = out + (int64_t)b0 * n_head * c->g.hd_kv;
+        p.part = c->part;
+        p.kc = c->K;
+        p.vc = c->V;
+        p.region_bytes = c->region_bytes;
+        p.scale_off = c->scale_off;
+        p.n = n;
+        p.n_head = n_head;
+        p.hd = hd;
+        p.n_head_kv = c->g.n_head_kv;
+        p.hd_kv = c->g.hd_kv;
+        p.n_layer = c->g.n_layer;
+        p.layer = layer;
+        p.kv_fmt = c->kv_fmt;
+        p.rows_per_chunk = (int32_t)rows;
+        p.qscale = log2e_times(scale);
+        int32_t chunks = 0;
+        for (int32_t i = 0; i < n; i++) {
+            p.pos[i] = runs ? 0 : pos[b0 + i];
+            p.seq[i] = seq_ids[b0 + i];
+            p.cbase[i] = chunks;
+            chunks += (int32_t)chunks_of(b0 + i);
+        }
+        p.cbase[n] = chunks;
+        p.total_chunks = chunks;
+        p.pieces = nullptr;
+        if (runs) {
+            std::vector<int32_t> pieces;
+            pieces.reserve((size_t)chunks * 2);
+            for (int32_t b = b0; b < b0 + n; b++)
+                for (int32_t r = run_off[b]; r < run_off[b + 1]; r++)
+                    for (int64_t o = 0; o < run_len[r]; o += rows) {
+                        pieces.push_back(run_start[r] + (int32_t)o);
+                        pieces.push_back((int32_t)std::min<int64_t>(rows, run_len[r] - o));
+                    }
+            kvc_status pst = staging_push(c->st, pieces, &p.pieces);
+            if (pst != KVC_OK) return pst;
+        }
+        hipError_t e = kvc::launch_decode(p, s);
+        if (e != hipSuccess) {
+            if (runs) staging_abort(c->st);
+            return hip_fail(e, "decode kernels");
+        }
+        if (runs) {
+            kvc_status cst = staging_commit(c->st, s);
+            if (cst != KVC_OK) return cst;
+        }
+    }
+    return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,79 +519,23 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
                                       out, msg);
     if (st != KVC_OK) return fail(st, msg);
     if (n_seq == 0) return KVC_OK;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return decode_driver(c, layer, n_seq, seq_ids, pos, nullptr, nullptr, nullptr, q, n_head, hd,
+                         scale, out, reinterpret_cast<hipStream_t>(stream));
+}
 
-    // Chunk size.  Small windows are launch-bound: one chunk per entry, no combine pass.
-    // Large ones: ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the
-    // per-chunk overheads (query load, merges, partial record, combine) stay small next
-    // to the stream.  KVC_SPLIT_ROWS overrides the size (tuning only, never the result).
-    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, c->kv_fmt);
-    int64_t total_rows = 0, max_rows = 0;
-    for (int32_t b = 0; b < n_seq; b++) {
-        total_rows += (int64_t)pos[b] + 1;
-        max_rows = std::max<int64_t>(max_rows, (int64_t)pos[b] + 1);
-    }
-    const int64_t work = total_rows * c->g.n_head_kv;
-    int64_t rows = env_split_rows();
-    if (rows <= 0) rows = work <= 131072 ? max_rows : std::max<int64_t>(512, work / 2048);
-    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
-
-    // Launches of up to kInlineEntries entries; the partials buffer fits the largest.
-    const int32_t E = kvc::kInlineEntries;
-    int64_t max_chunks = 0;
-    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
-        int64_t ch = 0;
-        for (int32_t b = b0; b < std::min(n_seq, b0 + E); b++) ch += ((int64_t)pos[b] + rows) / rows;
-        max_chunks = std::max(max_chunks, ch);
-    }
-    if (max_chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
-    const size_t need = (size_t)max_chunks * n_head * (c->g.hd_kv + 4);
-    if (need > c->part_cap) {
-        if (c->part) {
-            KVC_HIP(hipStreamSynchronize(s));
-            hipFree(c->part);
-            c->part = nullptr;
-            c->part_cap = 0;
-        }
-        const size_t cap = std::max(need, c->part_cap * 2);
-        if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
-            return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
-        c->part_cap = cap;
-    }
-
-    for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
-        const int32_t n = std::min(E, n_seq - b0);
-        kvc::DecodeParams p{};
-        p.q = q + (int64_t)b0 * n_head * hd;
-        p.out = out + (int64_t)b0 * n_head * c->g.hd_kv;
-        p.part = c->part;
-        p.kc = c->K;
-        p.vc = c->V;
-        p.region_bytes = c->region_bytes;
-        p.scale_off = c->scale_off;
-        p.n = n;
-        p.n_head = n_head;
-        p.hd = hd;
-        p.n_head_kv = c->g.n_head_kv;
-        p.hd_kv = c->g.hd_kv;
-        p.n_layer = c->g.n_layer;
-        p.layer = layer;
-        p.kv_fmt = c->kv_fmt;
-        p.rows_per_chunk = (int32_t)rows;
-        p.qscale = log2e_times(scale);
-        int32_t chunks = 0;
-        for (int32_t i = 0; i < n; i++) {
-            p.pos[i] = pos[b0 + i];
-            p.seq[i] = seq_ids[b0 + i];
-            p.cbase[i] = chunks;
-            chunks += (int32_t)(((int64_t)pos[b0 + i] + rows) / rows);
-        }
-        p.cbase[n] = chunks;
-        p.total_chunks = chunks;
-        hipError_t e = kvc::launch_decode(p, s);
-        if (e != hipSuccess) return hip_fail(e, "decode kernels");
-    }
-    return KVC_OK;
+kvc_status gqa_attn_decode_runs(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                                const int32_t *seq_ids, const int32_t *run_off,
+                                const int32_t *run_start, const int32_t *run_len, const float *q,
+                                int32_t n_head, int32_t hd, float scale, float *out, void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_decode_runs(c->g, layer, n_seq, seq_ids, run_off, run_start,
+                                           run_len, q, n_head, hd, scale, out, msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (n_seq == 0) return KVC_OK;
+    return decode_driver(c, layer, n_seq, seq_ids, nullptr, run_off, run_start, run_len, q,
+                         n_head, hd, scale, out, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

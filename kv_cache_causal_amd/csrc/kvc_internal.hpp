@@ -54,6 +54,10 @@ struct DecodeParams {
     float *out;              // [n][n_head][hd_kv]
     float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
     const void *kc, *vc;     // cache bases
+    // Explicit windows: chunk c reads rows [pieces[2c], pieces[2c] + pieces[2c+1]) of its
+    // entry's region (device-visible memory).  nullptr: entry b's window is rows
+    // [0, pos[b]], cut into chunks of rows_per_chunk rows.
+    const int32_t *pieces;
     int64_t region_bytes, scale_off;
     int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer, kv_fmt;
     int32_t rows_per_chunk, total_chunks;

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <utility>
 #include <vector>
 
 namespace kvc {
@@ -201,6 +202,72 @@ kvc_status check_decode(const Geometry &g, int32_t layer, int32_t n_seq, const i
     st = check_seq_ids(g, n_seq, seq_ids, msg);
     if (st != KVC_OK) return st;
     return check_positions(g, n_seq, pos, msg);
+}
+
+kvc_status check_decode_runs(const Geometry &g, int32_t layer, int32_t n_seq,
+                             const int32_t *seq_ids, const int32_t *run_off,
+                             const int32_t *run_start, const int32_t *run_len, const void *q,
+                             int32_t n_head, int32_t hd, float scale, const void *out,
+                             std::string &msg)
+{
+    if (layer < 0 || layer >= g.n_layer) {
+        msg = "layer " + s(layer) + " outside [0, " + s(g.n_layer) + ")";
+        return KVC_E_ARG;
+    }
+    if (n_seq < 0) {
+        msg = "n_seq < 0";
+        return KVC_E_ARG;
+    }
+    if (n_seq == 0) return KVC_OK;
+    if (!seq_ids || !run_off || !run_start || !run_len || !q || !out || !std::isfinite(scale)) {
+        msg = "seq_ids, run_off, run_start, run_len, q and out must be non-NULL and scale finite";
+        return KVC_E_ARG;
+    }
+    if (!aligned16(q) || !aligned16(out)) {
+        msg = "device tensors must be 16-byte aligned";
+        return KVC_E_ARG;
+    }
+    kvc_status st = check_heads(g, n_head, hd, msg);
+    if (st != KVC_OK) return st;
+    st = check_seq_ids(g, n_seq, seq_ids, msg);
+    if (st != KVC_OK) return st;
+    if (run_off[0] != 0) {
+        msg = "run_off[0] must be 0";
+        return KVC_E_ARG;
+    }
+    for (int32_t b = 0; b < n_seq; b++) {
+        if (run_off[b + 1] <= run_off[b]) {
+            msg = "entry " + s(b) + " has no run (run_off must increase)";
+            return KVC_E_ARG;
+        }
+    }
+    const int32_t nr = run_off[n_seq];
+    for (int32_t r = 0; r < nr; r++) {
+        if (run_len[r] <= 0) {
+            msg = "run " + s(r) + " is empty";
+            return KVC_E_ARG;
+        }
+    }
+    for (int32_t r = 0; r < nr; r++) {
+        if (run_start[r] < 0 || (int64_t)run_start[r] + run_len[r] > g.capacity) {
+            msg = "run " + s(r) + " [" + s(run_start[r]) + ", +" + s(run_len[r]) +
+                  ") outside the region's " + s(g.capacity) + " rows";
+            return KVC_E_RANGE;
+        }
+    }
+    std::vector<std::pair<int32_t, int32_t>> rs;
+    for (int32_t b = 0; b < n_seq; b++) {
+        rs.clear();
+        for (int32_t r = run_off[b]; r < run_off[b + 1]; r++) rs.emplace_back(run_start[r], run_len[r]);
+        std::sort(rs.begin(), rs.end());
+        for (size_t i = 1; i < rs.size(); i++) {
+            if ((int64_t)rs[i - 1].first + rs[i - 1].second > rs[i].first) {
+                msg = "entry " + s(b) + ": runs overlap at row " + s(rs[i].first);
+                return KVC_E_DUP;
+            }
+        }
+    }
+    return KVC_OK;
 }
 
 }  // namespace kvc

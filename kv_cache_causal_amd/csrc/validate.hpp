@@ -38,4 +38,10 @@ kvc_status check_decode(const Geometry &g, int32_t layer, int32_t n_seq, const i
                         const int32_t *pos, const void *q, int32_t n_head, int32_t hd,
                         float scale, const void *out, std::string &msg);
 
+kvc_status check_decode_runs(const Geometry &g, int32_t layer, int32_t n_seq,
+                             const int32_t *seq_ids, const int32_t *run_off,
+                             const int32_t *run_start, const int32_t *run_len, const void *q,
+                             int32_t n_head, int32_t hd, float scale, const void *out,
+                             std::string &msg);
+
 }  // namespace kvc

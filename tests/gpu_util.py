@@ -159,3 +159,14 @@ class Pair:
         st, want = self.o.attn_decode(layer, seq_ids, pos, q_host, n_head, hd, scale)
         assert st == 0
         return got, want
+
+    def decode_runs(self, layer, seq_ids, runs, q_dev, q_host, n_head, hd, scale):
+        """Explicit-window decode on both; returns (gpu out, oracle out)."""
+        import torch
+        n = len(seq_ids)
+        out = torch.empty((n, n_head, self.hd_kv), dtype=torch.float32, device="cuda")
+        self.kvc.gqa_attn_decode_runs(self.g, layer, seq_ids, runs, q_dev, n_head, hd, scale, out)
+        got = host(out)
+        st, want = self.o.attn_decode_runs(layer, seq_ids, runs, q_host, n_head, hd, scale)
+        assert st == 0, st
+        return got, want

@@ -573,7 +573,7 @@ def pin_q8_cache_store_and_attention(o: Oracle):
 
 # ------------------------------------------------------------------------------------
 # Explicit windows ("13 · The decode loop and graph reuse" §2.2 Budget 3: a query's
-# allowed cells are an input, a list of runs; "Pitfalls" item 4: stale cells past a
+# allowed cells are an input, a list of runs; §3.4 item 4: stale cells past a
 # rolled-back cursor are never read)
 # ------------------------------------------------------------------------------------
 

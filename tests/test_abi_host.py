@@ -78,6 +78,7 @@ def hc():
     L.hc_check_append.argtypes = [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, i32]
     L.hc_check_prefill.argtypes = [p, i32, i32, i32, p, p, i32, i32, f32, p]
     L.hc_check_decode.argtypes = [p, i32, i32, p, p, p, i32, i32, f32, p]
+    L.hc_check_decode_runs.argtypes = [p, i32, i32, p, p, p, p, p, i32, i32, f32, p]
     L.hc_last_message.restype = ctypes.c_char_p
     return L
 
@@ -218,3 +219,43 @@ def test_alloc_checks(hc):
             if h:
                 L.orc_cache_free(h)
     assert hc.hc_check_alloc(1, 1, 2, 16, 8, kvc.KV_Q8_0) == kvc.E_GEOMETRY
+
+
+RUNS_CASES = [
+    ("ok", dict()),
+    ("adjacent_runs_ok", dict(runs=[[(0, 3), (3, 2)], [(9, 1)]])),
+    ("out_of_order_ok", dict(runs=[[(6, 2), (0, 3)], [(0, 10)]])),
+    ("same_seq_twice_ok", dict(seq=[1, 1])),
+    ("seq_range", dict(seq=[0, 2])),
+    ("no_run", dict(runs=[[(0, 3)], []])),
+    ("empty_run", dict(runs=[[(0, 0)], [(1, 2)]])),
+    ("negative_start", dict(runs=[[(-1, 2)], [(1, 2)]])),
+    ("past_capacity", dict(runs=[[(8, 3)], [(1, 2)]])),
+    ("last_row_ok", dict(runs=[[(9, 1)], [(0, 10)]])),
+    ("overlap", dict(runs=[[(0, 4), (3, 2)], [(1, 2)]])),
+    ("same_run_twice", dict(runs=[[(2, 2), (2, 2)], [(1, 2)]])),
+    ("hd_lt_hd_kv", dict(hd=14)),
+    ("heads", dict(n_head=3)),
+    ("n_zero", dict(seq=[], runs=[])),
+]
+
+
+@pytest.mark.parametrize("name,kw", RUNS_CASES, ids=[c[0] for c in RUNS_CASES])
+def test_decode_runs_checks_match_oracle(hc, name, kw):
+    from oracle import runs_csr
+    seq = kw.get("seq", [0, 1])
+    runs = kw.get("runs", [[(0, 4), (6, 2)], [(2, 5)]])
+    n_head, hd = kw.get("n_head", 2), kw.get("hd", 16)
+    g, gp = g5()
+    s, sp = iarr(seq)
+    off, starts, lens = runs_csr(runs)
+    o, op = iarr(off)
+    st_, stp = iarr(starts if starts.size else [0])
+    ln, lnp = iarr(lens if lens.size else [0])
+    st_lib = hc.hc_check_decode_runs(gp, 0, len(seq), sp, op, stp, lnp, FAKE, n_head, hd, 0.25,
+                                     FAKE)
+    c = OracleCache(*GEOM)
+    st_orc, _ = c.attn_decode_runs(0, seq, runs, custom(5, (len(seq), max(n_head, 1), hd)),
+                                   n_head, hd, 0.25)
+    c.close()
+    assert st_lib == st_orc, (name, st_lib, st_orc, hc.hc_last_message())
