@@ -61,6 +61,9 @@ def _bind(lib):
         "orc_attn_decode_runs": (ctypes.c_int, [p, i32, i32, p, p, p, p, p, i32, i32, f32, p,
                                                 i32]),
         "orc_max_threads": (i32, []),
+        "orc_project": (ctypes.c_int, [p, p, p, i32, i32, i32, p]),
+        "orc_qkv_rope_append": (ctypes.c_int, [p, i32, i32, p, p, p, i32, p, p, p, p, p, p, i32,
+                                               i32, p, f32, f32, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -143,6 +146,18 @@ class Oracle:
         st = self.L.orc_q8_dequantize_row(_ptr(blocks), out.size, _ptr(out))
         if st:
             raise ValueError(f"orc_q8_dequantize_row status {st}")
+        return out
+
+    def project(self, x, w, b=None):
+        """x [nt][d] . w[rows][d]^T + b -> [nt][rows] (exact dot rounded to f32, then + b)."""
+        x, w = _f32(x), _f32(w)
+        b = None if b is None else _f32(b)
+        nt, d = x.shape
+        rows = w.shape[0]
+        out = np.zeros((nt, rows), np.float32)
+        st = self.L.orc_project(_ptr(x), _ptr(w), _ptr(b), nt, rows, d, _ptr(out))
+        if st:
+            raise ValueError(f"orc_project status {st}")
         return out
 
     def rope(self, x, pos, base, scale=1.0, style=ROPE_NEOX):
@@ -273,3 +288,16 @@ class OracleCache:
                                          _ptr(lens), _ptr(q), n_head, hd, scale, _ptr(out),
                                          nthreads)
         return st, out
+
+    def qkv_rope_append(self, layer, seq_ids, pos, x, wq, bq, wk, bk, wv, bv, n_head, hd, base,
+                        scale=1.0, style=ROPE_NEOX):
+        """Fused decode step; returns (status, rotated q [nt][n_head][hd])."""
+        seq_ids, pos = _i32(seq_ids), _i32(pos)
+        nt = int(pos.shape[0])
+        x = _f32(x)
+        ws = [None if a is None else _f32(a) for a in (wq, bq, wk, bk, wv, bv)]
+        q = np.zeros((nt, n_head, hd), np.float32)
+        st = self.L.orc_qkv_rope_append(self.h, layer, nt, _ptr(seq_ids), _ptr(pos), _ptr(x),
+                                        x.shape[-1], *[_ptr(a) for a in ws], n_head, hd, _ptr(q),
+                                        base, scale, style)
+        return st, q

@@ -401,6 +401,35 @@ int orc_append_rope(orc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_
 }
 
 /* ------------------------------------------------------------------------------ */
+/* Decode projections fused with the store ("13 · The decode loop and graph reuse"   */
+/* §2.3: on a GPU build a decode step (nt = 1) merges the q/k/v matmuls, their biases, */
+/* the two RoPEs and the two KV stores into one operation, and the fused and unfused   */
+/* paths must give bit-identical results, §3.4 item 5).                               */
+/* ------------------------------------------------------------------------------ */
+
+/* out[t][j] = (sum_i x[t][i] * w[j][i]) + b[j].  Reading of the matmul's precision (the
+ * pages fix only that fused and unfused agree bit for bit): the dot product is the f32
+ * nearest to its exact value (here accumulated in binary128, where every f32 x f32
+ * product is exact and 1024-term sums stay within ~1e-31 relative, then rounded once),
+ * and the bias is added in f32 (one more rounding).  b may be NULL (no bias).
+ * x: [nt][d]; w: [rows][d] (row j produces output j); out: [nt][rows]. */
+int orc_project(const float *x, const float *w, const float *b, int32_t nt, int32_t rows,
+                int32_t d, float *out)
+{
+    if (!x || !w || !out || nt < 0 || rows < 0 || d <= 0) return ORC_E_ARG;
+    for (int32_t t = 0; t < nt; t++)
+        for (int32_t j = 0; j < rows; j++) {
+            __float128 acc = 0;
+            const float *xr = x + (size_t)t * d, *wr = w + (size_t)j * d;
+            for (int32_t i = 0; i < d; i++) acc += (__float128)xr[i] * (__float128)wr[i];
+            float y = (float)acc;
+            if (b) y = y + b[j];
+            out[(size_t)t * rows + j] = y;
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
 /* Attention ([MINFER-11] §2.1 "What attention computes", §2.4 GQA, §3.2.4 "GQA    */
 /* attention", §3.2.5 softmax).                                                     */
 /* ------------------------------------------------------------------------------ */
@@ -466,6 +495,39 @@ static void attend_row(const float *qrow, const void *kreg, const void *vreg, in
         float w = scr[j];
         for (int32_t d = 0; d < hd_kv; d++) out[d] += w * vr[d];
     }
+}
+
+/* The fused decode step: q = x Wq^T + bq, k = x Wk^T + bk, v = x Wv^T + bv (orc_project),
+ * then exactly kv_append's work -- q rotated into q_out, k rotated and stored, v stored
+ * -- so its results are the unfused path's by construction.
+ * x: [nt][d_model]; wq: [n_head * hd][d_model]; wk, wv: [n_head_kv * hd_kv][d_model];
+ * biases NULL or [rows]; q_out: [nt][n_head][hd]. */
+int orc_qkv_rope_append(orc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                        const int32_t *pos, const float *x, int32_t d_model, const float *wq,
+                        const float *bq, const float *wk, const float *bk, const float *wv,
+                        const float *bv, int32_t n_head, int32_t hd, float *q_out,
+                        float freq_base, float freq_scale, int32_t style)
+{
+    if (!c || layer < 0 || layer >= c->n_layer || nt < 0) return ORC_E_ARG;
+    if (nt == 0) return ORC_OK;
+    if (!x || !wq || !wk || !wv || !q_out || d_model <= 0) return ORC_E_ARG;
+    if (n_head <= 0 || n_head % c->n_head_kv != 0) return ORC_E_ARG;
+    if (hd <= 0 || (hd & 1) || hd > ORC_MAX_HEAD_DIM) return ORC_E_ARG;
+    const int32_t nkt = c->n_head_kv * c->hd_kv;
+    float *k = (float *)malloc(sizeof(float) * (size_t)nt * nkt);
+    float *v = (float *)malloc(sizeof(float) * (size_t)nt * nkt);
+    float *q = (float *)malloc(sizeof(float) * (size_t)nt * n_head * hd);
+    int st = (!k || !v || !q) ? ORC_E_NOMEM : ORC_OK;
+    if (st == ORC_OK) st = orc_project(x, wq, bq, nt, n_head * hd, d_model, q);
+    if (st == ORC_OK) st = orc_project(x, wk, bk, nt, nkt, d_model, k);
+    if (st == ORC_OK) st = orc_project(x, wv, bv, nt, nkt, d_model, v);
+    /* orc_append_rope validates everything else before it writes anything. */
+    if (st == ORC_OK)
+        st = orc_append_rope(c, layer, nt, seq_ids, pos, q, n_head, hd, k, v, freq_base,
+                             freq_scale, style);
+    if (st == ORC_OK) memcpy(q_out, q, sizeof(float) * (size_t)nt * n_head * hd);
+    free(k); free(v); free(q);
+    return st;
 }
 
 static int check_heads(const orc_cache *c, int32_t n_head, int32_t hd)
@@ -591,8 +653,8 @@ static int cmp_run(const void *a, const void *b)
 
 /* Decode over explicit windows ("13 · The decode loop and graph reuse" §2.2, Budget 3:
  * the cells a query may read are an input -- a list of runs -- resolved by the caller,
- * not a bound derived from positions; "Pitfalls" item 4: rows past a rolled-back cursor
- * are never read because the window does not name them).
+ * not a bound derived from positions; §3.4 "Pitfalls & invariants" item 4: rows past a
+ * rolled-back cursor are never read because the window does not name them).
  * Query b attends, in its (seq_ids[b], layer) regions, the cells of its runs
  * r = run_off[b] .. run_off[b+1]-1, each run the rows [run_start[r], run_start[r] +
  * run_len[r]), taken in the listed order.  Reading of the run list (the pages name it but

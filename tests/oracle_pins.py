@@ -683,6 +683,104 @@ def pin_runs_errors(o: Oracle):
     c.close()
 
 
+# ------------------------------------------------------------------------------------
+# Fused decode projections ("13 · The decode loop and graph reuse" §2.3: q/k/v matmuls,
+# biases, two RoPEs and two KV stores as one operation; §3.4 item 5: fused and unfused
+# paths bit-identical)
+# ------------------------------------------------------------------------------------
+
+def rn32_fraction(r):
+    """The f32 nearest to the rational r (ties to even), by integer arithmetic."""
+    from fractions import Fraction
+    if r == 0:
+        return np.float32(0.0)
+    sign = -1 if r < 0 else 1
+    a = abs(Fraction(r))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum_exp = max(e - 23, -149)          # spacing of f32 values near a
+    m = a / Fraction(2) ** quantum_exp
+    q = m.numerator // m.denominator
+    rem = m - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return np.float32(sign * float(Fraction(q) * Fraction(2) ** quantum_exp))
+
+
+def pin_project_exact_rational(o: Oracle):
+    """Each projection output is the f32 nearest to the exact rational dot product, then
+    plus the bias in f32: against exact Fraction arithmetic, on rows with wide magnitude
+    ranges and heavy cancellation (where any f32 or f64 running sum goes wrong)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(140)
+    nt, rows, d = 3, 6, 37
+    x = (rng.standard_normal((nt, d)) * 10.0 ** rng.integers(-6, 7, (nt, d))).astype(np.float32)
+    w = (rng.standard_normal((rows, d)) * 10.0 ** rng.integers(-6, 7, (rows, d))).astype(np.float32)
+    x[0, :4] = [1e20, 1.0, -1e20, 0.5]     # row 0 of w below: exact result 1.5 (an f64
+    #                                          running sum loses the 1 next to 1e20)
+    w[0, :] = 0.0
+    w[0, :4] = 1.0
+    w[1] = -w[2] * np.float32(1.0)          # rows 1 and 2 cancel term by term
+    b = rng.standard_normal(rows).astype(np.float32)
+    got = o.project(x, w)
+    gotb = o.project(x, w, b)
+    for t in range(nt):
+        for j in range(rows):
+            exact = sum(Fraction(float(x[t, i])) * Fraction(float(w[j, i])) for i in range(d))
+            want = rn32_fraction(exact)
+            assert got[t, j].view(np.uint32) == want.view(np.uint32), (t, j, got[t, j], want)
+            assert gotb[t, j].view(np.uint32) == (want + b[j]).view(np.uint32), (t, j)
+    assert got[0, 0] == 1.5
+    assert np.array_equal(got[:, 1], -got[:, 2])
+
+
+def pin_fused_equals_unfused(o: Oracle):
+    """The fused step's rotated q, cache rows and high-water marks are those of the
+    projections (pinned above) followed by the pinned append, bit for bit, with and
+    without biases, in the three RoPE styles and the three region formats."""
+    from oracle import KV_F16 as F16, KV_Q8_0 as Q8
+    rng = np.random.default_rng(150)
+    d, nh, nkv, hd, hdk, cap = 96, 4, 2, 32, 32, 16
+    for style in (ROPE_NEOX, ROPE_INTERLEAVED, ROPE_NONE):
+        for dt in (0, F16, Q8):
+            for with_bias in (True, False):
+                x = rng.standard_normal((3, d)).astype(np.float32)
+                wq, wk, wv = (rng.standard_normal((r, d)).astype(np.float32) * np.float32(0.1)
+                              for r in (nh * hd, nkv * hdk, nkv * hdk))
+                bq, bk, bv = ((rng.standard_normal(r).astype(np.float32) if with_bias else None)
+                              for r in (nh * hd, nkv * hdk, nkv * hdk))
+                seqs, pos = [0, 1, 0], [3, 3, 15]
+                fused = OracleCache(2, 1, nkv, hdk, cap, o, dtype=dt)
+                st, qf = fused.qkv_rope_append(0, seqs, pos, x, wq, bq, wk, bk, wv, bv, nh, hd,
+                                               1e4, 1.0, style)
+                assert st == OK
+                plain = OracleCache(2, 1, nkv, hdk, cap, o, dtype=dt)
+                q = o.project(x, wq, bq).reshape(3, nh, hd)
+                k = o.project(x, wk, bk).reshape(3, nkv, hdk)
+                v = o.project(x, wv, bv).reshape(3, nkv, hdk)
+                st, qp = plain.append_rope(0, seqs, pos, q, nh, hd, k, v, 1e4, 1.0, style)
+                assert st == OK
+                assert np.array_equal(qf.view(np.uint32), qp.view(np.uint32))
+                for s_ in (0, 1):
+                    assert np.array_equal(fused.k(s_, 0), plain.k(s_, 0))
+                    assert np.array_equal(fused.v(s_, 0), plain.v(s_, 0))
+                    assert fused.seq_len(s_, 0) == plain.seq_len(s_, 0)
+                fused.close()
+                plain.close()
+    # Errors come from the same checks as the append: nothing is written.  (Two sequences:
+    # a broken range check then writes into the second region, not past the allocation.)
+    c = OracleCache(2, 1, nkv, hdk, cap, o)
+    x = rng.standard_normal((2, d)).astype(np.float32)
+    w = rng.standard_normal((nh * hd, d)).astype(np.float32)
+    wkv = rng.standard_normal((nkv * hdk, d)).astype(np.float32)
+    st, _ = c.qkv_rope_append(0, [0, 0], [1, 1], x, w, None, wkv, None, wkv, None, nh, hd, 1e4)
+    assert st == E_DUP and not c.k(0, 0).any() and c.seq_len(0, 0) == 0
+    st, _ = c.qkv_rope_append(0, [0, 0], [1, 16], x, w, None, wkv, None, wkv, None, nh, hd, 1e4)
+    assert st == E_RANGE and not c.k(0, 0).any()
+    c.close()
+
+
 ALL_PINS = [
     pin_inv_freq_correctly_rounded,
     pin_rope_worked_example,
@@ -711,4 +809,6 @@ ALL_PINS = [
     pin_runs_brute_force,
     pin_runs_stale_cells_and_shared_region,
     pin_runs_errors,
+    pin_project_exact_rational,
+    pin_fused_equals_unfused,
 ]

@@ -73,6 +73,15 @@ MUTANTS = {
                              "if ((int64_t)tmp[2 * (r - 1)] + tmp[2 * (r - 1) + 1] > tmp[2 * r] + 1) st = ORC_E_DUP;"),
     "runs_range_off_by_one": ("(int64_t)run_start[r] + run_len[r] > c->capacity) return ORC_E_RANGE;",
                               "(int64_t)run_start[r] + run_len[r] > c->capacity + 1) return ORC_E_RANGE;"),
+    # Fused decode projections
+    "project_products_rounded": ("acc += (__float128)xr[i] * (__float128)wr[i];",
+                                 "acc += (__float128)(xr[i] * wr[i]);"),
+    "project_f64_sum": ("__float128 acc = 0;", "double acc = 0;"),
+    "project_bias_dropped": ("if (b) y = y + b[j];", "(void)b;"),
+    "fused_k_from_wv": ("st = orc_project(x, wk, bk, nt, nkt, d_model, k);",
+                        "st = orc_project(x, wv, bk, nt, nkt, d_model, k);"),
+    "fused_q_unrotated": ("if (st == ORC_OK) memcpy(q_out, q, sizeof(float) * (size_t)nt * n_head * hd);",
+                          "if (st == ORC_OK) orc_project(x, wq, bq, nt, n_head * hd, d_model, q_out);"),
     "q8_store_skipped": ("orc_q8_quantize_row(src, n, (orc_q8_block *)region + off / ORC_Q8_BLOCK);",
                          "(void)src;"),
 }
