@@ -5,6 +5,7 @@
  *   kv_alloc        size the per-(sequence, layer) K and V regions once, zeroed
  *   kv_append_rope  rotate q and k (RoPE) at positions given as data, write K/V rows
  *                   in place at those positions
+ *   kv_qkv_rope_append  the decode step's q/k/v projections fused with RoPE and the store
  *   gqa_attn_prefill  nt query tokens of one sequence, token t attending rows [0, pos[t]]
  *   gqa_attn_decode   one query token per sequence for a batch of sequences
  *   gqa_attn_decode_runs  the same over explicit windows (lists of row runs)
@@ -190,6 +191,38 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
                           const int32_t *pos, float *q, int32_t n_head, int32_t hd,
                           const float *k, const float *v, float freq_base, float freq_scale,
                           kvc_rope_style style, void *stream);
+
+/*
+ * kv_qkv_rope_append -- the decode step before attention, fused: the q, k and v
+ * projections of nt input rows with their biases, RoPE on q and k, and the K/V store --
+ * one kernel instead of three matmuls, three bias adds, two rotations and two stores
+ * ([MINFER-13] §2.3: a GPU build fuses exactly these for one-token steps; §3.4 item 5:
+ * fused and unfused results must be identical bit for bit).
+ *
+ *   x           device [nt][d_model] f32: the layer's normalised input rows.
+ *   d_model     input width: a multiple of 4, at most 65536.
+ *   wq          device [n_head * hd][d_model]: row j produces q value j (head j / hd).
+ *   wk, wv      device [n_head_kv * hd_kv][d_model], likewise for k and v.
+ *   bq, bk, bv  device [rows] biases, or NULL for none.
+ *   q_out       device [nt][n_head][hd]: receives the rotated q.
+ *   layer, nt, seq_ids, pos, n_head, hd, freq_base, freq_scale, style: as in
+ *               kv_append_rope; nt is at most 64 (a decode batch).
+ * Each projection value is the f32 nearest to the exact dot product of x's row and the
+ * weight row, then plus the bias in f32 (a reading: the pages require only that fused
+ * and unfused agree; this definition makes the result independent of summation order).
+ * The k and v rows then go through exactly kv_append_rope's rotation and store, so the
+ * cache equals what kv_append_rope writes from those projections, bit for bit, in every
+ * region format; the high-water marks advance the same way.
+ * Errors: as kv_append_rope (checked before any device work), plus KVC_E_ARG for NULL
+ * inputs, a d_model that is not a multiple of 4 or too large, misaligned pointers (x,
+ * weights, q_out 16-byte; biases 4-byte) and nt above 64.
+ */
+kvc_status kv_qkv_rope_append(kvc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                              const int32_t *pos, const float *x, int32_t d_model,
+                              const float *wq, const float *bq, const float *wk, const float *bk,
+                              const float *wv, const float *bv, int32_t n_head, int32_t hd,
+                              float *q_out, float freq_base, float freq_scale,
+                              kvc_rope_style style, void *stream);
 
 /*
  * gqa_attn_prefill -- causal GQA attention for nt query tokens of one sequence.

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANG
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kv_alloc", "kv_alloc_typed", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
-           "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_runs", "kv_last_error")
+           "kv_qkv_rope_append", "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_runs", "kv_last_error")
 
 
 class KvcError(RuntimeError):
@@ -62,6 +62,8 @@ def lib(path: str = LIB_PATH):
         "kv_view": [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(p)],
         "kv_seq_len": [p, i32, i32, ctypes.POINTER(i32)],
         "kv_append_rope": [p, i32, i32, p, p, p, i32, i32, p, p, f32, f32, ctypes.c_int, p],
+        "kv_qkv_rope_append": [p, i32, i32, p, p, p, i32, p, p, p, p, p, p, i32, i32, p, f32, f32,
+                               ctypes.c_int, p],
         "gqa_attn_prefill": [p, i32, i32, i32, p, p, i32, i32, f32, p, p],
         "gqa_attn_decode": [p, i32, i32, p, p, p, i32, i32, f32, p, p],
         "gqa_attn_decode_runs": [p, i32, i32, p, p, p, p, p, i32, i32, f32, p, p],
@@ -181,6 +183,22 @@ def kv_append_rope(c: Cache, layer, seq_ids, pos, q, n_head, hd, k, v, freq_base
     _check(lib().kv_append_rope(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
                                 n_head, hd, _dev(k, "k"), _dev(v, "v"), freq_base, freq_scale,
                                 style, _stream(stream)))
+
+
+def kv_qkv_rope_append(c: Cache, layer, seq_ids, pos, x, wq, bq, wk, bk, wv, bv, n_head, hd,
+                       q_out, freq_base, freq_scale=1.0, style=ROPE_NEOX, stream=None):
+    """Fused decode step: projections (x [nt][d_model] against row-major weights, optional
+    biases), RoPE, K/V store; the rotated q goes to q_out [nt][n_head][hd]."""
+    s_arr, s_ptr = _host_i32(seq_ids)
+    p_arr, p_ptr = _host_i32(pos)
+    if s_arr.size != p_arr.size:
+        raise ValueError("seq_ids and pos differ in length")
+    d_model = int(x.shape[-1]) if hasattr(x, "shape") else 0
+    _check(lib().kv_qkv_rope_append(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(x, "x"),
+                                    d_model, _dev(wq, "wq"), _dev(bq, "bq"), _dev(wk, "wk"),
+                                    _dev(bk, "bk"), _dev(wv, "wv"), _dev(bv, "bv"), n_head, hd,
+                                    _dev(q_out, "q_out"), freq_base, freq_scale, style,
+                                    _stream(stream)))
 
 
 def gqa_attn_prefill(c: Cache, seq, layer, pos, q, n_head, hd, scale, out, stream=None):

@@ -21,7 +21,8 @@ OBJDIR = os.path.join(ROOT, "_build", "obj")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["k_rope.hip", "k_decode.hip", "k_prefill.hip", "kvc_api.cpp", "validate.cpp"]
+HIP_SOURCES = ["k_rope.hip", "k_qkv.hip", "k_decode.hip", "k_prefill.hip", "kvc_api.cpp",
+               "validate.cpp"]
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Packed fp32 instructions are kept out of the generated code.

@@ -62,4 +62,14 @@ int hc_check_decode_runs(const int32_t *g5, int32_t layer, int32_t n_seq, const 
                                   n_head, hd, scale, out, g_msg);
 }
 
+int hc_check_qkv(const int32_t *g5, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                 const int32_t *pos, const void *x, int32_t d_model, const void *wq,
+                 const void *bq, const void *wk, const void *bk, const void *wv, const void *bv,
+                 int32_t n_head, int32_t hd, const void *q_out, float freq_base,
+                 float freq_scale, int32_t style)
+{
+    return kvc::check_qkv(geom(g5), layer, nt, seq_ids, pos, x, d_model, wq, bq, wk, bk, wv, bv,
+                          n_head, hd, q_out, freq_base, freq_scale, style, g_msg);
+}
+
 }  // extern "C"

@@ -1,0 +1,256 @@
+// Fused decode step: q/k/v projections, their biases, RoPE on q and k, and the K/V
+// store, in one kernel.
+//
+// "13 · The decode loop and graph reuse" §2.3: on a GPU build a one-token step merges
+// three matmuls, three biases, two RoPEs and two KV stores into a single operation;
+// §3.4 item 5: the fused and the unfused paths must agree bit for bit.  Here "unfused"
+// is the projection followed by kv_append_rope, and the kernel reproduces it exactly:
+//   * each projection output is the f32 nearest to the exact dot product x . w_j: every
+//     f32 x f32 product is exact in f64, the sum is carried as an unevaluated pair of
+//     f64 values (hi + lo, hi accumulated with the error-free TwoSum and the errors in
+//     lo), lane partials are merged the same way, and the pair is rounded to f32 once,
+//     through round-to-odd at f64 precision (53 >= 24 + 2 bits makes that one correct
+//     rounding); the bias is then added in f32;
+//   * the rotation, the binary16 rounding and the Q8_0 quantization are the append
+//     kernel's own functions (kvc_device.hpp).
+// The pages' reading of the matmul's precision is only that fused and unfused agree;
+// the exact-then-round definition makes the result independent of summation order, so
+// it can be checked against any exact evaluation.
+//
+// Work split: a workgroup owns one "unit" -- up to 8 rotation pairs (32 for a Q8_0
+// cache, so that a unit holds whole 32-value blocks) of one head of q, k or v -- for a
+// group of up to 8 tokens.  NEOX pairs (i, i + D/2) and interleaved pairs (2i, 2i+1) of
+// a unit are computed together, so the rotation happens in LDS without another launch.
+// Rows are reduced by 16 lanes each (four rows per wave at a time), every lane streaming
+// 16-byte pieces of its row; the weight rows are read once per token group.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "kvc_device.hpp"
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
+constexpr int kMaxRows = 64;   // rows of a unit (32 pairs)
+constexpr int kLanesPerRow = 16;
+
+// Error-free sum: s + e == a + b exactly (s = fl(a + b)).
+__device__ __forceinline__ void two_sum(double a, double b, double &s, double &e)
+{
+#pragma clang fp contract(off)
+    s = a + b;
+    const double bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+// (hi, lo) += p, p exact.
+__device__ __forceinline__ void dd_add(double &hi, double &lo, double p)
+{
+#pragma clang fp contract(off)
+    double s, e;
+    two_sum(hi, p, s, e);
+    hi = s;
+    lo += e;
+}
+
+// (hi, lo) += (bhi, blo).
+__device__ __forceinline__ void dd_merge(double &hi, double &lo, double bhi, double blo)
+{
+#pragma clang fp contract(off)
+    double s, e;
+    two_sum(hi, bhi, s, e);
+    hi = s;
+    lo += e + blo;
+}
+
+// The f32 nearest to hi + lo: normalise, round to odd at f64 precision, round to f32.
+__device__ __forceinline__ float dd_to_f32(double hi, double lo)
+{
+    double h, l;
+    two_sum(hi, lo, h, l);
+    if (l != 0.0 && h != 0.0) {
+        unsigned long long bits = (unsigned long long)__double_as_longlong(h);
+        if (!(bits & 1ull)) {
+            // The neighbour of h on l's side is odd: step the magnitude up when l has h's
+            // sign, down otherwise.
+            bits = ((l > 0.0) == (h > 0.0)) ? bits + 1ull : bits - 1ull;
+            h = __longlong_as_double((long long)bits);
+        }
+    }
+    return (float)h;
+}
+
+template <int STYLE, typename KVT, int TT>
+__global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per_unit)
+{
+    __shared__ float ys[TT][kMaxRows];   // [token][local row]
+
+    // Unit -> (projection, head, pair range).
+    int unit = blockIdx.x;
+    int proj = 0;
+    if (unit >= p.units_q) {
+        unit -= p.units_q;
+        proj = 1;
+        if (unit >= p.units_kv) {
+            unit -= p.units_kv;
+            proj = 2;
+        }
+    }
+    const int D = proj == 0 ? p.hd : p.hd_kv;
+    const int half = D >> 1;
+    const int upr = (half + pairs_per_unit - 1) / pairs_per_unit;   // units per head
+    const int head = unit / upr;
+    const int i_begin = (unit - head * upr) * pairs_per_unit;
+    const int np = min(pairs_per_unit, half - i_begin);
+    const int R = 2 * np;
+    const bool rot = proj < 2 && STYLE != kNone;
+    const bool neox = rot && STYLE == kNeox;
+    // Local row lr -> index within the head.  NEOX: first the np first-half rows, then
+    // their partners; otherwise the unit's rows in order.
+    auto head_row = [&](int lr) {
+        if (neox) return lr < np ? i_begin + lr : half + i_begin + (lr - np);
+        return 2 * i_begin + lr;
+    };
+    const float *W = p.w[proj] + (int64_t)head * D * p.d;
+    const float *B = p.b[proj] ? p.b[proj] + head * D : nullptr;
+    const int t0 = blockIdx.y * TT;
+    const int ntk = min(TT, p.nt - t0);
+
+    // Projections.  Row lr is reduced by 16 lanes; lane li takes elements 4 li + 64 k.
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane % kLanesPerRow;
+    for (int base = 0; base < R; base += 16) {
+        const int lr = base + wave * 4 + lane / kLanesPerRow;
+        const bool row_ok = lr < R;
+        const float *wr = W + (int64_t)head_row(row_ok ? lr : 0) * p.d;
+        double hi[TT], lo[TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) hi[t] = lo[t] = 0.0;
+#pragma unroll 4
+        for (int i = li * 4; i < p.d; i += 4 * kLanesPerRow) {
+            const float4 w4 = *reinterpret_cast<const float4 *>(wr + i);
+#pragma unroll
+            for (int t = 0; t < TT; t++) {
+                if (t < ntk) {
+                    const float4 x4 = *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + i);
+                    dd_add(hi[t], lo[t], (double)x4.x * (double)w4.x);
+                    dd_add(hi[t], lo[t], (double)x4.y * (double)w4.y);
+                    dd_add(hi[t], lo[t], (double)x4.z * (double)w4.z);
+                    dd_add(hi[t], lo[t], (double)x4.w * (double)w4.w);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+#pragma unroll
+            for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
+                const double oh = __shfl_xor(hi[t], off);
+                const double ol = __shfl_xor(lo[t], off);
+                dd_merge(hi[t], lo[t], oh, ol);
+            }
+        }
+        if (row_ok && li == 0) {
+#pragma unroll
+            for (int t = 0; t < TT; t++) {
+                if (t < ntk) {
+                    float y = dd_to_f32(hi[t], lo[t]);
+                    if (B) y = y + B[head_row(lr)];
+                    ys[t][lr] = y;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // RoPE in LDS (q and k), with the append kernel's rotate_pair and table rows.
+    if (rot) {
+        const float2 *tab = proj == 0 ? p.tab_q : p.tab_k;
+        for (int idx = threadIdx.x; idx < ntk * np; idx += blockDim.x) {
+            const int t = idx / np;
+            const int il = idx - t * np;
+            const int lr0 = neox ? il : 2 * il;
+            const int lr1 = neox ? np + il : 2 * il + 1;
+            const float2 cs = tab[(int64_t)p.ipos[t0 + t] * half + i_begin + il];
+            float y0, y1;
+            rotate_pair(ys[t][lr0], ys[t][lr1], cs, y0, y1);
+            ys[t][lr0] = y0;
+            ys[t][lr1] = y1;
+        }
+        __syncthreads();
+    }
+
+    if (proj == 0) {
+        for (int idx = threadIdx.x; idx < ntk * R; idx += blockDim.x) {
+            const int t = idx / R;
+            const int lr = idx - t * R;
+            p.q_out[((int64_t)(t0 + t) * p.n_head + head) * p.hd + head_row(lr)] = ys[t][lr];
+        }
+        return;
+    }
+
+    // K or V rows: 4 consecutive local rows are 4 consecutive head dims (np is a
+    // multiple of 4 for every supported hd_kv); for Q8_0 the R/4 quads of a token are a
+    // multiple of 8, so the 8 lanes of a 32-value block are aligned and active together.
+    const int nkt = p.n_head_kv * p.hd_kv;
+    char *cache = static_cast<char *>(proj == 1 ? p.kc : p.vc);
+    const int nq = R / 4;
+    for (int idx = threadIdx.x; idx < ntk * nq; idx += blockDim.x) {
+        const int t = idx / nq;
+        const int qd = idx - t * nq;
+        const int lr = 4 * qd;
+        const float4 y = make_float4(ys[t][lr], ys[t][lr + 1], ys[t][lr + 2], ys[t][lr + 3]);
+        const int j = head * p.hd_kv + head_row(lr);   // value index in the row
+        const int64_t reg = ((int64_t)p.iseq[t0 + t] * p.n_layer + p.layer) * p.region_bytes;
+        const int64_t row = p.ipos[t0 + t];
+        if constexpr (std::is_same<KVT, int8_t>::value) {
+            int8_t *codes = reinterpret_cast<int8_t *>(cache + reg) + row * nkt;
+            _Float16 *scales = reinterpret_cast<_Float16 *>(cache + reg + p.scale_off) +
+                               row * (nkt / kQ8Block);
+            q8_store4(y, codes, scales, j, idx);
+        } else {
+            store4(reinterpret_cast<KVT *>(cache + reg) + row * nkt + j, y);
+        }
+    }
+}
+
+template <int STYLE, typename KVT>
+void launch_style_fmt(const QkvParams &p, int32_t ppu, hipStream_t s)
+{
+    const int units = p.units_q + 2 * p.units_kv;
+    if (p.nt == 1) {
+        qkv_kernel<STYLE, KVT, 1><<<dim3(units, 1), 256, 0, s>>>(p, ppu);
+    } else {
+        qkv_kernel<STYLE, KVT, 8><<<dim3(units, (p.nt + 7) / 8), 256, 0, s>>>(p, ppu);
+    }
+}
+
+template <typename KVT>
+void launch_fmt(const QkvParams &p, int32_t ppu, hipStream_t s)
+{
+    switch (p.style) {
+    case kNeox: launch_style_fmt<kNeox, KVT>(p, ppu, s); break;
+    case kInterleaved: launch_style_fmt<kInterleaved, KVT>(p, ppu, s); break;
+    default: launch_style_fmt<kNone, KVT>(p, ppu, s); break;
+    }
+}
+
+}  // namespace
+
+int32_t qkv_pairs_per_unit(int32_t kv_fmt) { return kv_fmt == kFmtQ8 ? 32 : 8; }
+
+hipError_t launch_qkv(const QkvParams &p, hipStream_t s)
+{
+    if (p.nt <= 0) return hipSuccess;
+    const int32_t ppu = qkv_pairs_per_unit(p.kv_fmt);
+    if (p.kv_fmt == kFmtQ8) launch_fmt<int8_t>(p, ppu, s);
+    else if (p.kv_fmt == kFmtF16) launch_fmt<_Float16>(p, ppu, s);
+    else launch_fmt<float>(p, ppu, s);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -16,41 +16,18 @@
 // nearest to cos/sin of the f32 angle f32(p) * speed_i, with speed_i the f32 nearest to
 // the exact expression.  Both are evaluated in f64 and rounded once to f32 (an f64
 // result sits within an f64 ulp or so of the exact value, far inside an f32 half-ulp
-// except at near-ties).  The rotation below is compiled with FMA contraction off, so each
-// product and each sum is rounded on its own and the result is the same bits as any
-// correctly rounded IEEE evaluation of the same formula.
+// except at near-ties).  The rotation (rotate_pair, kvc_device.hpp) is compiled with FMA
+// contraction off, so each product and each sum is rounded on its own and the result is
+// the same bits as any correctly rounded IEEE evaluation of the same formula.
 #include <hip/hip_runtime.h>
 
+#include "kvc_device.hpp"
 #include "kvc_internal.hpp"
 
 namespace kvc {
 namespace {
 
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
-
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Store 4 f32 values at dst: as they are for an f32 region, rounded to binary16 (nearest,
-// ties to even: v_cvt_f16_f32 in the default rounding mode) for a half region.
-__device__ __forceinline__ void store4(float *dst, float4 v)
-{
-    *reinterpret_cast<float4 *>(dst) = v;
-}
-__device__ __forceinline__ void store4(_Float16 *dst, float4 v)
-{
-    half4_t h;
-    h[0] = (_Float16)v.x;
-    h[1] = (_Float16)v.y;
-    h[2] = (_Float16)v.z;
-    h[3] = (_Float16)v.w;
-    *reinterpret_cast<half4_t *>(dst) = h;
-}
 
 __global__ void __launch_bounds__(256) rope_table_kernel(float2 *tab, int32_t rows, int32_t hd,
                                                          float freq_base, float freq_scale)
@@ -66,20 +43,6 @@ __global__ void __launch_bounds__(256) rope_table_kernel(float2 *tab, int32_t ro
         const float theta = __fmul_rn((float)p, speed);
         tab[idx] = make_float2((float)cos((double)theta), (float)sin((double)theta));
     }
-}
-
-// Rotate one pair.  Contraction is off for this function: four rounded products, one
-// rounded difference and one rounded sum.
-__device__ __forceinline__ void rotate_pair(float x0, float x1, float2 cs_sn, float &y0,
-                                            float &y1)
-{
-#pragma clang fp contract(off)
-    const float a = x0 * cs_sn.x;
-    const float b = x1 * cs_sn.y;
-    const float c = x0 * cs_sn.y;
-    const float d = x1 * cs_sn.x;
-    y0 = a - b;
-    y1 = c + d;
 }
 
 // Rotate nh heads of width w (even) from src into dst (dst may equal src), using the
@@ -221,29 +184,6 @@ __device__ __forceinline__ float4 rotated4(const float *x, int32_t e, int32_t w,
         y = *reinterpret_cast<const float4 *>(x + e);
     }
     return y;
-}
-
-// Q8_0 store of values j..j+3 of a row, held by lane group member (idx % 8) of the 8
-// aligned lanes that together hold block j / 32: the block's max |x| is reduced across
-// the 8 lanes (DPP within each half-row), every lane derives the same scale and
-// reciprocal (IEEE f32 division), writes its 4 codes as one dword, and the group's
-// first lane writes the binary16 scale.
-__device__ __forceinline__ void q8_store4(float4 y, int8_t *codes, _Float16 *scales, int32_t j,
-                                          int32_t idx)
-{
-#pragma clang fp contract(off)
-    float a = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
-    a = fmaxf(a, dpp<0xB1>(a));   // lane ^ 1
-    a = fmaxf(a, dpp<0x4E>(a));   // lane ^ 2
-    a = fmaxf(a, dpp<0x141>(a));  // i <-> 7 - i within 8 lanes: the other quad
-    const float d = a / 127.0f;
-    const float r = d != 0.0f ? 1.0f / d : 0.0f;
-    const int32_t c0 = (int32_t)roundf(y.x * r), c1 = (int32_t)roundf(y.y * r);
-    const int32_t c2 = (int32_t)roundf(y.z * r), c3 = (int32_t)roundf(y.w * r);
-    const uint32_t packed = (uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8) |
-                            ((uint32_t)(c2 & 0xff) << 16) | ((uint32_t)(c3 & 0xff) << 24);
-    *reinterpret_cast<uint32_t *>(codes + j) = packed;
-    if ((idx & 7) == 0) scales[j / kQ8Block] = (_Float16)d;
 }
 
 // Q8_0 variant of append_kernel: the same rotation, then each row is quantized block by

@@ -471,6 +471,63 @@ kvc_status kv_append_rope(kvc_cache *c, int32_t layer, int32_t nt, const int32_t
     return KVC_OK;
 }
 
+kvc_status kv_qkv_rope_append(kvc_cache *c, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                              const int32_t *pos, const float *x, int32_t d_model,
+                              const float *wq, const float *bq, const float *wk, const float *bk,
+                              const float *wv, const float *bv, int32_t n_head, int32_t hd,
+                              float *q_out, float freq_base, float freq_scale,
+                              kvc_rope_style style, void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_qkv(c->g, layer, nt, seq_ids, pos, x, d_model, wq, bq, wk, bk, wv,
+                                   bv, n_head, hd, q_out, freq_base, freq_scale, (int32_t)style,
+                                   msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (nt == 0) return KVC_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    kvc::QkvParams p{};
+    if (style != KVC_ROPE_NONE) {
+        if ((st = get_table(c, c->g.hd_kv, freq_base, freq_scale, s, &p.tab_k)) != KVC_OK) return st;
+        if ((st = get_table(c, hd, freq_base, freq_scale, s, &p.tab_q)) != KVC_OK) return st;
+    }
+    std::memcpy(p.ipos, pos, sizeof(int32_t) * nt);
+    std::memcpy(p.iseq, seq_ids, sizeof(int32_t) * nt);
+    p.x = x;
+    p.w[0] = wq;
+    p.w[1] = wk;
+    p.w[2] = wv;
+    p.b[0] = bq;
+    p.b[1] = bk;
+    p.b[2] = bv;
+    p.q_out = q_out;
+    p.kc = c->K;
+    p.vc = c->V;
+    p.region_bytes = c->region_bytes;
+    p.scale_off = c->scale_off;
+    p.d = d_model;
+    p.nt = nt;
+    p.n_head = n_head;
+    p.hd = hd;
+    p.n_head_kv = c->g.n_head_kv;
+    p.hd_kv = c->g.hd_kv;
+    p.n_layer = c->g.n_layer;
+    p.layer = layer;
+    p.style = (int32_t)style;
+    p.kv_fmt = c->kv_fmt;
+    const int32_t ppu = kvc::qkv_pairs_per_unit(c->kv_fmt);
+    p.units_q = n_head * ((hd / 2 + ppu - 1) / ppu);
+    p.units_kv = c->g.n_head_kv * ((c->g.hd_kv / 2 + ppu - 1) / ppu);
+    hipError_t e = kvc::launch_qkv(p, s);
+    if (e != hipSuccess) return hip_fail(e, "fused projection kernel");
+    for (int32_t t = 0; t < nt; t++) {
+        int32_t &w = c->hw[(size_t)seq_ids[t] * c->g.n_layer + layer];
+        w = std::max(w, pos[t] + 1);
+    }
+    return KVC_OK;
+}
+
 kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int32_t nt,
                             const int32_t *pos, const float *q, int32_t n_head, int32_t hd,
                             float scale, float *out, void *stream)

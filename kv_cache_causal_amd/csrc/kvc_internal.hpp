@@ -45,6 +45,24 @@ struct AppendParams {
 };
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 
+// ---- Fused decode step: q/k/v projections + biases + RoPE + K/V store -------------------
+// Up to kInlineTokens tokens per call (positions and sequence ids in the arguments).
+struct QkvParams {
+    const float *x;          // [nt][d]
+    const float *w[3];       // q, k, v weights: [rows][d], row j produces output j
+    const float *b[3];       // biases [rows] or nullptr
+    float *q_out;            // [nt][n_head][hd], rotated
+    void *kc, *vc;           // cache bases
+    const float2 *tab_q, *tab_k;  // RoPE tables (nullptr for style NONE)
+    int64_t region_bytes, scale_off;
+    int32_t d, nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style, kv_fmt;
+    int32_t units_q, units_kv;     // workgroup units of the q and of the k (= v) projection
+    int32_t ipos[kInlineTokens], iseq[kInlineTokens];
+};
+// Rotation pairs per workgroup unit (units per head = ceil((head dim / 2) / this)).
+int32_t qkv_pairs_per_unit(int32_t kv_fmt);
+hipError_t launch_qkv(const QkvParams &p, hipStream_t s);
+
 // ---- K2 + K3: split-K decode and log-sum-exp combine -----------------------------------
 // One launch covers up to kInlineEntries batch entries, whose positions, sequence ids
 // and chunk offsets ride in the kernel arguments.

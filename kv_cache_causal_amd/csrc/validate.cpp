@@ -12,6 +12,7 @@ namespace {
 std::string s(long long x) { return std::to_string(x); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // The query-head checks shared by every call that takes q.
 kvc_status check_heads(const Geometry &g, int32_t n_head, int32_t hd, std::string &msg)
@@ -202,6 +203,47 @@ kvc_status check_decode(const Geometry &g, int32_t layer, int32_t n_seq, const i
     st = check_seq_ids(g, n_seq, seq_ids, msg);
     if (st != KVC_OK) return st;
     return check_positions(g, n_seq, pos, msg);
+}
+
+kvc_status check_qkv(const Geometry &g, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                     const int32_t *pos, const void *x, int32_t d_model, const void *wq,
+                     const void *bq, const void *wk, const void *bk, const void *wv,
+                     const void *bv, int32_t n_head, int32_t hd, const void *q_out,
+                     float freq_base, float freq_scale, int32_t style, std::string &msg)
+{
+    if (layer < 0 || layer >= g.n_layer || nt < 0) {
+        msg = "layer out of range or nt < 0";
+        return KVC_E_ARG;
+    }
+    if (nt == 0) return KVC_OK;
+    if (!x || !wq || !wk || !wv || !q_out || d_model <= 0) {
+        msg = "x, wq, wk, wv and q_out must be non-NULL and d_model >= 1";
+        return KVC_E_ARG;
+    }
+    if (d_model % 4 != 0 || d_model > kMaxModelDim) {
+        msg = "d_model " + s(d_model) + " must be a multiple of 4, at most " + s(kMaxModelDim);
+        return KVC_E_ARG;
+    }
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) ||
+        !aligned16(q_out) || !aligned4(bq) || !aligned4(bk) || !aligned4(bv)) {
+        msg = "x, weights and q_out must be 16-byte aligned (biases 4-byte)";
+        return KVC_E_ARG;
+    }
+    if (nt > kMaxFusedTokens) {
+        msg = "the fused step takes at most " + s(kMaxFusedTokens) + " tokens, got " + s(nt);
+        return KVC_E_ARG;
+    }
+    // Shapes the projections need (the append repeats these and adds hd >= hd_kv after
+    // the style checks, in that order).
+    if (n_head <= 0 || n_head % g.n_head_kv != 0 || hd <= 0 || (hd & 1) ||
+        hd > KVC_MAX_HEAD_DIM) {
+        msg = "n_head must be a positive multiple of n_head_kv and hd even, 2.." +
+              s(KVC_MAX_HEAD_DIM);
+        return KVC_E_ARG;
+    }
+    // Everything the append checks (the projected k and v stand in for its k and v).
+    return check_append(g, layer, nt, seq_ids, pos, q_out, n_head, hd, q_out, q_out, freq_base,
+                        freq_scale, style, msg);
 }
 
 kvc_status check_decode_runs(const Geometry &g, int32_t layer, int32_t n_seq,

@@ -38,6 +38,16 @@ kvc_status check_decode(const Geometry &g, int32_t layer, int32_t n_seq, const i
                         const int32_t *pos, const void *q, int32_t n_head, int32_t hd,
                         float scale, const void *out, std::string &msg);
 
+// Limits of the fused decode step: input width and tokens per call.
+constexpr int32_t kMaxModelDim = 65536;
+constexpr int32_t kMaxFusedTokens = 64;
+
+kvc_status check_qkv(const Geometry &g, int32_t layer, int32_t nt, const int32_t *seq_ids,
+                     const int32_t *pos, const void *x, int32_t d_model, const void *wq,
+                     const void *bq, const void *wk, const void *bk, const void *wv,
+                     const void *bv, int32_t n_head, int32_t hd, const void *q_out,
+                     float freq_base, float freq_scale, int32_t style, std::string &msg);
+
 kvc_status check_decode_runs(const Geometry &g, int32_t layer, int32_t n_seq,
                              const int32_t *seq_ids, const int32_t *run_off,
                              const int32_t *run_start, const int32_t *run_len, const void *q,

@@ -294,10 +294,11 @@ class OracleCache:
         """Fused decode step; returns (status, rotated q [nt][n_head][hd])."""
         seq_ids, pos = _i32(seq_ids), _i32(pos)
         nt = int(pos.shape[0])
-        x = _f32(x)
         ws = [None if a is None else _f32(a) for a in (wq, bq, wk, bk, wv, bv)]
+        x = None if x is None else _f32(x)
+        d_model = ws[0].shape[-1] if x is None else x.shape[-1]
         q = np.zeros((nt, n_head, hd), np.float32)
         st = self.L.orc_qkv_rope_append(self.h, layer, nt, _ptr(seq_ids), _ptr(pos), _ptr(x),
-                                        x.shape[-1], *[_ptr(a) for a in ws], n_head, hd, _ptr(q),
+                                        d_model, *[_ptr(a) for a in ws], n_head, hd, _ptr(q),
                                         base, scale, style)
         return st, q

@@ -170,3 +170,17 @@ class Pair:
         st, want = self.o.attn_decode_runs(layer, seq_ids, runs, q_host, n_head, hd, scale)
         assert st == 0, st
         return got, want
+
+    def qkv(self, layer, seq_ids, pos, x, ws, n_head, hd, base=1e6, fscale=1.0, style=0):
+        """Fused projection + RoPE + store on both; ws = (wq, bq, wk, bk, wv, bv) numpy
+        (biases may be None).  Returns (gpu rotated q, oracle rotated q)."""
+        import torch
+        nt = len(pos)
+        q_out = torch.empty((nt, n_head, hd), dtype=torch.float32, device="cuda")
+        dws = [None if a is None else dev(a) for a in ws]
+        self.kvc.kv_qkv_rope_append(self.g, layer, seq_ids, pos, dev(x), *dws, n_head, hd, q_out,
+                                    base, fscale, style)
+        st, qo = self.o.qkv_rope_append(layer, seq_ids, pos, x, *ws, n_head, hd, base, fscale,
+                                        style)
+        assert st == 0, st
+        return host(q_out), qo

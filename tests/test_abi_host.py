@@ -79,6 +79,8 @@ def hc():
     L.hc_check_prefill.argtypes = [p, i32, i32, i32, p, p, i32, i32, f32, p]
     L.hc_check_decode.argtypes = [p, i32, i32, p, p, p, i32, i32, f32, p]
     L.hc_check_decode_runs.argtypes = [p, i32, i32, p, p, p, p, p, i32, i32, f32, p]
+    L.hc_check_qkv.argtypes = [p, i32, i32, p, p, p, i32, p, p, p, p, p, p, i32, i32, p, f32, f32,
+                               i32]
     L.hc_last_message.restype = ctypes.c_char_p
     return L
 
@@ -259,3 +261,65 @@ def test_decode_runs_checks_match_oracle(hc, name, kw):
                                    n_head, hd, 0.25)
     c.close()
     assert st_lib == st_orc, (name, st_lib, st_orc, hc.hc_last_message())
+
+
+QKV_CASES = [
+    ("ok", dict()),
+    ("no_bias_ok", dict(bias=False)),
+    ("dup", dict(pos=[3, 3], seq=[1, 1])),
+    ("pos_range", dict(pos=[3, 10])),
+    ("seq_range", dict(seq=[0, 2])),
+    ("hd_lt_hd_kv", dict(hd=8)),
+    ("heads", dict(n_head=3)),
+    ("hd_odd", dict(hd=17)),
+    ("style", dict(style=7)),
+    ("base", dict(base=0.0)),
+    ("base_ignored_for_none", dict(base=0.0, style=2)),
+    ("hd_lt_hd_kv_and_bad_style", dict(hd=8, style=9)),
+    ("nt_zero", dict(pos=[], seq=[])),
+    ("x_null", dict(x_null=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", QKV_CASES, ids=[c[0] for c in QKV_CASES])
+def test_qkv_checks_match_oracle(hc, name, kw):
+    seq, pos = kw.get("seq", [0, 1]), kw.get("pos", [3, 9])
+    n_head, hd, d = kw.get("n_head", 4), kw.get("hd", 16), 8
+    style, base = kw.get("style", 0), kw.get("base", 1e4)
+    nkt = GEOM[2] * GEOM[3]
+    g, gp = g5()
+    s_, sp = iarr(seq)
+    p_, pp = iarr(pos)
+    bias = FAKE if kw.get("bias", True) else None
+    xp = None if kw.get("x_null") else FAKE
+    st_lib = hc.hc_check_qkv(gp, 0, len(pos), sp, pp, xp, d, FAKE, bias, FAKE, bias, FAKE, bias,
+                             n_head, hd, FAKE, base, 1.0, style)
+    c = OracleCache(*GEOM)
+    nt = len(pos)
+    rng = np.random.default_rng(6)
+    x = None if kw.get("x_null") else rng.standard_normal((max(nt, 1), d)).astype(np.float32)
+    wq = rng.standard_normal((max(n_head * hd, 1), d)).astype(np.float32)
+    wkv = rng.standard_normal((nkt, d)).astype(np.float32)
+    bq = rng.standard_normal(max(n_head * hd, 1)).astype(np.float32) if bias else None
+    bkv = rng.standard_normal(nkt).astype(np.float32) if bias else None
+    st_orc, _ = c.qkv_rope_append(0, seq, pos, x, wq, bq, wkv, bkv, wkv, bkv, n_head, hd, base,
+                                  1.0, style)
+    c.close()
+    assert st_lib == st_orc, (name, st_lib, st_orc, hc.hc_last_message())
+
+
+def test_qkv_library_limits(hc):
+    """Limits the library adds (the oracle has none): d_model a multiple of 4, at most 64
+    tokens per call."""
+    g, gp = g5()
+    s_, sp = iarr([0])
+    p_, pp = iarr([1])
+    assert hc.hc_check_qkv(gp, 0, 1, sp, pp, FAKE, 6, FAKE, None, FAKE, None, FAKE, None, 4, 16,
+                           FAKE, 1e4, 1.0, 0) == kvc.E_ARG
+    s_, sp = iarr(list(range(2)) * 33)
+    p_, pp = iarr([i // 2 for i in range(66)])
+    geom = np.array((2, 2, 2, 16, 100), np.int32)
+    assert hc.hc_check_qkv(geom.ctypes.data, 0, 65, sp, pp, FAKE, 8, FAKE, None, FAKE, None,
+                           FAKE, None, 4, 16, FAKE, 1e4, 1.0, 0) == kvc.E_ARG
+    assert hc.hc_check_qkv(geom.ctypes.data, 0, 64, sp, pp, FAKE, 8, FAKE, None, FAKE, None,
+                           FAKE, None, 4, 16, FAKE, 1e4, 1.0, 0) == kvc.OK
