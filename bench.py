@@ -23,7 +23,7 @@ Reported:
   cpu_baseline   the plain C oracle on the host cores, on a bounded sample
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
-                       [--kv f32|f16|q8_0] [--decode-runs]
+                       [--kv f32|f16|q8_0] [--decode-runs] [--fused-qkv]
 """
 from __future__ import annotations
 
@@ -60,6 +60,10 @@ def main():
     ap.add_argument("--decode-runs", action="store_true",
                     help="stage 4 through gqa_attn_decode_runs: each sequence's window given "
                          "as two explicit runs, its second half first")
+    ap.add_argument("--fused-qkv", action="store_true",
+                    help="stage 3 through kv_qkv_rope_append: the 32 decode tokens' q/k/v are "
+                         "projected from d_model=1024 inputs with synthetic weights, rotated "
+                         "and stored in one kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before timing, so that "
                          "HBM counters (FETCH_SIZE / WRITE_SIZE) can be calibrated against "
@@ -118,6 +122,13 @@ def main():
     qd, kd, vd = (torch.from_numpy(a).to(dev) for a in W.decode_qkv(w, w.n_seq, 0, 0))
     out_pre = torch.empty((nt, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
     out_dec = torch.empty((w.n_seq, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
+    # Fused-step inputs: Qwen3-0.6B's hidden width, seeded N(0, 1/d) weights (synthetic).
+    D_MODEL = 1024
+    qkv_rows = (w.n_head * w.hd, w.n_head_kv * w.hd_kv, w.n_head_kv * w.hd_kv)
+    if args.fused_qkv:
+        wts = [torch.from_numpy(W.custom(900 + i, (r, D_MODEL)) * np.float32(D_MODEL ** -0.5)).to(dev)
+               for i, r in enumerate(qkv_rows)]
+        x_dec = torch.from_numpy(W.custom(910, (w.n_seq, D_MODEL))).to(dev)
     torch.cuda.synchronize()
     log(f"bench: setup {time.time() - t0:.1f}s; n_past[0] {n_past[0]}, "
         f"prefill {pre_flops / 1e9:.1f} GFLOP, decode {kv_bytes / 1e9:.3f} GB KV")
@@ -145,8 +156,13 @@ def main():
         e[1].record()
         kvc.gqa_attn_prefill(cache, 0, 0, pre_pos, qp, w.n_head, w.hd, w.scale, out_pre)
         e[2].record()
-        kvc.kv_append_rope(cache, 0, seqs, lens, qd, w.n_head, w.hd, kd, vd, w.base,
-                           w.freq_scale, w.style)
+        if args.fused_qkv:
+            kvc.kv_qkv_rope_append(cache, 0, seqs, lens, x_dec, wts[0], None, wts[1], None,
+                                   wts[2], None, w.n_head, w.hd, qd, w.base, w.freq_scale,
+                                   w.style)
+        else:
+            kvc.kv_append_rope(cache, 0, seqs, lens, qd, w.n_head, w.hd, kd, vd, w.base,
+                               w.freq_scale, w.style)
         e[3].record()
         if args.decode_runs:
             kvc.gqa_attn_decode_runs(cache, 0, seqs, win_runs, qd, w.n_head, w.hd, w.scale,
@@ -197,6 +213,8 @@ def main():
             "kv_dtype": args.kv,
             "decode_windows": "explicit runs, 2 per sequence" if args.decode_runs else
                               "position-derived [0, pos]",
+            "decode_append": "fused projections + RoPE + store" if args.fused_qkv else
+                             "kv_append_rope of given q/k/v",
             "n_seq": int(w.n_seq), "n_head": w.n_head, "n_head_kv": w.n_head_kv,
             "hd": w.hd, "hd_kv": w.hd_kv, "capacity": w.capacity,
             "n_past_seq0": int(n_past[0]), "prefill_tokens": nt,
@@ -212,6 +230,12 @@ def main():
             "decode_attn": round(float(t_dec.mean()) * 1e3, 2),
         },
         "append_gbs": round(app_bytes / (t_app_pre.mean() * 1e-3) / 1e9, 1),
+        **({"fused_qkv": {
+            "what": "kv_qkv_rope_append of the 32 decode tokens, d_model 1024, no biases",
+            "us": round(float(t_app_dec.mean()) * 1e3, 2),
+            "weight_bytes": 4 * D_MODEL * sum(qkv_rows),
+            "weight_gbs": round(4 * D_MODEL * sum(qkv_rows) / (t_app_dec.mean() * 1e-3) / 1e9, 1),
+        }} if args.fused_qkv else {}),
         "roofline": {
             "kernel": "prefill_kernel<128> (gqa_attn_prefill)",
             "bound": "mfma",

@@ -131,17 +131,46 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
         double hi[TT], lo[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) hi[t] = lo[t] = 0.0;
-#pragma unroll 4
-        for (int i = li * 4; i < p.d; i += 4 * kLanesPerRow) {
-            const float4 w4 = *reinterpret_cast<const float4 *>(wr + i);
+        if constexpr (TT == 1) {
+            // One token: the step streams the weights, so each lane first issues the loads
+            // of up to kBatch pieces of its row (and of x), then does their arithmetic.
+            constexpr int kBatch = 16;
+            const float *xr = p.x + (int64_t)t0 * p.d;
+            for (int i0 = li * 4; i0 < p.d; i0 += kBatch * 4 * kLanesPerRow) {
+                float4 wb[kBatch], xb[kBatch];
 #pragma unroll
-            for (int t = 0; t < TT; t++) {
-                if (t < ntk) {
-                    const float4 x4 = *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + i);
-                    dd_add(hi[t], lo[t], (double)x4.x * (double)w4.x);
-                    dd_add(hi[t], lo[t], (double)x4.y * (double)w4.y);
-                    dd_add(hi[t], lo[t], (double)x4.z * (double)w4.z);
-                    dd_add(hi[t], lo[t], (double)x4.w * (double)w4.w);
+                for (int k = 0; k < kBatch; k++) {
+                    const int i = i0 + k * 4 * kLanesPerRow;
+                    if (i < p.d) {
+                        wb[k] = *reinterpret_cast<const float4 *>(wr + i);
+                        xb[k] = *reinterpret_cast<const float4 *>(xr + i);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; k++) {
+                    if (i0 + k * 4 * kLanesPerRow < p.d) {
+                        dd_add(hi[0], lo[0], (double)xb[k].x * (double)wb[k].x);
+                        dd_add(hi[0], lo[0], (double)xb[k].y * (double)wb[k].y);
+                        dd_add(hi[0], lo[0], (double)xb[k].z * (double)wb[k].z);
+                        dd_add(hi[0], lo[0], (double)xb[k].w * (double)wb[k].w);
+                    }
+                }
+            }
+        } else {
+            // Several tokens: the f64 arithmetic dominates; each weight piece serves all.
+#pragma unroll 4
+            for (int i = li * 4; i < p.d; i += 4 * kLanesPerRow) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(wr + i);
+#pragma unroll
+                for (int t = 0; t < TT; t++) {
+                    if (t < ntk) {
+                        const float4 x4 =
+                            *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + i);
+                        dd_add(hi[t], lo[t], (double)x4.x * (double)w4.x);
+                        dd_add(hi[t], lo[t], (double)x4.y * (double)w4.y);
+                        dd_add(hi[t], lo[t], (double)x4.z * (double)w4.z);
+                        dd_add(hi[t], lo[t], (double)x4.w * (double)w4.w);
+                    }
                 }
             }
         }
