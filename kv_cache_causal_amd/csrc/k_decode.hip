@@ -98,11 +98,11 @@ typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
 
 // Where one kv head's slices live in a region: row r's values start at element
-// r * nkt + hk * HD; a Q8_0 region's scales of row r start at byte scale_off +
-// 2 * (r * nkt + hk * HD) / 32.
+// r * nkt + hk * HD; a Q8_0 region's scales of row r are at q8_scale_index (head-major
+// after byte scale_off, `rows` rows per head).
 struct Slice {
     const char *region;
-    int64_t scale_off;
+    int64_t scale_off, rows;
     int32_t nkt, hk;
 };
 
@@ -223,7 +223,8 @@ struct RowIO<int8_t, DPL, LPR> {
         const int64_t v0 = row * s.nkt + (int64_t)s.hk * HD + li * DPL;   // first value
         Raw r;
         r.c = *reinterpret_cast<const Codes *>(s.region + v0);
-        r.d = (float)*reinterpret_cast<const _Float16 *>(s.region + s.scale_off + 2 * (v0 / kQ8Block));
+        const int64_t si = ((int64_t)s.hk * s.rows + row) * (HD / kQ8Block) + li * DPL / kQ8Block;
+        r.d = (float)reinterpret_cast<const _Float16 *>(s.region + s.scale_off)[si];
         return r;
     }
     // Codes stay packed four to a register until used; a signed byte of a register
@@ -291,8 +292,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const int seq = p.seq[b];
     const int nkt = p.n_head_kv * HD;
     const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
-    const Slice K{static_cast<const char *>(p.kc) + reg, p.scale_off, nkt, hk};
-    const Slice V{static_cast<const char *>(p.vc) + reg, p.scale_off, nkt, hk};
+    const int64_t qrows = p.scale_off / nkt;   // region rows (Q8_0 only)
+    const Slice K{static_cast<const char *>(p.kc) + reg, p.scale_off, qrows, nkt, hk};
+    const Slice V{static_cast<const char *>(p.vc) + reg, p.scale_off, qrows, nkt, hk};
 
     // The lane's query values in the order its row values arrive (IO::dim).
     float qf[GP][kDimsPerLane];

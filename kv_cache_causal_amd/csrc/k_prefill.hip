@@ -201,9 +201,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     constexpr bool kQ8 = std::is_same<KVT, int8_t>::value;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
-    // Q8_0 scales of this head: row r's at byte scale_off + 2 * (r * nkt + hk * HD) / 32.
-    const char *Ksc = static_cast<const char *>(p.kc) + p.scale_off + 2 * (hk * HD / kQ8Block);
-    const char *Vsc = static_cast<const char *>(p.vc) + p.scale_off + 2 * (hk * HD / kQ8Block);
+    // Q8_0 scales of this head: head-major, HD / 32 per row, `rows` rows per head.
+    const int64_t qrows = p.scale_off / (p.n_head_kv * HD);
+    const char *Ksc = static_cast<const char *>(p.kc) + p.scale_off + 2 * (hk * qrows * (HD / kQ8Block));
+    const char *Vsc = static_cast<const char *>(p.vc) + p.scale_off + 2 * (hk * qrows * (HD / kQ8Block));
 
     // Tile staging: thread tid moves chunk #(tid + 256 j) of the tile, j < LD, i.e. row
     // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
@@ -220,7 +221,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     // copies into an aggregate copy and keeps the arrays in scratch memory.
     typename TIO::Raw kreg[LD], vreg[LD];
     float ksc[LD], vsc[LD];   // Q8_0 block scales (unused by the float formats)
-    const int nsb = nkt / kQ8Block;
+    const int nsb = HD / kQ8Block;   // scales per row of this head
     const uint32_t soff = (uint32_t)(trow * nsb + tcol / kQ8Block) * 2u;
     const int64_t sjstride = (int64_t)RSTEP * nsb * 2;
     auto fetch = [&](int key0) {

@@ -237,10 +237,10 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
         const int64_t reg = ((int64_t)p.iseq[t0 + t] * p.n_layer + p.layer) * p.region_bytes;
         const int64_t row = p.ipos[t0 + t];
         if constexpr (std::is_same<KVT, int8_t>::value) {
-            int8_t *codes = reinterpret_cast<int8_t *>(cache + reg) + row * nkt;
-            _Float16 *scales = reinterpret_cast<_Float16 *>(cache + reg + p.scale_off) +
-                               row * (nkt / kQ8Block);
-            q8_store4(y, codes, scales, j, idx);
+            int8_t *codes = reinterpret_cast<int8_t *>(cache + reg) + row * nkt + j;
+            _Float16 *scale = reinterpret_cast<_Float16 *>(cache + reg + p.scale_off) +
+                              q8_scale_index(row, j, p.hd_kv, p.scale_off / nkt);
+            q8_store4(y, codes, scale, idx);
         } else {
             store4(reinterpret_cast<KVT *>(cache + reg) + row * nkt + j, y);
         }

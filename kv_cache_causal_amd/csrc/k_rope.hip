@@ -204,8 +204,9 @@ __global__ void __launch_bounds__(256) append_q8_kernel(AppendParams p)
     char *vr = static_cast<char *>(p.vc) + reg;
     int8_t *kcodes = reinterpret_cast<int8_t *>(kr) + (int64_t)pos * nkt;
     int8_t *vcodes = reinterpret_cast<int8_t *>(vr) + (int64_t)pos * nkt;
-    _Float16 *kscales = reinterpret_cast<_Float16 *>(kr + p.scale_off) + (int64_t)pos * (nkt / kQ8Block);
-    _Float16 *vscales = reinterpret_cast<_Float16 *>(vr + p.scale_off) + (int64_t)pos * (nkt / kQ8Block);
+    _Float16 *kscales = reinterpret_cast<_Float16 *>(kr + p.scale_off);
+    _Float16 *vscales = reinterpret_cast<_Float16 *>(vr + p.scale_off);
+    const int64_t rows = p.scale_off / nkt;
     const float2 *tk = STYLE == kNone ? nullptr : p.tab_k + (int64_t)pos * (p.hd_kv >> 1);
 
     rotate_q<STYLE, QVEC>(p, t, pos);
@@ -214,8 +215,9 @@ __global__ void __launch_bounds__(256) append_q8_kernel(AppendParams p)
         const int32_t h = j / p.hd_kv;
         const int32_t e = j - h * p.hd_kv;
         const float4 y = rotated4<STYLE>(ksrc + (int64_t)h * p.hd_kv, e, p.hd_kv, tk);
-        q8_store4(y, kcodes, kscales, j, idx);
-        q8_store4(*reinterpret_cast<const float4 *>(vsrc + j), vcodes, vscales, j, idx);
+        const int64_t si = q8_scale_index(pos, j, p.hd_kv, rows);
+        q8_store4(y, kcodes + j, kscales + si, idx);
+        q8_store4(*reinterpret_cast<const float4 *>(vsrc + j), vcodes + j, vscales + si, idx);
     }
 }
 

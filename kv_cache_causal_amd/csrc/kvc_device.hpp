@@ -48,13 +48,12 @@ __device__ __forceinline__ void rotate_pair(float x0, float x1, float2 cs_sn, fl
     y1 = c + d;
 }
 
-// Q8_0 store of values j..j+3 of a row, held by lane group member (idx % 8) of the 8
-// aligned lanes that together hold block j / 32: the block's max |x| is reduced across
-// the 8 lanes (DPP within each half-row), every lane derives the same scale and
-// reciprocal (IEEE f32 division), writes its 4 codes as one dword, and the group's
-// first lane writes the binary16 scale.
-__device__ __forceinline__ void q8_store4(float4 y, int8_t *codes, _Float16 *scales, int32_t j,
-                                          int32_t idx)
+// Q8_0 store of 4 consecutive values of a row, held by lane group member (idx % 8) of the
+// 8 aligned lanes that together hold one 32-value block: the block's max |x| is reduced
+// across the 8 lanes (DPP within each half-row), every lane derives the same scale and
+// reciprocal (IEEE f32 division), writes its 4 codes as one dword at `codes`, and the
+// group's first lane writes the binary16 scale at `scale`.
+__device__ __forceinline__ void q8_store4(float4 y, int8_t *codes, _Float16 *scale, int32_t idx)
 {
 #pragma clang fp contract(off)
     float a = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
@@ -67,8 +66,8 @@ __device__ __forceinline__ void q8_store4(float4 y, int8_t *codes, _Float16 *sca
     const int32_t c2 = (int32_t)roundf(y.z * r), c3 = (int32_t)roundf(y.w * r);
     const uint32_t packed = (uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8) |
                             ((uint32_t)(c2 & 0xff) << 16) | ((uint32_t)(c3 & 0xff) << 24);
-    *reinterpret_cast<uint32_t *>(codes + j) = packed;
-    if ((idx & 7) == 0) scales[j / kQ8Block] = (_Float16)d;
+    *reinterpret_cast<uint32_t *>(codes) = packed;
+    if ((idx & 7) == 0) *scale = (_Float16)d;
 }
 
 }  // namespace kvc

@@ -83,7 +83,9 @@ def compare_q8_cache(lib_cache, orc_cache, seq, layer, what, rows=None):
     sel = slice(None) if rows is None else rows
     for name, (codes, scales), reg in zip("KV", kvc.kv_read(lib_cache, seq, layer),
                                           (orc_cache.k(seq, layer), orc_cache.v(seq, layer))):
-        codes, scales = host(codes), host(scales).view(np.uint16)
+        codes = host(codes)
+        # head-major [n_head_kv][rows][hd_kv/32] -> [rows][nkt/32] like the oracle's blocks
+        scales = host(scales).view(np.uint16).transpose(1, 0, 2).reshape(codes.shape[0], -1)
         osc, ocd = q8_split(reg)
         assert_equal(codes[:cap][sel], ocd.reshape(cap, nkt)[sel], f"{what} {name} codes [{seq}][{layer}]")
         assert_equal(scales[:cap][sel], osc[sel], f"{what} {name} scales [{seq}][{layer}]")
