@@ -445,16 +445,17 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     }
 }
 
-// K3: one workgroup per (batch entry, query head) with more than one chunk.  Pass 1
-// finds M = max_c m_c and L = sum_c 2^(m_c - M) l_c with the chunks spread over the
-// threads; pass 2 gives each thread one output dim and a slice of the chunks (loads of
-// different chunks are independent, so they overlap), then sums the slices in LDS.
+// K3: one workgroup per (batch entry, query head) with more than one chunk.  One pass:
+// each thread owns one output dim and a slice of the chunks, and folds its chunks'
+// records (m, l, acc[d]) into a running (M, L, A) by log-sum-exp, eight chunks per trip
+// (their loads are independent, so they are in flight together); the slices are then
+// merged the same way through LDS.  Every chunk record is read once, in one wave of
+// loads, so a merge costs one global-memory round trip.
 template <int HD>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
 {
     constexpr int SLICES = 256 / HD;   // chunk slices per output dim
-    __shared__ float red[256];
-    __shared__ float s_M, s_L;
+    __shared__ float sM[256], sL[256], sA[256];
     const int b = blockIdx.x;
     const int h = blockIdx.y;
     const int c0 = p.cbase[b], c1 = p.cbase[b + 1];
@@ -462,61 +463,60 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
     const int tid = threadIdx.x;
     const float *base = p.part + (int64_t)h * (HD + 4);
     const int64_t cstride = (int64_t)p.n_head * (HD + 4);
-
-    float mx = -INFINITY;
-    for (int c = c0 + tid; c < c1; c += 256) mx = fmaxf(mx, base[(int64_t)c * cstride]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    if (tid == 0) s_M = red[0];
-    __syncthreads();
-    const float M = s_M;
-    float ls = 0.0f;
-    for (int c = c0 + tid; c < c1; c += 256) {
-        const float *rec = base + (int64_t)c * cstride;
-        ls += fast_exp2(rec[0] - M) * rec[1];
-    }
-    red[tid] = ls;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    if (tid == 0) s_L = red[0];
-    __syncthreads();
-    const float L = s_L;
-    __syncthreads();
-
-    // Eight independent chunks per trip keep eight loads in flight per thread.
     const int d = tid % HD;
     const int slice = tid / HD;
-    float a = 0.0f;
+
+    float M = -INFINITY, L = 0.0f, A = 0.0f;
     int c = c0 + slice;
     for (; c + 7 * SLICES < c1; c += 8 * SLICES) {
-        float mm[8], vv[8];
+        float mm[8], ll[8], aa[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const float *rec = base + (int64_t)(c + j * SLICES) * cstride;
             mm[j] = rec[0];
-            vv[j] = rec[4 + d];
+            ll[j] = rec[1];
+            aa[j] = rec[4 + d];
         }
+        float mn = M;
 #pragma unroll
-        for (int j = 0; j < 8; j++) a += fast_exp2(mm[j] - M) * vv[j];
+        for (int j = 0; j < 8; j++) mn = fmaxf(mn, mm[j]);   // finite: chunks hold rows
+        const float r = fast_exp2(M - mn);                   // 0 while M is -inf
+        L *= r;
+        A *= r;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float w = fast_exp2(mm[j] - mn);
+            L += w * ll[j];
+            A += w * aa[j];
+        }
+        M = mn;
     }
     for (; c < c1; c += SLICES) {
         const float *rec = base + (int64_t)c * cstride;
-        a += fast_exp2(rec[0] - M) * rec[4 + d];
+        const float mc = rec[0];
+        const float mn = fmaxf(M, mc);
+        const float r = fast_exp2(M - mn), w = fast_exp2(mc - mn);
+        L = L * r + w * rec[1];
+        A = A * r + w * rec[4 + d];
+        M = mn;
     }
-    red[tid] = a;
+    sM[tid] = M;
+    sL[tid] = L;
+    sA[tid] = A;
     __syncthreads();
     if (tid < HD) {
-        float t = 0.0f;
+        float Mt = -INFINITY;
 #pragma unroll
-        for (int sl = 0; sl < SLICES; sl++) t += red[sl * HD + tid];
-        p.out[((int64_t)b * p.n_head + h) * HD + tid] = t / L;
+        for (int sl = 0; sl < SLICES; sl++) Mt = fmaxf(Mt, sM[sl * HD + tid]);
+        float Lt = 0.0f, At = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < SLICES; sl++) {
+            // A slice with no chunk has M = -inf and contributes exp2(-inf) * 0 = 0.
+            const float w = fast_exp2(sM[sl * HD + tid] - Mt);
+            Lt += w * sL[sl * HD + tid];
+            At += w * sA[sl * HD + tid];
+        }
+        p.out[((int64_t)b * p.n_head + h) * HD + tid] = At / Lt;
     }
 }
 
