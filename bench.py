@@ -64,6 +64,15 @@ def main():
                     help="stage 3 through kv_qkv_rope_append: the 32 decode tokens' q/k/v are "
                          "projected from d_model=1024 inputs with synthetic weights, rotated "
                          "and stored in one kernel")
+    ap.add_argument("--workload", choices=["batch", "long", "layer", "stack"], default="batch",
+                    help="batch: the 32-sequence Qwen3-0.6B step (default, the headline); "
+                         "long: one decode over 32,767 cached rows; layer: one Qwen2.5-0.5B "
+                         "layer decode at 511; stack: 28-layer Qwen3-0.6B prefill of 511 and "
+                         "decode steps (f32 regions; cold = 512 MB read between steps)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --workload long|layer|stack: replay each step's appends and "
+                         "decodes from HIP graphs captured once, so the host's per-call "
+                         "launch time is not measured")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before timing, so that "
                          "HBM counters (FETCH_SIZE / WRITE_SIZE) can be calibrated against "
@@ -78,6 +87,10 @@ def main():
 
     import kv_cache_causal_amd as kvc
     from tests import workloads as W
+
+    if args.workload != "batch":
+        other_workload(args)
+        return
 
     w = W.C5
     nt = w.extra["prefill"]
@@ -264,6 +277,141 @@ def main():
 
     if orc_cache is not None:
         result["cpu_baseline"] = cpu_baseline(orc_cache, w, seqs, lens, kv_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def other_workload(args):
+    """The long-context, single-layer and 28-layer workloads: each step appends one token
+    per layer, then decodes each layer; `cold` steps read 512 MB between steps (outside the
+    timed events) so the cache is read from HBM.  The stack workload also times its
+    28-layer prefill of 511 tokens once.  With --graph the appends and the decodes are
+    each captured once into a HIP graph and replayed, which takes the host's per-call
+    launch time out of the measurement."""
+    import torch
+
+    import kv_cache_causal_amd as kvc
+    from tests import workloads as W
+
+    w = {"long": W.C4, "layer": W.C2, "stack": W.C3}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    kvc.lib()
+    cache = kvc.kv_alloc(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity)
+    n_past = w.extra.get("n_past", w.extra.get("prefill"))
+    log(f"bench: workload {w.name}; filling {n_past} rows x {w.n_layer} layers")
+    pre_ev = None
+    if args.workload == "stack":
+        # The prefill itself is part of this workload: append + prefill of 511 per layer.
+        pos = np.arange(n_past, dtype=np.int32)
+        outp = torch.empty((n_past, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
+        qkv = [[torch.from_numpy(a).to(dev) for a in W.prefill_qkv(w, n_past, layer)]
+               for layer in range(w.n_layer)]
+        pre_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for rep_ in range(2):   # the second pass is the timed one (tables built)
+            qs = [t[0].clone() for t in qkv]   # the append rotates q in place
+            torch.cuda.synchronize()
+            pre_ev[0].record()
+            for layer in range(w.n_layer):
+                _, k, v = qkv[layer]
+                kvc.kv_append_rope(cache, layer, np.zeros(n_past, np.int32), pos, qs[layer],
+                                   w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
+                kvc.gqa_attn_prefill(cache, 0, layer, pos, qs[layer], w.n_head, w.hd, w.scale,
+                                     outp)
+            pre_ev[1].record()
+        torch.cuda.synchronize()
+    else:
+        chunk = w.extra.get("fill_chunk", 4096)
+        for ci, r0 in enumerate(range(0, n_past, chunk)):
+            r1 = min(n_past, r0 + chunk)
+            k, v = W.fill_rows(w, 0, 0, ci, r1 - r0)
+            kvc.kv_append_rope(cache, 0, np.zeros(r1 - r0, np.int32),
+                               np.arange(r0, r1, dtype=np.int32), None, 0, 0,
+                               torch.from_numpy(k.reshape(r1 - r0, w.n_head_kv, w.hd_kv)).to(dev),
+                               torch.from_numpy(v.reshape(r1 - r0, w.n_head_kv, w.hd_kv)).to(dev),
+                               w.base, w.freq_scale, w.style)
+    steps = [W.decode_qkv(w, 1, st % max(1, w.extra.get("decode_steps", 1)), layer)
+             for st in range(1) for layer in range(w.n_layer)]
+    dq = [[torch.from_numpy(a).to(dev) for a in t] for t in steps]
+    out = torch.empty((1, w.n_head, w.hd_kv), dtype=torch.float32, device=dev)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    pos = np.array([n_past], np.int32)
+    zero = np.zeros(1, np.int32)
+    win_bytes = (n_past + 1) * 2 * w.n_head_kv * w.hd_kv * 4 * w.n_layer
+
+    def appends():
+        for layer in range(w.n_layer):
+            q, k, v = dq[layer]
+            kvc.kv_append_rope(cache, layer, zero, pos, q, w.n_head, w.hd, k, v, w.base,
+                               w.freq_scale, w.style)
+
+    def decodes():
+        for layer in range(w.n_layer):
+            kvc.gqa_attn_decode(cache, layer, zero, pos, dq[layer][0], w.n_head, w.hd, w.scale,
+                                out)
+
+    app, dec = appends, decodes
+    if args.graph:
+        # Warm up eagerly (tables, scratch sizes), then capture each half of the step once;
+        # every replay launches the same kernels with the same arguments.
+        for _ in range(2):
+            appends()
+            decodes()
+        torch.cuda.synchronize()
+        g_app, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_app):
+            appends()
+        with torch.cuda.graph(g_dec):
+            decodes()
+        torch.cuda.synchronize()
+        app, dec = g_app.replay, g_dec.replay
+
+    res = {}
+    for mode in ("warm", "cold"):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.warmup + args.steps)]
+        for ev in evs:
+            if mode == "cold":
+                # 512 MB read (not written: dirty lines would make the timed step pay for
+                # their write-back) evicts the cache rows from L2 and the MALL.
+                scratch.sum()
+            ev[0].record()
+            app()
+            ev[1].record()
+            dec()
+            ev[2].record()
+        torch.cuda.synchronize()
+        timed = evs[args.warmup:]
+        step_us = np.array([e[0].elapsed_time(e[2]) * 1e3 for e in timed])
+        dec_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in timed])
+        res[mode] = (float(step_us.mean()), float(dec_us.mean()))
+        log(f"bench: {mode}: step {res[mode][0]:.1f} us, decode attention {res[mode][1]:.1f} us "
+            f"over {w.n_layer} layer(s)" + (" (HIP graph replay)" if args.graph else ""))
+    dec_gbs = win_bytes / (res["cold"][1] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["cold"][0] / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v and cache rows)",
+        "config": {"workload": f"{w.name}: {w.n_layer} layer(s), {w.n_head} q heads / "
+                               f"{w.n_head_kv} kv heads, head dim {w.hd_kv}, decode at {n_past} "
+                               f"(cold: 512 MB read between steps)"
+                               + ("; steps replayed from HIP graphs" if args.graph else ""),
+                   "n_layer": w.n_layer, "n_past": n_past, "capacity": w.capacity},
+        "decode_attn_us": {"cold": round(res["cold"][1], 2), "warm": round(res["warm"][1], 2)},
+        "step_us": {"cold": round(res["cold"][0], 2), "warm": round(res["warm"][0], 2)},
+        "decode_hbm_frac_cold": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_gbs_warm": round(win_bytes / (res["warm"][1] * 1e-6) / 1e9, 1),
+        "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel (gqa_attn_decode)",
+                     "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": win_bytes},
+    }
+    if pre_ev is not None:
+        pre_us = pre_ev[0].elapsed_time(pre_ev[1]) * 1e3
+        flops = 4 * w.n_head * w.hd_kv * (n_past * (n_past + 1) // 2) * w.n_layer
+        result["prefill_stack"] = {"what": f"append + prefill of {n_past} tokens, {w.n_layer} layers",
+                                   "us": round(pre_us, 1),
+                                   "attn_tflops_incl_append": round(flops / (pre_us * 1e-6) / 1e12, 2)}
     print(json.dumps(result), flush=True)
 
 
