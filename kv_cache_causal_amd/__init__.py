@@ -92,6 +92,9 @@ def _stream(stream):
     if stream is not None:
         return int(stream)
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)   # no Stream object built
+    if raw is not None:
+        return int(raw(torch.cuda.current_device()))
     return int(torch.cuda.current_stream().cuda_stream)
 
 
