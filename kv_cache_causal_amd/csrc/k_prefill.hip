@@ -25,12 +25,19 @@
 //   * Causality from data: a block scans key tiles up to the max position of its tokens;
 //     a wave skips tiles beyond its own max; the per-element mask (key > pos) is a select.
 //   * Heavy query tiles (late positions) are launched first to shorten the tail.
+//   * Short prompts give too few query tiles to fill 256 CUs, and each would walk its key
+//     tiles one after another.  Then the host cuts every query tile's key range into
+//     segments (same tile count each, the last one shorter); a workgroup scans one
+//     segment and writes its unnormalised (m, l, O) record, and a merge kernel combines a
+//     query's records by log-sum-exp (split-K, as for decode).
 //   * Region formats: binary16 is widened and Q8_0 dequantized (scale * code, exact in
 //     f32) while a tile is copied into LDS, so the products always see f32 values.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
+#include <vector>
 
 #include "kvc_internal.hpp"
 
@@ -121,10 +128,16 @@ struct TileIO<HD, int8_t> {
     }
 };
 
+// Split-K record of one (segment, token, head): O[HD] unnormalised, then m (base 2), l and,
+// in segment 0's record, the token's segment count.
+template <int HD>
+__device__ __forceinline__ float *part_record(const PrefillParams &p, int seg, int t, int h)
+{
+    return p.part + (((int64_t)seg * p.nt + t) * p.n_head + h) * (HD + 4);
+}
+
 template <int HD, typename KVT>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_t GB, int32_t TQ,
-                                                      int32_t n_qtiles, int32_t n_hsub,
-                                                      int32_t nblocks)
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_t nblocks)
 {
     using C = PrefillCfg<HD>;
     using TIO = TileIO<HD, KVT>;
@@ -139,14 +152,28 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
 
     // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
     // takes logical block (b % 8) * (nblocks / 8) + b / 8.  Each XCD then owns a
-    // contiguous range of logical blocks -- one kv head's query tiles when the counts
-    // divide -- and its L2 serves those tiles' shared K/V rows.  Within a range, heavy
+    // contiguous range of logical blocks -- one kv head's work units when the counts
+    // divide -- and its L2 serves those units' shared K/V rows.  Within a range, heavy
     // (late-position) query tiles come first.
+    const int GB = p.GB, TQ = p.TQ, n_hsub = p.n_hsub;
     const int per_xcd = (nblocks + 7) / 8;
     const int logical = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
     if (logical >= nblocks) return;
-    const int hgroup = logical / n_qtiles;
-    const int qtile = n_qtiles - 1 - (logical - hgroup * n_qtiles);
+    const int hgroup = logical / p.units_per_hgroup;
+    const int unit = logical - hgroup * p.units_per_hgroup;
+    // Work unit: a query tile and the key tiles [kt0, kt1) it scans.  Without a unit table
+    // a unit is a whole query tile (kt1 follows from its positions, below).
+    int qtile, kt0 = 0, kt1 = 0, seg = 0, nseg = 1;
+    if (p.units) {
+        const intx4 ud = reinterpret_cast<const intx4 *>(p.units)[unit];
+        qtile = ud[0];
+        kt0 = ud[1];
+        kt1 = ud[1] + ud[2];
+        seg = ud[3] >> 16;
+        nseg = ud[3] & 0xffff;
+    } else {
+        qtile = p.n_qtiles - 1 - unit;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -196,7 +223,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     float m = -INFINITY, l = 0.0f;
 
     __syncthreads();
-    const int ntiles = s_kmax / KT + 1;
+    if (!p.units) kt1 = s_kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
     constexpr bool kQ8 = std::is_same<KVT, int8_t>::value;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
@@ -242,9 +269,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             }
         }
     };
-    fetch(0);
+    fetch(kt0 * KT);
 
-    for (int kt = 0; kt < ntiles; kt++) {
+    for (int kt = kt0; kt < kt1; kt++) {
         const int key0 = kt * KT;
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
@@ -253,7 +280,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j], vsc[j]);
         }
         __syncthreads();
-        if (kt + 1 < ntiles) fetch(key0 + KT);
+        if (kt + 1 < kt1) fetch(key0 + KT);
 
         if (head_ok && key0 <= wmax) {
             // S^T = K Q^T for KB blocks of 16 keys; independent accumulators interleaved.
@@ -299,12 +326,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            // Key 0 is in tile 0 and every window holds it, so mn is finite from tile 0 on.
+            // Key 0 is in tile 0 and every window holds it, so from tile 0 on mn is finite;
+            // a segment that starts later can see a query none of whose keys it holds yet
+            // (mn = -inf): mref = 0 then keeps its weights at exp2(-inf) = 0.
             const float mn = fmaxf(m, tmax);
+            const float mref = mn == -INFINITY ? 0.0f : mn;
             // The running max moves rarely after the first tiles: rescale only when some
             // lane's did (alpha = 1 exactly otherwise).
             if (__any(mn != m)) {
-                const float alpha = fast_exp2(m - mn);
+                const float alpha = fast_exp2(m - mref);
                 l *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
@@ -313,7 +343,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const float pr = fast_exp2(sv[kb][r] - mn);
+                    const float pr = fast_exp2(sv[kb][r] - mref);
                     sv[kb][r] = pr;
                     l += pr;
                 }
@@ -350,9 +380,23 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     l += __shfl_xor(l, 32);
     if (head_ok && tok_ok) {
         // Block VEC*j + e, register r' holds dim 16*VEC*j + VEC*(4*grp + r') + e: for each
-        // (j, r') the VEC dims e = 0..VEC-1 are contiguous.
-        const float inv = 1.0f / l;
+        // (j, r') the VEC dims e = 0..VEC-1 are contiguous.  A split query tile writes
+        // its segment's record instead of the output; the merge kernel reads a token's
+        // segment count from segment 0's record.
+        float inv = 1.0f / l;
         float *orow = p.out + ((int64_t)t * p.n_head + h) * HD;
+        if (p.part) {
+            float *rec = part_record<HD>(p, seg, t, h);
+            if (grp == 0) {
+                rec[HD] = m;
+                rec[HD + 1] = l;
+                if (seg == 0) rec[HD + 2] = __int_as_float(nseg);
+            }
+            if (nseg > 1) {
+                orow = rec;
+                inv = 1.0f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NDB / VEC; j++)
 #pragma unroll
@@ -372,20 +416,69 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     }
 }
 
+// Merge of the split query tiles' segment records: thread group of HD/4 lanes per
+// (token, head), four dims per lane.  out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// folded online over batches of kBatch records whose loads are all in flight together
+// (the first batch's alongside the segment count: records below max_seg exist, and those
+// past the count are discarded by a select).
+template <int HD>
+__global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p)
+{
+    constexpr int TPR = HD / 4;           // threads per record
+    constexpr int kBatch = 8;
+    const int rec = (int)blockIdx.x * (256 / TPR) + (int)threadIdx.x / TPR;
+    const int d = ((int)threadIdx.x % TPR) * 4;
+    if (rec >= p.nt * p.n_head) return;
+    const int t = rec / p.n_head, h = rec - t * p.n_head;
+    const int nseg = __float_as_int(part_record<HD>(p, 0, t, h)[HD + 2]);
+    float M = -INFINITY, L = 0.0f;
+    floatx4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < p.max_seg; s0 += kBatch) {
+        float mi[kBatch], li[kBatch];
+        floatx4 oi[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+            const float *r = part_record<HD>(p, min(s0 + i, p.max_seg - 1), t, h);
+            mi[i] = r[HD];
+            li[i] = r[HD + 1];
+            oi[i] = *reinterpret_cast<const floatx4 *>(r + d);
+        }
+        if (s0 == 0 && nseg <= 1) return;   // written by its only segment
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+            if (s0 + i >= nseg) mi[i] = -INFINITY;
+            Mn = fmaxf(Mn, mi[i]);
+        }
+        // Segment 0 holds key 0, so Mn is finite from the first batch on.
+        const float a = fast_exp2(M - Mn);
+        L *= a;
+        O *= a;
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+            const bool live = s0 + i < nseg;   // 0 weight also for m = -inf (no key seen)
+            const float w = live ? fast_exp2(mi[i] - Mn) : 0.0f;
+            L += w * (live ? li[i] : 0.0f);
+            O += w * (live ? oi[i] : floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+        M = Mn;
+        if (s0 + kBatch >= nseg) break;
+    }
+    const float inv = 1.0f / L;
+    *reinterpret_cast<floatx4 *>(p.out + ((int64_t)t * p.n_head + h) * HD + d) = O * inv;
+}
+
 template <int HD, typename KVT>
 hipError_t launch_hd_t(const PrefillParams &p, hipStream_t s)
 {
-    const int G = p.n_head / p.n_head_kv;
-    // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
-    int GB = 1;
-    while (GB * 2 <= G && GB * 2 <= 4) GB *= 2;
-    const int TQ = 64 / GB;
-    const int n_hsub = (G + GB - 1) / GB;
-    const int n_qtiles = (p.nt + TQ - 1) / TQ;
-    const int nblocks = n_qtiles * p.n_head_kv * n_hsub;
+    const int nblocks = p.units_per_hgroup * p.n_head_kv * p.n_hsub;
     const int launched = (nblocks + 7) / 8 * 8;
-    prefill_kernel<HD, KVT><<<dim3((unsigned)launched), dim3(256), 0, s>>>(p, GB, TQ, n_qtiles,
-                                                                           n_hsub, nblocks);
+    prefill_kernel<HD, KVT><<<dim3((unsigned)launched), dim3(256), 0, s>>>(p, nblocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.part) return e;
+    const int per_block = 256 / (HD / 4);
+    const int64_t recs = (int64_t)p.nt * p.n_head;
+    prefill_merge_kernel<HD><<<dim3((unsigned)((recs + per_block - 1) / per_block)), dim3(256), 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -399,6 +492,55 @@ hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
 }
 
 }  // namespace
+
+PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
+                         int32_t hd_kv, int32_t force_seg)
+{
+    PrefillPlan pl;
+    const int G = n_head / n_head_kv;
+    // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
+    while (pl.GB * 2 <= G && pl.GB * 2 <= 4) pl.GB *= 2;
+    pl.TQ = 64 / pl.GB;
+    pl.n_hsub = (G + pl.GB - 1) / pl.GB;
+    pl.n_qtiles = (nt + pl.TQ - 1) / pl.TQ;
+    pl.KT = hd_kv >= 256 ? 32 : 64;   // PrefillCfg<hd_kv>::KT
+    pl.units_per_hgroup = pl.n_qtiles;
+    const int64_t hgroups = (int64_t)n_head_kv * pl.n_hsub;
+    // Two resident workgroups per CU: 512 query tiles fill the chip without a split.
+    constexpr int64_t kFill = 512;
+    if (force_seg < 0 || (force_seg == 0 && hgroups * pl.n_qtiles >= kFill)) return pl;
+    std::vector<int32_t> tiles(pl.n_qtiles);
+    int64_t total = 0;
+    for (int q = 0; q < pl.n_qtiles; q++) {
+        int32_t kmax = 0;
+        for (int t = q * pl.TQ; t < std::min(nt, (q + 1) * pl.TQ); t++) kmax = std::max(kmax, pos[t]);
+        tiles[q] = kmax / pl.KT + 1;
+        total += tiles[q];
+    }
+    // Segment length: the tiles spread over about kFill units, but no fewer than 3 per
+    // unit -- a lone workgroup keeps the matrix pipe under half busy, so a unit's start-up
+    // (query load, first tile fetch, record write) needs a few tiles to amortise.
+    const int64_t seg_tiles = force_seg > 0 ? force_seg
+                            : std::max<int64_t>(3, (total * hgroups + kFill - 1) / kFill);
+    int32_t max_seg = 1;
+    for (int q = 0; q < pl.n_qtiles; q++)
+        max_seg = std::max<int32_t>(max_seg, (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles));
+    if (max_seg == 1) return pl;   // every query tile is a single segment already
+    pl.max_seg = max_seg;
+    pl.units.clear();
+    for (int q = pl.n_qtiles - 1; q >= 0; q--) {   // heavy (late) query tiles first
+        const int32_t nseg = (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles);
+        for (int32_t sg = 0; sg < nseg; sg++) {
+            const int32_t k0 = (int32_t)(sg * seg_tiles);
+            pl.units.push_back(q);
+            pl.units.push_back(k0);
+            pl.units.push_back((int32_t)std::min<int64_t>(seg_tiles, tiles[q] - k0));
+            pl.units.push_back((sg << 16) | nseg);
+        }
+    }
+    pl.units_per_hgroup = (int32_t)(pl.units.size() / 4);
+    return pl;
+}
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {

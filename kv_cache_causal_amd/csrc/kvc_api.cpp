@@ -194,6 +194,33 @@ int32_t env_split_rows()
     return e ? std::max(0, std::atoi(e)) : 0;
 }
 
+// KVC_PREFILL_SEG sets the prefill's key tiles per segment: unset or 0 lets the plan
+// choose, n > 0 forces segments of n tiles, a negative value forbids splitting (tuning
+// and tests of both paths; results agree within rounding).
+int32_t env_prefill_seg()
+{
+    const char *e = std::getenv("KVC_PREFILL_SEG");
+    return e ? std::atoi(e) : 0;
+}
+
+// Grow the split-K partials buffer (shared by decode and prefill) to `need` floats.  The
+// old buffer may still be read by queued kernels on `s`, so it is freed after a sync.
+kvc_status ensure_part(const kvc_cache *c, size_t need, hipStream_t s)
+{
+    if (need <= c->part_cap) return KVC_OK;
+    if (c->part) {
+        KVC_HIP(hipStreamSynchronize(s));
+        hipFree(c->part);
+        c->part = nullptr;
+    }
+    const size_t cap = std::max(need, c->part_cap * 2);
+    c->part_cap = 0;
+    if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
+        return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
+    c->part_cap = cap;
+    return KVC_OK;
+}
+
 // Split-K decode of n_seq validated entries.  Entry b's window is rows [0, pos[b]]
 // (run_off == nullptr) or the union of its runs run_off[b] .. run_off[b+1]-1.
 kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
@@ -246,18 +273,8 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
     }
     if (max_chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
     const size_t need = (size_t)max_chunks * n_head * (c->g.hd_kv + 4);
-    if (need > c->part_cap) {
-        if (c->part) {
-            KVC_HIP(hipStreamSynchronize(s));
-            hipFree(c->part);
-            c->part = nullptr;
-            c->part_cap = 0;
-        }
-        const size_t cap = std::max(need, c->part_cap * 2);
-        if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
-            return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
-        c->part_cap = cap;
-    }
+    kvc_status pst = ensure_part(c, need, s);
+    if (pst != KVC_OK) return pst;
 
     for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
         const int32_t n = std::min(E, n_seq - b0);
@@ -544,11 +561,29 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     if (nt == 0) return KVC_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    std::vector<int32_t> ints(pos, pos + nt);
+    // Positions, then (16-byte aligned) the split-K unit table when the prompt is short.
+    const kvc::PrefillPlan pl = kvc::plan_prefill(pos, nt, n_head, c->g.n_head_kv, c->g.hd_kv,
+                                                    env_prefill_seg());
+    const size_t units_at = ((size_t)nt + 3) & ~size_t(3);
+    std::vector<int32_t> ints(units_at + pl.units.size(), 0);
+    std::copy(pos, pos + nt, ints.begin());
+    std::copy(pl.units.begin(), pl.units.end(), ints.begin() + units_at);
+    if (pl.max_seg > 1) {
+        st = ensure_part(c, (size_t)pl.max_seg * nt * n_head * (c->g.hd_kv + 4), s);
+        if (st != KVC_OK) return st;
+    }
     const int32_t *dev = nullptr;
     if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
     const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region_bytes;
     kvc::PrefillParams p{};
+    p.units = pl.units.empty() ? nullptr : dev + units_at;
+    p.part = pl.max_seg > 1 ? c->part : nullptr;
+    p.GB = pl.GB;
+    p.TQ = pl.TQ;
+    p.n_qtiles = pl.n_qtiles;
+    p.n_hsub = pl.n_hsub;
+    p.units_per_hgroup = pl.units_per_hgroup;
+    p.max_seg = pl.max_seg;
     p.q = q;
     p.out = out;
     p.kc = c->K + off;
