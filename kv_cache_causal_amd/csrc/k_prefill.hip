@@ -20,8 +20,8 @@
 //     never leaves registers.  The head-dim contraction of S^T is permuted so lane group
 //     g owns dims [g*hd/4, (g+1)*hd/4): Q and K fragments are contiguous (b128 reads).
 //   * Online softmax per query column: the row max is a max over 16 registers and two
-//     cross-group shuffles; the rescale factor is per lane; the row sum stays per lane
-//     group until the end.
+//     cross-group lane swaps (no LDS); the rescale factor is per lane; the row sum stays
+//     per lane group until the end.
 //   * Causality from data: a block scans key tiles up to the max position of its tokens;
 //     a wave skips tiles beyond its own max; the per-element mask (key > pos) is a select.
 //   * Heavy query tiles (late positions) are launched first to shorten the tail.
@@ -51,6 +51,32 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+
+// Combine a value with the lane 16 (32) positions away without an LDS round trip: the
+// gfx950 lane-swap instructions exchange rows of 16 lanes (halves of 32) between two
+// registers, so swapping a register with itself leaves each lane's value and its
+// partner's in the two results.
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int HD>
@@ -324,8 +350,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                         tmax = fmaxf(tmax, sv[kb][r]);
                     }
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_xor32(max_xor16(tmax));
             // Key 0 is in tile 0 and every window holds it, so from tile 0 on mn is finite;
             // a segment that starts later can see a query none of whose keys it holds yet
             // (mn = -inf): mref = 0 then keeps its weights at exp2(-inf) = 0.
@@ -348,36 +373,42 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                     l += pr;
                 }
             m = mn;
-            // O^T += V^T P^T.  k-step (kb, r) uses key kb*16 + 4*grp + r for lane group grp.
-            // Output block db = VEC*j + e takes, for A row i, dim 16*VEC*j + VEC*i + e, so
-            // one VEC-wide LDS read (dims 16*VEC*j + VEC*qc ...) feeds VEC blocks.
+            // O^T += V^T P^T.  k-step st = 4 kb + r uses key kb*16 + 4*grp + r for lane
+            // group grp.  Output block db = VEC*j + e takes, for A row i, dim
+            // 16*VEC*j + VEC*i + e, so one VEC-wide LDS read (dims 16*VEC*j + VEC*qc ...)
+            // feeds VEC blocks.  A step's V values are read while the previous step's
+            // MFMAs run (the scheduling barriers keep that order: left alone, the compiler
+            // puts each read just before its MFMAs and the wave waits on LDS every step).
+            auto load_v = [&](int st, float (&vv)[NDB]) {
+                const float *vrow = &Vs[((st >> 2) * 16 + grp * 4 + (st & 3)) * VSTR + VEC * qc];
 #pragma unroll
-            for (int kb = 0; kb < KB; kb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float *vrow = &Vs[(kb * 16 + grp * 4 + r) * VSTR + VEC * qc];
-#pragma unroll
-                    for (int j = 0; j < NDB / VEC; j++) {
-                        float vv[VEC];
-                        if constexpr (VEC == 4) {
-                            const float4 v4 = *reinterpret_cast<const float4 *>(vrow + 16 * VEC * j);
-                            vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
-                        } else if constexpr (VEC == 2) {
-                            const float2 v2 = *reinterpret_cast<const float2 *>(vrow + 16 * VEC * j);
-                            vv[0] = v2.x; vv[1] = v2.y;
-                        } else {
-                            vv[0] = vrow[16 * VEC * j];
-                        }
-#pragma unroll
-                        for (int e = 0; e < VEC; e++)
-                            oacc[VEC * j + e] = mfma4(vv[e], sv[kb][r], oacc[VEC * j + e]);
+                for (int j = 0; j < NDB / VEC; j++) {
+                    if constexpr (VEC == 4) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(vrow + 16 * VEC * j);
+                        vv[4 * j] = v4.x; vv[4 * j + 1] = v4.y; vv[4 * j + 2] = v4.z; vv[4 * j + 3] = v4.w;
+                    } else if constexpr (VEC == 2) {
+                        const float2 v2 = *reinterpret_cast<const float2 *>(vrow + 16 * VEC * j);
+                        vv[2 * j] = v2.x; vv[2 * j + 1] = v2.y;
+                    } else {
+                        vv[j] = vrow[16 * VEC * j];
                     }
                 }
+            };
+            float vbuf[2][NDB];
+            load_v(0, vbuf[0]);
+#pragma unroll
+            for (int st = 0; st < KB * 4; st++) {
+                if (st + 1 < KB * 4) load_v(st + 1, vbuf[(st + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < NDB; db++)
+                    oacc[db] = mfma4(vbuf[st & 1][db], sv[st >> 2][st & 3], oacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = add_xor32(add_xor16(l));
     if (head_ok && tok_ok) {
         // Block VEC*j + e, register r' holds dim 16*VEC*j + VEC*(4*grp + r') + e: for each
         // (j, r') the VEC dims e = 0..VEC-1 are contiguous.  A split query tile writes
