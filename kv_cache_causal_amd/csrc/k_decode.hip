@@ -47,6 +47,7 @@
 
 #include <cmath>
 
+#include "kvc_device.hpp"
 #include "kvc_internal.hpp"
 
 namespace kvc {
@@ -71,12 +72,6 @@ constexpr int dims_per_lane()
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
 // Sum over aligned groups of W lanes; every lane of a group gets the same bits (each step
 // adds a pair in both orders, which IEEE addition makes identical).
 template <int W>
@@ -86,13 +81,12 @@ __device__ __forceinline__ float group_sum(float x)
     if constexpr (W >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
     if constexpr (W >= 8) x += dpp<0x141>(x);  // row_half_mirror: i <-> 7 - i
     if constexpr (W >= 16) x += dpp<0x140>(x); // row_mirror: i <-> 15 - i
-    if constexpr (W >= 32) x += __shfl_xor(x, 16);
-    if constexpr (W >= 64) x += __shfl_xor(x, 32);
+    if constexpr (W >= 32) x = add_xor16(x);
+    if constexpr (W >= 64) x = add_xor32(x);
     return x;
 }
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));

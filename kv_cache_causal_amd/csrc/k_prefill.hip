@@ -39,6 +39,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "kvc_device.hpp"
 #include "kvc_internal.hpp"
 
 namespace kvc {
@@ -53,31 +54,6 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-
-// Combine a value with the lane 16 (32) positions away without an LDS round trip: the
-// gfx950 lane-swap instructions exchange rows of 16 lanes (halves of 32) between two
-// registers, so swapping a register with itself leaves each lane's value and its
-// partner's in the two results.
-__device__ __forceinline__ float max_xor16(float v)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float v)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float add_xor16(float v)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float add_xor32(float v)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int HD>
 struct PrefillCfg {
@@ -94,7 +70,6 @@ struct PrefillCfg {
     static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
 };
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));

@@ -1,5 +1,6 @@
-// Device helpers shared by the kernels that store K/V rows (k_rope.hip, k_qkv.hip), so
-// that every path rounds, rotates and quantizes with the same instructions.
+// Device helpers shared by the kernels: cross-lane moves, and the K/V row stores of
+// k_rope.hip and k_qkv.hip, so that every path rounds, rotates and quantizes with the same
+// instructions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,32 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Combine a value with the lane 16 (32) positions away without an LDS round trip: the
+// gfx950 lane-swap instructions exchange rows of 16 lanes (halves of 32) between two
+// registers, so swapping a register with itself leaves each lane's value and its
+// partner's in the two results.  Both lanes of a pair get the same bits (IEEE max and
+// addition are commutative).
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Store 4 f32 values at dst: as they are for an f32 region, rounded to binary16 (nearest,
