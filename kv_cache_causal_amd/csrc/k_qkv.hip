@@ -6,11 +6,13 @@
 // §3.4 item 5: the fused and the unfused paths must agree bit for bit.  Here "unfused"
 // is the projection followed by kv_append_rope, and the kernel reproduces it exactly:
 //   * each projection output is the f32 nearest to the exact dot product x . w_j: every
-//     f32 x f32 product is exact in f64, the sum is carried as an unevaluated pair of
-//     f64 values (hi + lo, hi accumulated with the error-free TwoSum and the errors in
-//     lo), lane partials are merged the same way, and the pair is rounded to f32 once,
-//     through round-to-odd at f64 precision (53 >= 24 + 2 bits makes that one correct
-//     rounding); the bias is then added in f32;
+//     f32 x f32 product is exact in f64; a plain f64 sum with a rigorous error bound
+//     settles the rounding whenever the bound's whole interval rounds to one f32 (all
+//     but a vanishing fraction of rows), and otherwise the wave recomputes the sum as an
+//     unevaluated pair of f64 values (hi + lo, hi accumulated with the error-free TwoSum
+//     and the errors in lo), merges lane partials the same way and rounds the pair to
+//     f32 once, through round-to-odd at f64 precision (53 >= 24 + 2 bits makes that one
+//     correct rounding); the bias is then added in f32;
 //   * the rotation, the binary16 rounding and the Q8_0 quantization are the append
 //     kernel's own functions (kvc_device.hpp).
 // The pages' reading of the matmul's precision is only that fused and unfused agree;
@@ -37,6 +39,17 @@ namespace {
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
 constexpr int kMaxRows = 64;   // rows of a unit (32 pairs)
 constexpr int kLanesPerRow = 16;
+constexpr int kXChunk = 512;   // x values per token staged in LDS at a time
+
+// LDS slot (in doubles) of the value pair (e + 2 half, e + 2 half + 1) of a staged x
+// chunk, e = 4 li + 64 k the first value of lane li's k-th piece: the pairs of one
+// (k, half) are contiguous over li, so the 16 lanes of a row read 256 consecutive bytes
+// (no bank conflicts; the other rows of the wave read the same bytes).
+__device__ __forceinline__ int xs_slot(int e, int half)
+{
+    const int k = e >> 6, li = (e >> 2) & 15;
+    return ((k * 2 + half) * 16 + li) * 2;
+}
 
 // Error-free sum: s + e == a + b exactly (s = fl(a + b)).
 __device__ __forceinline__ void two_sum(double a, double b, double &s, double &e)
@@ -88,6 +101,7 @@ template <int STYLE, typename KVT, int TT>
 __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per_unit)
 {
     __shared__ float ys[TT][kMaxRows];   // [token][local row]
+    __shared__ double xs[TT > 1 ? TT : 1][TT > 1 ? kXChunk : 1];   // x chunk, several tokens
 
     // Unit -> (projection, head, pair range).
     int unit = blockIdx.x;
@@ -128,18 +142,140 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
         const int lr = base + wave * 4 + lane / kLanesPerRow;
         const bool row_ok = lr < R;
         const float *wr = W + (int64_t)head_row(row_ok ? lr : 0) * p.d;
-        double hi[TT], lo[TT];
+        // Feed op(t, x, w) every (x, w) element pair of this lane's share of the row, as
+        // f64 (each f32 x f32 product is then exact): a lane takes elements 4 li + 64 k.
+        auto accumulate = [&](auto &&op) {
+            if constexpr (TT == 1) {
+                // One token: the step streams the weights, so each lane first issues the
+                // loads of up to kBatch pieces of its row (and of x), then does their
+                // arithmetic.
+                constexpr int kBatch = 16;
+                const float *xr = p.x + (int64_t)t0 * p.d;
+                for (int i0 = li * 4; i0 < p.d; i0 += kBatch * 4 * kLanesPerRow) {
+                    float4 wb[kBatch], xb[kBatch];
 #pragma unroll
-        for (int t = 0; t < TT; t++) hi[t] = lo[t] = 0.0;
-        if constexpr (TT == 1) {
-            // One token: the step streams the weights, so each lane first issues the loads
-            // of up to kBatch pieces of its row (and of x), then does their arithmetic.
-            constexpr int kBatch = 16;
-            const float *xr = p.x + (int64_t)t0 * p.d;
-            for (int i0 = li * 4; i0 < p.d; i0 += kBatch * 4 * kLanesPerRow) {
-                float4 wb[kBatch], xb[kBatch];
+                    for (int k = 0; k < kBatch; k++) {
+                        const int i = i0 + k * 4 * kLanesPerRow;
+                        if (i < p.d) {
+                            wb[k] = *reinterpret_cast<const float4 *>(wr + i);
+                            xb[k] = *reinterpret_cast<const float4 *>(xr + i);
+                        }
+                    }
 #pragma unroll
-                for (int k = 0; k < kBatch; k++) {
+                    for (int k = 0; k < kBatch; k++) {
+                        if (i0 + k * 4 * kLanesPerRow < p.d) {
+                            op(0, (double)xb[k].x, (double)wb[k].x);
+                            op(0, (double)xb[k].y, (double)wb[k].y);
+                            op(0, (double)xb[k].z, (double)wb[k].z);
+                            op(0, (double)xb[k].w, (double)wb[k].w);
+                        }
+                    }
+                }
+            } else {
+                // Several tokens: each weight piece serves all of them.  The group's x
+                // rows pass through LDS as f64 in chunks of kXChunk values (one batch of
+                // loads per thread; rows past the group's tokens read as zeros), and each
+                // lane loads its kPieces weight pieces of the chunk together, before the
+                // staging, so a chunk costs about one memory round trip.  The arithmetic runs over all TT tokens
+                // without branches, token-minor, so consecutive operations feed
+                // independent sums.  Every thread of the block reaches the barriers: the
+                // row loop is uniform across the block.  (Loading the next chunk during
+                // the current one's arithmetic needs ~250 registers and ran slower.)
+                constexpr int kPieces = kXChunk / (4 * kLanesPerRow);
+                for (int c0 = 0; c0 < p.d; c0 += kXChunk) {
+                    const int cn = min(kXChunk, p.d - c0);
+                    // This chunk's weight pieces are requested first: their round trip
+                    // overlaps the x staging and its barriers.
+                    float4 wb[kPieces];
+#pragma unroll
+                    for (int k = 0; k < kPieces; k++) {
+                        const int e = li * 4 + k * 4 * kLanesPerRow;
+                        if (e < cn) wb[k] = *reinterpret_cast<const float4 *>(wr + c0 + e);
+                    }
+                    __syncthreads();   // the previous chunk's readers are done
+                    for (int idx = threadIdx.x; idx < TT * (kXChunk / 4); idx += blockDim.x) {
+                        const int t = idx / (kXChunk / 4);
+                        const int e = (idx - t * (kXChunk / 4)) * 4;
+                        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        if (t < ntk && e < cn)
+                            v = *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + c0 + e);
+                        *reinterpret_cast<double2 *>(&xs[t][xs_slot(e, 0)]) = make_double2(v.x, v.y);
+                        *reinterpret_cast<double2 *>(&xs[t][xs_slot(e, 1)]) = make_double2(v.z, v.w);
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int k = 0; k < kPieces; k++) {
+                        const int e = li * 4 + k * 4 * kLanesPerRow;
+                        if (e < cn) {
+                            const double wv[4] = {wb[k].x, wb[k].y, wb[k].z, wb[k].w};
+                            double xv[TT][4];
+#pragma unroll
+                            for (int t = 0; t < TT; t++) {
+                                const double2 a = *reinterpret_cast<const double2 *>(&xs[t][xs_slot(e, 0)]);
+                                const double2 b = *reinterpret_cast<const double2 *>(&xs[t][xs_slot(e, 1)]);
+                                xv[t][0] = a.x; xv[t][1] = a.y; xv[t][2] = b.x; xv[t][3] = b.y;
+                            }
+#pragma unroll
+                            for (int c = 0; c < 4; c++)
+#pragma unroll
+                                for (int t = 0; t < TT; t++) op(t, xv[t][c], wv[c]);
+                        }
+                    }
+                }
+            }
+        };
+
+        // Fast path: the plain f64 sum S of the products and the sum A of their
+        // magnitudes.  Each product is exact and every partial sum is far from the f64
+        // range limits, so |S - exact| <= gamma_m * sum|products| with m <= d/16 + 8
+        // roundings on any path; err = 4 m u A + 2 u |S| (u = 2^-53) covers that bound,
+        // the rounding of A, and the rounding of S -/+ err themselves.  Rounding to f32
+        // is monotonic, so when both ends of [S - err, S + err] round to the same f32
+        // (bit for bit: a straddled zero has two signs), that f32 is the one nearest the
+        // exact sum.  Otherwise (a value within err of an f32 rounding boundary, or a
+        // non-finite sum) that row and token is recomputed exactly below.
+        double S[TT], A[TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) S[t] = A[t] = 0.0;
+        accumulate([&](int t, double xv, double wv) {
+            S[t] = fma(xv, wv, S[t]);
+            A[t] = fma(fabs(xv), fabs(wv), A[t]);
+        });
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+#pragma unroll
+            for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
+                S[t] += __shfl_xor(S[t], off);
+                A[t] += __shfl_xor(A[t], off);
+            }
+        }
+        // Longest rounding chain: a lane's ceil(d / 64) * 4 products plus 4 merge levels.
+        const double kErr = 4.0 * (double)(p.d / 16 + 8) * 0x1p-53;
+        uint32_t unsure = 0;   // tokens some row of this lane's wave could not settle
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+            const double err = kErr * A[t] + 0x1p-52 * fabs(S[t]);
+            const float lo32 = (float)(S[t] - err), hi32 = (float)(S[t] + err);
+            const bool certain = t >= ntk || (__builtin_isfinite(S[t]) && __builtin_isfinite(err) &&
+                                              __float_as_uint(lo32) == __float_as_uint(hi32));
+            if (__any(!certain)) unsure |= 1u << t;
+            if (row_ok && li == 0 && t < ntk) ys[t][lr] = B ? lo32 + B[head_row(lr)] : lo32;
+        }
+        // Exact sum for an unsettled token of this wave's rows (rare: a value within the
+        // bound of an f32 rounding boundary): an unevaluated pair of f64 values (hi + lo,
+        // hi accumulated with the error-free TwoSum and the errors in lo), lane partials
+        // merged the same way, the pair rounded to f32 once.  x and w come from global
+        // memory (no barrier: the choice is per wave); every row of the wave recomputes,
+        // and the exact value replaces the stored one (they agree where both exist).
+        while (unsure) {
+            const int t = __builtin_ctz(unsure);
+            unsure &= unsure - 1;
+            const float *xr = p.x + (int64_t)(t0 + t) * p.d;
+            double hi = 0.0, lo = 0.0;
+            for (int i0 = li * 4; i0 < p.d; i0 += 4 * 4 * kLanesPerRow) {
+                float4 wb[4], xb[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
                     const int i = i0 + k * 4 * kLanesPerRow;
                     if (i < p.d) {
                         wb[k] = *reinterpret_cast<const float4 *>(wr + i);
@@ -147,51 +283,23 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
                     }
                 }
 #pragma unroll
-                for (int k = 0; k < kBatch; k++) {
+                for (int k = 0; k < 4; k++) {
                     if (i0 + k * 4 * kLanesPerRow < p.d) {
-                        dd_add(hi[0], lo[0], (double)xb[k].x * (double)wb[k].x);
-                        dd_add(hi[0], lo[0], (double)xb[k].y * (double)wb[k].y);
-                        dd_add(hi[0], lo[0], (double)xb[k].z * (double)wb[k].z);
-                        dd_add(hi[0], lo[0], (double)xb[k].w * (double)wb[k].w);
+                        dd_add(hi, lo, (double)xb[k].x * (double)wb[k].x);
+                        dd_add(hi, lo, (double)xb[k].y * (double)wb[k].y);
+                        dd_add(hi, lo, (double)xb[k].z * (double)wb[k].z);
+                        dd_add(hi, lo, (double)xb[k].w * (double)wb[k].w);
                     }
                 }
             }
-        } else {
-            // Several tokens: the f64 arithmetic dominates; each weight piece serves all.
-#pragma unroll 4
-            for (int i = li * 4; i < p.d; i += 4 * kLanesPerRow) {
-                const float4 w4 = *reinterpret_cast<const float4 *>(wr + i);
-#pragma unroll
-                for (int t = 0; t < TT; t++) {
-                    if (t < ntk) {
-                        const float4 x4 =
-                            *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + i);
-                        dd_add(hi[t], lo[t], (double)x4.x * (double)w4.x);
-                        dd_add(hi[t], lo[t], (double)x4.y * (double)w4.y);
-                        dd_add(hi[t], lo[t], (double)x4.z * (double)w4.z);
-                        dd_add(hi[t], lo[t], (double)x4.w * (double)w4.w);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
 #pragma unroll
             for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
-                const double oh = __shfl_xor(hi[t], off);
-                const double ol = __shfl_xor(lo[t], off);
-                dd_merge(hi[t], lo[t], oh, ol);
+                const double oh = __shfl_xor(hi, off);
+                const double ol = __shfl_xor(lo, off);
+                dd_merge(hi, lo, oh, ol);
             }
-        }
-        if (row_ok && li == 0) {
-#pragma unroll
-            for (int t = 0; t < TT; t++) {
-                if (t < ntk) {
-                    float y = dd_to_f32(hi[t], lo[t]);
-                    if (B) y = y + B[head_row(lr)];
-                    ys[t][lr] = y;
-                }
-            }
+            const float ye = dd_to_f32(hi, lo);
+            if (row_ok && li == 0) ys[t][lr] = B ? ye + B[head_row(lr)] : ye;
         }
     }
     __syncthreads();
