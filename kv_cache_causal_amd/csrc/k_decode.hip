@@ -13,9 +13,9 @@
 //   * Workgroup = one (batch entry, kv head, chunk of rows); 4 wave64s.  Chunks are sized
 //     on the host so the grid fills the chip several times over; the workgroups of one
 //     chunk's kv heads are adjacent in dispatch order (DRAM page locality).
-//   * A row slice (hd_kv values of one kv head) is read by a group of LPR lanes, each
-//     holding 32 bytes of it (16 for groups of 3+ heads, to save registers): two float4
-//     loads of an f32 cache, or two 16-byte loads of packed halves of a binary16 cache
+//   * A row slice (hd_kv values of one kv head) is read by a group of LPR lanes: each
+//     lane holds 8 values (4 for larger head groups, to save registers) -- two float4
+//     loads of an f32 cache, or one 16-byte load of packed halves of a binary16 cache
 //     (widened to f32 as they are used); one load instruction across the wave covers
 //     64/LPR rows, whole 128-byte lines.  A Q8_0 cache gives each lane 8 codes (one
 //     8-byte load, all in one 32-value block) plus that block's binary16 scale; the
@@ -66,7 +66,7 @@ template <int GP, typename KVT>
 constexpr int dims_per_lane()
 {
     if constexpr (sizeof(KVT) == 1) return GP <= 4 ? 8 : 4;
-    if constexpr (sizeof(KVT) == 2) return GP <= 2 ? 16 : (GP <= 4 ? 8 : 4);
+    if constexpr (sizeof(KVT) == 2) return GP <= 4 ? 8 : 4;
     return GP <= 2 ? 8 : 4;
 }
 
@@ -107,8 +107,8 @@ struct Slice {
 // i-th value, so q is loaded in the same order.
 //   f32, 8 dims: two float4 at li*4 and 4*LPR + li*4 (each load instruction covers whole
 //                lines of several rows);  f32, 4 dims: one float4 at li*4;
-//   f16, 16 dims: two 16-byte loads of 8 halves at li*8 and 8*LPR + li*8;
-//   f16, 8 dims: one 16-byte load at li*8;  f16, 4 dims: 4 halves at li*4;
+//   f16, 8 dims: one 16-byte load at li*8;  f16, 4 dims: 4 halves at li*4 (16 halves
+//                per lane, as two loads, measured slower: more registers, fewer waves);
 //   Q8_0, DPL dims: DPL codes at li*DPL (16, 8 or 4 bytes) and the scale of their block.
 template <typename KVT, int DPL, int LPR>
 struct RowIO;
@@ -144,24 +144,6 @@ struct RowIO<float, 4, LPR> {
     static __device__ __forceinline__ float get(const Raw &r, int i) { return r[i]; }
     static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
-};
-template <int LPR>
-struct RowIO<_Float16, 16, LPR> {
-    struct Raw { half8_t a, b; };
-    static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
-    {
-        const _Float16 *p = slice_row<_Float16>(s, row, 16 * LPR);
-        Raw r;
-        r.a = *reinterpret_cast<const half8_t *>(p + li * 8);
-        r.b = *reinterpret_cast<const half8_t *>(p + 8 * LPR + li * 8);
-        return r;
-    }
-    static __device__ __forceinline__ float get(const Raw &r, int i)
-    {
-        return i < 8 ? (float)r.a[i] : (float)r.b[i - 8];
-    }
-    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
-    static __device__ __forceinline__ int dim(int li, int i) { return (i / 8) * 8 * LPR + li * 8 + (i % 8); }
 };
 template <int LPR>
 struct RowIO<_Float16, 8, LPR> {
@@ -548,7 +530,7 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt)
 {
     // The largest of the lane layouts' step sizes (all are powers of two).
-    const int lpr = hd_kv / (kv_fmt == kFmtF16 ? 16 : 8);
+    const int lpr = hd_kv / 8;
     return kWaves * (64 / lpr) * kUnroll;
 }
 
