@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["k_rope.hip", "k_qkv.hip", "k_decode.hip", "k_prefill.hip", "kvc_api.cpp",
-               "validate.cpp"]
+               "validate.cpp", "plan.cpp"]
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Packed fp32 instructions are kept out of the generated code.
@@ -58,7 +58,8 @@ def build(jobs: int = 8) -> str:
     os.replace(tmp, LIB)
     tmp = HOSTCHECK + ".tmp"
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
-          os.path.join(CSRC, "validate.cpp"), os.path.join(CSRC, "hostcheck.cpp"), "-o", tmp])
+          os.path.join(CSRC, "validate.cpp"), os.path.join(CSRC, "plan.cpp"),
+          os.path.join(CSRC, "hostcheck.cpp"), "-o", tmp])
     os.replace(tmp, HOSTCHECK)
     return LIB
 

@@ -1,9 +1,12 @@
-// Host-only shim over validate.cpp, built with g++ into libkvc_hostcheck.so.  It lets the
-// CPU test suite drive every argument check of the library without HIP or a GPU; the
-// library itself calls the same functions from kvc_api.cpp.
+// Host-only shim over validate.cpp and plan.cpp, built with g++ into
+// libkvc_hostcheck.so.  It lets the CPU test suite drive every argument check and every
+// launch-planning decision of the library without HIP or a GPU; the library itself calls
+// the same functions from kvc_api.cpp.
+#include <algorithm>
 #include <cstring>
 #include <string>
 
+#include "plan.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -70,6 +73,26 @@ int hc_check_qkv(const int32_t *g5, int32_t layer, int32_t nt, const int32_t *se
 {
     return kvc::check_qkv(geom(g5), layer, nt, seq_ids, pos, x, d_model, wq, bq, wk, bk, wv, bv,
                           n_head, hd, q_out, freq_base, freq_scale, style, g_msg);
+}
+
+// Prefill plan: meta[0..7] = GB, TQ, n_qtiles, n_hsub, KT, units_per_hgroup, max_seg,
+// number of unit ints; the unit table goes to units (at most cap ints).  Returns 0, or 1
+// if cap is too small.
+int hc_plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
+                    int32_t hd_kv, int32_t force_seg, int32_t *meta, int32_t *units, int32_t cap)
+{
+    const kvc::PrefillPlan pl = kvc::plan_prefill(pos, nt, n_head, n_head_kv, hd_kv, force_seg);
+    const int32_t m[8] = {pl.GB, pl.TQ, pl.n_qtiles, pl.n_hsub, pl.KT, pl.units_per_hgroup,
+                          pl.max_seg, (int32_t)pl.units.size()};
+    std::memcpy(meta, m, sizeof(m));
+    if ((int64_t)pl.units.size() > cap) return 1;
+    std::copy(pl.units.begin(), pl.units.end(), units);
+    return 0;
+}
+
+int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
+{
+    return kvc::decode_chunk_rows(work, br, forced);
 }
 
 }  // extern "C"

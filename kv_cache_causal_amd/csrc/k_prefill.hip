@@ -57,7 +57,7 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
 
 template <int HD>
 struct PrefillCfg {
-    static constexpr int KT = HD >= 256 ? 32 : 64;  // keys per tile
+    static constexpr int KT = prefill_key_tile(HD);  // keys per tile
     static constexpr int KB = KT / 16;              // 16-key blocks per tile
     static constexpr int DQ = HD / 4;               // dims per lane group
     // LDS row strides (floats), measured with a bank-conflict probe on gfx950: the
@@ -498,55 +498,6 @@ hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
 }
 
 }  // namespace
-
-PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
-                         int32_t hd_kv, int32_t force_seg)
-{
-    PrefillPlan pl;
-    const int G = n_head / n_head_kv;
-    // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
-    while (pl.GB * 2 <= G && pl.GB * 2 <= 4) pl.GB *= 2;
-    pl.TQ = 64 / pl.GB;
-    pl.n_hsub = (G + pl.GB - 1) / pl.GB;
-    pl.n_qtiles = (nt + pl.TQ - 1) / pl.TQ;
-    pl.KT = hd_kv >= 256 ? 32 : 64;   // PrefillCfg<hd_kv>::KT
-    pl.units_per_hgroup = pl.n_qtiles;
-    const int64_t hgroups = (int64_t)n_head_kv * pl.n_hsub;
-    // Two resident workgroups per CU: 512 query tiles fill the chip without a split.
-    constexpr int64_t kFill = 512;
-    if (force_seg < 0 || (force_seg == 0 && hgroups * pl.n_qtiles >= kFill)) return pl;
-    std::vector<int32_t> tiles(pl.n_qtiles);
-    int64_t total = 0;
-    for (int q = 0; q < pl.n_qtiles; q++) {
-        int32_t kmax = 0;
-        for (int t = q * pl.TQ; t < std::min(nt, (q + 1) * pl.TQ); t++) kmax = std::max(kmax, pos[t]);
-        tiles[q] = kmax / pl.KT + 1;
-        total += tiles[q];
-    }
-    // Segment length: the tiles spread over about kFill units, but no fewer than 3 per
-    // unit -- a lone workgroup keeps the matrix pipe under half busy, so a unit's start-up
-    // (query load, first tile fetch, record write) needs a few tiles to amortise.
-    const int64_t seg_tiles = force_seg > 0 ? force_seg
-                            : std::max<int64_t>(3, (total * hgroups + kFill - 1) / kFill);
-    int32_t max_seg = 1;
-    for (int q = 0; q < pl.n_qtiles; q++)
-        max_seg = std::max<int32_t>(max_seg, (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles));
-    if (max_seg == 1) return pl;   // every query tile is a single segment already
-    pl.max_seg = max_seg;
-    pl.units.clear();
-    for (int q = pl.n_qtiles - 1; q >= 0; q--) {   // heavy (late) query tiles first
-        const int32_t nseg = (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles);
-        for (int32_t sg = 0; sg < nseg; sg++) {
-            const int32_t k0 = (int32_t)(sg * seg_tiles);
-            pl.units.push_back(q);
-            pl.units.push_back(k0);
-            pl.units.push_back((int32_t)std::min<int64_t>(seg_tiles, tiles[q] - k0));
-            pl.units.push_back((sg << 16) | nseg);
-        }
-    }
-    pl.units_per_hgroup = (int32_t)(pl.units.size() / 4);
-    return pl;
-}
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {

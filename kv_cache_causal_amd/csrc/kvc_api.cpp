@@ -235,25 +235,11 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         for (int32_t r = run_off[b]; r < run_off[b + 1]; r++) t += run_len[r];
         return t;
     };
-    // Chunk size.  A workgroup streams its chunk in steps of br rows, each step a memory
-    // round trip, so a chunk of many steps is latency-bound unless many workgroups run.
-    // Large work: ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the
-    // per-chunk overheads (query load, merges, partial record, merge pass) stay small next
-    // to the stream.  Small work (a few 100 K row-heads, e.g. one layer's decode at a
-    // few hundred positions): chunks down to one step, aiming at ~512 workgroups, so the
-    // call costs two short launches instead of one long chain of dependent loads.
-    // KVC_SPLIT_ROWS overrides the size (tuning only, never the result).
+    // Chunk size (plan.cpp); KVC_SPLIT_ROWS overrides it (tuning only, never the result).
     const int32_t br = kvc::decode_block_rows(c->g.hd_kv, c->kv_fmt);
     int64_t total_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) total_rows += window_rows(b);
-    const int64_t work = total_rows * c->g.n_head_kv;
-    int64_t rows = env_split_rows();
-    if (rows <= 0) {
-        if (work > 2048 * 512) rows = work / 2048;
-        else if (work > 131072) rows = 512;
-        else rows = work / 512;
-    }
-    rows = std::max<int64_t>(br, (rows + br - 1) / br * br);
+    const int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, env_split_rows());
     // Chunks of entry b: its window cut into pieces of at most `rows` rows (each run on
     // its own for an explicit window).
     auto chunks_of = [&](int32_t b) -> int64_t {

@@ -6,7 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <vector>
+
+#include "plan.hpp"
 
 namespace kvc {
 
@@ -101,22 +102,6 @@ int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
-// A workgroup owns 64 query rows (GB heads of one kv group x TQ tokens: a "query tile")
-// and scans key tiles of KT keys.  When there are too few query tiles to fill the chip,
-// the host cuts each query tile's key range into segments of equal tile counts, one
-// workgroup each; segments write (m, l, unnormalised O) partials and a merge pass
-// combines them by log-sum-exp, as for decode.
-struct PrefillPlan {
-    int32_t GB = 1, TQ = 64, n_qtiles = 0, n_hsub = 1, KT = 64;
-    int32_t units_per_hgroup = 0;  // workgroups per (kv head, head subset)
-    int32_t max_seg = 1;           // most segments of any query tile (1: no split)
-    // Split only: per unit {query tile, first key tile, key tiles, segment << 16 | nseg}.
-    std::vector<int32_t> units;
-};
-// seg_tiles: 0 = choose, > 0 = force segments of that many key tiles, < 0 = never split.
-PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
-                         int32_t hd_kv, int32_t seg_tiles);
-
 struct PrefillParams {
     const float *q;          // [nt][n_head][hd]
     float *out;              // [nt][n_head][hd_kv]

@@ -1,0 +1,75 @@
+// Launch planning: prefill work units and decode chunk length (see plan.hpp).
+#include "plan.hpp"
+
+#include <algorithm>
+
+namespace kvc {
+
+PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
+                         int32_t hd_kv, int32_t force_seg)
+{
+    PrefillPlan pl;
+    const int G = n_head / n_head_kv;
+    // Heads per workgroup: the largest power of two <= min(G, 4); tokens fill the rest.
+    while (pl.GB * 2 <= G && pl.GB * 2 <= 4) pl.GB *= 2;
+    pl.TQ = 64 / pl.GB;
+    pl.n_hsub = (G + pl.GB - 1) / pl.GB;
+    pl.n_qtiles = (nt + pl.TQ - 1) / pl.TQ;
+    pl.KT = prefill_key_tile(hd_kv);
+    pl.units_per_hgroup = pl.n_qtiles;
+    const int64_t hgroups = (int64_t)n_head_kv * pl.n_hsub;
+    // Two resident workgroups per CU: 512 query tiles fill the chip without a split.
+    constexpr int64_t kFill = 512;
+    if (force_seg < 0 || (force_seg == 0 && hgroups * pl.n_qtiles >= kFill)) return pl;
+    std::vector<int32_t> tiles(pl.n_qtiles);
+    int64_t total = 0;
+    for (int q = 0; q < pl.n_qtiles; q++) {
+        int32_t kmax = 0;
+        for (int t = q * pl.TQ; t < std::min(nt, (q + 1) * pl.TQ); t++) kmax = std::max(kmax, pos[t]);
+        tiles[q] = kmax / pl.KT + 1;
+        total += tiles[q];
+    }
+    // Segment length: the tiles spread over about kFill units, but no fewer than 3 per
+    // unit, so a unit's start-up (query load, first tile fetch, record write) is spread
+    // over a few tiles.
+    const int64_t seg_tiles = force_seg > 0 ? force_seg
+                            : std::max<int64_t>(3, (total * hgroups + kFill - 1) / kFill);
+    int32_t max_seg = 1;
+    for (int q = 0; q < pl.n_qtiles; q++)
+        max_seg = std::max<int32_t>(max_seg, (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles));
+    if (max_seg == 1) return pl;   // every query tile is a single segment already
+    pl.max_seg = max_seg;
+    pl.units.clear();
+    for (int q = pl.n_qtiles - 1; q >= 0; q--) {   // heavy (late) query tiles first
+        const int32_t nseg = (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles);
+        for (int32_t sg = 0; sg < nseg; sg++) {
+            const int32_t k0 = (int32_t)(sg * seg_tiles);
+            pl.units.push_back(q);
+            pl.units.push_back(k0);
+            pl.units.push_back((int32_t)std::min<int64_t>(seg_tiles, tiles[q] - k0));
+            pl.units.push_back((sg << 16) | nseg);
+        }
+    }
+    pl.units_per_hgroup = (int32_t)(pl.units.size() / 4);
+    return pl;
+}
+
+int64_t decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
+{
+    // A workgroup streams its chunk in steps of br rows, each step a memory round trip,
+    // so a chunk of many steps is latency-bound unless many workgroups run.  Large work:
+    // ~2048 workgroups (8 per CU) and at least 512 rows per chunk, so the per-chunk
+    // overheads (query load, merges, partial record, merge pass) stay small next to the
+    // stream.  Small work (a few 100 K row-heads, e.g. one layer's decode at a few
+    // hundred positions): chunks down to one step, aiming at ~512 workgroups, so the call
+    // costs two short launches instead of one long chain of dependent loads.
+    int64_t rows = forced;
+    if (rows <= 0) {
+        if (work > 2048 * 512) rows = work / 2048;
+        else if (work > 131072) rows = 512;
+        else rows = work / 512;
+    }
+    return std::max<int64_t>(br, (rows + br - 1) / br * br);
+}
+
+}  // namespace kvc

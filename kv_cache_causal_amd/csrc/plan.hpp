@@ -1,0 +1,37 @@
+// Launch planning shared by the library and the host test shim: how a prefill's query
+// tiles are cut into workgroup units, and how long a decode chunk is.  Pure C++ (no HIP),
+// so the CPU test suite checks these decisions directly.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+namespace kvc {
+
+// Keys per prefill tile for a kv head dim (the prefill kernel's tile height).
+constexpr int prefill_key_tile(int hd_kv) { return hd_kv >= 256 ? 32 : 64; }
+
+// A prefill workgroup owns 64 query rows (GB heads of one kv group x TQ tokens: a "query
+// tile") and scans key tiles of KT keys.  When there are too few query tiles to fill the
+// chip, each query tile's key range is cut into segments of equal tile counts, one
+// workgroup each; segments write (m, l, unnormalised O) partials and a merge pass
+// combines them by log-sum-exp, as for decode.
+struct PrefillPlan {
+    int32_t GB = 1, TQ = 64, n_qtiles = 0, n_hsub = 1, KT = 64;
+    int32_t units_per_hgroup = 0;  // workgroups per (kv head, head subset)
+    int32_t max_seg = 1;           // most segments of any query tile (1: no split)
+    // Split only: per unit {query tile, first key tile, key tiles, segment << 16 | nseg},
+    // heavy (late) query tiles first.
+    std::vector<int32_t> units;
+};
+
+// pos: host [nt] positions of the prompt's tokens.  force_seg: 0 = choose, > 0 = force
+// segments of that many key tiles, < 0 = never split.
+PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
+                         int32_t hd_kv, int32_t force_seg);
+
+// Rows per decode chunk (a multiple of br, at least br) for `work` = total window rows x
+// kv heads of one call; forced > 0 overrides the choice (then rounded up to br).
+int64_t decode_chunk_rows(int64_t work, int32_t br, int64_t forced);
+
+}  // namespace kvc

@@ -1,0 +1,153 @@
+"""Launch planning on the host (plan.cpp through the host-only shim, no GPU): how a
+prefill's query tiles are cut into workgroup units, and the decode chunk length.
+
+The prefill kernel trusts the unit table completely (which key tiles a workgroup scans,
+whether it writes the output or a segment record, how many records the merge folds), so
+the properties here are the ones its correctness rests on: every query tile's key tiles
+[0, tiles) are covered exactly once, in segment order, each segment knows its index and
+its tile's segment count, and the key-tile count of a tile follows from its largest
+position."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HOSTCHECK = os.path.join(ROOT, "kv_cache_causal_amd", "lib", "libkvc_hostcheck.so")
+
+
+@pytest.fixture(scope="module")
+def hc():
+    if not os.path.exists(HOSTCHECK):
+        pytest.skip("host-check shim not built")
+    L = ctypes.CDLL(HOSTCHECK)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.hc_plan_prefill.argtypes = [p, i32, i32, i32, i32, i32, p, p, i32]
+    L.hc_decode_chunk_rows.argtypes = [i64, i32, i64]
+    L.hc_decode_chunk_rows.restype = i64
+    return L
+
+
+def plan(hc, pos, n_head, n_head_kv, hd_kv, force=0):
+    pos = np.ascontiguousarray(np.asarray(pos, np.int32))
+    meta = np.zeros(8, np.int32)
+    cap = 1 << 20
+    units = np.zeros(cap, np.int32)
+    assert hc.hc_plan_prefill(pos.ctypes.data, len(pos), n_head, n_head_kv, hd_kv, force,
+                              meta.ctypes.data, units.ctypes.data, cap) == 0
+    keys = ("GB", "TQ", "n_qtiles", "n_hsub", "KT", "units_per_hgroup", "max_seg", "n_units")
+    m = dict(zip(keys, (int(x) for x in meta)))
+    return m, units[:m["n_units"]].reshape(-1, 4)
+
+
+def tiles_of(pos, TQ, KT):
+    """Key tiles each query tile must scan: up to its largest position."""
+    return [int(pos[q:q + TQ].max()) // KT + 1 for q in range(0, len(pos), TQ)]
+
+
+def check_units(m, u, pos, seg_len):
+    tiles = tiles_of(np.asarray(pos), m["TQ"], m["KT"])
+    assert m["n_qtiles"] == len(tiles)
+    if m["max_seg"] == 1:
+        assert len(u) == 0 and m["units_per_hgroup"] == m["n_qtiles"]
+        return
+    assert m["units_per_hgroup"] == len(u)
+    seen = {}
+    for qt, k0, nk, code in u:
+        seg, nseg = code >> 16, code & 0xFFFF
+        seen.setdefault(int(qt), []).append((int(k0), int(nk), int(seg), int(nseg)))
+    assert sorted(seen) == list(range(len(tiles)))          # every query tile has units
+    order = [int(q) for q in u[:, 0]]
+    assert order == sorted(order, reverse=True)             # heavy (late) tiles first
+    for qt, segs in seen.items():
+        nseg = len(segs)
+        assert [s[2] for s in segs] == list(range(nseg))    # segment indices in order
+        assert all(s[3] == nseg for s in segs)              # each knows the count
+        assert nseg <= m["max_seg"]
+        k = 0
+        for k0, nk, _, _ in segs:                           # contiguous, exact cover
+            assert k0 == k and 1 <= nk <= seg_len
+            k += nk
+        assert k == tiles[qt]
+        assert all(nk == seg_len for _, nk, _, _ in segs[:-1])
+    assert m["max_seg"] == max(len(s) for s in seen.values())
+
+
+GEOMS = [  # n_head, n_head_kv, hd_kv
+    (16, 8, 128),   # Qwen3-0.6B: G = 2 -> 2 heads x 32 tokens per tile
+    (14, 2, 64),    # Qwen2.5-0.5B: G = 7 -> 4 heads x 16 tokens, two head subsets
+    (8, 4, 256),    # 32-key tiles
+    (4, 4, 16),     # G = 1 -> 64 tokens per tile
+    (16, 1, 128),   # G = 16 -> four head subsets
+]
+
+
+@pytest.mark.parametrize("g", GEOMS, ids=[f"h{a}kv{b}d{c}" for a, b, c in GEOMS])
+def test_tile_shape(hc, g):
+    n_head, n_head_kv, hd_kv = g
+    m, _ = plan(hc, np.arange(100), n_head, n_head_kv, hd_kv, force=-1)
+    G = n_head // n_head_kv
+    assert m["GB"] == min(4, 1 << (G.bit_length() - 1)) and m["GB"] * m["TQ"] == 64
+    assert m["n_hsub"] * m["GB"] >= G > (m["n_hsub"] - 1) * m["GB"]
+    assert m["KT"] == (32 if hd_kv >= 256 else 64)
+    assert m["n_qtiles"] == -(-100 // m["TQ"])
+
+
+@pytest.mark.parametrize("g", GEOMS, ids=[f"h{a}kv{b}d{c}" for a, b, c in GEOMS])
+def test_short_causal_prompts_split_with_the_documented_length(hc, g):
+    n_head, n_head_kv, hd_kv = g
+    for nt in (1, 40, 200, 511):
+        pos = np.arange(nt, dtype=np.int32)
+        m, u = plan(hc, pos, n_head, n_head_kv, hd_kv)
+        hgroups = n_head_kv * m["n_hsub"]
+        tiles = tiles_of(pos, m["TQ"], m["KT"])
+        if hgroups * m["n_qtiles"] >= 512:
+            assert m["max_seg"] == 1 and len(u) == 0
+            continue
+        seg_len = max(3, -(-sum(tiles) * hgroups // 512))
+        check_units(m, u, pos, seg_len)
+        assert (m["max_seg"] > 1) == (max(tiles) > seg_len)
+
+
+def test_continuation_and_scattered_positions(hc):
+    rng = np.random.default_rng(7)
+    cases = [np.arange(8000, 8064), np.arange(4000, 4256),
+             rng.integers(0, 3000, 90), np.array([0, 1, 2999, 2, 2500] + list(range(40)))]
+    for pos in cases:
+        for g in GEOMS:
+            m, u = plan(hc, pos, *g)
+            hgroups = g[1] * m["n_hsub"]
+            tiles = tiles_of(pos, m["TQ"], m["KT"])
+            seg_len = max(3, -(-sum(tiles) * hgroups // 512))
+            check_units(m, u, pos, seg_len)
+
+
+def test_forced_segment_lengths_and_no_split(hc):
+    pos = np.arange(3000, 3040, dtype=np.int32)
+    for force in (1, 2, 3, 7, 1000):
+        m, u = plan(hc, pos, 16, 8, 128, force)
+        check_units(m, u, pos, force)
+    m, u = plan(hc, pos, 16, 8, 128, -1)
+    assert m["max_seg"] == 1 and len(u) == 0
+    # Large prompts fill the chip unsplit, unless a length is forced.
+    big = np.arange(4096, dtype=np.int32)
+    m, u = plan(hc, big, 16, 8, 128)
+    assert m["max_seg"] == 1 and len(u) == 0 and m["units_per_hgroup"] == 128
+    m, u = plan(hc, big, 16, 8, 128, 16)
+    check_units(m, u, big, 16)
+
+
+def test_decode_chunk_rows(hc):
+    f = hc.hc_decode_chunk_rows
+    for br in (32, 64, 128):
+        prev = 0
+        for work in (1, 100, 10_000, 131_072, 131_073, 500_000, 1 << 20, (1 << 20) + 1, 1 << 26):
+            r = f(work, br, 0)
+            assert r >= br and r % br == 0
+            assert r >= prev                                  # never shrinks with work
+            prev = r
+        assert f(131_073, br, 0) == max(br, 512 // br * br)   # middle range: 512 rows
+        assert f(1 << 26, br, 0) == (1 << 26) // 2048         # large: ~2048 workgroups
+        assert f(512 * 40, br, 0) == max(br, -(-40 // br) * br)   # small: ~512 workgroups
+        assert f(10_000, br, 100) == -(-100 // br) * br        # forced, rounded up to br
