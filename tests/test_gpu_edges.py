@@ -269,3 +269,27 @@ def test_q8_geometry_is_checked():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_alloc(1, 1, 2, 16, 64, dtype=kvc.KV_Q8_0)
     assert e.value.status == kvc.E_GEOMETRY
+
+
+def test_maximum_capacity_and_last_position():
+    """The largest supported region (capacity 2^24 rows) with rows written at its first,
+    middle and last positions: RoPE table rows at the end, the stores, a decode whose
+    window is all 2^24 rows (split into thousands of chunks, unwritten rows reading as 0)
+    and a 3-token prefill at the last positions (split into hundreds of key segments)."""
+    cap = 1 << 24
+    say(f"maximum capacity {cap}")
+    nh, nkv, hd, hdk = 2, 1, 16, 16
+    p = Pair(1, 1, nkv, hdk, cap)
+    pos = np.array([0, 1, 1 << 23, cap - 3, cap - 2, cap - 1], np.int32)
+    q = custom(60, (len(pos), nh, hd))
+    k = custom(61, (len(pos), nkv, hdk))
+    v = custom(62, (len(pos), nkv, hdk))
+    p.append(0, [0] * len(pos), pos, q, nh, hd, k, v)
+    compare_cache(p.g, p.o, 0, 0, "max capacity", rows=pos)
+    qd = custom(63, (1, nh, hd))
+    got, want = p.decode(0, [0], [cap - 1], dev(qd), qd, nh, hd, 0.25)
+    assert_close(got, want, "decode over 2^24 rows")
+    qp = custom(64, (3, nh, hd))
+    got, want = p.prefill(0, 0, pos[-3:], dev(qp), qp, nh, hd, 0.25)
+    assert_close(got, want, "prefill at the last positions")
+    p.close()
