@@ -92,9 +92,9 @@ def main():
         other_workload(args)
         return
 
-    w = W.C5
+    w = W.QWEN3_BATCH
     nt = w.extra["prefill"]
-    n_past = W.c5_n_past(w)
+    n_past = W.batch_n_past(w)
     pre_pos = np.arange(n_past[0], n_past[0] + nt, dtype=np.int32)
     lens = n_past.copy()
     lens[0] += nt
@@ -292,7 +292,7 @@ def other_workload(args):
     import kv_cache_causal_amd as kvc
     from tests import workloads as W
 
-    w = {"long": W.C4, "layer": W.C2, "stack": W.C3}[args.workload]
+    w = {"long": W.QWEN3_LONG, "layer": W.QWEN25_LAYER, "stack": W.QWEN3_STACK}[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.init()
     kvc.lib()

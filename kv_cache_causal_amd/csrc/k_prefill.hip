@@ -7,8 +7,9 @@
 //          (any order, any gaps), so the mask is computed per (query, key) from pos.
 //   §2.5   on a GPU the (query, key) matrix is tiled and the softmax runs online.
 //
-// Prefill is a dense contraction (C5: >700 flop per byte), so both products run on
-// v_mfma_f32_16x16x4_f32, full fp32 in and out.  Design:
+// Prefill is a dense contraction (a 4,096-token prompt with Qwen3-0.6B heads: >700 flop
+// per byte), so both products run on v_mfma_f32_16x16x4_f32, full fp32 in and out.
+// Design:
 //   * Workgroup = 4 wave64s = 64 query rows of one kv head: GB heads of the kv group x TQ
 //     tokens (GB * TQ = 64), so one K/V tile in LDS serves all of them.  Each wave owns 16
 //     query rows (one head, 16 tokens).

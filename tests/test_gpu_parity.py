@@ -32,48 +32,48 @@ def fill(pair, w, seq, layer, n_rows, chunk=4096):
 
 
 @KV
-def test_c1_tiny(kv):
-    w = W.C1
+def test_tiny(kv):
+    w = W.TINY
     if kv == 2:
         pytest.skip("Q8_0 blocks need hd_kv a multiple of 32; this workload has hd_kv 16")
-    say(f"C1 {w.name} kv={kv}")
+    say(f"{w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     nt = w.extra["prefill"]
     pos = np.arange(nt, dtype=np.int32)
     q, k, v = W.prefill_qkv(w, nt, 0)
     qd, qo = p.append(0, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
-    compare_cache(p.g, p.o, 0, 0, "C1 prefill")
+    compare_cache(p.g, p.o, 0, 0, "tiny prefill")
     got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale)
-    assert_close(got, want, "C1 prefill out")
+    assert_close(got, want, "tiny prefill out")
     for step in range(w.extra["decode_steps"]):
         ps = [nt + step]
         q, k, v = W.decode_qkv(w, 1, step, 0)
         qd, qo = p.append(0, [0], ps, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
         got, want = p.decode(0, [0], ps, qd, qo, w.n_head, w.hd, w.scale)
-        assert_close(got, want, f"C1 decode step {step}")
-    compare_cache(p.g, p.o, 0, 0, "C1 after decode")
+        assert_close(got, want, f"tiny decode step {step}")
+    compare_cache(p.g, p.o, 0, 0, "tiny after decode")
     p.close()
 
 
 @KV
-def test_c2_qwen25_layer(kv):
-    w = W.C2
-    say(f"C2 {w.name} kv={kv}")
+def test_qwen25_layer(kv):
+    w = W.QWEN25_LAYER
+    say(f"{w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     n_past = w.extra["n_past"]
     fill(p, w, 0, 0, n_past)
     q, k, v = W.decode_qkv(w, 1, 0, 0)
     qd, qo = p.append(0, [0], [n_past], q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
-    compare_cache(p.g, p.o, 0, 0, "C2")
+    compare_cache(p.g, p.o, 0, 0, "qwen2.5 layer")
     got, want = p.decode(0, [0], [n_past], qd, qo, w.n_head, w.hd, w.scale)
-    assert_close(got, want, "C2 decode")
+    assert_close(got, want, "qwen2.5 layer decode")
     p.close()
 
 
 @KV
-def test_c3_qwen3_stack(kv):
-    w = W.C3
-    say(f"C3 {w.name} kv={kv}")
+def test_qwen3_stack(kv):
+    w = W.QWEN3_STACK
+    say(f"{w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     nt = w.extra["prefill"]
     pos = np.arange(nt, dtype=np.int32)
@@ -83,7 +83,7 @@ def test_c3_qwen3_stack(kv):
         qd, qo = p.append(layer, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale,
                           w.style)
         got, want = p.prefill(0, layer, pos, qd, qo, w.n_head, w.hd, w.scale)
-        assert_close(got, want, f"C3 prefill layer {layer}")
+        assert_close(got, want, f"qwen3 stack prefill layer {layer}")
     for step in range(w.extra["decode_steps"]):
         ps = [nt + step]
         for layer in range(w.n_layer):
@@ -95,33 +95,33 @@ def test_c3_qwen3_stack(kv):
             err = np.abs(got.astype(np.float64) - want)
             assert (err <= ATOL + RTOL * np.abs(want)).all(), (step, layer, err.max())
             worst = max(worst, float(err.max()))
-    say(f"  C3 decode 64 steps x 28 layers: max-abs {worst:.3e}")
+    say(f"  qwen3 stack decode 64 steps x 28 layers: max-abs {worst:.3e}")
     for layer in range(w.n_layer):
-        compare_cache(p.g, p.o, 0, layer, "C3")
+        compare_cache(p.g, p.o, 0, layer, "qwen3 stack")
     p.close()
 
 
 @KV
-def test_c4_long_context(kv):
-    w = W.C4
-    say(f"C4 {w.name} kv={kv}")
+def test_qwen3_long_context(kv):
+    w = W.QWEN3_LONG
+    say(f"{w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
     n_past = w.extra["n_past"]
     fill(p, w, 0, 0, n_past, w.extra["fill_chunk"])
     q, k, v = W.decode_qkv(w, 1, 0, 0)
     qd, qo = p.append(0, [0], [n_past], q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
-    compare_cache(p.g, p.o, 0, 0, "C4")
+    compare_cache(p.g, p.o, 0, 0, "qwen3 long")
     got, want = p.decode(0, [0], [n_past], qd, qo, w.n_head, w.hd, w.scale)
-    assert_close(got, want, "C4 decode")
+    assert_close(got, want, "qwen3 long decode")
     p.close()
 
 
 @KV
-def test_c5_batch(kv):
-    w = W.C5
-    say(f"C5 {w.name} kv={kv}")
+def test_qwen3_batch(kv):
+    w = W.QWEN3_BATCH
+    say(f"{w.name} kv={kv}")
     p = Pair(w.n_seq, w.n_layer, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
-    n_past = W.c5_n_past(w)
+    n_past = W.batch_n_past(w)
     say(f"  n_past {n_past.tolist()}")
     for s in range(w.n_seq):
         fill(p, w, s, 0, int(n_past[s]), w.extra["fill_chunk"])
@@ -134,7 +134,7 @@ def test_c5_batch(kv):
     sample = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, nt - 33, nt - 1],
                                        rng.integers(0, nt, 56)]))
     got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale, sample=sample)
-    assert_close(got, want, f"C5 prefill ({len(sample)} sampled tokens)")
+    assert_close(got, want, f"qwen3 batch prefill ({len(sample)} sampled tokens)")
     # One decode step for all 32 sequences.
     lens = n_past.copy()
     lens[0] += nt
@@ -142,7 +142,7 @@ def test_c5_batch(kv):
     seqs = np.arange(w.n_seq, dtype=np.int32)
     qd, qo = p.append(0, seqs, lens, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
     got, want = p.decode(0, seqs, lens, qd, qo, w.n_head, w.hd, w.scale)
-    assert_close(got, want, "C5 batched decode")
+    assert_close(got, want, "qwen3 batch batched decode")
     for s in range(w.n_seq):
-        compare_cache(p.g, p.o, s, 0, "C5")
+        compare_cache(p.g, p.o, s, 0, "qwen3 batch")
     p.close()

@@ -41,10 +41,10 @@ def random_runs(rng, cap, n_runs, max_len):
 @FORMATS
 def test_single_run_matches_position_window(kv):
     """The batch workload's 32 windows as one run each: bit-identical to gqa_attn_decode."""
-    w = W.C5
+    w = W.QWEN3_BATCH
     say(f"runs = causal windows, batch workload, kv={kv}")
     p = Pair(w.n_seq, 1, w.n_head_kv, w.hd_kv, w.capacity, dtype=kv)
-    n_past = W.c5_n_past(w)
+    n_past = W.batch_n_past(w)
     for s in range(w.n_seq):
         rows = int(n_past[s])
         for ci, r0 in enumerate(range(0, rows, 4096)):

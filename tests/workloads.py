@@ -13,17 +13,19 @@ Workload shapes (the pages' model geometries: Qwen2.5-0.5B has 14 query heads of
 over 2 KV heads; Qwen3-0.6B has 16 query heads of 128 over 8 KV heads, 28 layers,
 a 40,960-token context; both use NEOX RoPE with base 1e6):
 
-  C1 tiny         1 layer, 2 q heads, 1 kv head, hd = hd_kv = 16; prefill of 8 tokens,
-                  then 4 decode steps.  Capacity 8 + 512.
-  C2 qwen25       one Qwen2.5-0.5B-shaped layer; rows 0..510 cached, one decode at 511.
-                  Capacity 511 + 512.
-  C3 qwen3-stack  28 Qwen3-0.6B-shaped layers; prefill of 511 tokens per layer, then 64
-                  decode steps, each appending one row per layer.  Capacity 511 + 512.
-  C4 qwen3-long   one Qwen3-0.6B-shaped layer with 32,767 rows cached (context 40,960),
-                  one decode at position 32,767.
-  C5 qwen3-batch  32 Qwen3-0.6B-shaped sequences with n_past drawn uniformly from
-                  [128, 8192]; a 4,096-token continuation prefill on sequence 0, then
-                  one decode step for all 32.  Capacity 8192 + 4096 + 512.
+  TINY          1 layer, 2 q heads, 1 kv head, hd = hd_kv = 16; prefill of 8 tokens,
+                then 4 decode steps.  Capacity 8 + 512.
+  QWEN25_LAYER  one Qwen2.5-0.5B-shaped layer; rows 0..510 cached, one decode at 511.
+                Capacity 511 + 512.
+  QWEN3_STACK   28 Qwen3-0.6B-shaped layers; prefill of 511 tokens per layer, then 64
+                decode steps, each appending one row per layer.  Capacity 511 + 512.
+  QWEN3_LONG    one Qwen3-0.6B-shaped layer with 32,767 rows cached (context 40,960),
+                one decode at position 32,767.
+  QWEN3_BATCH   32 Qwen3-0.6B-shaped sequences with n_past drawn uniformly from
+                [128, 8192]; a 4,096-token continuation prefill on sequence 0, then
+                one decode step for all 32.  Capacity 8192 + 4096 + 512.
+
+The integer id of each workload (1..5) only seeds its tensors.
 """
 from __future__ import annotations
 
@@ -64,16 +66,16 @@ class Workload:
 _SCALE = {16: 0.25, 64: 0.125, 128: float(np.float32(0.08838834764831845))}
 
 
-C1 = Workload(1, "tiny", 1, 1, 2, 1, 16, 16, 8 + 512, extra=dict(prefill=8, decode_steps=4))
-C2 = Workload(2, "qwen2.5-0.5b-layer", 1, 1, 14, 2, 64, 64, 511 + 512, extra=dict(n_past=511))
-C3 = Workload(3, "qwen3-0.6b-stack", 1, 28, 16, 8, 128, 128, 511 + 512,
-              extra=dict(prefill=511, decode_steps=64))
-C4 = Workload(4, "qwen3-0.6b-long", 1, 1, 16, 8, 128, 128, 40960,
-              extra=dict(n_past=32767, fill_chunk=4096))
-C5 = Workload(5, "qwen3-0.6b-batch", 32, 1, 16, 8, 128, 128, 8192 + 4096 + 512,
-              extra=dict(prefill=4096, past_lo=128, past_hi=8192, fill_chunk=4096))
+TINY = Workload(1, "tiny", 1, 1, 2, 1, 16, 16, 8 + 512, extra=dict(prefill=8, decode_steps=4))
+QWEN25_LAYER = Workload(2, "qwen2.5-0.5b-layer", 1, 1, 14, 2, 64, 64, 511 + 512, extra=dict(n_past=511))
+QWEN3_STACK = Workload(3, "qwen3-0.6b-stack", 1, 28, 16, 8, 128, 128, 511 + 512,
+                       extra=dict(prefill=511, decode_steps=64))
+QWEN3_LONG = Workload(4, "qwen3-0.6b-long", 1, 1, 16, 8, 128, 128, 40960,
+                      extra=dict(n_past=32767, fill_chunk=4096))
+QWEN3_BATCH = Workload(5, "qwen3-0.6b-batch", 32, 1, 16, 8, 128, 128, 8192 + 4096 + 512,
+                       extra=dict(prefill=4096, past_lo=128, past_hi=8192, fill_chunk=4096))
 
-ALL = {w.cid: w for w in (C1, C2, C3, C4, C5)}
+ALL = {w.cid: w for w in (TINY, QWEN25_LAYER, QWEN3_STACK, QWEN3_LONG, QWEN3_BATCH)}
 
 
 def rng(cid: int, *tag: int) -> np.random.Generator:
@@ -91,7 +93,7 @@ def normal(cid: int, shape, *tag: int) -> np.ndarray:
 T_FILL_K, T_FILL_V, T_PRE_Q, T_PRE_K, T_PRE_V, T_DEC_Q, T_DEC_K, T_DEC_V, T_NPAST = range(1, 10)
 
 
-def c5_n_past(w: Workload = C5) -> np.ndarray:
+def batch_n_past(w: Workload = QWEN3_BATCH) -> np.ndarray:
     """Ragged cached lengths of the batch workload, uniform in [lo, hi] inclusive."""
     g = rng(w.cid, T_NPAST)
     return g.integers(w.extra["past_lo"], w.extra["past_hi"], size=w.n_seq,
