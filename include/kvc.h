@@ -241,6 +241,11 @@ kvc_status kv_qkv_rope_append(kvc_cache *c, int32_t layer, int32_t nt, const int
  *   scale       multiplies every dot product (the model's 1/sqrt(hd); finite).
  *   out         device [nt][n_head][hd_kv], overwritten.
  *
+ * Positions (and, for short prompts, the work-unit table) are staged in pinned host
+ * memory that the kernels read in place.  A prompt too short to fill the GPU has each
+ * 64-query tile's key range split across workgroups whose (max, sum, output) records are
+ * merged by log-sum-exp (§2.5's split, as in gqa_attn_decode); the records live in the
+ * handle's scratch memory, which grows on demand (KVC_E_NOMEM if it cannot).
  * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE (a position >= capacity), KVC_E_NOMEM,
  * KVC_E_HIP.
  */
@@ -263,6 +268,9 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
  *   n_head, hd, scale  as in gqa_attn_prefill.
  *   out         device [n_seq][n_head][hd_kv], overwritten.
  *
+ * Positions and sequence ids travel in the kernel arguments (64 entries per launch).
+ * The split-K partial records live in the handle's scratch memory, which grows on demand
+ * (KVC_E_NOMEM if it cannot).
  * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE, KVC_E_NOMEM, KVC_E_HIP.
  */
 kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
