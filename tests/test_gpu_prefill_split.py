@@ -59,11 +59,12 @@ def test_scattered_positions_leave_segments_empty(monkeypatch, seg, kv):
     p.close()
 
 
+@FORMATS
 @SEGS
-def test_continuation_far_into_the_cache(monkeypatch, seg):
+def test_continuation_far_into_the_cache(monkeypatch, seg, kv):
     """40 tokens continuing at position 3000 (tens of segments per query tile)."""
-    say(f"split prefill continuation seg={seg}")
-    p = filled(120, 16, 8, 128, 128, 3072, 3040, 0)
+    say(f"split prefill continuation seg={seg} kv={kv}")
+    p = filled(120, 16, 8, 128, 128, 3072, 3040, kv)
     pos = np.arange(3000, 3040, dtype=np.int32)
     run(monkeypatch, seg, p, pos, 16, 128, 121, sample=[0, 7, 19, 31, 32, 39])
     p.close()
