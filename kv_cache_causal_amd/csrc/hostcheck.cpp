@@ -90,6 +90,8 @@ int hc_plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_he
     return 0;
 }
 
+int64_t hc_max_part_bytes(void) { return kvc::kMaxPartBytes; }
+
 int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
 {
     return kvc::decode_chunk_rows(work, br, forced);

@@ -32,8 +32,15 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
     // Segment length: the tiles spread over about kFill units, but no fewer than 3 per
     // unit, so a unit's start-up (query load, first tile fetch, record write) is spread
     // over a few tiles.
-    const int64_t seg_tiles = force_seg > 0 ? force_seg
-                            : std::max<int64_t>(3, (total * hgroups + kFill - 1) / kFill);
+    int64_t seg_tiles = force_seg > 0 ? force_seg
+                      : std::max<int64_t>(3, (total * hgroups + kFill - 1) / kFill);
+    // The partial records take max_seg x nt x n_head x (hd_kv + 4) floats.  A query tile
+    // with far more key tiles than the rest (one late position among early ones) could
+    // need hundreds of records per query row, so segments grow until they fit the cap.
+    const int64_t rec_bytes = (int64_t)nt * n_head * (hd_kv + 4) * (int64_t)sizeof(float);
+    const int64_t max_recs = std::max<int64_t>(1, kMaxPartBytes / rec_bytes);
+    const int64_t tiles_max = *std::max_element(tiles.begin(), tiles.end());
+    seg_tiles = std::max<int64_t>(seg_tiles, (tiles_max + max_recs - 1) / max_recs);
     int32_t max_seg = 1;
     for (int q = 0; q < pl.n_qtiles; q++)
         max_seg = std::max<int32_t>(max_seg, (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles));

@@ -25,8 +25,12 @@ struct PrefillPlan {
     std::vector<int32_t> units;
 };
 
+// Most bytes of split-K partial records one prefill may use.
+constexpr int64_t kMaxPartBytes = int64_t(256) << 20;
+
 // pos: host [nt] positions of the prompt's tokens.  force_seg: 0 = choose, > 0 = force
-// segments of that many key tiles, < 0 = never split.
+// segments of that many key tiles (still grown to respect kMaxPartBytes), < 0 = never
+// split.
 PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
                          int32_t hd_kv, int32_t force_seg);
 

@@ -26,7 +26,16 @@ def hc():
     L.hc_plan_prefill.argtypes = [p, i32, i32, i32, i32, i32, p, p, i32]
     L.hc_decode_chunk_rows.argtypes = [i64, i32, i64]
     L.hc_decode_chunk_rows.restype = i64
+    L.hc_max_part_bytes.restype = i64
     return L
+
+
+def seg_length(hc, tiles, hgroups, nt, n_head, hd_kv, force=0):
+    """The documented segment length: tiles spread over ~512 units, at least 3 (or the
+    forced length), grown until max_seg records per query row fit the scratch cap."""
+    s = force if force > 0 else max(3, -(-sum(tiles) * hgroups // 512))
+    max_recs = max(1, hc.hc_max_part_bytes() // (nt * n_head * (hd_kv + 4) * 4))
+    return max(s, -(-max(tiles) // max_recs))
 
 
 def plan(hc, pos, n_head, n_head_kv, hd_kv, force=0):
@@ -105,7 +114,7 @@ def test_short_causal_prompts_split_with_the_documented_length(hc, g):
         if hgroups * m["n_qtiles"] >= 512:
             assert m["max_seg"] == 1 and len(u) == 0
             continue
-        seg_len = max(3, -(-sum(tiles) * hgroups // 512))
+        seg_len = seg_length(hc, tiles, hgroups, nt, n_head, hd_kv)
         check_units(m, u, pos, seg_len)
         assert (m["max_seg"] > 1) == (max(tiles) > seg_len)
 
@@ -119,7 +128,7 @@ def test_continuation_and_scattered_positions(hc):
             m, u = plan(hc, pos, *g)
             hgroups = g[1] * m["n_hsub"]
             tiles = tiles_of(pos, m["TQ"], m["KT"])
-            seg_len = max(3, -(-sum(tiles) * hgroups // 512))
+            seg_len = seg_length(hc, tiles, hgroups, len(pos), g[0], g[2])
             check_units(m, u, pos, seg_len)
 
 
@@ -136,6 +145,23 @@ def test_forced_segment_lengths_and_no_split(hc):
     assert m["max_seg"] == 1 and len(u) == 0 and m["units_per_hgroup"] == 128
     m, u = plan(hc, big, 16, 8, 128, 16)
     check_units(m, u, big, 16)
+
+
+def test_partial_records_stay_within_the_cap(hc):
+    """One late position among thousands of early ones: the late query tile alone would
+    want hundreds of segments; they grow until max_seg x nt x n_head x (hd_kv + 4) floats
+    fit the scratch cap, and the cover stays exact."""
+    cap = hc.hc_max_part_bytes()
+    for n_head, n_head_kv, hd_kv, nt in ((4, 1, 256, 8000), (16, 8, 128, 1000), (4, 4, 16, 4000)):
+        pos = np.arange(nt, dtype=np.int32) % 64
+        pos[-1] = (1 << 24) - 1
+        m, u = plan(hc, pos, n_head, n_head_kv, hd_kv)
+        hgroups = n_head_kv * m["n_hsub"]
+        if hgroups * m["n_qtiles"] >= 512:
+            continue
+        tiles = tiles_of(pos, m["TQ"], m["KT"])
+        check_units(m, u, pos, seg_length(hc, tiles, hgroups, nt, n_head, hd_kv))
+        assert m["max_seg"] * nt * n_head * (hd_kv + 4) * 4 <= cap
 
 
 def test_decode_chunk_rows(hc):
