@@ -56,7 +56,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--kv", choices=["f32", "f16", "q8_0"], default="f32",
-                    help="region format: f32, or binary16 (half the bytes; arithmetic in f32)")
+                    help="region format: f32, binary16 (half the bytes) or Q8_0 (34 bytes per 32 "
+                         "values); the arithmetic is f32 in every case")
     ap.add_argument("--decode-runs", action="store_true",
                     help="stage 4 through gqa_attn_decode_runs: each sequence's window given "
                          "as two explicit runs, its second half first")
