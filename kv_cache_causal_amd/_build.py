@@ -31,6 +31,8 @@ HIP_FLAGS = [
 ]
 LIB = os.path.join(LIBDIR, "libkvc.so")
 HOSTCHECK = os.path.join(LIBDIR, "libkvc_hostcheck.so")
+ABI_DEMO = os.path.join(LIBDIR, "abi_demo")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def _run(cmd):
@@ -61,6 +63,13 @@ def build(jobs: int = 8) -> str:
           os.path.join(CSRC, "validate.cpp"), os.path.join(CSRC, "plan.cpp"),
           os.path.join(CSRC, "hostcheck.cpp"), "-o", tmp])
     os.replace(tmp, HOSTCHECK)
+    # The ABI used from plain C (a GPU test runs it): gcc, C11, against the HIP runtime.
+    tmp = ABI_DEMO + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{ROCM}/include", f"-I{INCLUDE}", os.path.join(ROOT, "tests", "c_abi", "abi_demo.c"),
+          f"-L{LIBDIR}", "-lkvc", f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN",
+          f"-Wl,-rpath,{ROCM}/lib", "-o", tmp])
+    os.replace(tmp, ABI_DEMO)
     return LIB
 
 
