@@ -87,13 +87,13 @@ namespace {
 void staging_release(Staging &st)
 {
     for (auto &u : st.inflight) {
-        hipEventSynchronize(u.ev);
-        hipEventDestroy(u.ev);
+        (void)hipEventSynchronize(u.ev);
+        (void)hipEventDestroy(u.ev);
     }
     st.inflight.clear();
-    for (auto ev : st.pool) hipEventDestroy(ev);
+    for (auto ev : st.pool) (void)hipEventDestroy(ev);
     st.pool.clear();
-    if (st.host) hipHostFree(st.host);
+    if (st.host) (void)hipHostFree(st.host);
     st.host = nullptr;
     st.dev = nullptr;
     st.cap = st.head = 0;
@@ -177,7 +177,7 @@ kvc_status get_table(const kvc_cache *c, int32_t hd, float base, float fscale, h
         return fail(KVC_E_NOMEM, "RoPE table allocation failed");
     hipError_t e = kvc::launch_rope_table(t.dev, c->g.capacity, hd, base, fscale, s);
     if (e != hipSuccess) {
-        hipFree(t.dev);
+        (void)hipFree(t.dev);
         return hip_fail(e, "rope table kernel");
     }
     c->tables.push_back(t);
@@ -210,7 +210,7 @@ kvc_status ensure_part(const kvc_cache *c, size_t need, hipStream_t s)
     if (need <= c->part_cap) return KVC_OK;
     if (c->part) {
         KVC_HIP(hipStreamSynchronize(s));
-        hipFree(c->part);
+        (void)hipFree(c->part);
         c->part = nullptr;
     }
     const size_t cap = std::max(need, c->part_cap * 2);
@@ -357,8 +357,8 @@ kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32
     const size_t bytes = (size_t)n_seq * n_layer * (size_t)c->region_bytes;
 
     auto cleanup = [&](kvc_status code, const std::string &m) {
-        if (c->K) hipFree(c->K);
-        if (c->V) hipFree(c->V);
+        if (c->K) (void)hipFree(c->K);
+        if (c->V) (void)hipFree(c->V);
         staging_release(c->st);
         delete c;
         return fail(code, m);
@@ -386,10 +386,10 @@ kvc_status kv_free(kvc_cache *c)
     if (!c) return KVC_OK;
     hipError_t e = hipDeviceSynchronize();
     staging_release(c->st);
-    for (RopeTable &t : c->tables) hipFree(t.dev);
-    if (c->part) hipFree(c->part);
-    hipFree(c->K);
-    hipFree(c->V);
+    for (RopeTable &t : c->tables) (void)hipFree(t.dev);
+    if (c->part) (void)hipFree(c->part);
+    (void)hipFree(c->K);
+    (void)hipFree(c->V);
     delete c;
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     return KVC_OK;
