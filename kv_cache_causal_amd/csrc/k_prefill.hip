@@ -31,8 +31,9 @@
 //     segments (same tile count each, the last one shorter); a workgroup scans one
 //     segment and writes its unnormalised (m, l, O) record, and a merge kernel combines a
 //     query's records by log-sum-exp (split-K, as for decode).
-//   * Region formats: binary16 is widened and Q8_0 dequantized (scale * code, exact in
-//     f32) while a tile is copied into LDS, so the products always see f32 values.
+//   * Region formats: binary16 is widened while a tile is copied into LDS; a Q8_0
+//     window is dequantized once (scale * code, exact in f32) into an f32 copy that the
+//     f32 kernel reads, so the products always see f32 values.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -72,7 +73,6 @@ struct PrefillCfg {
 };
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
 
 // Signed byte k of w as f32 (one conversion with a sign-extending byte select).
@@ -97,7 +97,7 @@ template <int HD>
 struct TileIO<HD, float> {
     static constexpr int CH = 4;
     typedef floatx4 Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r, float)
+    static __device__ __forceinline__ void put(float *lds, const Raw &r)
     {
         *reinterpret_cast<floatx4 *>(lds) = r;
     }
@@ -106,27 +106,12 @@ template <int HD>
 struct TileIO<HD, _Float16> {
     static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 8 ? 8 : 4;
     typedef typename std::conditional<CH == 8, half8_t, half4_t>::type Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r, float)
+    static __device__ __forceinline__ void put(float *lds, const Raw &r)
     {
         *reinterpret_cast<floatx4 *>(lds) = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
         if constexpr (CH == 8)
             *reinterpret_cast<floatx4 *>(lds + 4) =
                 floatx4{(float)r[4], (float)r[5], (float)r[6], (float)r[7]};
-    }
-};
-
-// Q8_0: CH codes (all inside one 32-value block) and that block's scale d.
-template <int HD>
-struct TileIO<HD, int8_t> {
-    static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 16 ? 16 : 8;
-    typedef typename std::conditional<CH == 16, intx4, intx2>::type Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r, float d)
-    {
-#pragma unroll
-        for (int w = 0; w < CH / 4; w++)
-            *reinterpret_cast<floatx4 *>(lds + 4 * w) =
-                floatx4{d * code_to_f32(r[w], 0), d * code_to_f32(r[w], 1),
-                        d * code_to_f32(r[w], 2), d * code_to_f32(r[w], 3)};
     }
 };
 
@@ -227,13 +212,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     __syncthreads();
     if (!p.units) kt1 = s_kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
-    constexpr bool kQ8 = std::is_same<KVT, int8_t>::value;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
-    // Q8_0 scales of this head: head-major, HD / 32 per row, `rows` rows per head.
-    const int64_t qrows = p.scale_off / (p.n_head_kv * HD);
-    const char *Ksc = static_cast<const char *>(p.kc) + p.scale_off + 2 * (hk * qrows * (HD / kQ8Block));
-    const char *Vsc = static_cast<const char *>(p.vc) + p.scale_off + 2 * (hk * qrows * (HD / kQ8Block));
 
     // Tile staging: thread tid moves chunk #(tid + 256 j) of the tile, j < LD, i.e. row
     // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
@@ -249,10 +229,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     // Native vector registers: with struct types the compiler turns these unconditional
     // copies into an aggregate copy and keeps the arrays in scratch memory.
     typename TIO::Raw kreg[LD], vreg[LD];
-    float ksc[LD], vsc[LD];   // Q8_0 block scales (unused by the float formats)
-    const int nsb = HD / kQ8Block;   // scales per row of this head
-    const uint32_t soff = (uint32_t)(trow * nsb + tcol / kQ8Block) * 2u;
-    const int64_t sjstride = (int64_t)RSTEP * nsb * 2;
     auto fetch = [&](int key0) {
         const char *kb0 = reinterpret_cast<const char *>(Kh + (int64_t)key0 * nkt);
         const char *vb0 = reinterpret_cast<const char *>(Vh + (int64_t)key0 * nkt);
@@ -260,15 +236,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         for (int j = 0; j < LD; j++) {
             kreg[j] = *reinterpret_cast<const typename TIO::Raw *>(kb0 + j * jstride + toff);
             vreg[j] = *reinterpret_cast<const typename TIO::Raw *>(vb0 + j * jstride + toff);
-        }
-        if constexpr (kQ8) {
-            const char *ks0 = Ksc + (int64_t)key0 * nsb * 2;
-            const char *vs0 = Vsc + (int64_t)key0 * nsb * 2;
-#pragma unroll
-            for (int j = 0; j < LD; j++) {
-                ksc[j] = (float)*reinterpret_cast<const _Float16 *>(ks0 + j * sjstride + soff);
-                vsc[j] = (float)*reinterpret_cast<const _Float16 *>(vs0 + j * sjstride + soff);
-            }
         }
     };
     fetch(kt0 * KT);
@@ -278,8 +245,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j], ksc[j]);
-            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j], vsc[j]);
+            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
+            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
         }
         __syncthreads();
         if (kt + 1 < kt1) fetch(key0 + KT);
@@ -492,17 +459,39 @@ hipError_t launch_hd_t(const PrefillParams &p, hipStream_t s)
 template <int HD>
 hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
 {
-    if constexpr (HD % kQ8Block == 0) {
-        if (p.kv_fmt == kFmtQ8) return launch_hd_t<HD, int8_t>(p, s);
-    }
     return p.kv_fmt == kFmtF16 ? launch_hd_t<HD, _Float16>(p, s) : launch_hd_t<HD, float>(p, s);
 }
 
-}  // namespace
-
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
+// Q8_0 regions: rows [0, dq_rows) of the window are dequantized once into an f32 copy
+// with the region's row layout (value = scale * code, exact in f32), and the f32 kernel
+// runs on the copy.  Dequantizing inside every workgroup's tile copy instead repeats it
+// for each query tile of a kv head.  A workgroup converts 1024 groups of 4 values (one
+// code word, one scale each), lane-contiguous in every load and store; blockIdx.y = 0
+// reads the K region into dst[0, 4 * n4), 1 the V region after it.
+__global__ void __launch_bounds__(256) dequant_q8_kernel(const char *kreg, const char *vreg,
+                                                         int64_t scale_off, int32_t nkt,
+                                                         int32_t hd_kv, int64_t n4, float *dst)
 {
-    if (p.nt <= 0) return hipSuccess;
+    const char *region = blockIdx.y ? vreg : kreg;
+    dst += blockIdx.y * n4 * 4;
+    const int64_t rows = scale_off / nkt;
+    const _Float16 *sc = reinterpret_cast<const _Float16 *>(region + scale_off);
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const int64_t g = (int64_t)blockIdx.x * 1024 + w * 256 + threadIdx.x;
+        if (g >= n4) return;
+        const int64_t v0 = g * 4;
+        const int64_t row = v0 / nkt;
+        const int32_t c = *reinterpret_cast<const int32_t *>(region + v0);
+        const float d = (float)sc[q8_scale_index(row, (int32_t)(v0 - row * nkt), hd_kv, rows)];
+        reinterpret_cast<floatx4 *>(dst)[g] =
+            floatx4{d * (float)(int8_t)c, d * (float)(int8_t)(c >> 8),
+                    d * (float)(int8_t)(c >> 16), d * (float)(int8_t)(c >> 24)};
+    }
+}
+
+hipError_t launch_by_hd(const PrefillParams &p, hipStream_t s)
+{
     switch (p.hd_kv) {
     case 16: return launch_hd<16>(p, s);
     case 32: return launch_hd<32>(p, s);
@@ -511,6 +500,30 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     case 256: return launch_hd<256>(p, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
+{
+    if (p.nt <= 0) return hipSuccess;
+    if (p.kv_fmt != kFmtQ8) return launch_by_hd(p, s);
+    if (!p.dq || p.dq_rows <= 0) return hipErrorInvalidValue;
+    const int32_t nkt = p.n_head_kv * p.hd_kv;
+    const int64_t vals = (int64_t)p.dq_rows * nkt;
+    const int64_t n4 = vals / 4;
+    const unsigned blocks = (unsigned)((n4 + 1023) / 1024);
+    PrefillParams f = p;
+    f.kc = p.dq;
+    f.vc = p.dq + vals;
+    f.kv_fmt = kFmtF32;
+    f.scale_off = 0;
+    dequant_q8_kernel<<<dim3(blocks, 2), dim3(256), 0, s>>>(
+        static_cast<const char *>(p.kc), static_cast<const char *>(p.vc), p.scale_off, nkt,
+        p.hd_kv, n4, p.dq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_by_hd(f, s);
 }
 
 }  // namespace kvc

@@ -80,6 +80,8 @@ struct kvc_cache {
     mutable std::vector<RopeTable> tables;
     mutable float *part = nullptr;  // split-K partials
     mutable size_t part_cap = 0;    // floats
+    mutable float *dq = nullptr;    // Q8_0 prefill: the window's K and V dequantized to f32
+    mutable size_t dq_cap = 0;      // floats
 };
 
 namespace {
@@ -203,22 +205,29 @@ int32_t env_prefill_seg()
     return e ? std::atoi(e) : 0;
 }
 
-// Grow the split-K partials buffer (shared by decode and prefill) to `need` floats.  The
-// old buffer may still be read by queued kernels on `s`, so it is freed after a sync.
+// Grow a scratch buffer of the handle to `need` floats.  The old buffer may still be
+// read by queued kernels on `s`, so it is freed after a sync.
+kvc_status ensure_scratch(float *&buf, size_t &buf_cap, size_t need, hipStream_t s,
+                          const char *what)
+{
+    if (need <= buf_cap) return KVC_OK;
+    if (buf) {
+        KVC_HIP(hipStreamSynchronize(s));
+        (void)hipFree(buf);
+        buf = nullptr;
+    }
+    const size_t cap = std::max(need, buf_cap * 2);
+    buf_cap = 0;
+    if (hipMalloc(reinterpret_cast<void **>(&buf), cap * sizeof(float)) != hipSuccess)
+        return fail(KVC_E_NOMEM, std::string(what) + " scratch allocation failed");
+    buf_cap = cap;
+    return KVC_OK;
+}
+
+// The split-K partials buffer, shared by decode and prefill.
 kvc_status ensure_part(const kvc_cache *c, size_t need, hipStream_t s)
 {
-    if (need <= c->part_cap) return KVC_OK;
-    if (c->part) {
-        KVC_HIP(hipStreamSynchronize(s));
-        (void)hipFree(c->part);
-        c->part = nullptr;
-    }
-    const size_t cap = std::max(need, c->part_cap * 2);
-    c->part_cap = 0;
-    if (hipMalloc(reinterpret_cast<void **>(&c->part), cap * sizeof(float)) != hipSuccess)
-        return fail(KVC_E_NOMEM, "split-K scratch allocation failed");
-    c->part_cap = cap;
-    return KVC_OK;
+    return ensure_scratch(c->part, c->part_cap, need, s, "split-K");
 }
 
 // Split-K decode of n_seq validated entries.  Entry b's window is rows [0, pos[b]]
@@ -388,6 +397,7 @@ kvc_status kv_free(kvc_cache *c)
     staging_release(c->st);
     for (RopeTable &t : c->tables) (void)hipFree(t.dev);
     if (c->part) (void)hipFree(c->part);
+    if (c->dq) (void)hipFree(c->dq);
     (void)hipFree(c->K);
     (void)hipFree(c->V);
     delete c;
@@ -558,12 +568,24 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
         st = ensure_part(c, (size_t)pl.max_seg * nt * n_head * (c->g.hd_kv + 4), s);
         if (st != KVC_OK) return st;
     }
+    // Q8_0: the kernels read an f32 copy of rows [0, dq_rows) (whole 64-row groups up to
+    // the largest position), written by a dequantization pass on the same stream.
+    int32_t dq_rows = 0;
+    if (c->kv_fmt == kvc::kFmtQ8) {
+        const int32_t top = *std::max_element(pos, pos + nt) + 1;
+        dq_rows = (top + kvc::kRegionRowAlign - 1) / kvc::kRegionRowAlign * kvc::kRegionRowAlign;
+        const size_t nkt = (size_t)c->g.n_head_kv * c->g.hd_kv;
+        st = ensure_scratch(c->dq, c->dq_cap, 2 * (size_t)dq_rows * nkt, s, "Q8_0 window");
+        if (st != KVC_OK) return st;
+    }
     const int32_t *dev = nullptr;
     if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
     const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region_bytes;
     kvc::PrefillParams p{};
     p.units = pl.units.empty() ? nullptr : dev + units_at;
     p.part = pl.max_seg > 1 ? c->part : nullptr;
+    p.dq = dq_rows ? c->dq : nullptr;
+    p.dq_rows = dq_rows;
     p.GB = pl.GB;
     p.TQ = pl.TQ;
     p.n_qtiles = pl.n_qtiles;
