@@ -54,20 +54,24 @@ namespace kvc {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kUnroll = 4;        // rows per lane group per step (two steps in flight)
 
 // Dims of a row slice each lane holds.  f32: 8 (two float4) for kv groups of up to 2
 // query heads, 4 (one float4) for larger groups, whose per-head registers would otherwise
-// crowd out the load buffers.  binary16: 16 dims (32 bytes per lane) for groups of up to
-// 2, 8 for up to 4, 4 beyond.  Q8_0: 8 codes (8 bytes) for groups of up to 4, 4 beyond:
-// with 16 the code conversions held so many registers that only 2 waves fit per SIMD;
-// with 8, 3 fit and the batch workload's decode measured ~10% faster.
+// crowd out the load buffers.  binary16: 8 dims (16 bytes per lane) for groups of up to
+// 4, 4 beyond.  Q8_0: 8 codes (8 bytes) for groups of up to 4, 4 beyond.
 template <int GP, typename KVT>
 constexpr int dims_per_lane()
 {
     if constexpr (sizeof(KVT) == 1) return GP <= 4 ? 8 : 4;
     if constexpr (sizeof(KVT) == 2) return GP <= 4 ? 8 : 4;
     return GP <= 2 ? 8 : 4;
+}
+
+// Rows per lane group per step (two steps in flight).
+template <int GP, typename KVT>
+constexpr int rows_per_step()
+{
+    return 4;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -241,6 +245,7 @@ template <int HD, int GP, typename KVT>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
 {
     constexpr int kDimsPerLane = dims_per_lane<GP, KVT>();
+    constexpr int kUnroll = rows_per_step<GP, KVT>();
     constexpr int LPR = HD / kDimsPerLane;   // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave per unrolled step
     using IO = RowIO<KVT, kDimsPerLane, LPR>;
@@ -318,7 +323,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     };
     auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], int step) {
         const int rb = r0 + step * BR;
-        float sc[kUnroll][GP];
+        float sc[kUnroll][GP], pv[kUnroll][GP];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const bool valid = rb + (u * kWaves + wave) * RPW + rg < r1;
@@ -352,9 +357,17 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             for (int u = 0; u < kUnroll; u++) {
                 const float pu = fast_exp2(sc[u][g] - ref);
                 l[g] += pu;
-                const float pv = pu * IO::scale(vf[u]);
+                pv[u][g] = pu * IO::scale(vf[u]);
+            }
+        }
+        // Each V value is widened once and feeds every head of the group.
 #pragma unroll
-                for (int i = 0; i < kDimsPerLane; i++) acc[g][i] += pv * IO::get(vf[u], i);
+        for (int u = 0; u < kUnroll; u++) {
+#pragma unroll
+            for (int i = 0; i < kDimsPerLane; i++) {
+                const float x = IO::get(vf[u], i);
+#pragma unroll
+                for (int g = 0; g < GP; g++) acc[g][i] += pv[u][g] * x;
             }
         }
     };
@@ -538,9 +551,9 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 
 int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt)
 {
-    // The largest of the lane layouts' step sizes (all are powers of two).
-    const int lpr = hd_kv / 8;
-    return kWaves * (64 / lpr) * kUnroll;
+    // The largest of the lane layouts' step sizes (all are powers of two): a wave covers
+    // 64 * dims / hd_kv rows per unrolled row, and dims * rows_per_step is at most 32.
+    return kWaves * 64 * 32 / hd_kv;
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
