@@ -120,11 +120,12 @@ kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_h
  * everything else (layout, calls, errors) is as for kv_alloc.  With KVC_KV_Q8_0 a
  * region is rows * nkt int8 codes laid out [rows][nkt] (nkt = n_head_kv * hd_kv, the
  * code of value i of row p at byte p * nkt + i), followed directly by rows * nkt / 32
- * binary16 scales laid out [n_head_kv][rows][hd_kv / 32] (the scale of value i of row
- * p, in kv head h = i / hd_kv, is entry (h * rows + p) * hd_kv / 32 + (i % hd_kv) / 32):
- * the same 34 bytes per 32 values as the interleaved block, as two planes so that code
- * rows are aligned for vector loads and one kv head's scales of consecutive rows are
- * contiguous.  Zero bytes decode to +0.0.
+ * binary16 scales laid out [n_head_kv][rows / 4][hd_kv / 32][4] (the scale of value i of
+ * row p, in kv head h = i / hd_kv and block b = (i % hd_kv) / 32, is entry
+ * ((h * rows / 4 + p / 4) * hd_kv / 32 + b) * 4 + p % 4): the same 34 bytes per 32 values
+ * as the interleaved block, as two planes so that code rows are aligned for vector loads,
+ * with the scales of one block for 4 consecutive rows (4q .. 4q+3) in 8 contiguous bytes.
+ * Zero bytes decode to +0.0.
  * Errors: as kv_alloc, plus KVC_E_ARG for an unknown format and KVC_E_GEOMETRY for a
  * Q8_0 cache whose hd_kv is not a multiple of 32.
  */

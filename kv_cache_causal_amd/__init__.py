@@ -248,7 +248,8 @@ def kv_read(c: Cache, seq: int, layer: int, stream=None):
     [capacity][n_head_kv * hd_kv] torch tensors (float32, or float16 for a binary16
     cache).  For a Q8_0 cache each of K and V is a pair (codes int8 [rows][nkt], scales
     int16 holding binary16 bits [n_head_kv][rows][hd_kv / 32]) over all rows = capacity
-    rounded up to 64.  For inspection and tests."""
+    rounded up to 64; the scales come in that logical order (the region interleaves them
+    by row quads, see kv_alloc_typed).  For inspection and tests."""
     global _hip
     import torch
     if _hip is None:
@@ -267,7 +268,9 @@ def kv_read(c: Cache, seq: int, layer: int, stream=None):
             if e != 0:
                 raise RuntimeError(f"hipMemcpyAsync failed: {e}")
             codes = t[: rows * c.nkt].view(torch.int8).reshape(rows, c.nkt)
-            scales = t[rows * c.nkt:].view(torch.int16).reshape(c.n_head_kv, rows, c.hd_kv // 32)
+            scales = (t[rows * c.nkt:].view(torch.int16)
+                      .reshape(c.n_head_kv, rows // 4, c.hd_kv // 32, 4)
+                      .permute(0, 1, 3, 2).reshape(c.n_head_kv, rows, c.hd_kv // 32))
             out.append((codes, scales))
         return out[0], out[1]
     for src in (kp, vp):

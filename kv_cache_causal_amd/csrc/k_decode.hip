@@ -96,19 +96,22 @@ typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
 
 // Where one kv head's slices live in a region: row r's values start at element
-// r * nkt + hk * HD; a Q8_0 region's scales of row r are at q8_scale_index (head-major
-// after byte scale_off, `rows` rows per head).
+// r * nkt + hk * HD; a Q8_0 region's scales start at `scales` (q8_scale_index: head-major,
+// `rows` rows per head, interleaved by row quads).
 struct Slice {
-    const char *region;
-    int64_t scale_off, rows;
+    const char *region, *scales;
+    int64_t rows;
     int32_t nkt, hk;
 };
 
 // How a lane group reads its DPL dims of a row slice (LPR lanes per row).  Raw is what
 // one row occupies in registers until it is used (binary16 and codes stay packed);
-// get(r, i) is the lane's i-th value (a code for Q8_0), scale(r) the factor that turns
-// codes into values (1 for the float formats); dim(li, i) is the head dim of the lane's
-// i-th value, so q is loaded in the same order.
+// get(r, i) is the lane's i-th value (a code for Q8_0); dim(li, i) is the head dim of the
+// lane's i-th value, so q is loaded in the same order.  Per-row factors that turn codes
+// into values come per quad of rows: with kQuads, a lane group's rows of a step are
+// 4 consecutive rows 4p .. 4p+3, load_quad(s, p, li) fetches their factors for the
+// lane's dims in one load and scale(quad, u) is row 4p+u's; the float formats have none
+// (scale 1).
 //   f32, 8 dims: two float4 at li*4 and 4*LPR + li*4 (each load instruction covers whole
 //                lines of several rows);  f32, 4 dims: one float4 at li*4;
 //   f16, 8 dims: one 16-byte load at li*8;  f16, 4 dims: 4 halves at li*4 (16 halves
@@ -116,6 +119,13 @@ struct Slice {
 //   Q8_0, DPL dims: DPL codes at li*DPL (16, 8 or 4 bytes) and the scale of their block.
 template <typename KVT, int DPL, int LPR>
 struct RowIO;
+
+struct NoRowScale {
+    static constexpr bool kQuads = false;
+    struct Quad {};
+    static __device__ __forceinline__ Quad load_quad(const Slice &, int64_t, int) { return {}; }
+    static __device__ __forceinline__ float scale(const Quad &, int) { return 1.0f; }
+};
 
 // Every K/V byte of a decode window is read exactly once, so row loads are nontemporal:
 // they stream past the caches instead of displacing lines other work will reuse
@@ -133,7 +143,7 @@ __device__ __forceinline__ const KVT *slice_row(const Slice &s, int64_t row, int
 }
 
 template <int LPR>
-struct RowIO<float, 8, LPR> {
+struct RowIO<float, 8, LPR> : NoRowScale {
     struct Raw { floatx4 a, b; };
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
@@ -144,40 +154,36 @@ struct RowIO<float, 8, LPR> {
         return r;
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
-    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return (i / 4) * 4 * LPR + li * 4 + (i % 4); }
 };
 template <int LPR>
-struct RowIO<float, 4, LPR> {
+struct RowIO<float, 4, LPR> : NoRowScale {
     typedef floatx4 Raw;
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
         return stream_load<floatx4>(slice_row<float>(s, row, 4 * LPR) + li * 4);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return r[i]; }
-    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
 };
 template <int LPR>
-struct RowIO<_Float16, 8, LPR> {
+struct RowIO<_Float16, 8, LPR> : NoRowScale {
     typedef half8_t Raw;
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
         return stream_load<half8_t>(slice_row<_Float16>(s, row, 8 * LPR) + li * 8);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
-    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 8 + i; }
 };
 template <int LPR>
-struct RowIO<_Float16, 4, LPR> {
+struct RowIO<_Float16, 4, LPR> : NoRowScale {
     typedef half4_t Raw;
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
         return stream_load<half4_t>(slice_row<_Float16>(s, row, 4 * LPR) + li * 4);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
-    static __device__ __forceinline__ float scale(const Raw &) { return 1.0f; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
 };
 
@@ -206,15 +212,18 @@ template <int DPL, int LPR>
 struct RowIO<int8_t, DPL, LPR> {
     static constexpr int HD = DPL * LPR;
     typedef typename CodeVec<DPL>::T Codes;
-    struct Raw { Codes c; float d; };
+    struct Raw { Codes c; };
+    static constexpr bool kQuads = true;
+    typedef half4_t Quad;   // the scales of the lane's block for 4 consecutive rows
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
         const int64_t v0 = row * s.nkt + (int64_t)s.hk * HD + li * DPL;   // first value
-        Raw r;
-        r.c = stream_load<Codes>(s.region + v0);
-        const int64_t si = ((int64_t)s.hk * s.rows + row) * (HD / kQ8Block) + li * DPL / kQ8Block;
-        r.d = (float)stream_load<_Float16>(s.region + s.scale_off + 2 * si);
-        return r;
+        return Raw{stream_load<Codes>(s.region + v0)};
+    }
+    static __device__ __forceinline__ Quad load_quad(const Slice &s, int64_t quad, int li)
+    {
+        const int64_t si = (((int64_t)s.hk * (s.rows >> 2) + quad) * (HD / kQ8Block) + li * DPL / kQ8Block) * 4;
+        return stream_load<Quad>(s.scales + 2 * si);
     }
     // Codes stay packed four to a register until used; a signed byte of a register
     // converts in one instruction (sign-extending byte select on the operand).
@@ -225,7 +234,7 @@ struct RowIO<int8_t, DPL, LPR> {
         else w = r.c[i / 4];
         return code_to_f32(w, i % 4);
     }
-    static __device__ __forceinline__ float scale(const Raw &r) { return r.d; }
+    static __device__ __forceinline__ float scale(const Quad &q, int u) { return (float)q[u]; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * DPL + i; }
 };
 
@@ -283,8 +292,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const int nkt = p.n_head_kv * HD;
     const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
     const int64_t qrows = p.scale_off / nkt;   // region rows (Q8_0 only)
-    const Slice K{static_cast<const char *>(p.kc) + reg, p.scale_off, qrows, nkt, hk};
-    const Slice V{static_cast<const char *>(p.vc) + reg, p.scale_off, qrows, nkt, hk};
+    const char *kreg = static_cast<const char *>(p.kc) + reg;
+    const char *vreg = static_cast<const char *>(p.vc) + reg;
+    const Slice K{kreg, kreg + p.scale_off, qrows, nkt, hk};
+    const Slice V{vreg, vreg + p.scale_off, qrows, nkt, hk};
 
     // The lane's query values in the order its row values arrive (IO::dim).
     float qf[GP][kDimsPerLane];
@@ -306,33 +317,57 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     }
 
     // Rows are consumed in steps of BR per workgroup; two register sets alternate so the
-    // loads of step i+1 are in flight while step i is reduced.
+    // loads of step i+1 are in flight while step i is reduced.  Row of unrolled row u of
+    // a step starting at rb: instruction u of the wave reads RPW rows, RPW apart with row
+    // quads (the lane group's rows are the quad rb + 4 (wave RPW + rg) + 0..3, so steps
+    // start at r0 rounded down to a quad; rows before r0 are read and masked), adjacent
+    // otherwise.
     constexpr int BR = kWaves * RPW * kUnroll;
-    const int nsteps = (r1 - r0 + BR - 1) / BR;
+    constexpr bool kQuads = IO::kQuads;
+    static_assert(!kQuads || kUnroll == 4, "row quads need 4 rows per lane group per step");
+    const int rbase = kQuads ? (r0 & ~3) : r0;
+    const int nsteps = (r1 - rbase + BR - 1) / BR;
+    auto row_of = [&](int rb, int u) {
+        return kQuads ? rb + (wave * RPW + rg) * 4 + u : rb + (u * kWaves + wave) * RPW + rg;
+    };
+    using Quad = typename IO::Quad;
     Raw kA[kUnroll], vA[kUnroll], kB[kUnroll], vB[kUnroll];
+    Quad kqA, vqA, kqB, vqB;
 
-    auto load = [&](Raw (&kf)[kUnroll], Raw (&vf)[kUnroll], int step) {
-        const int rb = r0 + step * BR;
+    auto load = [&](Raw (&kf)[kUnroll], Raw (&vf)[kUnroll], Quad &kq, Quad &vq, int step) {
+        const int rb = rbase + step * BR;
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            int row = rb + (u * kWaves + wave) * RPW + rg;
+            int row = row_of(rb, u);
             row = row < r1 ? row : r0;  // rows past the chunk re-read row r0 and are masked
             kf[u] = IO::load(K, row, li);
             vf[u] = IO::load(V, row, li);
         }
+        if constexpr (kQuads) {
+            // A quad wholly past the chunk re-reads r0's quad (inside the region).
+            const int q4 = row_of(rb, 0);
+            const int quad = (q4 < r1 ? q4 : r0) >> 2;
+            kq = IO::load_quad(K, quad, li);
+            vq = IO::load_quad(V, quad, li);
+        }
     };
-    auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], int step) {
-        const int rb = r0 + step * BR;
-        float sc[kUnroll][GP], pv[kUnroll][GP];
+    auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], const Quad &kq,
+                       const Quad &vq, int step) {
+        const int rb = rbase + step * BR;
+        float sc[kUnroll][GP], pv[kUnroll][GP], vs[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            const bool valid = rb + (u * kWaves + wave) * RPW + rg < r1;
+            const int row = row_of(rb, u);
+            const bool valid = row < r1 && (!kQuads || row >= r0);
+            // A masked row's weight is 0; its own V factor (a row outside the window,
+            // possibly holding an infinite scale) must not turn that into NaN.
+            vs[u] = (kQuads && !valid) ? 0.0f : IO::scale(vq, u);
 #pragma unroll
             for (int g = 0; g < GP; g++) {
                 float s = 0.0f;
 #pragma unroll
                 for (int i = 0; i < kDimsPerLane; i++) s += qf[g][i] * IO::get(kf[u], i);
-                s = group_sum<LPR>(s * IO::scale(kf[u]));
+                s = group_sum<LPR>(s * IO::scale(kq, u));
                 sc[u][g] = valid ? s : -INFINITY;
             }
         }
@@ -357,7 +392,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             for (int u = 0; u < kUnroll; u++) {
                 const float pu = fast_exp2(sc[u][g] - ref);
                 l[g] += pu;
-                pv[u][g] = pu * IO::scale(vf[u]);
+                pv[u][g] = pu * vs[u];
             }
         }
         // Each V value is widened once and feeds every head of the group.
@@ -372,13 +407,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         }
     };
 
-    load(kA, vA, 0);
+    load(kA, vA, kqA, vqA, 0);
     for (int st = 0; st < nsteps; st += 2) {
-        if (st + 1 < nsteps) load(kB, vB, st + 1);
-        consume(kA, vA, st);
+        if (st + 1 < nsteps) load(kB, vB, kqB, vqB, st + 1);
+        consume(kA, vA, kqA, vqA, st);
         if (st + 1 >= nsteps) break;
-        if (st + 2 < nsteps) load(kA, vA, st + 2);
-        consume(kB, vB, st + 1);
+        if (st + 2 < nsteps) load(kA, vA, kqA, vqA, st + 2);
+        consume(kB, vB, kqB, vqB, st + 1);
     }
 
     // Merge the row groups of the wave (lanes that share li).

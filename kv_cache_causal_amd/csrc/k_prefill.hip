@@ -210,7 +210,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     float m = -INFINITY, l = 0.0f;
 
     __syncthreads();
-    if (!p.units) kt1 = s_kmax / KT + 1;
+    const int kmax = s_kmax;
+    if (!p.units) kt1 = kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
@@ -242,10 +243,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
 
     for (int kt = kt0; kt < kt1; kt++) {
         const int key0 = kt * KT;
+        // V rows past the largest position among the block's queries have weight 0 for
+        // every query; they are stored as zeros, so that a non-finite value in a row no
+        // window of the block contains cannot turn 0 * V into NaN.
+        const bool tail = key0 + KT - 1 > kmax;
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
             TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
+            if (tail && key0 + trow + j * RSTEP > kmax) vreg[j] = typename TIO::Raw{};
             TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
         }
         __syncthreads();

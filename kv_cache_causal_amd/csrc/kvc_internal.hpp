@@ -16,9 +16,10 @@ namespace kvc {
 // nkt = n_head_kv * hd_kv values:
 //   kFmtF32, kFmtF16: [rows][nkt] f32 or binary16 values;
 //   kFmtQ8:           [rows][nkt] int8 codes, then at byte `scale_off` (= rows * nkt)
-//                     [n_head_kv][rows][hd_kv / 32] binary16 block scales (Q8_0: 32
-//                     values per block, value = scale * code).  Head-major, so the
-//                     scales one kv head reads for consecutive rows are contiguous.
+//                     [n_head_kv][rows / 4][hd_kv / 32][4] binary16 block scales (Q8_0:
+//                     32 values per block, value = scale * code).  Head-major and
+//                     interleaved by row quads, so the scales of one block of one kv
+//                     head for 4 consecutive rows (4p .. 4p+3) are 8 contiguous bytes.
 // Rows at or past the capacity stay zero and are never inside a window; they let the
 // prefill kernel load whole key tiles unconditionally.
 constexpr int kRegionRowAlign = 64;
@@ -26,12 +27,13 @@ enum KvFmt : int32_t { kFmtF32 = 0, kFmtF16 = 1, kFmtQ8 = 2 };
 constexpr int kQ8Block = 32;
 
 // Index (in binary16 units from the scales' start) of the scale of value j of row `row`
-// of a Q8_0 region with `rows` rows.
+// of a Q8_0 region with `rows` rows (a multiple of 4).
 __host__ __device__ inline int64_t q8_scale_index(int64_t row, int32_t j, int32_t hd_kv,
                                                   int64_t rows)
 {
     const int32_t h = j / hd_kv;
-    return ((int64_t)h * rows + row) * (hd_kv / kQ8Block) + (j - h * hd_kv) / kQ8Block;
+    const int32_t blk = (j - h * hd_kv) / kQ8Block;
+    return (((int64_t)h * (rows >> 2) + (row >> 2)) * (hd_kv / kQ8Block) + blk) * 4 + (row & 3);
 }
 
 // ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------

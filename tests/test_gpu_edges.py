@@ -258,10 +258,39 @@ def test_q8_store_edges(style):
     k, v = k.reshape(100, 2, 64), v.reshape(100, 2, 64)
     p.append(0, [0] * 100, np.arange(100), None, 4, 64, k, v, 1e6, 1.0, style)
     compare_cache(p.g, p.o, 0, 0, "q8 edges")
-    # Attention over the worked rows only (a 1e7 block's scale overflows to infinity).
+    # Attention over the worked rows only (a 1e7 block's scale overflows to infinity; the
+    # rows past the windows hold such blocks, and must not leak into the results).
     q = custom(92, (3, 4, 64))
     got, want = p.decode(0, [0, 0, 0], [0, 2, 4], dev(q), q, 4, 64, 0.125)
     assert_close(got, want, "q8 decode over edge blocks")
+    q5 = custom(93, (5, 4, 64))
+    got, want = p.prefill(0, 0, np.arange(5, dtype=np.int32), dev(q5), q5, 4, 64, 0.125)
+    assert_close(got, want, "q8 prefill over edge blocks")
+    p.close()
+
+
+@pytest.mark.parametrize("kv", [0, 1], ids=["f32", "f16"])
+def test_non_finite_rows_outside_every_window(kv):
+    """Rows past every query's window holding inf, -inf and NaN (written at later
+    positions): attention sums only over [0, pos], so decode and prefill results stay
+    finite and match the oracle, including the prefill's last key tile, which holds
+    such rows beside the window's own."""
+    say(f"non-finite rows outside the windows, kv {kv}")
+    nh, nkv, hd = 4, 2, 64
+    p = Pair(1, 1, nkv, hd, 128, dtype=kv)
+    k, v = custom(94, (100, nkv, hd)), custom(95, (100, nkv, hd))
+    bad = np.array([np.inf, -np.inf, np.nan], np.float32)
+    rng = np.random.default_rng(96)
+    for a in (k, v):
+        a[40:] = bad[rng.integers(0, 3, a[40:].shape)]
+    p.append(0, [0] * 100, np.arange(100, dtype=np.int32), None, nh, hd, k, v)
+    q = custom(97, (3, nh, hd))
+    got, want = p.decode(0, [0, 0, 0], [0, 17, 39], dev(q), q, nh, hd, 0.125)
+    assert_close(got, want, "decode beside non-finite rows")
+    for nt in (40, 8):
+        qp = custom(98 + nt, (nt, nh, hd))
+        got, want = p.prefill(0, 0, np.arange(nt, dtype=np.int32), dev(qp), qp, nh, hd, 0.125)
+        assert_close(got, want, f"prefill of {nt} beside non-finite rows")
     p.close()
 
 
