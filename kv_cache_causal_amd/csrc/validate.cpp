@@ -133,13 +133,28 @@ kvc_status check_append(const Geometry &g, int32_t layer, int32_t nt, const int3
         kvc_status st = check_heads(g, n_head, hd, msg);
         if (st != KVC_OK) return st;
     }
-    kvc_status st = check_seq_ids(g, nt, seq_ids, msg);
-    if (st != KVC_OK) return st;
-    st = check_positions(g, nt, pos, msg);
-    if (st != KVC_OK) return st;
+    // One pass: ranges, and whether the (sequence, position) keys are strictly
+    // increasing (a prompt's positions, a batch of distinct sequences), in which case no
+    // key repeats; the error messages come from the per-array checks.
+    bool in_range = true, increasing = true;
+    int64_t prev = -1;
+    for (int32_t t = 0; t < nt; t++) {
+        in_range &= seq_ids[t] >= 0 && seq_ids[t] < g.n_seq && pos[t] >= 0 && pos[t] < g.capacity;
+        const int64_t key = ((int64_t)seq_ids[t] << 32) | (int64_t)(uint32_t)pos[t];
+        increasing &= key > prev;
+        prev = key;
+    }
+    if (!in_range) {
+        kvc_status st = check_seq_ids(g, nt, seq_ids, msg);
+        if (st != KVC_OK) return st;
+        st = check_positions(g, nt, pos, msg);
+        if (st != KVC_OK) return st;
+    }
+    if (increasing) return KVC_OK;
     // Two rows aimed at one (sequence, position) would race on the device.
+    auto key = [&](int32_t t) { return ((int64_t)seq_ids[t] << 32) | (int64_t)pos[t]; };
     std::vector<int64_t> keys((size_t)nt);
-    for (int32_t t = 0; t < nt; t++) keys[t] = ((int64_t)seq_ids[t] << 32) | (int64_t)pos[t];
+    for (int32_t t = 0; t < nt; t++) keys[t] = key(t);
     std::sort(keys.begin(), keys.end());
     for (size_t i = 1; i < keys.size(); i++) {
         if (keys[i] == keys[i - 1]) {

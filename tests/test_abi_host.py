@@ -106,6 +106,10 @@ APPEND_CASES = [
     ("pos_at_capacity", dict(pos=[3, 10])),
     ("pos_negative", dict(pos=[-1, 3])),
     ("dup", dict(pos=[4, 4], seq=[1, 1])),
+    ("dup_unsorted", dict(seq=[1, 0, 1], pos=[4, 2, 4])),
+    ("decreasing_ok", dict(seq=[1, 1, 0], pos=[5, 3, 9])),
+    ("dup_after_increasing_run", dict(seq=[0] * 6, pos=[0, 1, 2, 3, 4, 2])),
+    ("range_beside_dup", dict(seq=[0, 0, 0], pos=[3, 3, 10])),
     ("seq_range", dict(seq=[0, 2])),
     ("hd_lt_hd_kv", dict(hd=8)),
     ("hd_odd", dict(hd=17)),
