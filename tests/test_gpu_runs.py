@@ -100,20 +100,23 @@ def test_runs_head_shapes(nh, nkv, hd, hdk):
     p.close()
 
 
-def test_stale_rows_outside_the_window_are_not_read():
-    """Rolled-back rows past the window are rewritten with huge values: the output is the
-    same to the bit."""
-    say("runs rollback")
+@FORMATS
+def test_stale_rows_outside_the_window_are_not_read(kv):
+    """Rolled-back rows past the window are rewritten with huge values (infinite as
+    binary16, an overflowed scale as Q8_0): the output is the same to the bit.  The run
+    edges are not multiples of 4, so rewritten rows share a Q8_0 row quad with rows of
+    the window."""
+    say(f"runs rollback kv={kv}")
     cap, nkv, hdk, nh = 3000, 2, 64, 4
-    p = Pair(1, 1, nkv, hdk, cap)
+    p = Pair(1, 1, nkv, hdk, cap, dtype=kv)
     fill(p, 220, 1, cap, nkv, hdk)
-    runs = [[(0, 1500)], [(0, 700), (2000, 1000)]]
+    runs = [[(0, 1501)], [(0, 701), (2002, 998)]]
     q = custom(221, (2, nh, hdk))
     qd = dev(q)
     before, want = p.decode_runs(0, [0, 0], runs, qd, q, nh, hdk, 0.125)
     assert_close(before, want, "before rollback")
-    junk = np.full((1300, nkv, hdk), 1e30, np.float32)
-    p.append(0, [0] * 1300, np.arange(700, 2000), None, 0, 0, junk, junk, 1e6, 1.0, 2)
+    junk = np.full((1301, nkv, hdk), 1e30, np.float32)
+    p.append(0, [0] * 1301, np.arange(701, 2002), None, 0, 0, junk, junk, 1e6, 1.0, 2)
     after, _ = p.decode_runs(0, [0], [runs[1]], qd[1:], q[1:], nh, hdk, 0.125)
     assert_bitwise(after, before[1:], "window unchanged by stale rows")
     p.close()
