@@ -8,7 +8,7 @@
 //   * each projection output is the f32 nearest to the exact dot product x . w_j: every
 //     f32 x f32 product is exact in f64; a plain f64 sum with a rigorous error bound
 //     settles the rounding whenever the bound's whole interval rounds to one f32 (all
-//     but a vanishing fraction of rows), and otherwise the wave recomputes the sum as an
+//     but a vanishing fraction of rows), and otherwise a wave recomputes the sum as an
 //     unevaluated pair of f64 values (hi + lo, hi accumulated with the error-free TwoSum
 //     and the errors in lo), merges lane partials the same way and rounds the pair to
 //     f32 once, through round-to-odd at f64 precision (53 >= 24 + 2 bits makes that one
@@ -20,11 +20,14 @@
 // it can be checked against any exact evaluation.
 //
 // Work split: a workgroup owns one "unit" -- up to 8 rotation pairs (32 for a Q8_0
-// cache, so that a unit holds whole 32-value blocks) of one head of q, k or v -- for a
-// group of up to 8 tokens.  NEOX pairs (i, i + D/2) and interleaved pairs (2i, 2i+1) of
-// a unit are computed together, so the rotation happens in LDS without another launch.
-// Rows are reduced by 16 lanes each (four rows per wave at a time), every lane streaming
-// 16-byte pieces of its row; the weight rows are read once per token group.
+// cache, so that a unit holds whole 32-value blocks) of one head of q, k or v -- for all
+// the call's tokens.  NEOX pairs (i, i + D/2) and interleaved pairs (2i, 2i+1) of a unit
+// are computed together, so the rotation happens in LDS without another launch.
+//   * One token (qkv_one_kernel): rows are reduced by 16 lanes each (four rows per wave
+//     at a time), every lane streaming 16-byte pieces of its row.
+//   * Several tokens (qkv_mfma_kernel, one workgroup per unit and tile of 16 tokens):
+//     the unit's rows times the tokens' x as f64 matrix products
+//     (v_mfma_f64_16x16x4f64), so each operand a lane holds feeds 16 products.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -39,17 +42,7 @@ namespace {
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
 constexpr int kMaxRows = 64;   // rows of a unit (32 pairs)
 constexpr int kLanesPerRow = 16;
-constexpr int kXChunk = 512;   // x values per token staged in LDS at a time
-
-// LDS slot (in doubles) of the value pair (e + 2 half, e + 2 half + 1) of a staged x
-// chunk, e = 4 li + 64 k the first value of lane li's k-th piece: the pairs of one
-// (k, half) are contiguous over li, so the 16 lanes of a row read 256 consecutive bytes
-// (no bank conflicts; the other rows of the wave read the same bytes).
-__device__ __forceinline__ int xs_slot(int e, int half)
-{
-    const int k = e >> 6, li = (e >> 2) & 15;
-    return ((k * 2 + half) * 16 + li) * 2;
-}
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // Error-free sum: s + e == a + b exactly (s = fl(a + b)).
 __device__ __forceinline__ void two_sum(double a, double b, double &s, double &e)
@@ -97,222 +90,99 @@ __device__ __forceinline__ float dd_to_f32(double hi, double lo)
     return (float)h;
 }
 
-template <int STYLE, typename KVT, int TT>
-__global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per_unit)
-{
-    __shared__ float ys[TT][kMaxRows];   // [token][local row]
-    __shared__ double xs[TT > 1 ? TT : 1][TT > 1 ? kXChunk : 1];   // x chunk, several tokens
-
-    // Unit -> (projection, head, pair range).
-    int unit = blockIdx.x;
-    int proj = 0;
-    if (unit >= p.units_q) {
-        unit -= p.units_q;
-        proj = 1;
-        if (unit >= p.units_kv) {
-            unit -= p.units_kv;
-            proj = 2;
-        }
-    }
-    const int D = proj == 0 ? p.hd : p.hd_kv;
-    const int half = D >> 1;
-    const int upr = (half + pairs_per_unit - 1) / pairs_per_unit;   // units per head
-    const int head = unit / upr;
-    const int i_begin = (unit - head * upr) * pairs_per_unit;
-    const int np = min(pairs_per_unit, half - i_begin);
-    const int R = 2 * np;
-    const bool rot = proj < 2 && STYLE != kNone;
-    const bool neox = rot && STYLE == kNeox;
+// What a workgroup computes: rows [0, R) of projection `proj` (0 q, 1 k, 2 v) of head
+// `head` (head dim D), the R = 2 np rows of rotation pairs [i_begin, i_begin + np).
+struct Unit {
+    int proj, D, half, head, i_begin, np, R;
+    bool rot, neox;
     // Local row lr -> index within the head.  NEOX: first the np first-half rows, then
     // their partners; otherwise the unit's rows in order.
-    auto head_row = [&](int lr) {
+    __device__ int head_row(int lr) const
+    {
         if (neox) return lr < np ? i_begin + lr : half + i_begin + (lr - np);
         return 2 * i_begin + lr;
-    };
-    const float *W = p.w[proj] + (int64_t)head * D * p.d;
-    const float *B = p.b[proj] ? p.b[proj] + head * D : nullptr;
-    const int t0 = blockIdx.y * TT;
-    const int ntk = min(TT, p.nt - t0);
+    }
+};
 
-    // Projections.  Row lr is reduced by 16 lanes; lane li takes elements 4 li + 64 k.
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int li = lane % kLanesPerRow;
-    for (int base = 0; base < R; base += 16) {
-        const int lr = base + wave * 4 + lane / kLanesPerRow;
-        const bool row_ok = lr < R;
-        const float *wr = W + (int64_t)head_row(row_ok ? lr : 0) * p.d;
-        // Feed op(t, x, w) every (x, w) element pair of this lane's share of the row, as
-        // f64 (each f32 x f32 product is then exact): a lane takes elements 4 li + 64 k.
-        auto accumulate = [&](auto &&op) {
-            if constexpr (TT == 1) {
-                // One token: the step streams the weights, so each lane first issues the
-                // loads of up to kBatch pieces of its row (and of x), then does their
-                // arithmetic.
-                constexpr int kBatch = 16;
-                const float *xr = p.x + (int64_t)t0 * p.d;
-                for (int i0 = li * 4; i0 < p.d; i0 += kBatch * 4 * kLanesPerRow) {
-                    float4 wb[kBatch], xb[kBatch];
-#pragma unroll
-                    for (int k = 0; k < kBatch; k++) {
-                        const int i = i0 + k * 4 * kLanesPerRow;
-                        if (i < p.d) {
-                            wb[k] = *reinterpret_cast<const float4 *>(wr + i);
-                            xb[k] = *reinterpret_cast<const float4 *>(xr + i);
-                        }
-                    }
-#pragma unroll
-                    for (int k = 0; k < kBatch; k++) {
-                        if (i0 + k * 4 * kLanesPerRow < p.d) {
-                            op(0, (double)xb[k].x, (double)wb[k].x);
-                            op(0, (double)xb[k].y, (double)wb[k].y);
-                            op(0, (double)xb[k].z, (double)wb[k].z);
-                            op(0, (double)xb[k].w, (double)wb[k].w);
-                        }
-                    }
-                }
-            } else {
-                // Several tokens: each weight piece serves all of them.  The group's x
-                // rows pass through LDS as f64 in chunks of kXChunk values (one batch of
-                // loads per thread; rows past the group's tokens read as zeros), and each
-                // lane loads its kPieces weight pieces of the chunk together, before the
-                // staging, so a chunk costs about one memory round trip.  The arithmetic runs over all TT tokens
-                // without branches, token-minor, so consecutive operations feed
-                // independent sums.  Every thread of the block reaches the barriers: the
-                // row loop is uniform across the block.  (Loading the next chunk during
-                // the current one's arithmetic needs ~250 registers and ran slower.)
-                constexpr int kPieces = kXChunk / (4 * kLanesPerRow);
-                for (int c0 = 0; c0 < p.d; c0 += kXChunk) {
-                    const int cn = min(kXChunk, p.d - c0);
-                    // This chunk's weight pieces are requested first: their round trip
-                    // overlaps the x staging and its barriers.
-                    float4 wb[kPieces];
-#pragma unroll
-                    for (int k = 0; k < kPieces; k++) {
-                        const int e = li * 4 + k * 4 * kLanesPerRow;
-                        if (e < cn) wb[k] = *reinterpret_cast<const float4 *>(wr + c0 + e);
-                    }
-                    __syncthreads();   // the previous chunk's readers are done
-                    for (int idx = threadIdx.x; idx < TT * (kXChunk / 4); idx += blockDim.x) {
-                        const int t = idx / (kXChunk / 4);
-                        const int e = (idx - t * (kXChunk / 4)) * 4;
-                        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                        if (t < ntk && e < cn)
-                            v = *reinterpret_cast<const float4 *>(p.x + (int64_t)(t0 + t) * p.d + c0 + e);
-                        *reinterpret_cast<double2 *>(&xs[t][xs_slot(e, 0)]) = make_double2(v.x, v.y);
-                        *reinterpret_cast<double2 *>(&xs[t][xs_slot(e, 1)]) = make_double2(v.z, v.w);
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (int k = 0; k < kPieces; k++) {
-                        const int e = li * 4 + k * 4 * kLanesPerRow;
-                        if (e < cn) {
-                            const double wv[4] = {wb[k].x, wb[k].y, wb[k].z, wb[k].w};
-                            double xv[TT][4];
-#pragma unroll
-                            for (int t = 0; t < TT; t++) {
-                                const double2 a = *reinterpret_cast<const double2 *>(&xs[t][xs_slot(e, 0)]);
-                                const double2 b = *reinterpret_cast<const double2 *>(&xs[t][xs_slot(e, 1)]);
-                                xv[t][0] = a.x; xv[t][1] = a.y; xv[t][2] = b.x; xv[t][3] = b.y;
-                            }
-#pragma unroll
-                            for (int c = 0; c < 4; c++)
-#pragma unroll
-                                for (int t = 0; t < TT; t++) op(t, xv[t][c], wv[c]);
-                        }
-                    }
-                }
-            }
-        };
-
-        // Fast path: the plain f64 sum S of the products and the sum A of their
-        // magnitudes.  Each product is exact and every partial sum is far from the f64
-        // range limits, so |S - exact| <= gamma_m * sum|products| with m <= d/16 + 8
-        // roundings on any path; err = 4 m u A + 2 u |S| (u = 2^-53) covers that bound,
-        // the rounding of A, and the rounding of S -/+ err themselves.  Rounding to f32
-        // is monotonic, so when both ends of [S - err, S + err] round to the same f32
-        // (bit for bit: a straddled zero has two signs), that f32 is the one nearest the
-        // exact sum.  Otherwise (a value within err of an f32 rounding boundary, or a
-        // non-finite sum) that row and token is recomputed exactly below.
-        double S[TT], A[TT];
-#pragma unroll
-        for (int t = 0; t < TT; t++) S[t] = A[t] = 0.0;
-        accumulate([&](int t, double xv, double wv) {
-            S[t] = fma(xv, wv, S[t]);
-            A[t] = fma(fabs(xv), fabs(wv), A[t]);
-        });
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
-#pragma unroll
-            for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
-                S[t] += __shfl_xor(S[t], off);
-                A[t] += __shfl_xor(A[t], off);
-            }
-        }
-        // Longest rounding chain: a lane's ceil(d / 64) * 4 products plus 4 merge levels.
-        const double kErr = 4.0 * (double)(p.d / 16 + 8) * 0x1p-53;
-        uint32_t unsure = 0;   // tokens some row of this lane's wave could not settle
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
-            const double err = kErr * A[t] + 0x1p-52 * fabs(S[t]);
-            const float lo32 = (float)(S[t] - err), hi32 = (float)(S[t] + err);
-            const bool certain = t >= ntk || (__builtin_isfinite(S[t]) && __builtin_isfinite(err) &&
-                                              __float_as_uint(lo32) == __float_as_uint(hi32));
-            if (__any(!certain)) unsure |= 1u << t;
-            if (row_ok && li == 0 && t < ntk) ys[t][lr] = B ? lo32 + B[head_row(lr)] : lo32;
-        }
-        // Exact sum for an unsettled token of this wave's rows (rare: a value within the
-        // bound of an f32 rounding boundary): an unevaluated pair of f64 values (hi + lo,
-        // hi accumulated with the error-free TwoSum and the errors in lo), lane partials
-        // merged the same way, the pair rounded to f32 once.  x and w come from global
-        // memory (no barrier: the choice is per wave); every row of the wave recomputes,
-        // and the exact value replaces the stored one (they agree where both exist).
-        while (unsure) {
-            const int t = __builtin_ctz(unsure);
-            unsure &= unsure - 1;
-            const float *xr = p.x + (int64_t)(t0 + t) * p.d;
-            double hi = 0.0, lo = 0.0;
-            for (int i0 = li * 4; i0 < p.d; i0 += 4 * 4 * kLanesPerRow) {
-                float4 wb[4], xb[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const int i = i0 + k * 4 * kLanesPerRow;
-                    if (i < p.d) {
-                        wb[k] = *reinterpret_cast<const float4 *>(wr + i);
-                        xb[k] = *reinterpret_cast<const float4 *>(xr + i);
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    if (i0 + k * 4 * kLanesPerRow < p.d) {
-                        dd_add(hi, lo, (double)xb[k].x * (double)wb[k].x);
-                        dd_add(hi, lo, (double)xb[k].y * (double)wb[k].y);
-                        dd_add(hi, lo, (double)xb[k].z * (double)wb[k].z);
-                        dd_add(hi, lo, (double)xb[k].w * (double)wb[k].w);
-                    }
-                }
-            }
-#pragma unroll
-            for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
-                const double oh = __shfl_xor(hi, off);
-                const double ol = __shfl_xor(lo, off);
-                dd_merge(hi, lo, oh, ol);
-            }
-            const float ye = dd_to_f32(hi, lo);
-            if (row_ok && li == 0) ys[t][lr] = B ? ye + B[head_row(lr)] : ye;
+template <int STYLE>
+__device__ __forceinline__ Unit unit_of(const QkvParams &p, int unit, int pairs_per_unit)
+{
+    Unit u;
+    u.proj = 0;
+    if (unit >= p.units_q) {
+        unit -= p.units_q;
+        u.proj = 1;
+        if (unit >= p.units_kv) {
+            unit -= p.units_kv;
+            u.proj = 2;
         }
     }
-    __syncthreads();
+    u.D = u.proj == 0 ? p.hd : p.hd_kv;
+    u.half = u.D >> 1;
+    const int upr = (u.half + pairs_per_unit - 1) / pairs_per_unit;   // units per head
+    u.head = unit / upr;
+    u.i_begin = (unit - u.head * upr) * pairs_per_unit;
+    u.np = min(pairs_per_unit, u.half - u.i_begin);
+    u.R = 2 * u.np;
+    u.rot = u.proj < 2 && STYLE != kNone;
+    u.neox = u.rot && STYLE == kNeox;
+    return u;
+}
 
-    // RoPE in LDS (q and k), with the append kernel's rotate_pair and table rows.
-    if (rot) {
-        const float2 *tab = proj == 0 ? p.tab_q : p.tab_k;
-        for (int idx = threadIdx.x; idx < ntk * np; idx += blockDim.x) {
-            const int t = idx / np;
-            const int il = idx - t * np;
-            const int lr0 = neox ? il : 2 * il;
-            const int lr1 = neox ? np + il : 2 * il + 1;
-            const float2 cs = tab[(int64_t)p.ipos[t0 + t] * half + i_begin + il];
+// The certified rounding of a plain f64 sum S: |S - exact| <= gamma_m * A for a bound A
+// on the sum of the products' magnitudes and m roundings on the longest chain;
+// err = 4 m u A + 2 u |S| (u = 2^-53) covers that, the rounding of A, and the rounding
+// of S -/+ err themselves.  Rounding to f32 is monotonic, so when both ends of
+// [S - err, S + err] round to the same f32 (bit for bit: a straddled zero has two signs),
+// that f32 is the one nearest the exact sum.  Otherwise (a value within err of an f32
+// rounding boundary, or a non-finite sum) the caller recomputes it exactly.
+__device__ __forceinline__ bool certify(double S, double A, int m, float &y)
+{
+    const double err = 4.0 * (double)m * 0x1p-53 * A + 0x1p-52 * fabs(S);
+    const float lo32 = (float)(S - err), hi32 = (float)(S + err);
+    y = lo32;
+    return __builtin_isfinite(S) && __builtin_isfinite(err) &&
+           __float_as_uint(lo32) == __float_as_uint(hi32);
+}
+
+// The exact f32 projection of x-row xr on weight row wr by 64 lanes (an unevaluated f64
+// pair per lane, TwoSum-merged across the wave, rounded once).
+__device__ float exact_row_wave(const float *xr, const float *wr, int d, int lane)
+{
+    double hi = 0.0, lo = 0.0;
+    for (int i = lane * 4; i < d; i += 4 * 64) {
+        const float4 wb = *reinterpret_cast<const float4 *>(wr + i);
+        const float4 xb = *reinterpret_cast<const float4 *>(xr + i);
+        dd_add(hi, lo, (double)xb.x * (double)wb.x);
+        dd_add(hi, lo, (double)xb.y * (double)wb.y);
+        dd_add(hi, lo, (double)xb.z * (double)wb.z);
+        dd_add(hi, lo, (double)xb.w * (double)wb.w);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oh = __shfl_xor(hi, off);
+        const double ol = __shfl_xor(lo, off);
+        dd_merge(hi, lo, oh, ol);
+    }
+    return dd_to_f32(hi, lo);
+}
+
+// RoPE in LDS (q and k) with the append kernel's rotate_pair and table rows, then the
+// stores: q to q_out, k/v rows to the cache with the append's own binary16 / Q8_0
+// functions.  ys[t][lr] holds the projection (bias added) of local row lr, token t0 + t.
+// Every thread of the block calls it after a barrier that made ys complete.
+template <int STYLE, typename KVT>
+__device__ void finish_unit(const QkvParams &p, const Unit &u, float (*ys)[kMaxRows], int t0,
+                            int ntk)
+{
+    if (u.rot) {
+        const float2 *tab = u.proj == 0 ? p.tab_q : p.tab_k;
+        for (int idx = threadIdx.x; idx < ntk * u.np; idx += blockDim.x) {
+            const int t = idx / u.np;
+            const int il = idx - t * u.np;
+            const int lr0 = u.neox ? il : 2 * il;
+            const int lr1 = u.neox ? u.np + il : 2 * il + 1;
+            const float2 cs = tab[(int64_t)p.ipos[t0 + t] * u.half + u.i_begin + il];
             float y0, y1;
             rotate_pair(ys[t][lr0], ys[t][lr1], cs, y0, y1);
             ys[t][lr0] = y0;
@@ -321,11 +191,11 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
         __syncthreads();
     }
 
-    if (proj == 0) {
-        for (int idx = threadIdx.x; idx < ntk * R; idx += blockDim.x) {
-            const int t = idx / R;
-            const int lr = idx - t * R;
-            p.q_out[((int64_t)(t0 + t) * p.n_head + head) * p.hd + head_row(lr)] = ys[t][lr];
+    if (u.proj == 0) {
+        for (int idx = threadIdx.x; idx < ntk * u.R; idx += blockDim.x) {
+            const int t = idx / u.R;
+            const int lr = idx - t * u.R;
+            p.q_out[((int64_t)(t0 + t) * p.n_head + u.head) * p.hd + u.head_row(lr)] = ys[t][lr];
         }
         return;
     }
@@ -334,14 +204,14 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
     // multiple of 4 for every supported hd_kv); for Q8_0 the R/4 quads of a token are a
     // multiple of 8, so the 8 lanes of a 32-value block are aligned and active together.
     const int nkt = p.n_head_kv * p.hd_kv;
-    char *cache = static_cast<char *>(proj == 1 ? p.kc : p.vc);
-    const int nq = R / 4;
+    char *cache = static_cast<char *>(u.proj == 1 ? p.kc : p.vc);
+    const int nq = u.R / 4;
     for (int idx = threadIdx.x; idx < ntk * nq; idx += blockDim.x) {
         const int t = idx / nq;
         const int qd = idx - t * nq;
         const int lr = 4 * qd;
         const float4 y = make_float4(ys[t][lr], ys[t][lr + 1], ys[t][lr + 2], ys[t][lr + 3]);
-        const int j = head * p.hd_kv + head_row(lr);   // value index in the row
+        const int j = u.head * p.hd_kv + u.head_row(lr);   // value index in the row
         const int64_t reg = ((int64_t)p.iseq[t0 + t] * p.n_layer + p.layer) * p.region_bytes;
         const int64_t row = p.ipos[t0 + t];
         if constexpr (std::is_same<KVT, int8_t>::value) {
@@ -355,15 +225,213 @@ __global__ void __launch_bounds__(256) qkv_kernel(QkvParams p, int32_t pairs_per
     }
 }
 
+// One token: the step streams the weights.  Row lr is reduced by 16 lanes; lane li takes
+// elements 4 li + 64 k, first issuing the loads of up to kBatch pieces of its row (and of
+// x), then doing their arithmetic: the plain f64 sum S of the exact products and A, the
+// sum of their magnitudes.
+template <int STYLE, typename KVT>
+__global__ void __launch_bounds__(256) qkv_one_kernel(QkvParams p, int32_t pairs_per_unit)
+{
+    __shared__ float ys[1][kMaxRows];
+    const Unit u = unit_of<STYLE>(p, blockIdx.x, pairs_per_unit);
+    const float *W = p.w[u.proj] + (int64_t)u.head * u.D * p.d;
+    const float *B = p.b[u.proj] ? p.b[u.proj] + u.head * u.D : nullptr;
+    const float *xr = p.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane % kLanesPerRow;
+    // Longest rounding chain: a lane's ceil(d / 64) * 4 products plus 4 merge levels.
+    const int m = p.d / 16 + 8;
+    for (int base = 0; base < u.R; base += 16) {
+        const int lr = base + wave * 4 + lane / kLanesPerRow;
+        const bool row_ok = lr < u.R;
+        const float *wr = W + (int64_t)u.head_row(row_ok ? lr : 0) * p.d;
+        constexpr int kBatch = 16;
+        double S = 0.0, A = 0.0;
+        for (int i0 = li * 4; i0 < p.d; i0 += kBatch * 4 * kLanesPerRow) {
+            float4 wb[kBatch], xb[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; k++) {
+                const int i = i0 + k * 4 * kLanesPerRow;
+                if (i < p.d) {
+                    wb[k] = *reinterpret_cast<const float4 *>(wr + i);
+                    xb[k] = *reinterpret_cast<const float4 *>(xr + i);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; k++) {
+                if (i0 + k * 4 * kLanesPerRow < p.d) {
+                    const double xv[4] = {xb[k].x, xb[k].y, xb[k].z, xb[k].w};
+                    const double wv[4] = {wb[k].x, wb[k].y, wb[k].z, wb[k].w};
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        S = fma(xv[c], wv[c], S);
+                        A = fma(fabs(xv[c]), fabs(wv[c]), A);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
+            S += __shfl_xor(S, off);
+            A += __shfl_xor(A, off);
+        }
+        float y;
+        const bool certain = certify(S, A, m, y);
+        if (row_ok && li == 0) ys[0][lr] = B ? y + B[u.head_row(lr)] : y;
+        // Exact sum when some row of the wave is unsettled (rare: a value within the
+        // bound of an f32 rounding boundary), 16 lanes per row; x and w come from global
+        // memory (no barrier: the choice is per wave), and the exact value replaces the
+        // stored one (they agree where both exist).
+        if (__any(!certain)) {
+            double hi = 0.0, lo = 0.0;
+            for (int i = li * 4; i < p.d; i += 4 * kLanesPerRow) {
+                const float4 wb = *reinterpret_cast<const float4 *>(wr + i);
+                const float4 xb = *reinterpret_cast<const float4 *>(xr + i);
+                dd_add(hi, lo, (double)xb.x * (double)wb.x);
+                dd_add(hi, lo, (double)xb.y * (double)wb.y);
+                dd_add(hi, lo, (double)xb.z * (double)wb.z);
+                dd_add(hi, lo, (double)xb.w * (double)wb.w);
+            }
+#pragma unroll
+            for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) {
+                const double oh = __shfl_xor(hi, off);
+                const double ol = __shfl_xor(lo, off);
+                dd_merge(hi, lo, oh, ol);
+            }
+            const float ye = dd_to_f32(hi, lo);
+            if (row_ok && li == 0) ys[0][lr] = B ? ye + B[u.head_row(lr)] : ye;
+        }
+    }
+    __syncthreads();
+    finish_unit<STYLE, KVT>(p, u, ys, 0, 1);
+}
+
+// Several tokens (2 .. kInlineTokens): a workgroup takes one unit and one tile of up
+// to 16 tokens (blockIdx.y).  The unit's R rows form nrt tiles of 16 (rows past R repeat
+// row 0 and are dropped; x of absent tokens is 0); each wave takes one row tile and one
+// of ks = 4 / nrt parts of the reduction dimension, and accumulates D[row][token] with
+// v_mfma_f64_16x16x4f64 (A = 16 rows x 4 weight values, B = 4 x values x 16 tokens;
+// A[i][k] and B[k][j] come from lane i + 16 k, resp. j + 16 k, and D[i][j] lands in
+// register i / 4 of lane j + 16 (i % 4) -- checked on the hardware).  Within a group of
+// 16 reduction indices, step c of the 4 takes index 4 k + c in slot k, so a lane's 4
+// values of a group are one float4 of its weight row and one of its token's x row.
+// Products of f32 values are exact in f64; per output, a wave's chain has at most kper
+// additions (4 per step, however the matrix core orders them) and the ks partials add
+// ks - 1 more.  The error bound takes A = |x|_2 |w|_2 (1 + 2^-30) (Cauchy-Schwarz),
+// from f64 sums of squares, each within a relative gamma_d of its exact value, far
+// inside the margin; a bound that is less tight only sends more values to the exact path.
+template <int STYLE, typename KVT>
+__global__ void __launch_bounds__(256) qkv_mfma_kernel(QkvParams p, int32_t pairs_per_unit)
+{
+    constexpr int TM = 16;   // tokens per workgroup
+    __shared__ float ys[TM][kMaxRows];
+    __shared__ double sp[4][16 * TM];      // per wave: D[i][t] at i * TM + t
+    __shared__ double swq[4][16];          // per wave: sum of w^2 of its tile's rows
+    __shared__ double sxq[4][TM];          // per wave: sum of x^2 of each token
+    __shared__ unsigned long long s_unsure[TM];   // per token: rows to recompute exactly
+
+    const Unit u = unit_of<STYLE>(p, blockIdx.x, pairs_per_unit);
+    const float *W = p.w[u.proj] + (int64_t)u.head * u.D * p.d;
+    const float *B = p.b[u.proj] ? p.b[u.proj] + u.head * u.D : nullptr;
+    const int t0 = blockIdx.y * TM;
+    const int ntk = min(TM, p.nt - t0);
+    const int nrt = (u.R + 15) >> 4;
+    const int ks = 4 / nrt;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, kk = lane >> 4;
+    const int rt = wave % nrt, kp = wave / nrt;
+    const bool active = kp < ks;
+    const int kper = (p.d + 16 * ks - 1) / (16 * ks) * 16;   // reduction indices per part
+    const int kb = kp * kper, ke = min(p.d, kb + kper);
+    if (threadIdx.x < TM) s_unsure[threadIdx.x] = 0ull;
+
+    doublex4 acc = doublex4{0.0, 0.0, 0.0, 0.0};
+    double wsq = 0.0, xsq = 0.0;
+    if (active) {
+        const int lr = rt * 16 + l16;
+        const float *wr = W + (int64_t)u.head_row(lr < u.R ? lr : 0) * p.d;
+        const float *xr = l16 < ntk ? p.x + (int64_t)(t0 + l16) * p.d : nullptr;
+        // Groups of 16 reduction indices, kG at a time: all their loads are issued
+        // before any of their products.
+        constexpr int kG = 4;
+        for (int g0 = kb; g0 < ke; g0 += 16 * kG) {
+            float4 wv[kG], xv[kG];
+#pragma unroll
+            for (int g = 0; g < kG; g++) {
+                const int e = g0 + 16 * g + 4 * kk;   // e < ke implies e + 3 < ke
+                const bool in = e < ke;
+                wv[g] = in ? *reinterpret_cast<const float4 *>(wr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+                xv[g] = (in && xr) ? *reinterpret_cast<const float4 *>(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int g = 0; g < kG; g++) {
+                const double w4[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
+                const double x4[4] = {xv[g].x, xv[g].y, xv[g].z, xv[g].w};
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    wsq = fma(w4[c], w4[c], wsq);
+                    xsq = fma(x4[c], x4[c], xsq);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(w4[c], x4[c], acc, 0, 0, 0);
+                }
+            }
+        }
+        // Lane (l16, kk) holds its slot's share of row l16's and token l16's squares.
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            wsq += __shfl_xor(wsq, off);
+            xsq += __shfl_xor(xsq, off);
+        }
+        if (kk == 0) {
+            swq[wave][l16] = wsq;
+            sxq[wave][l16] = xsq;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) sp[wave][(4 * r + kk) * TM + l16] = acc[r];
+    }
+    __syncthreads();
+
+    // Sum the parts (in part order), certify, and mark what needs the exact path.
+    const int m = kper + ks + 8;
+    for (int idx = threadIdx.x; idx < u.R * ntk; idx += blockDim.x) {
+        const int lr = idx / ntk;
+        const int t = idx - lr * ntk;
+        const int trt = lr >> 4, i = lr & 15;
+        double S = 0.0, w2 = 0.0, x2 = 0.0;
+        for (int q = 0; q < ks; q++) {
+            const int w = trt + q * nrt;
+            S += sp[w][i * TM + t];
+            w2 += swq[w][i];
+            x2 += sxq[q * nrt][t];
+        }
+        const double A = sqrt(x2) * sqrt(w2) * (1.0 + 0x1p-30);
+        float y;
+        if (!certify(S, A, m, y)) atomicOr(&s_unsure[t], 1ull << lr);
+        ys[t][lr] = B ? y + B[u.head_row(lr)] : y;
+    }
+    __syncthreads();
+
+    // Exact path for the marked (row, token) pairs: wave w takes tokens w, w + 4, ...
+    for (int t = wave; t < ntk; t += 4) {
+        unsigned long long rows = s_unsure[t];
+        while (rows) {
+            const int lr = __builtin_ctzll(rows);
+            rows &= rows - 1;
+            const float ye = exact_row_wave(p.x + (int64_t)(t0 + t) * p.d,
+                                            W + (int64_t)u.head_row(lr) * p.d, p.d, lane);
+            if (lane == 0) ys[t][lr] = B ? ye + B[u.head_row(lr)] : ye;
+        }
+    }
+    __syncthreads();
+    finish_unit<STYLE, KVT>(p, u, ys, t0, ntk);
+}
+
 template <int STYLE, typename KVT>
 void launch_style_fmt(const QkvParams &p, int32_t ppu, hipStream_t s)
 {
     const int units = p.units_q + 2 * p.units_kv;
-    if (p.nt == 1) {
-        qkv_kernel<STYLE, KVT, 1><<<dim3(units, 1), 256, 0, s>>>(p, ppu);
-    } else {
-        qkv_kernel<STYLE, KVT, 8><<<dim3(units, (p.nt + 7) / 8), 256, 0, s>>>(p, ppu);
-    }
+    if (p.nt == 1) qkv_one_kernel<STYLE, KVT><<<dim3(units), 256, 0, s>>>(p, ppu);
+    else qkv_mfma_kernel<STYLE, KVT><<<dim3(units, (p.nt + 15) / 16), 256, 0, s>>>(p, ppu);
 }
 
 template <typename KVT>

@@ -101,14 +101,16 @@ def test_exact_dot_products():
     p.close()
 
 
-def test_rounding_boundaries():
+@pytest.mark.parametrize("nt", [1, 3], ids=["one_token", "three_tokens"])
+def test_rounding_boundaries(nt):
     """Dot products at or within 2^-80 of an f32 rounding boundary (a plain f64 sum cannot
     tell which way they round) and one comfortably inside an f32 interval, with values
-    worked out by hand: x = (1, 2^-24, 2^-60, 0, ...)."""
-    say("fused qkv rounding boundaries")
+    worked out by hand: x = (1, 2^-24, 2^-60, 0, ...) for every token (one token and the
+    several-token path)."""
+    say(f"fused qkv rounding boundaries nt={nt}")
     d, nh, nkv, hd = 128, 2, 1, 16
-    x = np.zeros((1, d), np.float32)
-    x[0, :3] = [1.0, 2.0 ** -24, 2.0 ** -60]
+    x = np.zeros((nt, d), np.float32)
+    x[:, :3] = [1.0, 2.0 ** -24, 2.0 ** -60]
     wq, _, wk, _, wv, _ = weights(350, d, nh, hd, nkv, hd, bias=False)
     rows = {0: ([1, 1, 0], 1.0),                              # 1 + 2^-24: tie -> even (1)
             1: ([1, 1, 2.0 ** -20], 1.0 + 2.0 ** -23),        # tie + 2^-80 -> up
@@ -119,10 +121,12 @@ def test_rounding_boundaries():
         wq[r] = 0.0
         wq[r, :3] = w3
     p = Pair(1, 1, nkv, hd, 8)
-    qg, qo = p.qkv(0, [0], [0], x, (wq, None, wk, None, wv, None), nh, hd, 1e4, 1.0, 2)
+    qg, qo = p.qkv(0, [0] * nt, list(range(nt)), x, (wq, None, wk, None, wv, None), nh, hd,
+                   1e4, 1.0, 2)
     assert_bitwise(qg, qo, "q (no rotation)")
-    for r, (_, want) in rows.items():
-        assert qg[0, 0, r] == np.float32(want), (r, qg[0, 0, r], want)
+    for t in range(nt):
+        for r, (_, want) in rows.items():
+            assert qg[t, 0, r] == np.float32(want), (t, r, qg[t, 0, r], want)
     compare_cache(p.g, p.o, 0, 0, "k/v")
     p.close()
 
