@@ -584,7 +584,7 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 
 }  // namespace
 
-int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt)
+int32_t decode_block_rows(int32_t hd_kv)
 {
     // The largest of the lane layouts' step sizes (all are powers of two): a wave covers
     // 64 * dims / hd_kv rows per unrolled row, and dims * rows_per_step is at most 32.

@@ -100,7 +100,7 @@ struct DecodeParams {
 };
 // Rows per block iteration of the split-K kernel for a kv head dim (chunks should be a
 // multiple of it).
-int32_t decode_block_rows(int32_t hd_kv, int32_t kv_fmt);
+int32_t decode_block_rows(int32_t hd_kv);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
