@@ -23,8 +23,9 @@
 // cache, so that a unit holds whole 32-value blocks) of one head of q, k or v -- for all
 // the call's tokens.  NEOX pairs (i, i + D/2) and interleaved pairs (2i, 2i+1) of a unit
 // are computed together, so the rotation happens in LDS without another launch.
-//   * One token (qkv_one_kernel): rows are reduced by 16 lanes each (four rows per wave
-//     at a time), every lane streaming 16-byte pieces of its row.
+//   * Up to 4 tokens (qkv_one_kernel, one workgroup per unit and token): rows are
+//     reduced by 16 lanes each (four rows per wave at a time), every lane streaming
+//     16-byte pieces of its row.
 //   * Several tokens (qkv_mfma_kernel, one workgroup per unit and tile of 16 tokens):
 //     the unit's rows times the tokens' x as f64 matrix products
 //     (v_mfma_f64_16x16x4f64), so each operand a lane holds feeds 16 products.
@@ -42,6 +43,7 @@ namespace {
 constexpr int kNeox = 0, kInterleaved = 1, kNone = 2;
 constexpr int kMaxRows = 64;   // rows of a unit (32 pairs)
 constexpr int kLanesPerRow = 16;
+constexpr int kOneTokenMax = 4;   // up to this many tokens: a workgroup per (unit, token)
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // Error-free sum: s + e == a + b exactly (s = fl(a + b)).
@@ -225,10 +227,10 @@ __device__ void finish_unit(const QkvParams &p, const Unit &u, float (*ys)[kMaxR
     }
 }
 
-// One token: the step streams the weights.  Row lr is reduced by 16 lanes; lane li takes
-// elements 4 li + 64 k, first issuing the loads of up to kBatch pieces of its row (and of
-// x), then doing their arithmetic: the plain f64 sum S of the exact products and A, the
-// sum of their magnitudes.
+// One token per workgroup (token blockIdx.y): the step streams the weights.  Row lr is
+// reduced by 16 lanes; lane li takes elements 4 li + 64 k, first issuing the loads of up
+// to kBatch pieces of its row (and of x), then doing their arithmetic: the plain f64 sum
+// S of the exact products and A, the sum of their magnitudes.
 template <int STYLE, typename KVT>
 __global__ void __launch_bounds__(256) qkv_one_kernel(QkvParams p, int32_t pairs_per_unit)
 {
@@ -236,7 +238,8 @@ __global__ void __launch_bounds__(256) qkv_one_kernel(QkvParams p, int32_t pairs
     const Unit u = unit_of<STYLE>(p, blockIdx.x, pairs_per_unit);
     const float *W = p.w[u.proj] + (int64_t)u.head * u.D * p.d;
     const float *B = p.b[u.proj] ? p.b[u.proj] + u.head * u.D : nullptr;
-    const float *xr = p.x;
+    const int t0 = blockIdx.y;
+    const float *xr = p.x + (int64_t)t0 * p.d;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int li = lane % kLanesPerRow;
@@ -304,7 +307,7 @@ __global__ void __launch_bounds__(256) qkv_one_kernel(QkvParams p, int32_t pairs
         }
     }
     __syncthreads();
-    finish_unit<STYLE, KVT>(p, u, ys, 0, 1);
+    finish_unit<STYLE, KVT>(p, u, ys, t0, 1);
 }
 
 // Several tokens (2 .. kInlineTokens): a workgroup takes one unit and one tile of up
@@ -430,7 +433,7 @@ template <int STYLE, typename KVT>
 void launch_style_fmt(const QkvParams &p, int32_t ppu, hipStream_t s)
 {
     const int units = p.units_q + 2 * p.units_kv;
-    if (p.nt == 1) qkv_one_kernel<STYLE, KVT><<<dim3(units), 256, 0, s>>>(p, ppu);
+    if (p.nt <= kOneTokenMax) qkv_one_kernel<STYLE, KVT><<<dim3(units, p.nt), 256, 0, s>>>(p, ppu);
     else qkv_mfma_kernel<STYLE, KVT><<<dim3(units, (p.nt + 15) / 16), 256, 0, s>>>(p, ppu);
 }
 

@@ -101,12 +101,12 @@ def test_exact_dot_products():
     p.close()
 
 
-@pytest.mark.parametrize("nt", [1, 3], ids=["one_token", "three_tokens"])
+@pytest.mark.parametrize("nt", [1, 3, 5], ids=["one_token", "three_tokens", "five_tokens"])
 def test_rounding_boundaries(nt):
     """Dot products at or within 2^-80 of an f32 rounding boundary (a plain f64 sum cannot
     tell which way they round) and one comfortably inside an f32 interval, with values
-    worked out by hand: x = (1, 2^-24, 2^-60, 0, ...) for every token (one token and the
-    several-token path)."""
+    worked out by hand: x = (1, 2^-24, 2^-60, 0, ...) for every token (up to 4 tokens take
+    a workgroup per token, more the fp64 matrix-core path)."""
     say(f"fused qkv rounding boundaries nt={nt}")
     d, nh, nkv, hd = 128, 2, 1, 16
     x = np.zeros((nt, d), np.float32)
