@@ -26,7 +26,7 @@ def case(seed):
                 kv=int(rng.choice(fmts)), style=int(rng.integers(0, 3)), rng=rng)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(200))
 def test_random_case(seed):
     c = case(seed)
     rng = c.pop("rng")
