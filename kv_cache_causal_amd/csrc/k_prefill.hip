@@ -135,7 +135,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     static_assert(LD * 256 * CH == KT * HD && LD >= 1, "tile split");
     __shared__ float Ks[KT * KSTR];
     __shared__ float Vs[KT * VSTR];
-    __shared__ int s_kmax;
+    __shared__ int s_kmax, s_kmin;
+    __shared__ int s_vbad;   // 1 once a tile of this block held a non-finite V value
 
     // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
     // takes logical block (b % 8) * (nblocks / 8) + b / 8.  Each XCD then owns a
@@ -180,11 +181,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     const int pq = tok_ok ? p.pos[t] : 0;
 
     // Largest position among this block's tokens.
-    if (tid == 0) s_kmax = 0;
+    if (tid == 0) {
+        s_kmax = 0;
+        s_kmin = 0x7fffffff;
+        s_vbad = 0;
+    }
     __syncthreads();
     if (tid < TQ) {
         const int tt = qtile * TQ + tid;
-        if (tt < p.nt) atomicMax(&s_kmax, p.pos[tt]);
+        if (tt < p.nt) {
+            atomicMax(&s_kmax, p.pos[tt]);
+            atomicMin(&s_kmin, p.pos[tt]);
+        }
     }
     // Smallest and largest position among this wave's 16 tokens (invalid columns do not
     // count towards the minimum).
@@ -210,7 +218,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     float m = -INFINITY, l = 0.0f;
 
     __syncthreads();
-    const int kmax = s_kmax;
+    const int kmax = s_kmax, kmin = s_kmin;
     if (!p.units) kt1 = kmax / KT + 1;
     const int nkt = p.n_head_kv * HD;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
@@ -247,6 +255,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         // every query; they are stored as zeros, so that a non-finite value in a row no
         // window of the block contains cannot turn 0 * V into NaN.
         const bool tail = key0 + KT - 1 > kmax;
+        // Tiles reaching past the smallest position hold keys some query must not weigh.
+        const bool diag = key0 + KT - 1 > kmin;
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int j = 0; j < LD; j++) {
@@ -255,6 +265,26 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
         }
         __syncthreads();
+        // In such a tile a non-finite V value becomes 0 (its neighbours unchanged; each
+        // thread cleans the chunks it stored) and the block is flagged: 0 * inf in the
+        // products would turn the zero weight of a query whose window does not hold it
+        // into NaN; the queries whose windows hold one add it at the end.  In the other
+        // tiles every weight is positive and the products carry inf and NaN as they are.
+        if (diag) {
+            bool vbad = false;
+#pragma unroll
+            for (int j = 0; j < LD; j++) {
+                float *vp = &Vs[(trow + j * RSTEP) * VSTR + tcol];
+#pragma unroll
+                for (int i = 0; i < CH; i++) {
+                    const bool f = __builtin_isfinite(vp[i]);
+                    vbad |= !f;
+                    if (!f) vp[i] = 0.0f;
+                }
+            }
+            if (vbad) s_vbad = 1;
+            __syncthreads();
+        }
         if (kt + 1 < kt1) fetch(key0 + KT);
 
         if (head_ok && key0 <= wmax) {
@@ -354,6 +384,25 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                     oacc[db] = mfma4(vbuf[st & 1][db], sv[st >> 2][st & 3], oacc[db]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        }
+    }
+
+    // Non-finite V values inside this lane's window (keys of this unit's tiles up to its
+    // position): the weighted sum is non-finite whatever their (positive) weights, and
+    // adding the values themselves gives the same inf, -inf or NaN (adding again one that
+    // the products already carried changes nothing).  The flag was set before the last
+    // tile's barrier, so every wave reads the same value.
+    if (s_vbad && head_ok && tok_ok) {
+        const int kend = min(kt1 * KT, pq + 1);
+        for (int key = kt0 * KT; key < kend; key++) {
+            const KVT *vrow = Vh + (int64_t)key * nkt;
+#pragma unroll
+            for (int db = 0; db < NDB; db++)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    const float v = (float)vrow[16 * VEC * (db / VEC) + VEC * (4 * grp + rr) + db % VEC];
+                    if (!__builtin_isfinite(v)) oacc[db][rr] += v;
+                }
         }
     }
 

@@ -294,6 +294,35 @@ def test_non_finite_rows_outside_every_window(kv):
     p.close()
 
 
+@pytest.mark.parametrize("kv", [0, 1, 2], ids=["f32", "f16", "q8_0"])
+def test_non_finite_values_inside_the_prompt(kv):
+    """A prompt whose later tokens' v rows hold inf, -inf and NaN: the earlier queries
+    share those rows' key tile (the causal diagonal) but not their windows, so their
+    results stay finite and match the oracle; the later queries' results are non-finite
+    exactly where the oracle's are (same inf / -inf / NaN)."""
+    say(f"non-finite values inside the prompt, kv {kv}")
+    nh, nkv, hd, nt, first_bad = 4, 2, 64, 48, 30
+    p = Pair(1, 1, nkv, hd, 128, dtype=kv)
+    k, v = custom(110, (nt, nkv, hd)), custom(111, (nt, nkv, hd))
+    big = 1e7 if kv == 2 else np.inf      # Q8_0: a block whose scale overflows
+    rng = np.random.default_rng(112)
+    pick = rng.integers(0, 4, v[first_bad:].shape)
+    v[first_bad:] = np.where(pick == 0, big, np.where(pick == 1, -big, v[first_bad:]))
+    if kv != 2:
+        v[first_bad + 3, 0, 5] = np.nan
+    p.append(0, [0] * nt, np.arange(nt, dtype=np.int32), None, nh, hd, k, v)
+    qp = custom(113, (nt, nh, hd))
+    got, want = p.prefill(0, 0, np.arange(nt, dtype=np.int32), dev(qp), qp, nh, hd, 0.125)
+    assert_close(got[:first_bad], want[:first_bad], "queries before the non-finite rows")
+    g, w = got[first_bad:], want[first_bad:]
+    assert not np.isfinite(w).all(), "the case must reach non-finite results"
+    assert np.array_equal(np.isnan(g), np.isnan(w)), "NaN pattern"
+    assert np.array_equal(np.isposinf(g), np.isposinf(w)) and np.array_equal(np.isneginf(g), np.isneginf(w)), "inf pattern"
+    fin = np.isfinite(w)
+    assert_close(np.where(fin, g, 0.0), np.where(fin, w, 0.0), "finite part of the later queries")
+    p.close()
+
+
 def test_q8_geometry_is_checked():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_alloc(1, 1, 2, 16, 64, dtype=kvc.KV_Q8_0)
