@@ -294,15 +294,19 @@ def test_non_finite_rows_outside_every_window(kv):
     p.close()
 
 
+@pytest.mark.parametrize("nt,first_bad,seg", [(48, 30, 0), (200, 150, 0), (200, 150, 1)],
+                         ids=["48_tokens", "200_tokens", "200_tokens_split"])
 @pytest.mark.parametrize("kv", [0, 1, 2], ids=["f32", "f16", "q8_0"])
-def test_non_finite_values_inside_the_prompt(kv):
+def test_non_finite_values_inside_the_prompt(monkeypatch, kv, nt, first_bad, seg):
     """A prompt whose later tokens' v rows hold inf, -inf and NaN: the earlier queries
     share those rows' key tile (the causal diagonal) but not their windows, so their
     results stay finite and match the oracle; the later queries' results are non-finite
-    exactly where the oracle's are (same inf / -inf / NaN)."""
-    say(f"non-finite values inside the prompt, kv {kv}")
-    nh, nkv, hd, nt, first_bad = 4, 2, 64, 48, 30
-    p = Pair(1, 1, nkv, hd, 128, dtype=kv)
+    exactly where the oracle's are (same inf / -inf / NaN).  Also with every key tile a
+    segment of its own (split-K records and their merge carrying the values)."""
+    say(f"non-finite values inside the prompt, kv {kv}, nt {nt}, seg {seg}")
+    monkeypatch.setenv("KVC_PREFILL_SEG", str(seg))
+    nh, nkv, hd = 4, 2, 64
+    p = Pair(1, 1, nkv, hd, 256, dtype=kv)
     k, v = custom(110, (nt, nkv, hd)), custom(111, (nt, nkv, hd))
     big = 1e7 if kv == 2 else np.inf      # Q8_0: a block whose scale overflows
     rng = np.random.default_rng(112)
