@@ -247,8 +247,9 @@ kvc_status kv_qkv_rope_append(kvc_cache *c, int32_t layer, int32_t nt, const int
  * 64-query tile's key range split across workgroups whose (max, sum, output) records are
  * merged by log-sum-exp (§2.5's split, as in gqa_attn_decode); the records live in the
  * handle's scratch memory, which grows on demand (KVC_E_NOMEM if it cannot).  With a
- * Q8_0 cache, K and V rows [0, 64 * ceil((max pos + 1) / 64)) are first dequantized into
- * f32 scratch (8 bytes per value pair; same growth and error), which the attention reads.
+ * binary16 or Q8_0 cache, K and V rows [0, 64 * ceil((max pos + 1) / 64)) are first
+ * widened / dequantized into f32 scratch (8 bytes per value pair; same growth and error),
+ * which the attention reads.
  * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE (a position >= capacity), KVC_E_NOMEM,
  * KVC_E_HIP.
  */

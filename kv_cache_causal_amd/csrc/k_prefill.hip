@@ -31,9 +31,9 @@
 //     segments (same tile count each, the last one shorter); a workgroup scans one
 //     segment and writes its unnormalised (m, l, O) record, and a merge kernel combines a
 //     query's records by log-sum-exp (split-K, as for decode).
-//   * Region formats: binary16 is widened while a tile is copied into LDS; a Q8_0
-//     window is dequantized once (scale * code, exact in f32) into an f32 copy that the
-//     f32 kernel reads, so the products always see f32 values.
+//   * Region formats: a binary16 window is widened, a Q8_0 window dequantized (scale *
+//     code, exact in f32), once into an f32 copy that the f32 kernel reads, so the
+//     products always see f32 values.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -72,7 +72,6 @@ struct PrefillCfg {
     static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
 };
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
 
 // Signed byte k of w as f32 (one conversion with a sign-extending byte select).
@@ -102,19 +101,6 @@ struct TileIO<HD, float> {
         *reinterpret_cast<floatx4 *>(lds) = r;
     }
 };
-template <int HD>
-struct TileIO<HD, _Float16> {
-    static constexpr int CH = PrefillCfg<HD>::KT * HD / 256 >= 8 ? 8 : 4;
-    typedef typename std::conditional<CH == 8, half8_t, half4_t>::type Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r)
-    {
-        *reinterpret_cast<floatx4 *>(lds) = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
-        if constexpr (CH == 8)
-            *reinterpret_cast<floatx4 *>(lds + 4) =
-                floatx4{(float)r[4], (float)r[5], (float)r[6], (float)r[7]};
-    }
-};
-
 // Split-K record of one (segment, token, head): O[HD] unnormalised, then m (base 2), l and,
 // in segment 0's record, the token's segment count.
 template <int HD>
@@ -514,7 +500,20 @@ hipError_t launch_hd_t(const PrefillParams &p, hipStream_t s)
 template <int HD>
 hipError_t launch_hd(const PrefillParams &p, hipStream_t s)
 {
-    return p.kv_fmt == kFmtF16 ? launch_hd_t<HD, _Float16>(p, s) : launch_hd_t<HD, float>(p, s);
+    return launch_hd_t<HD, float>(p, s);
+}
+
+// binary16 regions: rows [0, dq_rows) of the window widened once into an f32 copy (each
+// thread 4 consecutive values; blockIdx.y = 0 the K region, 1 the V region after it).
+__global__ void __launch_bounds__(256) widen_f16_kernel(const _Float16 *kreg, const _Float16 *vreg,
+                                                        int64_t n4, float *dst)
+{
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= n4) return;
+    const _Float16 *src = blockIdx.y ? vreg : kreg;
+    const half4_t h = reinterpret_cast<const half4_t *>(src)[g];
+    reinterpret_cast<floatx4 *>(dst + blockIdx.y * n4 * 4)[g] =
+        floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
 
 // Q8_0 regions: rows [0, dq_rows) of the window are dequantized once into an f32 copy
@@ -562,20 +561,24 @@ hipError_t launch_by_hd(const PrefillParams &p, hipStream_t s)
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {
     if (p.nt <= 0) return hipSuccess;
-    if (p.kv_fmt != kFmtQ8) return launch_by_hd(p, s);
+    if (p.kv_fmt == kFmtF32) return launch_by_hd(p, s);
     if (!p.dq || p.dq_rows <= 0) return hipErrorInvalidValue;
     const int32_t nkt = p.n_head_kv * p.hd_kv;
     const int64_t vals = (int64_t)p.dq_rows * nkt;
     const int64_t n4 = vals / 4;
-    const unsigned blocks = (unsigned)((n4 + 1023) / 1024);
     PrefillParams f = p;
     f.kc = p.dq;
     f.vc = p.dq + vals;
     f.kv_fmt = kFmtF32;
     f.scale_off = 0;
-    dequant_q8_kernel<<<dim3(blocks, 2), dim3(256), 0, s>>>(
-        static_cast<const char *>(p.kc), static_cast<const char *>(p.vc), p.scale_off, nkt,
-        p.hd_kv, n4, p.dq);
+    if (p.kv_fmt == kFmtQ8) {
+        dequant_q8_kernel<<<dim3((unsigned)((n4 + 1023) / 1024), 2), dim3(256), 0, s>>>(
+            static_cast<const char *>(p.kc), static_cast<const char *>(p.vc), p.scale_off, nkt,
+            p.hd_kv, n4, p.dq);
+    } else {
+        widen_f16_kernel<<<dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s>>>(
+            static_cast<const _Float16 *>(p.kc), static_cast<const _Float16 *>(p.vc), n4, p.dq);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_by_hd(f, s);

@@ -80,7 +80,7 @@ struct kvc_cache {
     mutable std::vector<RopeTable> tables;
     mutable float *part = nullptr;  // split-K partials
     mutable size_t part_cap = 0;    // floats
-    mutable float *dq = nullptr;    // Q8_0 prefill: the window's K and V dequantized to f32
+    mutable float *dq = nullptr;    // binary16 / Q8_0 prefill: the window's K and V as f32
     mutable size_t dq_cap = 0;      // floats
 };
 
@@ -568,14 +568,15 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
         st = ensure_part(c, (size_t)pl.max_seg * nt * n_head * (c->g.hd_kv + 4), s);
         if (st != KVC_OK) return st;
     }
-    // Q8_0: the kernels read an f32 copy of rows [0, dq_rows) (whole 64-row groups up to
-    // the largest position), written by a dequantization pass on the same stream.
+    // binary16 and Q8_0: the kernels read an f32 copy of rows [0, dq_rows) (whole 64-row
+    // groups up to the largest position), written by a widening / dequantization pass on
+    // the same stream.
     int32_t dq_rows = 0;
-    if (c->kv_fmt == kvc::kFmtQ8) {
+    if (c->kv_fmt != kvc::kFmtF32) {
         const int32_t top = *std::max_element(pos, pos + nt) + 1;
         dq_rows = (top + kvc::kRegionRowAlign - 1) / kvc::kRegionRowAlign * kvc::kRegionRowAlign;
         const size_t nkt = (size_t)c->g.n_head_kv * c->g.hd_kv;
-        st = ensure_scratch(c->dq, c->dq_cap, 2 * (size_t)dq_rows * nkt, s, "Q8_0 window");
+        st = ensure_scratch(c->dq, c->dq_cap, 2 * (size_t)dq_rows * nkt, s, "f32 window copy");
         if (st != KVC_OK) return st;
     }
     const int32_t *dev = nullptr;

@@ -112,7 +112,7 @@ struct PrefillParams {
     const int32_t *pos;      // device [nt]
     const int32_t *units;    // device copy of plan.units, or nullptr (no split)
     float *part;             // split only: [max_seg][nt][n_head][hd_kv + 4]: O, m, l, nseg
-    float *dq;               // Q8_0 only: f32 copies of rows [0, dq_rows) of K, then of V
+    float *dq;               // binary16 / Q8_0: f32 copies of rows [0, dq_rows) of K, then V
     int32_t dq_rows;         // a multiple of 64 covering every position of the call
     int32_t nt, n_head, hd, n_head_kv, hd_kv, capacity, kv_fmt;
     int32_t GB, TQ, n_qtiles, n_hsub, units_per_hgroup;
