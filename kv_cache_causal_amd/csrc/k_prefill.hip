@@ -87,9 +87,9 @@ __device__ __forceinline__ float code_to_f32(int32_t w, int k)
     return f;
 }
 
-// How the 256 threads stage one K or V tile (KT rows x HD values) from a region of KVT
-// elements into the f32 LDS tile: each thread moves NCH chunks of CH consecutive values
-// (one load each), widening binary16 to f32 on the way.
+// How the 256 threads stage one K or V tile (KT rows x HD values) from an f32 region (or
+// the f32 copy of a binary16 / Q8_0 window) into the LDS tile: each thread moves LD
+// chunks of CH consecutive values, one 16-byte load each.
 template <int HD, typename KVT>
 struct TileIO;
 template <int HD>
