@@ -355,11 +355,11 @@ __global__ void __launch_bounds__(256) qkv_mfma_kernel(QkvParams p, int32_t pair
         const int lr = rt * 16 + l16;
         const float *wr = W + (int64_t)u.head_row(lr < u.R ? lr : 0) * p.d;
         const float *xr = l16 < ntk ? p.x + (int64_t)(t0 + l16) * p.d : nullptr;
-        // Groups of 16 reduction indices, kG at a time: all their loads are issued
-        // before any of their products.
+        // Groups of 16 reduction indices, kG at a time, in two register sets: the loads
+        // of the next batch are in flight while this one's products run.
         constexpr int kG = 4;
-        for (int g0 = kb; g0 < ke; g0 += 16 * kG) {
-            float4 wv[kG], xv[kG];
+        float4 wA[kG], xA[kG], wB[kG], xB[kG];
+        auto load = [&](float4 (&wv)[kG], float4 (&xv)[kG], int g0) {
 #pragma unroll
             for (int g = 0; g < kG; g++) {
                 const int e = g0 + 16 * g + 4 * kk;   // e < ke implies e + 3 < ke
@@ -367,6 +367,8 @@ __global__ void __launch_bounds__(256) qkv_mfma_kernel(QkvParams p, int32_t pair
                 wv[g] = in ? *reinterpret_cast<const float4 *>(wr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
                 xv[g] = (in && xr) ? *reinterpret_cast<const float4 *>(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
+        };
+        auto products = [&](const float4 (&wv)[kG], const float4 (&xv)[kG]) {
 #pragma unroll
             for (int g = 0; g < kG; g++) {
                 const double w4[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
@@ -378,6 +380,15 @@ __global__ void __launch_bounds__(256) qkv_mfma_kernel(QkvParams p, int32_t pair
                     acc = __builtin_amdgcn_mfma_f64_16x16x4f64(w4[c], x4[c], acc, 0, 0, 0);
                 }
             }
+        };
+        const int nb = (ke - kb + 16 * kG - 1) / (16 * kG);   // batches (0 if kb >= ke)
+        if (nb > 0) load(wA, xA, kb);
+        for (int b = 0; b < nb; b += 2) {
+            if (b + 1 < nb) load(wB, xB, kb + (b + 1) * 16 * kG);
+            products(wA, xA);
+            if (b + 1 >= nb) break;
+            if (b + 2 < nb) load(wA, xA, kb + (b + 2) * 16 * kG);
+            products(wB, xB);
         }
         // Lane (l16, kk) holds its slot's share of row l16's and token l16's squares.
 #pragma unroll
