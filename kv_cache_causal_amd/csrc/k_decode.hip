@@ -584,11 +584,30 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 
 }  // namespace
 
-int32_t decode_block_rows(int32_t hd_kv)
+namespace {
+// Rows per step of the split kernel for a query-head group of GP: a wave covers 64 * dims
+// / hd_kv rows per unrolled row.
+template <int GP, typename KVT>
+int32_t step_rows(int32_t hd_kv)
 {
-    // The largest of the lane layouts' step sizes (all are powers of two): a wave covers
-    // 64 * dims / hd_kv rows per unrolled row, and dims * rows_per_step is at most 32.
-    return kWaves * 64 * 32 / hd_kv;
+    return kWaves * (64 * dims_per_lane<GP, KVT>() / hd_kv) * rows_per_step<GP, KVT>();
+}
+template <typename KVT>
+int32_t step_rows_fmt(int32_t hd_kv, int32_t G)
+{
+    // The group of the first pass (launch_split): 8 heads from 5 up, then 4, 2, 1.
+    if (G >= 5) return step_rows<8, KVT>(hd_kv);
+    if (G >= 3) return step_rows<4, KVT>(hd_kv);
+    if (G == 2) return step_rows<2, KVT>(hd_kv);
+    return step_rows<1, KVT>(hd_kv);
+}
+}  // namespace
+
+int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt)
+{
+    if (kv_fmt == kFmtQ8) return step_rows_fmt<int8_t>(hd_kv, G);
+    if (kv_fmt == kFmtF16) return step_rows_fmt<_Float16>(hd_kv, G);
+    return step_rows_fmt<float>(hd_kv, G);
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)

@@ -245,7 +245,7 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         return t;
     };
     // Chunk size (plan.cpp); KVC_SPLIT_ROWS overrides it (tuning only, never the result).
-    const int32_t br = kvc::decode_block_rows(c->g.hd_kv);
+    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, n_head / c->g.n_head_kv, c->kv_fmt);
     int64_t total_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) total_rows += window_rows(b);
     const int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, env_split_rows());

@@ -98,9 +98,10 @@ struct DecodeParams {
     int32_t seq[kInlineEntries];
     int32_t cbase[kInlineEntries + 1];  // first chunk of entry b; cbase[n] = total_chunks
 };
-// Rows per block iteration of the split-K kernel for a kv head dim (chunks should be a
+// Rows per step of the split-K kernel that a call with query-head group G (n_head /
+// n_head_kv) launches first, for a kv head dim and region format (chunks should be a
 // multiple of it).
-int32_t decode_block_rows(int32_t hd_kv);
+int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
