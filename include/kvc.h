@@ -24,14 +24,33 @@
  *     ordinary host memory, read before the call returns (the caller may reuse them at
  *     once).  Device buffers must stay valid until the work queued on `stream` is done.
  *   - Device pointers must be 16-byte aligned and the tensors dense (row-major, no gaps).
- *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only queues work;
- *     nothing synchronises with the host except kv_alloc / kv_free.  Calls on one handle
- *     must be issued from one host thread onto one stream (or be otherwise ordered):
- *     the handle's staging and scratch memory is reused call after call.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls queue work and return;
+ *     kv_alloc and kv_free wait for the device.  The other calls make the host wait only
+ *     when handle-owned memory must grow or be reused:
+ *       * a scratch buffer grows (split-K records of gqa_attn_prefill / gqa_attn_decode /
+ *         gqa_attn_decode_runs, or the f32 window copy of a binary16 / Q8_0 prefill): the
+ *         library waits for `stream` (hipStreamSynchronize) before freeing the old one;
+ *       * the pinned staging ring wraps onto slots that queued kernels still read
+ *         (hipEventSynchronize on those kernels), or grows for a call that needs more
+ *         than it holds (every queued use is waited for first);
+ *       * the first call with a new (head dim, base, freq_scale) allocates and builds
+ *         its RoPE table (hipMalloc, one kernel).
+ *     Sizes only grow, so after one call of each kind at its largest size no further
+ *     call allocates or waits.  HIP graph capture: make those warm-up calls before
+ *     capturing; a growth during capture fails with KVC_E_HIP (a capturing stream cannot
+ *     be synchronised).  Calls on one handle must be issued from one host thread onto
+ *     one stream (or be otherwise ordered): the handle's staging and scratch memory is
+ *     reused call after call.
  *   - Store before attention: a row must be appended (on the same stream, earlier) before
  *     an attention call that reads it ([MINFER-11] §3.4).  Rows never written read as 0.
- *   - Every argument is checked on the host before any device work.  On any non-OK
- *     status nothing is written: no cache row, no q element, no output element.
+ *   - Every argument is checked on the host before any device work, and every
+ *     allocation and staging a call needs is made before its first kernel is queued.
+ *     On any non-OK status from those checks (KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE,
+ *     KVC_E_DUP, KVC_E_NOMEM, and KVC_E_HIP from an allocation or a wait) nothing is
+ *     written: no cache row, no q element, no output element.  The one exception is a
+ *     kernel launch that the HIP runtime refuses (KVC_E_HIP naming the kernels): the
+ *     launches queued before it in the same call (a decode of more than 64 entries runs
+ *     one launch per 64) may already have written their outputs.
  *     kv_last_error() then returns a message for the calling thread.
  *   - nt == 0 / n_seq == 0 is an OK no-op (after the handle and layer are checked).
  *
@@ -134,6 +153,10 @@ kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32
 
 /*
  * kv_free -- wait for the device, then release every region, table and scratch buffer.
+ * The regions live from kv_alloc to kv_free, across every call in between: the caller,
+ * not any one call, decides when the cache ends ([MINFER-13] §2.5: the KV regions belong
+ * to the cache and survive every rebuild of the step; [ZEROCOPY] "A Vec with capacity
+ * is already a preallocated buffer": storage reserved once and kept).
  * Pointers from kv_view become invalid.  NULL is accepted (no-op).
  */
 kvc_status kv_free(kvc_cache *c);
@@ -274,7 +297,7 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
  *
  * Positions and sequence ids travel in the kernel arguments (64 entries per launch).
  * The split-K partial records live in the handle's scratch memory, which grows on demand
- * (KVC_E_NOMEM if it cannot).
+ * (KVC_E_NOMEM if it cannot) before the first launch.
  * Errors: KVC_E_ARG, KVC_E_GEOMETRY, KVC_E_RANGE, KVC_E_NOMEM, KVC_E_HIP.
  */
 kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
@@ -300,10 +323,11 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
  *   q, n_head, hd, scale, out  as in gqa_attn_decode.
  * The result is attention over the union of the entry's runs; the order of the runs
  * changes only the rounding (within the same tolerance as gqa_attn_decode).
- * The chunk table is staged in pinned host memory that the kernels read in place.
+ * The chunk table of every launch of the call is staged at once, before the first
+ * launch, in pinned host memory that the kernels read in place.
  * Errors: KVC_E_ARG (also for a malformed run list), KVC_E_GEOMETRY, KVC_E_RANGE (a run
  * outside the region), KVC_E_DUP (two runs of one entry share a row), KVC_E_NOMEM,
- * KVC_E_HIP.  On error nothing is queued.
+ * KVC_E_HIP.
  */
 kvc_status gqa_attn_decode_runs(const kvc_cache *c, int32_t layer, int32_t n_seq,
                                 const int32_t *seq_ids, const int32_t *run_off,
@@ -311,8 +335,11 @@ kvc_status gqa_attn_decode_runs(const kvc_cache *c, int32_t layer, int32_t n_seq
                                 int32_t n_head, int32_t hd, float scale, float *out, void *stream);
 
 /*
- * kv_last_error -- text of the calling thread's last non-OK status ("" if none).  The
- * string is owned by the library and valid until the thread's next call.
+ * kv_last_error -- text of the calling thread's last non-OK status ("" if none): the
+ * message half of an error, beside the status code each call returns ([MINFER-11] §3.2.3:
+ * a failing store returns an error carrying its reason, e.g. the position and n_ctx, and
+ * the run stops rather than clamping).  The string is owned by the library and valid
+ * until the thread's next call.
  */
 const char *kv_last_error(void);
 

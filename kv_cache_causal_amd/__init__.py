@@ -98,8 +98,10 @@ def _stream(stream):
     return int(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(t, name):
-    """Device pointer of a dense f32 torch CUDA tensor (or None / a raw int pointer)."""
+def _dev(t, name, numel=0):
+    """Device pointer of a dense f32 torch CUDA tensor (or None / a raw int pointer).
+    numel: elements the call reads or writes through it; a shorter tensor raises
+    ValueError (the kernels would run past its end).  A raw pointer is taken as is."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -108,6 +110,8 @@ def _dev(t, name):
         raise TypeError(f"{name} must be an f32 tensor on the GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call uses {numel}")
     return t.data_ptr()
 
 
@@ -183,9 +187,11 @@ def kv_append_rope(c: Cache, layer, seq_ids, pos, q, n_head, hd, k, v, freq_base
     p_arr, p_ptr = _host_i32(pos)
     if s_arr.size != p_arr.size:
         raise ValueError("seq_ids and pos differ in length")
-    _check(lib().kv_append_rope(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
-                                n_head, hd, _dev(k, "k"), _dev(v, "v"), freq_base, freq_scale,
-                                style, _stream(stream)))
+    nt = int(p_arr.size)
+    nq = nt * n_head * hd if style != ROPE_NONE else 0   # NONE leaves q untouched
+    _check(lib().kv_append_rope(c.handle, layer, nt, s_ptr, p_ptr, _dev(q, "q", nq),
+                                n_head, hd, _dev(k, "k", nt * c.nkt), _dev(v, "v", nt * c.nkt),
+                                freq_base, freq_scale, style, _stream(stream)))
 
 
 def kv_qkv_rope_append(c: Cache, layer, seq_ids, pos, x, wq, bq, wk, bk, wv, bv, n_head, hd,
@@ -197,17 +203,21 @@ def kv_qkv_rope_append(c: Cache, layer, seq_ids, pos, x, wq, bq, wk, bk, wv, bv,
     if s_arr.size != p_arr.size:
         raise ValueError("seq_ids and pos differ in length")
     d_model = int(x.shape[-1]) if hasattr(x, "shape") else 0
-    _check(lib().kv_qkv_rope_append(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(x, "x"),
-                                    d_model, _dev(wq, "wq"), _dev(bq, "bq"), _dev(wk, "wk"),
-                                    _dev(bk, "bk"), _dev(wv, "wv"), _dev(bv, "bv"), n_head, hd,
-                                    _dev(q_out, "q_out"), freq_base, freq_scale, style,
+    nt, rq, rkv = int(p_arr.size), n_head * hd, c.nkt
+    _check(lib().kv_qkv_rope_append(c.handle, layer, nt, s_ptr, p_ptr, _dev(x, "x", nt * d_model),
+                                    d_model, _dev(wq, "wq", rq * d_model), _dev(bq, "bq", rq),
+                                    _dev(wk, "wk", rkv * d_model), _dev(bk, "bk", rkv),
+                                    _dev(wv, "wv", rkv * d_model), _dev(bv, "bv", rkv), n_head, hd,
+                                    _dev(q_out, "q_out", nt * rq), freq_base, freq_scale, style,
                                     _stream(stream)))
 
 
 def gqa_attn_prefill(c: Cache, seq, layer, pos, q, n_head, hd, scale, out, stream=None):
     p_arr, p_ptr = _host_i32(pos)
-    _check(lib().gqa_attn_prefill(c.handle, seq, layer, int(p_arr.size), p_ptr, _dev(q, "q"),
-                                  n_head, hd, scale, _dev(out, "out"), _stream(stream)))
+    nt = int(p_arr.size)
+    _check(lib().gqa_attn_prefill(c.handle, seq, layer, nt, p_ptr, _dev(q, "q", nt * n_head * hd),
+                                  n_head, hd, scale, _dev(out, "out", nt * n_head * c.hd_kv),
+                                  _stream(stream)))
 
 
 def gqa_attn_decode(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out, stream=None):
@@ -215,8 +225,10 @@ def gqa_attn_decode(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out, st
     p_arr, p_ptr = _host_i32(pos)
     if s_arr.size != p_arr.size:
         raise ValueError("seq_ids and pos differ in length")
-    _check(lib().gqa_attn_decode(c.handle, layer, int(p_arr.size), s_ptr, p_ptr, _dev(q, "q"),
-                                 n_head, hd, scale, _dev(out, "out"), _stream(stream)))
+    n = int(p_arr.size)
+    _check(lib().gqa_attn_decode(c.handle, layer, n, s_ptr, p_ptr, _dev(q, "q", n * n_head * hd),
+                                 n_head, hd, scale, _dev(out, "out", n * n_head * c.hd_kv),
+                                 _stream(stream)))
 
 
 def gqa_attn_decode_runs(c: Cache, layer, seq_ids, runs, q, n_head, hd, scale, out,
@@ -235,9 +247,10 @@ def gqa_attn_decode_runs(c: Cache, layer, seq_ids, runs, q, n_head, hd, scale, o
     o_arr, o_ptr = _host_i32(off)
     st_arr, st_ptr = _host_i32(starts if starts else [0])
     ln_arr, ln_ptr = _host_i32(lens if lens else [0])
-    _check(lib().gqa_attn_decode_runs(c.handle, layer, int(s_arr.size), s_ptr, o_ptr, st_ptr,
-                                      ln_ptr, _dev(q, "q"), n_head, hd, scale, _dev(out, "out"),
-                                      _stream(stream)))
+    n = int(s_arr.size)
+    _check(lib().gqa_attn_decode_runs(c.handle, layer, n, s_ptr, o_ptr, st_ptr, ln_ptr,
+                                      _dev(q, "q", n * n_head * hd), n_head, hd, scale,
+                                      _dev(out, "out", n * n_head * c.hd_kv), _stream(stream)))
 
 
 _hip = None

@@ -351,9 +351,20 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
             vq = IO::load_quad(V, quad, li);
         }
     };
-    auto consume = [&](const Raw (&kf)[kUnroll], const Raw (&vf)[kUnroll], const Quad &kq,
+    auto consume = [&](const Raw (&kf)[kUnroll], Raw (&vf)[kUnroll], const Quad &kq,
                        const Quad &vq, int step) {
         const int rb = rbase + step * BR;
+        if constexpr (!kQuads) {
+            // The chunk's last step: its rows past r1 hold row r0's values (see load).
+            // Their weight is 0, but 0 * inf is NaN, so a non-finite V value of row r0
+            // would leak into the result through them: their V registers become 0.
+            // (Q8_0 codes are finite, and a masked row's V factor is 0 instead.)
+            if (rb + BR > r1) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; u++)
+                    if (row_of(rb, u) >= r1) vf[u] = Raw{};
+            }
+        }
         float sc[kUnroll][GP], pv[kUnroll][GP], vs[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {

@@ -3,8 +3,12 @@
 // Per call: every argument is checked on the host (validate.cpp) before anything is
 // queued.  Host-side integer arrays (positions, sequence ids, chunk offsets) ride in the
 // kernel arguments when short, or in a pinned staging ring the kernels read in place
-// when long; then the kernels are queued on the caller's stream.  Nothing here waits
-// for the device except kv_alloc (zero fill) and kv_free.
+// when long; then the kernels are queued on the caller's stream.  The host waits for
+// the device in kv_alloc (zero fill) and kv_free, and otherwise only when handle-owned
+// memory grows or is reused: a scratch buffer replaced by a larger one (ensure_scratch),
+// a staging slot still read by queued kernels (staging_push), or the staging ring grown
+// (staging_release).  Every allocation and staging step of a call comes before its first
+// launch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -271,6 +275,21 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
     kvc_status pst = ensure_part(c, need, s);
     if (pst != KVC_OK) return pst;
 
+    // Explicit windows: the (first row, rows) table of every chunk of every launch, staged
+    // once before the first launch, so no staging step can fail after a launch.
+    const int32_t *pieces_dev = nullptr;
+    if (runs) {
+        std::vector<int32_t> pieces;
+        for (int32_t b = 0; b < n_seq; b++)
+            for (int32_t r = run_off[b]; r < run_off[b + 1]; r++)
+                for (int64_t o = 0; o < run_len[r]; o += rows) {
+                    pieces.push_back(run_start[r] + (int32_t)o);
+                    pieces.push_back((int32_t)std::min<int64_t>(rows, run_len[r] - o));
+                }
+        if ((pst = staging_push(c->st, pieces, &pieces_dev)) != KVC_OK) return pst;
+    }
+
+    int64_t chunk0 = 0;   // chunks of the entries before this launch's first
     for (int32_t b0 = 0; b0 < n_seq; b0 += E) {
         const int32_t n = std::min(E, n_seq - b0);
         kvc::DecodeParams p{};
@@ -300,30 +319,16 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         }
         p.cbase[n] = chunks;
         p.total_chunks = chunks;
-        p.pieces = nullptr;
-        if (runs) {
-            std::vector<int32_t> pieces;
-            pieces.reserve((size_t)chunks * 2);
-            for (int32_t b = b0; b < b0 + n; b++)
-                for (int32_t r = run_off[b]; r < run_off[b + 1]; r++)
-                    for (int64_t o = 0; o < run_len[r]; o += rows) {
-                        pieces.push_back(run_start[r] + (int32_t)o);
-                        pieces.push_back((int32_t)std::min<int64_t>(rows, run_len[r] - o));
-                    }
-            kvc_status pst = staging_push(c->st, pieces, &p.pieces);
-            if (pst != KVC_OK) return pst;
-        }
+        p.pieces = runs ? pieces_dev + 2 * chunk0 : nullptr;
+        chunk0 += chunks;
         hipError_t e = kvc::launch_decode(p, s);
         if (e != hipSuccess) {
-            if (runs) staging_abort(c->st);
+            // Record the slot's release behind whatever was queued before the failure.
+            if (runs) (void)staging_commit(c->st, s);
             return hip_fail(e, "decode kernels");
         }
-        if (runs) {
-            kvc_status cst = staging_commit(c->st, s);
-            if (cst != KVC_OK) return cst;
-        }
     }
-    return KVC_OK;
+    return runs ? staging_commit(c->st, s) : KVC_OK;
 }
 
 }  // namespace

@@ -105,6 +105,64 @@ def pin_cos_sin_correctly_rounded(o: Oracle):
                 assert sn[i] == rn32(mpmath.sin(th)), (hd, p, i)
 
 
+# Head dims and positions of every RoPE table the workloads and the GPU tests build:
+# kv head dims 16, 64, 128 and query head dims above them (48, 96, 192), positions up to
+# the long-context capacity 40,960 (which covers the 520, 1,023 and 12,800 of the others).
+ROPE_GRID_HDS = (16, 48, 64, 96, 128, 192)
+ROPE_GRID_POSITIONS = 40960
+
+
+def rn32_f64_certified(y: np.ndarray, ulps: float = 8.0):
+    """Round f64 approximations y of exact values to f32, and say where that is certainly
+    the correctly rounded f32 of the exact value: y within `ulps` f64 ulps of it and no
+    f32 rounding boundary (midpoint of two neighbouring f32) that close to y."""
+    f = y.astype(np.float32)
+    lo = np.nextafter(f, np.float32(-np.inf)).astype(np.float64)
+    hi = np.nextafter(f, np.float32(np.inf)).astype(np.float64)
+    fd = f.astype(np.float64)
+    margin = np.minimum(y - (fd + lo) / 2, (fd + hi) / 2 - y)
+    return f, margin > ulps * np.spacing(np.abs(y))
+
+
+def pin_cos_sin_exhaustive_grid(o: Oracle):
+    """Every cos/sin entry of every table on the workload grid (all positions below
+    40,960, all pairs of head dims 16 to 192, base 1e6) is the correctly rounded f32 of
+    cos/sin of the f32 angle: against numpy's f64 cos/sin where that rounding is certain
+    (8 ulps of slack for the f64 functions), else against mpmath at 40 digits."""
+    mpmath.mp.dps = 40
+    P = np.arange(ROPE_GRID_POSITIONS, dtype=np.float32)[:, None]
+    for hd in ROPE_GRID_HDS:
+        inv = o.rope_inv_freq(hd, 1.0e6, 1.0)
+        th = P * inv[None, :]                      # f32 products, as in the definition
+        assert th.dtype == np.float32
+        got_c = np.empty(th.shape, np.float32)
+        got_s = np.empty(th.shape, np.float32)
+        for p in range(ROPE_GRID_POSITIONS):
+            got_c[p], got_s[p] = o.rope_cos_sin(hd, 1.0e6, 1.0, p)
+        for name, fn, mfn, got in (("cos", np.cos, mpmath.cos, got_c),
+                                   ("sin", np.sin, mpmath.sin, got_s)):
+            want, sure = rn32_f64_certified(fn(th.astype(np.float64)))
+            bad = sure & (f32bits(got) != f32bits(want))
+            assert not bad.any(), (hd, name, np.argwhere(bad)[:4].tolist())
+            for p, i in np.argwhere(~sure):
+                w = rn32(mfn(mpmath.mpf(float(th[p, i]))))
+                assert f32bits(got[p, i]) == f32bits(w), (hd, name, int(p), int(i))
+
+
+def pin_cos_sin_mpmath_sample(o: Oracle):
+    """10,000 seeded (position, pair) entries of the grid's tables against mpmath
+    correct rounding (an arbitrary-precision check of the same entries)."""
+    mpmath.mp.dps = 40
+    rng = np.random.default_rng(12)
+    for hd in ROPE_GRID_HDS:
+        inv = o.rope_inv_freq(hd, 1.0e6, 1.0)
+        n = 10000 // len(ROPE_GRID_HDS) + 1
+        for p, i in zip(rng.integers(0, ROPE_GRID_POSITIONS, n), rng.integers(0, hd // 2, n)):
+            cs, sn = o.rope_cos_sin(hd, 1.0e6, 1.0, int(p))
+            th = mpmath.mpf(float(np.float32(p) * inv[i]))
+            assert cs[i] == rn32(mpmath.cos(th)) and sn[i] == rn32(mpmath.sin(th)), (hd, p, i)
+
+
 def pin_rope_pos0_identity(o: Oracle):
     """Position 0 turns every pair by 0 rad: RoPE is the identity, bit for bit, on
     N(0,1) data (which never holds a signed zero)."""
@@ -780,6 +838,14 @@ def pin_fused_equals_unfused(o: Oracle):
     assert st == E_RANGE and not c.k(0, 0).any()
     c.close()
 
+
+# Pins too slow to repeat for each planted mistake of the mutant test (seconds each):
+# run once by tests/test_oracle_pins.py.  The mutants they would catch are caught by the
+# sampled pins above as well.
+SWEEP_PINS = [
+    pin_cos_sin_exhaustive_grid,
+    pin_cos_sin_mpmath_sample,
+]
 
 ALL_PINS = [
     pin_inv_freq_correctly_rounded,

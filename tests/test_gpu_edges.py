@@ -163,6 +163,31 @@ def test_errors_leave_everything_untouched():
     p.close()
 
 
+def test_binding_refuses_short_tensors():
+    """The binding checks each tensor's size against the call before the library sees
+    it (a short tensor would be read or written past its end): ValueError, nothing
+    written."""
+    import torch
+    say("binding size checks")
+    p = build(45, 1, 4, 2, 64, 64, 32, 8)
+    q = dev(custom(46, (2, 4, 64)))
+    k = dev(custom(47, (2, 2, 64)))
+    out = torch.full((2, 4, 64), 7.0, device="cuda")
+    with pytest.raises(ValueError):
+        kvc.kv_append_rope(p.g, 0, [0, 0], [8, 9], q, 4, 64, k[:1], k, 1e6)
+    with pytest.raises(ValueError):
+        kvc.kv_append_rope(p.g, 0, [0, 0], [8, 9], q[:1], 4, 64, k, k, 1e6)
+    with pytest.raises(ValueError):
+        kvc.gqa_attn_decode(p.g, 0, [0, 0], [3, 4], q, 4, 64, 0.125, out[:1])
+    with pytest.raises(ValueError):
+        kvc.gqa_attn_prefill(p.g, 0, 0, [3, 4], q[:1], 4, 64, 0.125, out)
+    with pytest.raises(ValueError):
+        kvc.gqa_attn_decode_runs(p.g, 0, [0, 0], [[(0, 4)], [(2, 3)]], q, 4, 64, 0.125, out[:1])
+    assert (host(out) == 7.0).all()
+    compare_cache(p.g, p.o, 0, 0, "after refused calls")
+    p.close()
+
+
 def test_empty_calls_are_noops():
     say("nt = 0")
     p = Pair(1, 1, 2, 16, 8)
@@ -324,6 +349,51 @@ def test_non_finite_values_inside_the_prompt(monkeypatch, kv, nt, first_bad, seg
     assert np.array_equal(np.isposinf(g), np.isposinf(w)) and np.array_equal(np.isneginf(g), np.isneginf(w)), "inf pattern"
     fin = np.isfinite(w)
     assert_close(np.where(fin, g, 0.0), np.where(fin, w, 0.0), "finite part of the later queries")
+    p.close()
+
+
+def assert_same_nonfinite(got, want, what):
+    """Non-finite results equal the oracle's kind for kind (NaN, +inf, -inf); the finite
+    ones pass the allclose bar."""
+    assert not np.isfinite(want).all(), f"{what}: the case must reach non-finite results"
+    assert np.array_equal(np.isnan(got), np.isnan(want)), f"{what}: NaN pattern"
+    assert np.array_equal(np.isposinf(got), np.isposinf(want)), f"{what}: +inf pattern"
+    assert np.array_equal(np.isneginf(got), np.isneginf(want)), f"{what}: -inf pattern"
+    fin = np.isfinite(want)
+    assert_close(np.where(fin, got, 0.0), np.where(fin, want, 0.0), f"{what} (finite part)")
+
+
+@pytest.mark.parametrize("kv", [0, 1, 2], ids=["f32", "f16", "q8_0"])
+def test_decode_non_finite_value_at_a_chunk_start(monkeypatch, kv):
+    """A V row holding +inf, -inf and NaN at the first row of a decode chunk whose window
+    ends inside a step: the chunk's last step reads rows past its end (masked, weight 0),
+    and 0 * inf must not turn the result into NaN where the oracle has +inf or -inf.
+    Position windows (chunks of 128 rows over a 300-row window: the last chunk starts at
+    row 256 and holds 44 rows) and explicit windows (runs cut into the same chunks, one
+    starting at the non-finite row)."""
+    say(f"non-finite V at a decode chunk's first row, kv {kv}")
+    monkeypatch.setenv("KVC_SPLIT_ROWS", "128")
+    nh, nkv, hd = 4, 2, 64
+    p = Pair(1, 1, nkv, hd, 320, dtype=kv)
+    k, v = custom(120, (300, nkv, hd)), custom(121, (300, nkv, hd))
+    if kv == 2:
+        # Q8_0 holds finite inputs only; a block whose scale overflows binary16 decodes to
+        # +inf, -inf (codes of either sign) and NaN (code 0).
+        for row in (256, 278):
+            v[row, 0, :32] = np.float32(1e7) * np.sign(custom(122 + row, (32,)))
+            v[row, 0, 5] = 0.0
+    else:
+        for row in (256, 278):
+            v[row, 0, 3], v[row, 0, 7], v[row, 0, 11] = np.inf, -np.inf, np.nan
+            v[row, 1, 20] = -np.inf
+    p.append(0, [0] * 300, np.arange(300, dtype=np.int32), None, nh, hd, k, v)
+    q = custom(123, (2, nh, hd))
+    got, want = p.decode(0, [0, 0], [299, 255], dev(q), q, nh, hd, 0.125)
+    assert_same_nonfinite(got[0], want[0], "decode, window [0, 299]")
+    assert_close(got[1], want[1], "decode, window [0, 255] (before the non-finite rows)")
+    # Runs [150, 300) then [0, 100): pieces [150, 278), [278, 300), [0, 100).
+    got, want = p.decode_runs(0, [0], [[(150, 150), (0, 100)]], dev(q[:1]), q[:1], nh, hd, 0.125)
+    assert_same_nonfinite(got, want, "decode over runs")
     p.close()
 
 

@@ -2,11 +2,12 @@
 
 Each test drives the HIP library and the oracle with the same seeded inputs
 (tests/workloads.py) and compares: caches, rotated q and high-water marks bit for bit,
-attention outputs within the allclose bar of tests/gpu_util.py.  Where the oracle would
-take minutes (the 4,096-token prefill of the batch workload), it computes a sample of
-query rows one by one; the GPU computes all of them in the benchmark's launch
-configuration.
+attention outputs within the allclose bar of tests/gpu_util.py.  Every output of every
+call is compared, including all 4,096 x 16 x 128 values of the batch workload's prefill
+(in the benchmark's launch configuration; the oracle takes 10-30 s of host time for it).
 """
+import time
+
 import numpy as np
 import pytest
 
@@ -130,11 +131,11 @@ def test_qwen3_batch(kv):
     pos = np.arange(n_past[0], n_past[0] + nt, dtype=np.int32)
     q, k, v = W.prefill_qkv(w, nt, 0, 0)
     qd, qo = p.append(0, [0] * nt, pos, q, w.n_head, w.hd, k, v, w.base, w.freq_scale, w.style)
-    rng = np.random.default_rng(5)
-    sample = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, nt - 33, nt - 1],
-                                       rng.integers(0, nt, 56)]))
-    got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale, sample=sample)
-    assert_close(got, want, f"qwen3 batch prefill ({len(sample)} sampled tokens)")
+    t0 = time.time()
+    got, want = p.prefill(0, 0, pos, qd, qo, w.n_head, w.hd, w.scale)
+    say(f"  prefill of {nt} tokens at {pos[0]}..{pos[-1]}: oracle and GPU done in "
+        f"{time.time() - t0:.1f}s")
+    assert_close(got, want, f"qwen3 batch prefill (all {nt} tokens)")
     # One decode step for all 32 sequences.
     lens = n_past.copy()
     lens[0] += nt

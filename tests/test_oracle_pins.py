@@ -2,7 +2,7 @@
 import pytest
 
 from oracle import Oracle
-from tests.oracle_pins import ALL_PINS
+from tests.oracle_pins import ALL_PINS, SWEEP_PINS
 
 
 @pytest.fixture(scope="module")
@@ -10,6 +10,7 @@ def orc():
     return Oracle()
 
 
-@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+@pytest.mark.parametrize("pin", ALL_PINS + SWEEP_PINS,
+                         ids=[p.__name__ for p in ALL_PINS + SWEEP_PINS])
 def test_pin(orc, pin):
     pin(orc)
