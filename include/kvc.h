@@ -305,6 +305,34 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
                            int32_t n_head, int32_t hd, float scale, float *out, void *stream);
 
 /*
+ * gqa_attn_decode_noalloc -- gqa_attn_decode for callers that cannot allocate memory
+ * while they run: code recorded into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, same kernels, same chunking and the same results
+ * bit for bit; the split-K records go to a fixed scratch array of the library in device
+ * memory instead of the handle's scratch, so the call never allocates, frees or waits
+ * (no hipMalloc, hipFree, synchronisation or staging) and queues only the decode
+ * kernels.
+ *
+ * Limit: the records of one launch (up to 64 entries) must fit the fixed scratch,
+ * KVC_STATIC_SCRATCH_BYTES (16 MiB): chunks x n_head x (hd_kv + 4) floats, where a
+ * window of L rows takes about L x n_head_kv x n_seq / 2048 / 512 chunks when large
+ * (e.g. 32 Qwen3-0.6B-shaped sequences of 8,192 rows: about 2.3 MB).  A call that needs
+ * more is refused with KVC_E_ARG before anything is queued.
+ * Every call on one GPU shares that GPU's one copy of the array (it is held until the
+ * process ends), so calls that overlap on one GPU -- on different streams, or from
+ * different threads or handles without ordering -- race on it; calls ordered on one
+ * stream do not.  Nothing in it needs clearing: every record a call reads is written
+ * earlier in the same call.
+ * Errors: as gqa_attn_decode (KVC_E_ARG also for a call beyond the limit); KVC_E_HIP if
+ * the scratch array's address could not be found (looked up at kv_alloc).
+ */
+#define KVC_STATIC_SCRATCH_BYTES (16u << 20)
+kvc_status gqa_attn_decode_noalloc(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                                   const int32_t *seq_ids, const int32_t *pos, const float *q,
+                                   int32_t n_head, int32_t hd, float scale, float *out,
+                                   void *stream);
+
+/*
  * gqa_attn_decode_runs -- gqa_attn_decode over explicit windows: entry b attends the
  * rows its runs name instead of rows [0, pos[b]] ([MINFER-13] §2.2, Budget 3: the cells a
  * query may read are an input resolved by the caller, a list of runs, not a bound derived

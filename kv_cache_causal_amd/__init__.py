@@ -28,7 +28,9 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_E_ARG", 2: "KVC_E_GEOMETRY", 3: "KVC_E_RANG
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kv_alloc", "kv_alloc_typed", "kv_free", "kv_view", "kv_seq_len", "kv_append_rope",
-           "kv_qkv_rope_append", "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_runs", "kv_last_error")
+           "kv_qkv_rope_append", "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_noalloc",
+           "gqa_attn_decode_runs", "kv_last_error")
+STATIC_SCRATCH_BYTES = 16 << 20   # the fixed scratch of gqa_attn_decode_noalloc
 
 
 class KvcError(RuntimeError):
@@ -66,6 +68,7 @@ def lib(path: str = LIB_PATH):
                                ctypes.c_int, p],
         "gqa_attn_prefill": [p, i32, i32, i32, p, p, i32, i32, f32, p, p],
         "gqa_attn_decode": [p, i32, i32, p, p, p, i32, i32, f32, p, p],
+        "gqa_attn_decode_noalloc": [p, i32, i32, p, p, p, i32, i32, f32, p, p],
         "gqa_attn_decode_runs": [p, i32, i32, p, p, p, p, p, i32, i32, f32, p, p],
     }
     for name, args in sig.items():
@@ -229,6 +232,20 @@ def gqa_attn_decode(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out, st
     _check(lib().gqa_attn_decode(c.handle, layer, n, s_ptr, p_ptr, _dev(q, "q", n * n_head * hd),
                                  n_head, hd, scale, _dev(out, "out", n * n_head * c.hd_kv),
                                  _stream(stream)))
+
+
+def gqa_attn_decode_noalloc(c: Cache, layer, seq_ids, pos, q, n_head, hd, scale, out,
+                            stream=None):
+    """gqa_attn_decode with its split-K records in the library's fixed scratch: the call
+    allocates nothing (see kvc.h for the size limit and the sharing rule)."""
+    s_arr, s_ptr = _host_i32(seq_ids)
+    p_arr, p_ptr = _host_i32(pos)
+    if s_arr.size != p_arr.size:
+        raise ValueError("seq_ids and pos differ in length")
+    n = int(p_arr.size)
+    _check(lib().gqa_attn_decode_noalloc(c.handle, layer, n, s_ptr, p_ptr,
+                                         _dev(q, "q", n * n_head * hd), n_head, hd, scale,
+                                         _dev(out, "out", n * n_head * c.hd_kv), _stream(stream)))
 
 
 def gqa_attn_decode_runs(c: Cache, layer, seq_ids, runs, q, n_head, hd, scale, out,

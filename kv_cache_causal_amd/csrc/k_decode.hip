@@ -45,7 +45,9 @@
 //     merge are otherwise the same -- a chunk is a contiguous row range either way.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "kvc_device.hpp"
 #include "kvc_internal.hpp"
@@ -613,6 +615,44 @@ int32_t step_rows_fmt(int32_t hd_kv, int32_t G)
     return step_rows<1, KVT>(hd_kv);
 }
 }  // namespace
+
+// ---- Fixed scratch for the allocation-free decode (gqa_attn_decode_noalloc) ----------
+// The split-K records of that entry point live in this array instead of in handle-owned
+// memory that grows on demand.  Each GPU the library runs on holds its own copy, at its
+// own address, for the life of the process.  On the host the name `scratch` stands for
+// the variable, not for device memory: kernels get the address hipGetSymbolAddress
+// returns for the device, kept per device below.
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch_addr(int device, float **addr)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    float *a = g_scratch_addr[device].load(std::memory_order_acquire);
+    if (!a) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        a = g_scratch_addr[device].load(std::memory_order_relaxed);
+        if (!a) {
+            // The address of the device's copy is looked up with that device current.
+            int cur = -1;
+            hipError_t e = hipGetDevice(&cur);
+            if (e != hipSuccess) return e;
+            if (cur != device) return hipErrorInvalidDevice;
+            void *p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            a = static_cast<float *>(p);
+            g_scratch_addr[device].store(a, std::memory_order_release);
+        }
+    }
+    *addr = a;
+    return hipSuccess;
+}
 
 int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt)
 {

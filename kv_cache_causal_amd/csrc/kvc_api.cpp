@@ -235,11 +235,14 @@ kvc_status ensure_part(const kvc_cache *c, size_t need, hipStream_t s)
 }
 
 // Split-K decode of n_seq validated entries.  Entry b's window is rows [0, pos[b]]
-// (run_off == nullptr) or the union of its runs run_off[b] .. run_off[b+1]-1.
+// (run_off == nullptr) or the union of its runs run_off[b] .. run_off[b+1]-1.  The
+// split-K records go to the handle's scratch (grown on demand), or, with fixed != nullptr,
+// to the fixed_cap floats at `fixed` (a call that needs more is refused, nothing queued).
 kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const int32_t *seq_ids,
                          const int32_t *pos, const int32_t *run_off, const int32_t *run_start,
                          const int32_t *run_len, const float *q, int32_t n_head, int32_t hd,
-                         float scale, float *out, hipStream_t s)
+                         float scale, float *out, hipStream_t s, float *fixed = nullptr,
+                         size_t fixed_cap = 0)
 {
     const bool runs = run_off != nullptr;
     auto window_rows = [&](int32_t b) -> int64_t {
@@ -272,8 +275,17 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
     }
     if (max_chunks > (1 << 30)) return fail(KVC_E_ARG, "too many split-K chunks");
     const size_t need = (size_t)max_chunks * n_head * (c->g.hd_kv + 4);
-    kvc_status pst = ensure_part(c, need, s);
-    if (pst != KVC_OK) return pst;
+    kvc_status pst = KVC_OK;
+    if (fixed) {
+        if (need > fixed_cap)
+            return fail(KVC_E_ARG, "the call needs " + std::to_string(need) +
+                                       " floats of split-K records; the fixed scratch holds " +
+                                       std::to_string(fixed_cap) +
+                                       " (fewer entries or shorter windows per call)");
+    } else if ((pst = ensure_part(c, need, s)) != KVC_OK) {
+        return pst;
+    }
+    float *part = fixed ? fixed : c->part;
 
     // Explicit windows: the (first row, rows) table of every chunk of every launch, staged
     // once before the first launch, so no staging step can fail after a launch.
@@ -295,7 +307,7 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         kvc::DecodeParams p{};
         p.q = q + (int64_t)b0 * n_head * hd;
         p.out = out + (int64_t)b0 * n_head * c->g.hd_kv;
-        p.part = c->part;
+        p.part = part;
         p.kc = c->K;
         p.vc = c->V;
         p.region_bytes = c->region_bytes;
@@ -391,6 +403,12 @@ kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32
     if (staging_alloc(c->st, 65536) != KVC_OK) return cleanup(KVC_E_NOMEM, "staging allocation failed");
     if ((e = hipStreamSynchronize(s)) != hipSuccess)
         return cleanup(KVC_E_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    // Look up (once per device) the fixed scratch of gqa_attn_decode_noalloc while this
+    // device is current, so that entry point itself makes no runtime call to find it.  A
+    // failure here only disables that entry point, which then reports it.
+    float *fixed = nullptr;
+    (void)kvc::static_scratch_addr(c->device, &fixed);
+    (void)hipGetLastError();
     *out = c;
     return KVC_OK;
 }
@@ -632,6 +650,25 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
     if (n_seq == 0) return KVC_OK;
     return decode_driver(c, layer, n_seq, seq_ids, pos, nullptr, nullptr, nullptr, q, n_head, hd,
                          scale, out, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvc_status gqa_attn_decode_noalloc(const kvc_cache *c, int32_t layer, int32_t n_seq,
+                                   const int32_t *seq_ids, const int32_t *pos, const float *q,
+                                   int32_t n_head, int32_t hd, float scale, float *out,
+                                   void *stream)
+{
+    if (!c) return fail(KVC_E_ARG, "NULL handle");
+    std::string msg;
+    kvc_status st = kvc::check_decode(c->g, layer, n_seq, seq_ids, pos, q, n_head, hd, scale,
+                                      out, msg);
+    if (st != KVC_OK) return fail(st, msg);
+    if (n_seq == 0) return KVC_OK;
+    float *fixed = nullptr;
+    hipError_t e = kvc::static_scratch_addr(c->device, &fixed);
+    if (e != hipSuccess) return hip_fail(e, "fixed decode scratch (hipGetSymbolAddress)");
+    return decode_driver(c, layer, n_seq, seq_ids, pos, nullptr, nullptr, nullptr, q, n_head, hd,
+                         scale, out, reinterpret_cast<hipStream_t>(stream), fixed,
+                         kvc::kStaticScratchFloats);
 }
 
 kvc_status gqa_attn_decode_runs(const kvc_cache *c, int32_t layer, int32_t n_seq,

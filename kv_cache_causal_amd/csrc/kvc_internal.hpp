@@ -98,6 +98,13 @@ struct DecodeParams {
     int32_t seq[kInlineEntries];
     int32_t cbase[kInlineEntries + 1];  // first chunk of entry b; cbase[n] = total_chunks
 };
+// The allocation-free decode keeps its split-K records in a fixed device array of this
+// many floats (16 MiB per GPU).  static_scratch_addr returns the device address of the
+// array's copy on `device`; the first lookup for a device must run with that device
+// current, later ones only read the kept address.
+constexpr size_t kStaticScratchFloats = size_t(4) << 20;
+hipError_t static_scratch_addr(int device, float **addr);
+
 // Rows per step of the split-K kernel that a call with query-head group G (n_head /
 // n_head_kv) launches first, for a kv head dim and region format (chunks should be a
 // multiple of it).

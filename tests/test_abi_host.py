@@ -48,6 +48,11 @@ def test_header_enum_values_match_binding():
         assert m and int(m.group(1)) == val, name
 
 
+def test_header_fixed_scratch_size_matches_binding():
+    m = re.search(r"#define KVC_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kvc.STATIC_SCRATCH_BYTES
+
+
 def test_null_handle_is_rejected_without_device_work():
     L = kvc.lib()
     pos = (ctypes.c_int32 * 1)(0)
@@ -55,6 +60,7 @@ def test_null_handle_is_rejected_without_device_work():
     assert st == kvc.E_ARG and "NULL" in kvc.kv_last_error()
     assert L.gqa_attn_decode(None, 0, 1, pos, pos, 16, 1, 16, 0.25, 16, None) == kvc.E_ARG
     assert L.gqa_attn_prefill(None, 0, 0, 1, pos, 16, 1, 16, 0.25, 16, None) == kvc.E_ARG
+    assert L.gqa_attn_decode_noalloc(None, 0, 1, pos, pos, 16, 1, 16, 0.25, 16, None) == kvc.E_ARG
     assert L.kv_free(None) == kvc.OK
     out = ctypes.c_void_p()
     assert L.kv_alloc(ctypes.byref(out), 1, 1, 1, 24, 8, None) == kvc.E_ARG
