@@ -3,7 +3,8 @@
     python -m kv_cache_causal_amd._build
 
 Compiles every source under csrc/ with hipcc for gfx950 (in parallel), links
-lib/libkvc.so, and builds lib/libkvc_hostcheck.so (validate.cpp + hostcheck.cpp with g++,
+lib/libkvc.so, builds lib/libkvc_probe.so (the benchmark's streaming-read helper, not
+part of the library) and lib/libkvc_hostcheck.so (validate.cpp + hostcheck.cpp with g++,
 no HIP) so the argument checks can be tested on a machine without a GPU.
 """
 from __future__ import annotations
@@ -31,6 +32,7 @@ HIP_FLAGS = [
 ]
 LIB = os.path.join(LIBDIR, "libkvc.so")
 HOSTCHECK = os.path.join(LIBDIR, "libkvc_hostcheck.so")
+PROBE = os.path.join(LIBDIR, "libkvc_probe.so")
 ABI_DEMO = os.path.join(LIBDIR, "abi_demo")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -58,6 +60,11 @@ def build(jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    # The benchmark's measurement helper (read ceiling, cache flush): a library of its own.
+    probe_obj = _compile("read_probe.hip")
+    tmp = PROBE + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", tmp])
+    os.replace(tmp, PROBE)
     tmp = HOSTCHECK + ".tmp"
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
           os.path.join(CSRC, "validate.cpp"), os.path.join(CSRC, "plan.cpp"),
