@@ -75,15 +75,15 @@ int hc_check_qkv(const int32_t *g5, int32_t layer, int32_t nt, const int32_t *se
                           n_head, hd, q_out, freq_base, freq_scale, style, g_msg);
 }
 
-// Prefill plan: meta[0..7] = GB, TQ, n_qtiles, n_hsub, KT, units_per_hgroup, max_seg,
-// number of unit ints; the unit table goes to units (at most cap ints).  Returns 0, or 1
-// if cap is too small.
+// Prefill plan: meta[0..8] = GB, TQ, n_qtiles, n_hsub, KT, units_per_hgroup, max_seg,
+// number of unit ints, contiguous positions (0/1); the unit table goes to units (at most
+// cap ints).  Returns 0, or 1 if cap is too small.
 int hc_plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_head_kv,
                     int32_t hd_kv, int32_t force_seg, int32_t *meta, int32_t *units, int32_t cap)
 {
     const kvc::PrefillPlan pl = kvc::plan_prefill(pos, nt, n_head, n_head_kv, hd_kv, force_seg);
-    const int32_t m[8] = {pl.GB, pl.TQ, pl.n_qtiles, pl.n_hsub, pl.KT, pl.units_per_hgroup,
-                          pl.max_seg, (int32_t)pl.units.size()};
+    const int32_t m[9] = {pl.GB, pl.TQ, pl.n_qtiles, pl.n_hsub, pl.KT, pl.units_per_hgroup,
+                          pl.max_seg, (int32_t)pl.units.size(), pl.contiguous ? 1 : 0};
     std::memcpy(meta, m, sizeof(m));
     if ((int64_t)pl.units.size() > cap) return 1;
     std::copy(pl.units.begin(), pl.units.end(), units);

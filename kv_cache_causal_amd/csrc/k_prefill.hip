@@ -121,7 +121,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     static_assert(LD * 256 * CH == KT * HD && LD >= 1, "tile split");
     __shared__ float Ks[KT * KSTR];
     __shared__ float Vs[KT * VSTR];
-    __shared__ int s_kmax, s_kmin;
     __shared__ int s_vbad;   // 1 once a tile of this block held a non-finite V value
 
     // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
@@ -135,19 +134,22 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     if (logical >= nblocks) return;
     const int hgroup = logical / p.units_per_hgroup;
     const int unit = logical - hgroup * p.units_per_hgroup;
-    // Work unit: a query tile and the key tiles [kt0, kt1) it scans.  Without a unit table
-    // a unit is a whole query tile (kt1 follows from its positions, below).
-    int qtile, kt0 = 0, kt1 = 0, seg = 0, nseg = 1;
+    // Work unit (from the kernel arguments, or from device-visible memory for long
+    // tables): a query tile, the key tiles [kt0, kt1) it scans, its segment index and the
+    // tile's segment count, and the largest and smallest position among the tile's tokens
+    // (computed on the host, so no workgroup reduces positions before its first load).
+    intx4 ua, ub;
     if (p.units) {
-        const intx4 ud = reinterpret_cast<const intx4 *>(p.units)[unit];
-        qtile = ud[0];
-        kt0 = ud[1];
-        kt1 = ud[1] + ud[2];
-        seg = ud[3] >> 16;
-        nseg = ud[3] & 0xffff;
+        ua = reinterpret_cast<const intx4 *>(p.units)[2 * unit];
+        ub = reinterpret_cast<const intx4 *>(p.units)[2 * unit + 1];
     } else {
-        qtile = p.n_qtiles - 1 - unit;
+        const int *u = p.iunits + unit * kUnitInts;
+        ua = intx4{u[0], u[1], u[2], u[3]};
+        ub = intx4{u[4], u[5], u[6], u[7]};
     }
+    const int qtile = ua[0], kt0 = ua[1], kt1 = ua[1] + ua[2];
+    const int seg = ua[3] >> 16, nseg = ua[3] & 0xffff;
+    const int kmax = ub[0], kmin = ub[1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,48 +166,13 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     const int h = hk * G + (head_ok ? g : 0);
     const int t = qtile * TQ + (wave % wpt) * 16 + qc;
     const bool tok_ok = t < p.nt;
-    const int pq = tok_ok ? p.pos[t] : 0;
+    // This lane's position: contiguous prompts carry only the first one (no memory read
+    // before the first tile's loads); other prompts read theirs.
+    int pq = p.pos0 + t;
+    if (p.pos) pq = p.pos[tok_ok ? t : 0];
+    if (!tok_ok) pq = 0;
 
-    // Largest position among this block's tokens.
-    if (tid == 0) {
-        s_kmax = 0;
-        s_kmin = 0x7fffffff;
-        s_vbad = 0;
-    }
-    __syncthreads();
-    if (tid < TQ) {
-        const int tt = qtile * TQ + tid;
-        if (tt < p.nt) {
-            atomicMax(&s_kmax, p.pos[tt]);
-            atomicMin(&s_kmin, p.pos[tt]);
-        }
-    }
-    // Smallest and largest position among this wave's 16 tokens (invalid columns do not
-    // count towards the minimum).
-    int wmax = pq, wmin = tok_ok ? pq : 0x7fffffff;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        wmax = max(wmax, __shfl_xor(wmax, off));
-        wmin = min(wmin, __shfl_xor(wmin, off));
-    }
-
-    // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h), pre-multiplied by
-    // scale * log2(e) so the S^T accumulators are already in base-2 units.
-    float qf[DQ];
-    {
-        const float *qrow = p.q + ((int64_t)(tok_ok ? t : 0) * p.n_head + h) * p.hd + grp * DQ;
-#pragma unroll
-        for (int s = 0; s < DQ; s++) qf[s] = qrow[s] * p.qscale;
-    }
-
-    floatx4 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -INFINITY, l = 0.0f;
-
-    __syncthreads();
-    const int kmax = s_kmax, kmin = s_kmin;
-    if (!p.units) kt1 = kmax / KT + 1;
+    s_vbad = 0;   // every thread, before the loop's first barrier orders it before any use
     const int nkt = p.n_head_kv * HD;
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
@@ -214,8 +181,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
     // uniform tile base plus a per-thread 32-bit byte offset.  Regions are padded to a
     // whole number of 64-row tiles (zero rows past the capacity, beyond every position and
-    // so masked), so every tile load is inside the region.  The next tile's loads are
-    // issued before this tile's MFMAs.
+    // so masked), so every tile load is inside the region.  The first tile's loads are
+    // issued before the query's; each next tile's before this tile's MFMAs.
     constexpr int RSTEP = 256 * CH / HD;       // rows between a thread's chunks
     const int trow = tid / (HD / CH);
     const int tcol = (tid % (HD / CH)) * CH;
@@ -234,6 +201,29 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         }
     };
     fetch(kt0 * KT);
+
+    // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h), pre-multiplied by
+    // scale * log2(e) so the S^T accumulators are already in base-2 units.
+    float qf[DQ];
+    {
+        const float *qrow = p.q + ((int64_t)(tok_ok ? t : 0) * p.n_head + h) * p.hd + grp * DQ;
+#pragma unroll
+        for (int s = 0; s < DQ; s++) qf[s] = qrow[s] * p.qscale;
+    }
+
+    // Smallest and largest position among this wave's 16 tokens (invalid columns do not
+    // count towards the minimum).
+    int wmax = pq, wmin = tok_ok ? pq : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, off));
+        wmin = min(wmin, __shfl_xor(wmin, off));
+    }
+
+    floatx4 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY, l = 0.0f;
 
     for (int kt = kt0; kt < kt1; kt++) {
         const int key0 = kt * KT;

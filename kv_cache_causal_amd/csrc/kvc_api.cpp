@@ -580,13 +580,18 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     if (nt == 0) return KVC_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    // Positions, then (16-byte aligned) the split-K unit table when the prompt is short.
+    // Work units (plan.cpp); positions travel only when they are not one contiguous run,
+    // the unit table only when it is too long for the kernel arguments.
     const kvc::PrefillPlan pl = kvc::plan_prefill(pos, nt, n_head, c->g.n_head_kv, c->g.hd_kv,
                                                     env_prefill_seg());
-    const size_t units_at = ((size_t)nt + 3) & ~size_t(3);
-    std::vector<int32_t> ints(units_at + pl.units.size(), 0);
-    std::copy(pos, pos + nt, ints.begin());
-    std::copy(pl.units.begin(), pl.units.end(), ints.begin() + units_at);
+    const bool units_inline = pl.units_per_hgroup <= kvc::kInlineUnits;
+    std::vector<int32_t> ints;
+    if (!pl.contiguous) ints.assign(pos, pos + nt);
+    const size_t units_at = (ints.size() + 7) & ~size_t(7);   // 32-byte aligned
+    if (!units_inline) {
+        ints.resize(units_at, 0);
+        ints.insert(ints.end(), pl.units.begin(), pl.units.end());
+    }
     if (pl.max_seg > 1) {
         st = ensure_part(c, (size_t)pl.max_seg * nt * n_head * (c->g.hd_kv + 4), s);
         if (st != KVC_OK) return st;
@@ -603,10 +608,14 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
         if (st != KVC_OK) return st;
     }
     const int32_t *dev = nullptr;
-    if ((st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
+    const bool staged = !ints.empty();
+    if (staged && (st = staging_push(c->st, ints, &dev)) != KVC_OK) return st;
     const size_t off = ((size_t)seq * c->g.n_layer + layer) * (size_t)c->region_bytes;
     kvc::PrefillParams p{};
-    p.units = pl.units.empty() ? nullptr : dev + units_at;
+    p.pos = pl.contiguous ? nullptr : dev;
+    p.pos0 = pos[0];
+    p.units = units_inline ? nullptr : dev + units_at;
+    if (units_inline) std::copy(pl.units.begin(), pl.units.end(), p.iunits);
     p.part = pl.max_seg > 1 ? c->part : nullptr;
     p.dq = dq_rows ? c->dq : nullptr;
     p.dq_rows = dq_rows;
@@ -622,7 +631,6 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     p.vc = c->V + off;
     p.kv_fmt = c->kv_fmt;
     p.scale_off = c->scale_off;
-    p.pos = dev;
     p.nt = nt;
     p.n_head = n_head;
     p.hd = hd;
@@ -632,10 +640,10 @@ kvc_status gqa_attn_prefill(const kvc_cache *c, int32_t seq, int32_t layer, int3
     p.qscale = log2e_times(scale);
     hipError_t e = kvc::launch_prefill(p, s);
     if (e != hipSuccess) {
-        staging_abort(c->st);
+        if (staged) staging_abort(c->st);
         return hip_fail(e, "prefill kernel");
     }
-    return staging_commit(c->st, s);
+    return staged ? staging_commit(c->st, s) : KVC_OK;
 }
 
 kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,

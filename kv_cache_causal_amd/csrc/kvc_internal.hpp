@@ -112,13 +112,16 @@ int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------
+// Unit tables of up to kInlineUnits units ride in the kernel arguments.
+constexpr int kInlineUnits = 64;
 struct PrefillParams {
     const float *q;          // [nt][n_head][hd]
     float *out;              // [nt][n_head][hd_kv]
     const void *kc, *vc;     // this (seq, layer)'s K and V regions
     int64_t scale_off;       // Q8_0: byte offset of the scales in a region
-    const int32_t *pos;      // device [nt]
-    const int32_t *units;    // device copy of plan.units, or nullptr (no split)
+    const int32_t *pos;      // device-visible [nt], or nullptr: pos[t] = pos0 + t
+    int32_t pos0;
+    const int32_t *units;    // device-visible plan.units, or nullptr: iunits holds them
     float *part;             // split only: [max_seg][nt][n_head][hd_kv + 4]: O, m, l, nseg
     float *dq;               // binary16 / Q8_0: f32 copies of rows [0, dq_rows) of K, then V
     int32_t dq_rows;         // a multiple of 64 covering every position of the call
@@ -126,6 +129,7 @@ struct PrefillParams {
     int32_t GB, TQ, n_qtiles, n_hsub, units_per_hgroup;
     int32_t max_seg;         // split only: records per (token, head) in `part`
     float qscale;            // scale * log2(e)
+    int32_t iunits[kInlineUnits * kUnitInts];
 };
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 

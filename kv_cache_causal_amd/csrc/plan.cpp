@@ -17,18 +17,36 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
     pl.n_qtiles = (nt + pl.TQ - 1) / pl.TQ;
     pl.KT = prefill_key_tile(hd_kv);
     pl.units_per_hgroup = pl.n_qtiles;
-    const int64_t hgroups = (int64_t)n_head_kv * pl.n_hsub;
-    // Two resident workgroups per CU: 512 query tiles fill the chip without a split.
-    constexpr int64_t kFill = 512;
-    if (force_seg < 0 || (force_seg == 0 && hgroups * pl.n_qtiles >= kFill)) return pl;
-    std::vector<int32_t> tiles(pl.n_qtiles);
+    pl.contiguous = true;
+    for (int t = 1; t < nt && pl.contiguous; t++) pl.contiguous = pos[t] == pos[0] + t;
+    // Key tiles of each query tile, up to its largest position.
+    std::vector<int32_t> tiles(pl.n_qtiles), qmax(pl.n_qtiles), qmin(pl.n_qtiles);
     int64_t total = 0;
     for (int q = 0; q < pl.n_qtiles; q++) {
-        int32_t kmax = 0;
-        for (int t = q * pl.TQ; t < std::min(nt, (q + 1) * pl.TQ); t++) kmax = std::max(kmax, pos[t]);
+        int32_t kmax = 0, kmin = 0x7fffffff;
+        for (int t = q * pl.TQ; t < std::min(nt, (q + 1) * pl.TQ); t++) {
+            kmax = std::max(kmax, pos[t]);
+            kmin = std::min(kmin, pos[t]);
+        }
+        qmax[q] = kmax;
+        qmin[q] = kmin;
         tiles[q] = kmax / pl.KT + 1;
         total += tiles[q];
     }
+    auto push_unit = [&](int q, int32_t k0, int32_t nk, int32_t sg, int32_t nseg) {
+        const int32_t u[kUnitInts] = {q, k0, nk, (sg << 16) | nseg, qmax[q], qmin[q], 0, 0};
+        pl.units.insert(pl.units.end(), u, u + kUnitInts);
+    };
+    auto whole_tiles = [&]() {   // one unit per query tile, heavy (late) tiles first
+        pl.units.clear();
+        for (int q = pl.n_qtiles - 1; q >= 0; q--) push_unit(q, 0, tiles[q], 0, 1);
+        pl.units_per_hgroup = pl.n_qtiles;
+        return pl;
+    };
+    const int64_t hgroups = (int64_t)n_head_kv * pl.n_hsub;
+    // Two resident workgroups per CU: 512 query tiles fill the chip without a split.
+    constexpr int64_t kFill = 512;
+    if (force_seg < 0 || (force_seg == 0 && hgroups * pl.n_qtiles >= kFill)) return whole_tiles();
     // Segment length: the tiles spread over about kFill units, but no fewer than 3 per
     // unit, so a unit's start-up (query load, first tile fetch, record write) is spread
     // over a few tiles.
@@ -44,20 +62,17 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
     int32_t max_seg = 1;
     for (int q = 0; q < pl.n_qtiles; q++)
         max_seg = std::max<int32_t>(max_seg, (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles));
-    if (max_seg == 1) return pl;   // every query tile is a single segment already
+    if (max_seg == 1) return whole_tiles();   // every query tile is one segment already
     pl.max_seg = max_seg;
     pl.units.clear();
     for (int q = pl.n_qtiles - 1; q >= 0; q--) {   // heavy (late) query tiles first
         const int32_t nseg = (int32_t)((tiles[q] + seg_tiles - 1) / seg_tiles);
         for (int32_t sg = 0; sg < nseg; sg++) {
             const int32_t k0 = (int32_t)(sg * seg_tiles);
-            pl.units.push_back(q);
-            pl.units.push_back(k0);
-            pl.units.push_back((int32_t)std::min<int64_t>(seg_tiles, tiles[q] - k0));
-            pl.units.push_back((sg << 16) | nseg);
+            push_unit(q, k0, (int32_t)std::min<int64_t>(seg_tiles, tiles[q] - k0), sg, nseg);
         }
     }
-    pl.units_per_hgroup = (int32_t)(pl.units.size() / 4);
+    pl.units_per_hgroup = (int32_t)(pl.units.size() / kUnitInts);
     return pl;
 }
 

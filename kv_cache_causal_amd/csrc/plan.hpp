@@ -16,12 +16,16 @@ constexpr int prefill_key_tile(int hd_kv) { return hd_kv >= 256 ? 32 : 64; }
 // chip, each query tile's key range is cut into segments of equal tile counts, one
 // workgroup each; segments write (m, l, unnormalised O) partials and a merge pass
 // combines them by log-sum-exp, as for decode.
+constexpr int kUnitInts = 8;   // ints per work unit
 struct PrefillPlan {
     int32_t GB = 1, TQ = 64, n_qtiles = 0, n_hsub = 1, KT = 64;
     int32_t units_per_hgroup = 0;  // workgroups per (kv head, head subset)
     int32_t max_seg = 1;           // most segments of any query tile (1: no split)
-    // Split only: per unit {query tile, first key tile, key tiles, segment << 16 | nseg},
-    // heavy (late) query tiles first.
+    bool contiguous = false;       // pos[t] == pos[0] + t for every token
+    // Per unit, kUnitInts ints: {query tile, first key tile, key tiles, segment << 16 |
+    // segments of the tile, largest and smallest position among the tile's tokens, 0, 0};
+    // heavy (late) query tiles first.  Without a split each query tile is one unit that
+    // scans key tiles [0, largest position / KT + 1).
     std::vector<int32_t> units;
 };
 

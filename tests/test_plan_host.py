@@ -38,16 +38,20 @@ def seg_length(hc, tiles, hgroups, nt, n_head, hd_kv, force=0):
     return max(s, -(-max(tiles) // max_recs))
 
 
+UNIT_INTS = 8
+
+
 def plan(hc, pos, n_head, n_head_kv, hd_kv, force=0):
     pos = np.ascontiguousarray(np.asarray(pos, np.int32))
-    meta = np.zeros(8, np.int32)
+    meta = np.zeros(9, np.int32)
     cap = 1 << 20
     units = np.zeros(cap, np.int32)
     assert hc.hc_plan_prefill(pos.ctypes.data, len(pos), n_head, n_head_kv, hd_kv, force,
                               meta.ctypes.data, units.ctypes.data, cap) == 0
-    keys = ("GB", "TQ", "n_qtiles", "n_hsub", "KT", "units_per_hgroup", "max_seg", "n_units")
+    keys = ("GB", "TQ", "n_qtiles", "n_hsub", "KT", "units_per_hgroup", "max_seg", "n_units",
+            "contiguous")
     m = dict(zip(keys, (int(x) for x in meta)))
-    return m, units[:m["n_units"]].reshape(-1, 4)
+    return m, units[:m["n_units"]].reshape(-1, UNIT_INTS)
 
 
 def tiles_of(pos, TQ, KT):
@@ -56,15 +60,22 @@ def tiles_of(pos, TQ, KT):
 
 
 def check_units(m, u, pos, seg_len):
-    tiles = tiles_of(np.asarray(pos), m["TQ"], m["KT"])
+    """The unit table: every query tile's key tiles covered exactly once, in segment order
+    (one whole-tile unit per query tile when nothing is split), heavy tiles first, and
+    each unit carrying its query tile's largest and smallest position."""
+    pos = np.asarray(pos)
+    tiles = tiles_of(pos, m["TQ"], m["KT"])
     assert m["n_qtiles"] == len(tiles)
-    if m["max_seg"] == 1:
-        assert len(u) == 0 and m["units_per_hgroup"] == m["n_qtiles"]
-        return
     assert m["units_per_hgroup"] == len(u)
+    assert m["contiguous"] == int(bool(np.all(np.diff(pos) == 1)))
+    if m["max_seg"] == 1:
+        seg_len = max(tiles)
+        assert len(u) == m["n_qtiles"]
     seen = {}
-    for qt, k0, nk, code in u:
+    for qt, k0, nk, code, kmax, kmin, z0, z1 in u:
         seg, nseg = code >> 16, code & 0xFFFF
+        toks = pos[qt * m["TQ"]:(qt + 1) * m["TQ"]]
+        assert kmax == toks.max() and kmin == toks.min() and z0 == 0 and z1 == 0
         seen.setdefault(int(qt), []).append((int(k0), int(nk), int(seg), int(nseg)))
     assert sorted(seen) == list(range(len(tiles)))          # every query tile has units
     order = [int(q) for q in u[:, 0]]
@@ -79,7 +90,8 @@ def check_units(m, u, pos, seg_len):
             assert k0 == k and 1 <= nk <= seg_len
             k += nk
         assert k == tiles[qt]
-        assert all(nk == seg_len for _, nk, _, _ in segs[:-1])
+        if m["max_seg"] > 1:
+            assert all(nk == seg_len for _, nk, _, _ in segs[:-1])
     assert m["max_seg"] == max(len(s) for s in seen.values())
 
 
@@ -112,7 +124,8 @@ def test_short_causal_prompts_split_with_the_documented_length(hc, g):
         hgroups = n_head_kv * m["n_hsub"]
         tiles = tiles_of(pos, m["TQ"], m["KT"])
         if hgroups * m["n_qtiles"] >= 512:
-            assert m["max_seg"] == 1 and len(u) == 0
+            assert m["max_seg"] == 1
+            check_units(m, u, pos, 0)
             continue
         seg_len = seg_length(hc, tiles, hgroups, nt, n_head, hd_kv)
         check_units(m, u, pos, seg_len)
@@ -138,11 +151,13 @@ def test_forced_segment_lengths_and_no_split(hc):
         m, u = plan(hc, pos, 16, 8, 128, force)
         check_units(m, u, pos, force)
     m, u = plan(hc, pos, 16, 8, 128, -1)
-    assert m["max_seg"] == 1 and len(u) == 0
+    assert m["max_seg"] == 1
+    check_units(m, u, pos, 0)
     # Large prompts fill the chip unsplit, unless a length is forced.
     big = np.arange(4096, dtype=np.int32)
     m, u = plan(hc, big, 16, 8, 128)
-    assert m["max_seg"] == 1 and len(u) == 0 and m["units_per_hgroup"] == 128
+    assert m["max_seg"] == 1 and m["units_per_hgroup"] == 128
+    check_units(m, u, big, 0)
     m, u = plan(hc, big, 16, 8, 128, 16)
     check_units(m, u, big, 16)
 
