@@ -491,17 +491,21 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     }
 }
 
-// K3: one workgroup per (batch entry, query head) with more than one chunk.  One pass:
-// each thread owns one output dim and a slice of the chunks, and folds its chunks'
-// records (m, l, acc[d]) into a running (M, L, A) by log-sum-exp, eight chunks per trip
-// (their loads are independent, so they are in flight together); the slices are then
-// merged the same way through LDS.  Every chunk record is read once, in one wave of
-// loads, so a merge costs one global-memory round trip.
+// K3: one workgroup per (batch entry, query head) with more than one chunk.  Each thread
+// owns 4 consecutive output dims (one 16-byte load per record) and a slice of the chunks
+// (256 / (HD/4) slices: 8 for head dim 128), and folds its chunks' records (m, l,
+// acc[d..d+3]) into a running (M, L, A) by log-sum-exp, eight chunks per trip (their
+// loads are independent, so they are in flight together); the slices are then merged
+// the same way through LDS.  A window of up to 8 x slices chunks (64 for head dim 128)
+// is merged in one trip of loads.
 template <int HD>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
 {
-    constexpr int SLICES = 256 / HD;   // chunk slices per output dim
-    __shared__ float sM[256], sL[256], sA[256];
+    constexpr int QPR = HD / 4;                          // dim quads per record
+    constexpr int SLICES = 256 / QPR;                    // chunk slices
+    constexpr int NT = QPR * SLICES;                     // threads with a (quad, slice)
+    __shared__ float sM[NT], sL[NT];
+    __shared__ floatx4 sA[NT];
     const int b = blockIdx.x;
     const int h = blockIdx.y;
     const int c0 = p.cbase[b], c1 = p.cbase[b + 1];
@@ -509,60 +513,65 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
     const int tid = threadIdx.x;
     const float *base = p.part + (int64_t)h * (HD + 4);
     const int64_t cstride = (int64_t)p.n_head * (HD + 4);
-    const int d = tid % HD;
-    const int slice = tid / HD;
+    const int quad = tid % QPR;
+    const int slice = tid / QPR;
 
-    float M = -INFINITY, L = 0.0f, A = 0.0f;
-    int c = c0 + slice;
-    for (; c + 7 * SLICES < c1; c += 8 * SLICES) {
-        float mm[8], ll[8], aa[8];
+    float M = -INFINITY, L = 0.0f;
+    floatx4 A = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < NT) {
+        int c = c0 + slice;
+        for (; c + 7 * SLICES < c1; c += 8 * SLICES) {
+            float mm[8], ll[8];
+            floatx4 aa[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float *rec = base + (int64_t)(c + j * SLICES) * cstride;
-            mm[j] = rec[0];
-            ll[j] = rec[1];
-            aa[j] = rec[4 + d];
+            for (int j = 0; j < 8; j++) {
+                const float *rec = base + (int64_t)(c + j * SLICES) * cstride;
+                mm[j] = rec[0];
+                ll[j] = rec[1];
+                aa[j] = *reinterpret_cast<const floatx4 *>(rec + 4 + 4 * quad);
+            }
+            float mn = M;
+#pragma unroll
+            for (int j = 0; j < 8; j++) mn = fmaxf(mn, mm[j]);   // finite: chunks hold rows
+            const float r = fast_exp2(M - mn);                   // 0 while M is -inf
+            L *= r;
+            A *= r;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float w = fast_exp2(mm[j] - mn);
+                L += w * ll[j];
+                A += w * aa[j];
+            }
+            M = mn;
         }
-        float mn = M;
-#pragma unroll
-        for (int j = 0; j < 8; j++) mn = fmaxf(mn, mm[j]);   // finite: chunks hold rows
-        const float r = fast_exp2(M - mn);                   // 0 while M is -inf
-        L *= r;
-        A *= r;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float w = fast_exp2(mm[j] - mn);
-            L += w * ll[j];
-            A += w * aa[j];
+        for (; c < c1; c += SLICES) {
+            const float *rec = base + (int64_t)c * cstride;
+            const float mc = rec[0];
+            const float mn = fmaxf(M, mc);
+            const float r = fast_exp2(M - mn), w = fast_exp2(mc - mn);
+            L = L * r + w * rec[1];
+            A = A * r + w * *reinterpret_cast<const floatx4 *>(rec + 4 + 4 * quad);
+            M = mn;
         }
-        M = mn;
+        sM[tid] = M;
+        sL[tid] = L;
+        sA[tid] = A;
     }
-    for (; c < c1; c += SLICES) {
-        const float *rec = base + (int64_t)c * cstride;
-        const float mc = rec[0];
-        const float mn = fmaxf(M, mc);
-        const float r = fast_exp2(M - mn), w = fast_exp2(mc - mn);
-        L = L * r + w * rec[1];
-        A = A * r + w * rec[4 + d];
-        M = mn;
-    }
-    sM[tid] = M;
-    sL[tid] = L;
-    sA[tid] = A;
     __syncthreads();
-    if (tid < HD) {
+    if (tid < QPR) {
         float Mt = -INFINITY;
 #pragma unroll
-        for (int sl = 0; sl < SLICES; sl++) Mt = fmaxf(Mt, sM[sl * HD + tid]);
-        float Lt = 0.0f, At = 0.0f;
+        for (int sl = 0; sl < SLICES; sl++) Mt = fmaxf(Mt, sM[sl * QPR + tid]);
+        float Lt = 0.0f;
+        floatx4 At = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int sl = 0; sl < SLICES; sl++) {
             // A slice with no chunk has M = -inf and contributes exp2(-inf) * 0 = 0.
-            const float w = fast_exp2(sM[sl * HD + tid] - Mt);
-            Lt += w * sL[sl * HD + tid];
-            At += w * sA[sl * HD + tid];
+            const float w = fast_exp2(sM[sl * QPR + tid] - Mt);
+            Lt += w * sL[sl * QPR + tid];
+            At += w * sA[sl * QPR + tid];
         }
-        p.out[((int64_t)b * p.n_head + h) * HD + tid] = At / Lt;
+        *reinterpret_cast<floatx4 *>(p.out + ((int64_t)b * p.n_head + h) * HD + 4 * tid) = At / Lt;
     }
 }
 
