@@ -7,6 +7,7 @@
 #include <string>
 
 #include "plan.hpp"
+#include "rope_consts.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -91,6 +92,17 @@ int hc_plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t n_he
 }
 
 int64_t hc_max_part_bytes(void) { return kvc::kMaxPartBytes; }
+
+// The constants of the RoPE table's exact evaluation: the digits of 2/pi (words) and
+// pi/2, ln 2 as hi/lo pairs (dd = {pi/2 hi, lo, ln 2 hi, lo}).  Returns the word count.
+int32_t hc_rope_consts(uint32_t *words, double *dd)
+{
+    static const uint32_t w[KVC_TWO_OVER_PI_NWORDS] = {KVC_TWO_OVER_PI_WORDS};
+    std::copy(w, w + KVC_TWO_OVER_PI_NWORDS, words);
+    const double d[4] = {KVC_PI_2_HI, KVC_PI_2_LO, KVC_LN2_HI, KVC_LN2_LO};
+    std::copy(d, d + 4, dd);
+    return KVC_TWO_OVER_PI_NWORDS;
+}
 
 int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
 {

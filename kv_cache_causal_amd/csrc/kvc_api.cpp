@@ -168,6 +168,15 @@ void staging_abort(Staging &st)
     if (!st.inflight.empty() && st.inflight.back().ev == nullptr) st.inflight.pop_back();
 }
 
+// KVC_ROPE_EXACT=1 builds RoPE tables with every entry evaluated in double-double
+// rather than only the few the f64 evaluation cannot certify (tests of that path; the
+// entries are the same).
+bool env_rope_exact()
+{
+    const char *e = std::getenv("KVC_ROPE_EXACT");
+    return e && std::atoi(e) != 0;
+}
+
 kvc_status get_table(const kvc_cache *c, int32_t hd, float base, float fscale, hipStream_t s,
                      const float2 **out)
 {
@@ -181,7 +190,8 @@ kvc_status get_table(const kvc_cache *c, int32_t hd, float base, float fscale, h
     const size_t bytes = (size_t)c->g.capacity * (size_t)(hd / 2) * sizeof(float2);
     if (hipMalloc(reinterpret_cast<void **>(&t.dev), bytes) != hipSuccess)
         return fail(KVC_E_NOMEM, "RoPE table allocation failed");
-    hipError_t e = kvc::launch_rope_table(t.dev, c->g.capacity, hd, base, fscale, s);
+    hipError_t e = kvc::launch_rope_table(t.dev, c->g.capacity, hd, base, fscale,
+                                          env_rope_exact(), s);
     if (e != hipSuccess) {
         (void)hipFree(t.dev);
         return hip_fail(e, "rope table kernel");

@@ -37,8 +37,10 @@ __host__ __device__ inline int64_t q8_scale_index(int64_t row, int32_t j, int32_
 }
 
 // ---- RoPE cos/sin table: tab[p][i] = (cos, sin) of f32(p) * speed_i, p < rows ---------
+// Every entry is the correctly rounded f32; exact = true skips the certified f64 fast
+// path and evaluates every entry in double-double (tests of that path).
 hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
-                             float freq_scale, hipStream_t s);
+                             float freq_scale, bool exact, hipStream_t s);
 
 // ---- K1: RoPE(q, k) + in-place K/V row store ------------------------------------------
 // Up to kInlineTokens positions / sequence ids ride in the kernel arguments (no upload);

@@ -163,6 +163,28 @@ def pin_cos_sin_mpmath_sample(o: Oracle):
             assert cs[i] == rn32(mpmath.cos(th)) and sn[i] == rn32(mpmath.sin(th)), (hd, p, i)
 
 
+def pin_rope_near_ties(o: Oracle):
+    """At angles and speeds whose exact cos, sin or speed lies within about 2^-53 of the
+    midpoint of two f32 values (tests/golden/rope_near_ties.json, found by a seeded
+    search), the oracle still gives the correctly rounded f32 (mpmath at 60 digits).
+    An angle is read through pair 0 at position 1 (speed freq_scale, so the angle is
+    freq_scale itself); a speed fs / base^(1/2) through pair 1 of head dim 4."""
+    g = golden("rope_near_ties.json")
+    with mpmath.workdps(60):
+        for a in g["angles"]:
+            th = np.uint32(a["theta_bits"]).view(np.float32)
+            cs, sn = o.rope_cos_sin(2, 1.0e4, float(th), 1)
+            t = mpmath.mpf(float(th))
+            assert f32bits(cs[0]) == f32bits(rn32(mpmath.cos(t))), float(th)
+            assert f32bits(sn[0]) == f32bits(rn32(mpmath.sin(t))), float(th)
+        for sp in g["speeds"]:
+            fs = np.uint32(sp["freq_scale_bits"]).view(np.float32)
+            base = np.uint32(sp["base_bits"]).view(np.float32)
+            inv = o.rope_inv_freq(4, float(base), float(fs))
+            want = rn32(mpmath.mpf(float(fs)) / mpmath.sqrt(mpmath.mpf(float(base))))
+            assert f32bits(inv[1]) == f32bits(want), (float(fs), float(base))
+
+
 def pin_rope_pos0_identity(o: Oracle):
     """Position 0 turns every pair by 0 rad: RoPE is the identity, bit for bit, on
     N(0,1) data (which never holds a signed zero)."""
@@ -851,6 +873,7 @@ ALL_PINS = [
     pin_inv_freq_correctly_rounded,
     pin_rope_worked_example,
     pin_cos_sin_correctly_rounded,
+    pin_rope_near_ties,
     pin_rope_pos0_identity,
     pin_rope_brute_force,
     pin_rope_norm_and_relative_position,

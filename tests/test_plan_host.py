@@ -192,3 +192,21 @@ def test_decode_chunk_rows(hc):
         assert f(1 << 26, br, 0) == (1 << 26) // 2048         # large: ~2048 workgroups
         assert f(512 * 40, br, 0) == max(br, -(-40 // br) * br)   # small: ~512 workgroups
         assert f(10_000, br, 100) == -(-100 // br) * br        # forced, rounded up to br
+
+
+def test_rope_exact_evaluation_constants(hc):
+    """The digits of 2/pi and the double-double pi/2 and ln 2 the RoPE table's exact path
+    uses, against 400-bit values: every word, and hi/lo the nearest doubles to the value
+    and to its remainder."""
+    import mpmath
+    hc.hc_rope_consts.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hc.hc_rope_consts.restype = ctypes.c_int32
+    words = np.zeros(16, np.uint32)
+    dd = np.zeros(4, np.float64)
+    n = hc.hc_rope_consts(words.ctypes.data, dd.ctypes.data)
+    with mpmath.workprec(400):
+        digits = int(mpmath.floor(2 / mpmath.pi * mpmath.mpf(2) ** (32 * n)))
+        want = [(digits >> (32 * (n - 1 - k))) & 0xFFFFFFFF for k in range(n)]
+        assert [int(w) for w in words[:n]] == want
+        for (hi, lo), x in (((dd[0], dd[1]), mpmath.pi / 2), ((dd[2], dd[3]), mpmath.log(2))):
+            assert hi == float(x) and lo == float(x - mpmath.mpf(float(x)))
