@@ -299,14 +299,16 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
     const Slice K{kreg, kreg + p.scale_off, qrows, nkt, hk};
     const Slice V{vreg, vreg + p.scale_off, qrows, nkt, hk};
 
-    // The lane's query values in the order its row values arrive (IO::dim).
+    // The lane's query values in the order its row values arrive (IO::dim).  Loaded here,
+    // scaled only after the first step's row loads are issued (below), so that the query
+    // and the first rows are in flight together.
     float qf[GP][kDimsPerLane];
 #pragma unroll
     for (int g = 0; g < GP; g++) {
         const bool ok = g0 + g < G;
         const float *qrow = p.q + ((int64_t)b * p.n_head + (hk * G + (ok ? g0 + g : 0))) * p.hd;
 #pragma unroll
-        for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = ok ? qrow[IO::dim(li, i)] * p.qscale : 0.0f;
+        for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = qrow[IO::dim(li, i)];
     }
 
     float m[GP], l[GP], acc[GP][kDimsPerLane];
@@ -420,7 +422,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         }
     };
 
+    __builtin_amdgcn_sched_barrier(0);
     load(kA, vA, kqA, vqA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < GP; g++) {
+        const bool ok = g0 + g < G;
+#pragma unroll
+        for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = ok ? qf[g][i] * p.qscale : 0.0f;
+    }
     for (int st = 0; st < nsteps; st += 2) {
         if (st + 1 < nsteps) load(kB, vB, kqB, vqB, st + 1);
         consume(kA, vA, kqA, vqA, st);
