@@ -234,33 +234,28 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         // Tiles reaching past the smallest position hold keys some query must not weigh.
         const bool diag = key0 + KT - 1 > kmin;
         __syncthreads();  // every wave is done with the previous tile
+        // In such a tile a non-finite V value is stored as 0 (its neighbours unchanged;
+        // checked in registers before the store) and the block is flagged: 0 * inf in the
+        // products would turn the zero weight of a query whose window does not hold it into
+        // NaN; the queries whose windows hold one add it at the end.  In the other tiles
+        // every weight is positive and the products carry inf and NaN as they are.
+        bool vbad = false;
 #pragma unroll
         for (int j = 0; j < LD; j++) {
             TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
             if (tail && key0 + trow + j * RSTEP > kmax) vreg[j] = typename TIO::Raw{};
-            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
-        }
-        __syncthreads();
-        // In such a tile a non-finite V value becomes 0 (its neighbours unchanged; each
-        // thread cleans the chunks it stored) and the block is flagged: 0 * inf in the
-        // products would turn the zero weight of a query whose window does not hold it
-        // into NaN; the queries whose windows hold one add it at the end.  In the other
-        // tiles every weight is positive and the products carry inf and NaN as they are.
-        if (diag) {
-            bool vbad = false;
-#pragma unroll
-            for (int j = 0; j < LD; j++) {
-                float *vp = &Vs[(trow + j * RSTEP) * VSTR + tcol];
+            if (diag) {
 #pragma unroll
                 for (int i = 0; i < CH; i++) {
-                    const bool f = __builtin_isfinite(vp[i]);
+                    const bool f = __builtin_isfinite(vreg[j][i]);
                     vbad |= !f;
-                    if (!f) vp[i] = 0.0f;
+                    vreg[j][i] = f ? vreg[j][i] : 0.0f;
                 }
             }
-            if (vbad) s_vbad = 1;
-            __syncthreads();
+            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
         }
+        if (vbad) s_vbad = 1;
+        __syncthreads();
         if (kt + 1 < kt1) fetch(key0 + KT);
 
         if (head_ok && key0 <= wmax) {
