@@ -26,6 +26,12 @@
 //   * Causality from data: a block scans key tiles up to the max position of its tokens;
 //     a wave skips tiles beyond its own max; the per-element mask (key > pos) is a select.
 //   * Heavy query tiles (late positions) are launched first to shorten the tail.
+//   * K and V tiles come into LDS by direct-to-LDS loads, each half of a tile while the
+//     other half's products run: K(t+1)'s loads are issued once every wave has read K(t)
+//     (they land during PV(t)), V(t+1)'s once every wave has read V(t) (they land during
+//     S(t+1)).  No registers hold the tiles in flight and no LDS stores are issued for
+//     them (staging through registers and LDS stores took a quarter of each tile's time
+//     on a 4,096-token prompt, by per-tile timestamps, and was 2-4% slower).
 //   * Short prompts give too few query tiles to fill 256 CUs, and each would walk its key
 //     tiles one after another.  Then the host cuts every query tile's key range into
 //     segments (same tile count each, the last one shorter); a workgroup scans one
@@ -62,11 +68,15 @@ struct PrefillCfg {
     static constexpr int KT = prefill_key_tile(HD);  // keys per tile
     static constexpr int KB = KT / 16;              // 16-key blocks per tile
     static constexpr int DQ = HD / 4;               // dims per lane group
-    // LDS row strides (floats), measured with a bank-conflict probe on gfx950: the
-    // K-fragment reads (16 rows, one column) cost the least with 4 floats of padding,
-    // the V-fragment reads (contiguous row pieces) are conflict-free unpadded.
-    static constexpr int KSTR = HD + 4;
+    // LDS row strides (floats): rows are unpadded, since the direct-to-LDS tile loads
+    // write contiguous 1 KB pieces.  The K-fragment reads (16 rows, one column) are spread
+    // over the banks by a swizzle instead (KSWZ below), which a bank-conflict probe on
+    // gfx950 measured as good as 4 floats of padding; the V-fragment reads (contiguous row
+    // pieces) are conflict-free unpadded.
+    static constexpr int KSTR = HD;
     static constexpr int VSTR = HD;
+    // K swizzle: 16-byte chunk c of tile row r sits at chunk position c ^ (r mod KSWZ).
+    static constexpr int KSWZ = (HD / 4) < 16 ? (HD / 4) : 16;
     static constexpr int NDB = HD / 16;             // 16-dim output blocks
     static constexpr int VEC = NDB >= 4 ? 4 : NDB;  // output blocks fed by one V read
     static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
@@ -87,20 +97,29 @@ __device__ __forceinline__ float code_to_f32(int32_t w, int k)
     return f;
 }
 
-// How the 256 threads stage one K or V tile (KT rows x HD values) from an f32 region (or
-// the f32 copy of a binary16 / Q8_0 window) into the LDS tile: each thread moves LD
-// chunks of CH consecutive values, one 16-byte load each.
-template <int HD, typename KVT>
-struct TileIO;
-template <int HD>
-struct TileIO<HD, float> {
-    static constexpr int CH = 4;
-    typedef floatx4 Raw;
-    static __device__ __forceinline__ void put(float *lds, const Raw &r)
-    {
-        *reinterpret_cast<floatx4 *>(lds) = r;
-    }
-};
+// K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at the LDS address in M0 + 16 l; no registers hold them and no LDS store
+// instructions are issued).  The load is written in inline assembly: the compiler's wait
+// insertion treats every LDS read after such a load as depending on it and drains all
+// loads in flight first, which would serialise the next tile's loads with this tile's
+// reads.  The kernel waits for its own loads instead (wait_tile_dma), at points where
+// only one tile's loads are outstanding.  M0 is saved and restored around the load (the
+// kernel uses it nowhere else), with the wait states the hardware needs after writing it.
+__device__ __forceinline__ void tile_dma16(const void *g, uint32_t lds_base)
+{
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "s_nop 1\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_nop 1\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "v"(g), "s"(lds_base)
+                 : "memory");
+}
+__device__ __forceinline__ void wait_tile_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Split-K record of one (segment, token, head): O[HD] unnormalised, then m (base 2), l and,
 // in segment 0's record, the token's segment count.
 template <int HD>
@@ -112,15 +131,14 @@ __device__ __forceinline__ float *part_record(const PrefillParams &p, int seg, i
 template <int HD, typename KVT>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_t nblocks)
 {
+    static_assert(std::is_same<KVT, float>::value, "f32 tiles (other formats are widened first)");
     using C = PrefillCfg<HD>;
-    using TIO = TileIO<HD, KVT>;
     constexpr int KT = C::KT, KB = C::KB, DQ = C::DQ, NDB = C::NDB, VEC = C::VEC;
-    constexpr int KSTR = C::KSTR, VSTR = C::VSTR;
-    constexpr int CH = TIO::CH;
-    constexpr int LD = KT * HD / (256 * CH);   // chunks per thread per tile (K or V)
-    static_assert(LD * 256 * CH == KT * HD && LD >= 1, "tile split");
-    __shared__ float Ks[KT * KSTR];
-    __shared__ float Vs[KT * VSTR];
+    constexpr int KSTR = C::KSTR, VSTR = C::VSTR, F = C::KSWZ;
+    constexpr int LD = KT * HD / (256 * 4);   // 1 KB loads per wave per tile (K or V)
+    static_assert(LD * 256 * 4 == KT * HD && LD >= 1, "tile split");
+    __shared__ __align__(16) float Ks[KT * KSTR];
+    __shared__ __align__(16) float Vs[KT * VSTR];
     __shared__ int s_vbad;   // 1 once a tile of this block held a non-finite V value
 
     // XCD-aware mapping: consecutive workgroups go to the 8 XCDs in turn, so workgroup b
@@ -177,30 +195,35 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     const KVT *Kh = static_cast<const KVT *>(p.kc) + hk * HD;
     const KVT *Vh = static_cast<const KVT *>(p.vc) + hk * HD;
 
-    // Tile staging: thread tid moves chunk #(tid + 256 j) of the tile, j < LD, i.e. row
-    // tid / (HD/CH) + j * RSTEP, values (tid % (HD/CH)) * CH onwards.  Addresses are a
-    // uniform tile base plus a per-thread 32-bit byte offset.  Regions are padded to a
+    // Tile staging: load j of wave w moves bytes [(w LD + j) 1024, +1024) of the K (V)
+    // tile, lane l's 16 bytes at + 16 l, K rows swizzled (KSWZ).  Regions are padded to a
     // whole number of 64-row tiles (zero rows past the capacity, beyond every position and
-    // so masked), so every tile load is inside the region.  The first tile's loads are
-    // issued before the query's; each next tile's before this tile's MFMAs.
-    constexpr int RSTEP = 256 * CH / HD;       // rows between a thread's chunks
-    const int trow = tid / (HD / CH);
-    const int tcol = (tid % (HD / CH)) * CH;
-    const uint32_t toff = (uint32_t)(trow * nkt + tcol) * (uint32_t)sizeof(KVT);
-    const int64_t jstride = (int64_t)RSTEP * nkt * (int64_t)sizeof(KVT);
-    // Native vector registers: with struct types the compiler turns these unconditional
-    // copies into an aggregate copy and keeps the arrays in scratch memory.
-    typename TIO::Raw kreg[LD], vreg[LD];
-    auto fetch = [&](int key0) {
+    // so masked), so every tile row read is inside the region.
+    constexpr int RBYTES = HD * 4;
+    const uint32_t ks_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) float *)Ks) + wave * LD * 1024);
+    const uint32_t vs_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) float *)Vs) + wave * LD * 1024);
+    auto dma_k = [&](int key0) {
         const char *kb0 = reinterpret_cast<const char *>(Kh + (int64_t)key0 * nkt);
+#pragma unroll
+        for (int j = 0; j < LD; j++) {
+            const int o = (wave * LD + j) * 1024 + lane * 16;
+            const int r = o / RBYTES, pch = (o % RBYTES) / 16;
+            tile_dma16(kb0 + (int64_t)r * nkt * 4 + (pch ^ (r & (F - 1))) * 16, ks_base + j * 1024);
+        }
+    };
+    auto dma_v = [&](int key0) {
         const char *vb0 = reinterpret_cast<const char *>(Vh + (int64_t)key0 * nkt);
 #pragma unroll
         for (int j = 0; j < LD; j++) {
-            kreg[j] = *reinterpret_cast<const typename TIO::Raw *>(kb0 + j * jstride + toff);
-            vreg[j] = *reinterpret_cast<const typename TIO::Raw *>(vb0 + j * jstride + toff);
+            const int o = (wave * LD + j) * 1024 + lane * 16;
+            const int r = o / RBYTES, pch = (o % RBYTES) / 16;
+            tile_dma16(vb0 + (int64_t)r * nkt * 4 + pch * 16, vs_base + j * 1024);
         }
     };
-    fetch(kt0 * KT);
+    dma_k(kt0 * KT);
+    dma_v(kt0 * KT);
 
     // Q fragment: dims [grp*DQ, grp*DQ + DQ) of query row (t, h), pre-multiplied by
     // scale * log2(e) so the S^T accumulators are already in base-2 units.
@@ -225,40 +248,25 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
     for (int db = 0; db < NDB; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f;
 
+    // Per tile: S and the softmax read K(t); a barrier; K(t+1)'s loads are issued (they
+    // land while PV(t) runs); PV reads V(t); a barrier once this wave's K(t+1) has
+    // landed; V(t+1)'s loads are issued (they land while S(t+1) runs) and waited for
+    // before the next barrier.  The first tile's K and V were issued before the query.
+    float sv[KB][4];
     for (int kt = kt0; kt < kt1; kt++) {
         const int key0 = kt * KT;
         // V rows past the largest position among the block's queries have weight 0 for
-        // every query; they are stored as zeros, so that a non-finite value in a row no
+        // every query; they are set to zero, so that a non-finite value in a row no
         // window of the block contains cannot turn 0 * V into NaN.
         const bool tail = key0 + KT - 1 > kmax;
         // Tiles reaching past the smallest position hold keys some query must not weigh.
         const bool diag = key0 + KT - 1 > kmin;
-        __syncthreads();  // every wave is done with the previous tile
-        // In such a tile a non-finite V value is stored as 0 (its neighbours unchanged;
-        // checked in registers before the store) and the block is flagged: 0 * inf in the
-        // products would turn the zero weight of a query whose window does not hold it into
-        // NaN; the queries whose windows hold one add it at the end.  In the other tiles
-        // every weight is positive and the products carry inf and NaN as they are.
-        bool vbad = false;
-#pragma unroll
-        for (int j = 0; j < LD; j++) {
-            TIO::put(&Ks[(trow + j * RSTEP) * KSTR + tcol], kreg[j]);
-            if (tail && key0 + trow + j * RSTEP > kmax) vreg[j] = typename TIO::Raw{};
-            if (diag) {
-#pragma unroll
-                for (int i = 0; i < CH; i++) {
-                    const bool f = __builtin_isfinite(vreg[j][i]);
-                    vbad |= !f;
-                    vreg[j][i] = f ? vreg[j][i] : 0.0f;
-                }
-            }
-            TIO::put(&Vs[(trow + j * RSTEP) * VSTR + tcol], vreg[j]);
+        const bool active = head_ok && key0 <= wmax;
+        if (kt == kt0) {
+            wait_tile_dma();
+            __syncthreads();
         }
-        if (vbad) s_vbad = 1;
-        __syncthreads();
-        if (kt + 1 < kt1) fetch(key0 + KT);
-
-        if (head_ok && key0 <= wmax) {
+        if (active) {
             // S^T = K Q^T for KB blocks of 16 keys; independent accumulators interleaved.
             floatx4 sacc[KB];
 #pragma unroll
@@ -268,7 +276,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                 float4 kf[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++)
-                    kf[kb] = *reinterpret_cast<const float4 *>(&Ks[(kb * 16 + qc) * KSTR + grp * DQ + s]);
+                    kf[kb] = *reinterpret_cast<const float4 *>(&Ks[(kb * 16 + qc) * KSTR + (((grp * DQ + s) / 4) ^ (qc & (F - 1))) * 4]);
 #pragma unroll
                 for (int kb = 0; kb < KB; kb++) sacc[kb] = mfma4(kf[kb].x, qf[s + 0], sacc[kb]);
 #pragma unroll
@@ -280,7 +288,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
             }
             // Mask keys beyond this query's position (only tiles that reach past the
             // wave's smallest position need the compare).
-            float sv[KB][4];
             float tmax = -INFINITY;
             if (key0 + KT - 1 <= wmin) {
 #pragma unroll
@@ -323,6 +330,42 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                     l += pr;
                 }
             m = mn;
+        }
+        wait_tile_dma();   // V(t) landed (issued last tile, or with K for the first)
+        __syncthreads();   // K(t) read by every wave; V(t) landed everywhere
+        if (kt + 1 < kt1) dma_k(key0 + KT);
+        // In a tile past the smallest position a non-finite V value is set to 0 (its
+        // neighbours unchanged) and the block is flagged: 0 * inf in the products would
+        // turn the zero weight of a query whose window does not hold it into NaN; the
+        // queries whose windows hold one add it at the end.  In the other tiles every
+        // weight is positive and the products carry inf and NaN as they are.  This pass
+        // reads and rewrites the tile in LDS (one more barrier), on such tiles only.
+        if (tail || diag) {
+            bool vbad = false;
+#pragma unroll
+            for (int j = 0; j < LD; j++) {
+                const int idx = (tid + 256 * j) * 4;
+                const int row = idx / HD;
+                floatx4 v = *reinterpret_cast<const floatx4 *>(&Vs[idx]);
+                bool chg = false;
+                if (tail && key0 + row > kmax) {
+                    v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                    chg = true;
+                } else if (diag) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const bool f = __builtin_isfinite(v[i]);
+                        vbad |= !f;
+                        chg |= !f;
+                        v[i] = f ? v[i] : 0.0f;
+                    }
+                }
+                if (chg) *reinterpret_cast<floatx4 *>(&Vs[idx]) = v;
+            }
+            if (vbad) s_vbad = 1;
+            __syncthreads();
+        }
+        if (active) {
             // O^T += V^T P^T.  k-step st = 4 kb + r uses key kb*16 + 4*grp + r for lane
             // group grp.  Output block db = VEC*j + e takes, for A row i, dim
             // 16*VEC*j + VEC*i + e, so one VEC-wide LDS read (dims 16*VEC*j + VEC*qc ...)
@@ -356,6 +399,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        wait_tile_dma();   // K(t+1) landed
+        __syncthreads();   // V(t) read by every wave; K(t+1) landed everywhere
+        if (kt + 1 < kt1) dma_v(key0 + KT);
     }
 
     // Non-finite V values inside this lane's window (keys of this unit's tiles up to its
