@@ -105,17 +105,21 @@ __device__ __forceinline__ float code_to_f32(int32_t w, int k)
 // reads.  The kernel waits for its own loads instead (wait_tile_dma), at points where
 // only one tile's loads are outstanding.  M0 is saved and restored around the load (the
 // kernel uses it nowhere else), with the wait states the hardware needs after writing it.
-__device__ __forceinline__ void tile_dma16(const void *g, uint32_t lds_base)
+// The address is a uniform 64-bit base in SGPRs plus a 32-bit per-lane offset: one VGPR
+// read per lane instead of two (the 64-bit per-lane form measured 4% slower on the
+// 4,096-token prompt, the loads being issued while the other wave of the SIMD runs its
+// MFMAs).
+__device__ __forceinline__ void tile_dma16(const void *base, uint32_t off, uint32_t lds_base)
 {
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %2\n\t"
+                 "s_mov_b32 m0, %3\n\t"
                  "s_nop 1\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
                  "s_nop 1\n\t"
                  "s_mov_b32 m0, %0"
                  : "=&s"(save)
-                 : "v"(g), "s"(lds_base)
+                 : "v"(off), "s"(base), "s"(lds_base)
                  : "memory");
 }
 __device__ __forceinline__ void wait_tile_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         for (int j = 0; j < LD; j++) {
             const int o = (wave * LD + j) * 1024 + lane * 16;
             const int r = o / RBYTES, pch = (o % RBYTES) / 16;
-            tile_dma16(kb0 + (int64_t)r * nkt * 4 + (pch ^ (r & (F - 1))) * 16, ks_base + j * 1024);
+            tile_dma16(kb0, (uint32_t)(r * nkt * 4 + (pch ^ (r & (F - 1))) * 16), ks_base + j * 1024);
         }
     };
     auto dma_v = [&](int key0) {
@@ -219,7 +223,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p, int32_
         for (int j = 0; j < LD; j++) {
             const int o = (wave * LD + j) * 1024 + lane * 16;
             const int r = o / RBYTES, pch = (o % RBYTES) / 16;
-            tile_dma16(vb0 + (int64_t)r * nkt * 4 + pch * 16, vs_base + j * 1024);
+            tile_dma16(vb0, (uint32_t)(r * nkt * 4 + pch * 16), vs_base + j * 1024);
         }
     };
     dma_k(kt0 * KT);
