@@ -32,7 +32,7 @@ Reported:
                  decode kernels did not)
   cpu_baseline   the plain C oracle on the host cores, on bounded samples
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 15] [--no-cpu-baseline]
                        [--no-long-context] [--kv f32|f16|q8_0] [--decode-runs] [--fused-qkv]
        python bench.py --workload long|layer|stack [--graph]
 """
@@ -145,7 +145,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU's clock ramps up over the first ~25 ms of sustained work: in a kernel trace of
+    # this step the prefill kernel took 2.16 ms on its first launch and settled at
+    # 1.83-1.85 ms from about the twelfth.  Fifteen untimed steps (~35 ms) reach that state.
+    ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the long-context decode object of the default run")
