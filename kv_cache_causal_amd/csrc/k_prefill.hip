@@ -79,23 +79,9 @@ struct PrefillCfg {
     static constexpr int KSWZ = (HD / 4) < 16 ? (HD / 4) : 16;
     static constexpr int NDB = HD / 16;             // 16-dim output blocks
     static constexpr int VEC = NDB >= 4 ? 4 : NDB;  // output blocks fed by one V read
-    static constexpr int LD = KT * (HD / 4) / 256;  // float4 per thread per tile (K or V)
 };
 
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
-
-// Signed byte k of w as f32 (one conversion with a sign-extending byte select).
-__device__ __forceinline__ float code_to_f32(int32_t w, int k)
-{
-    float f;
-    switch (k) {
-    case 0: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f) : "v"(w)); break;
-    case 1: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(w)); break;
-    case 2: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(w)); break;
-    default: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(w)); break;
-    }
-    return f;
-}
 
 // K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
 // bytes land at the LDS address in M0 + 16 l; no registers hold them and no LDS store
