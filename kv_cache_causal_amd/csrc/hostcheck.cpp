@@ -104,9 +104,9 @@ int32_t hc_rope_consts(uint32_t *words, double *dd)
     return KVC_TWO_OVER_PI_NWORDS;
 }
 
-int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
+int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
 {
-    return kvc::decode_chunk_rows(work, br, forced);
+    return kvc::decode_chunk_rows(work, br, hpb, forced);
 }
 
 }  // extern "C"

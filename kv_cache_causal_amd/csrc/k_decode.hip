@@ -10,9 +10,15 @@
 // Decode is a pure stream over K and V: every cached byte of the window is read once and
 // used G = n_head / n_head_kv times, so it is bound by HBM bandwidth (G/2 flop per byte).
 // Design for gfx950:
-//   * Workgroup = one (batch entry, kv head, chunk of rows); 4 wave64s.  Chunks are sized
-//     on the host so the grid fills the chip several times over; the workgroups of one
-//     chunk's kv heads are adjacent in dispatch order (DRAM page locality).
+//   * Workgroup = one (batch entry, chunk of rows, block of HPB kv heads); 4 wave64s, of
+//     which 4 / HPB share each kv head's rows.  Chunks are sized on the host so the grid
+//     fills the chip several times over; the workgroups of one chunk's head blocks are
+//     adjacent in dispatch order.  binary16 regions take 2 heads per workgroup (HPB = 2):
+//     each workgroup then reads 2 adjacent 256-byte slices of every row of its chunk,
+//     which streamed 6% faster in the batch decode than one slice per row.  f32 slices
+//     (512 bytes) stream best one head per workgroup (2 or 4 heads: 6-8% slower), and
+//     Q8_0 gained nothing from 2 or 4 (its decode is bound by its per-value arithmetic as
+//     much as by its 128-byte slices).
 //   * A row slice (hd_kv values of one kv head) is read by a group of LPR lanes: each
 //     lane holds 8 values (4 for larger head groups, to save registers) -- two float4
 //     loads of an f32 cache, or one 16-byte load of packed halves of a binary16 cache
@@ -252,26 +258,31 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
     m = mn;
 }
 
-template <int HD, int GP, typename KVT>
+template <int HD, int GP, typename KVT, int HPB>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
 {
     constexpr int kDimsPerLane = dims_per_lane<GP, KVT>();
     constexpr int kUnroll = rows_per_step<GP, KVT>();
     constexpr int LPR = HD / kDimsPerLane;   // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave per unrolled step
+    constexpr int WPH = kWaves / HPB;        // waves per kv head
     using IO = RowIO<KVT, kDimsPerLane, LPR>;
     using Raw = typename IO::Raw;
     static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "head dim");
+    static_assert(kWaves % HPB == 0, "heads per workgroup");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int li = lane % LPR;
     const int rg = lane / LPR;
-    // Linear grid, kv head fastest: the n_head_kv workgroups of one chunk are dispatched
-    // together and read the slices of the same rows at about the same time, so each row
-    // (n_head_kv * hd_kv floats, contiguous) is fetched while its DRAM page is open.
-    const int hk = blockIdx.x % p.n_head_kv;
-    const int cg = blockIdx.x / p.n_head_kv;
+    // Linear grid, head block fastest: the workgroups of one chunk are dispatched together
+    // and read the slices of the same rows at about the same time.  Waves wh * WPH ..
+    // wh * WPH + WPH - 1 take kv head hb * HPB + wh; wr numbers them within the head.
+    const int nhb = p.n_head_kv / HPB;
+    const int wh = wave / WPH;
+    const int wr = wave - wh * WPH;
+    const int hk = (blockIdx.x % nhb) * HPB + wh;
+    const int cg = blockIdx.x / nhb;
     const int G = p.n_head / p.n_head_kv;
 
     // Batch entry owning this chunk: cbase[b] <= cg < cbase[b + 1] (kernel arguments).
@@ -320,19 +331,19 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
         for (int d = 0; d < kDimsPerLane; d++) acc[g][d] = 0.0f;
     }
 
-    // Rows are consumed in steps of BR per workgroup; two register sets alternate so the
+    // Rows are consumed in steps of BR per kv head; two register sets alternate so the
     // loads of step i+1 are in flight while step i is reduced.  Row of unrolled row u of
     // a step starting at rb: instruction u of the wave reads RPW rows, RPW apart with row
-    // quads (the lane group's rows are the quad rb + 4 (wave RPW + rg) + 0..3, so steps
+    // quads (the lane group's rows are the quad rb + 4 (wr RPW + rg) + 0..3, so steps
     // start at r0 rounded down to a quad; rows before r0 are read and masked), adjacent
     // otherwise.
-    constexpr int BR = kWaves * RPW * kUnroll;
+    constexpr int BR = WPH * RPW * kUnroll;
     constexpr bool kQuads = IO::kQuads;
     static_assert(!kQuads || kUnroll == 4, "row quads need 4 rows per lane group per step");
     const int rbase = kQuads ? (r0 & ~3) : r0;
     const int nsteps = (r1 - rbase + BR - 1) / BR;
     auto row_of = [&](int rb, int u) {
-        return kQuads ? rb + (wave * RPW + rg) * 4 + u : rb + (u * kWaves + wave) * RPW + rg;
+        return kQuads ? rb + (wr * RPW + rg) * 4 + u : rb + (u * WPH + wr) * RPW + rg;
     };
     using Quad = typename IO::Quad;
     Raw kA[kUnroll], vA[kUnroll], kB[kUnroll], vB[kUnroll];
@@ -473,21 +484,23 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
 
     const int ngp = min(GP, G - g0);   // heads of this pass that exist
     float *out_b = p.out + (int64_t)b * p.n_head * HD;
-    for (int idx = threadIdx.x; idx < ngp * HD; idx += blockDim.x) {
-        const int g = idx / HD;
-        const int d = idx - g * HD;
+    for (int idx = threadIdx.x; idx < HPB * ngp * HD; idx += blockDim.x) {
+        const int bh = idx / (ngp * HD);   // kv head of the block
+        const int g = (idx - bh * ngp * HD) / HD;
+        const int d = idx - (bh * ngp + g) * HD;
+        const int w0 = bh * WPH;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm[w][g][0]);
+        for (int w = 0; w < WPH; w++) M = fmaxf(M, sm[w0 + w][g][0]);
         const float ref = (M == -INFINITY) ? 0.0f : M;
         float L = 0.0f, A = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) {
-            const float f = fast_exp2(sm[w][g][0] - ref);
-            L += f * sm[w][g][1];
-            A += f * sm[w][g][2 + d];
+        for (int w = 0; w < WPH; w++) {
+            const float f = fast_exp2(sm[w0 + w][g][0] - ref);
+            L += f * sm[w0 + w][g][1];
+            A += f * sm[w0 + w][g][2 + d];
         }
-        const int h = hk * G + g0 + g;
+        const int h = (hk - wh + bh) * G + g0 + g;
         if (nchunks == 1) {
             out_b[(int64_t)h * HD + d] = A / L;
         } else {
@@ -585,18 +598,27 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
     }
 }
 
+template <int HD, typename KVT, int HPB>
+void launch_split_hpb(const DecodeParams &p, hipStream_t s)
+{
+    const int G = p.n_head / p.n_head_kv;
+    const dim3 grid((unsigned)p.total_chunks * (unsigned)(p.n_head_kv / HPB)), block(256);
+    for (int g0 = 0; g0 < G; g0 += 8) {
+        const int left = G - g0;
+        if (left >= 5) decode_split_kernel<HD, 8, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
+        else if (left >= 3) decode_split_kernel<HD, 4, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
+        else if (left == 2) decode_split_kernel<HD, 2, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
+        else decode_split_kernel<HD, 1, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
+    }
+}
+
 template <int HD, typename KVT>
 void launch_split(const DecodeParams &p, hipStream_t s)
 {
-    const int G = p.n_head / p.n_head_kv;
-    const dim3 grid((unsigned)p.total_chunks * (unsigned)p.n_head_kv), block(256);
-    for (int g0 = 0; g0 < G; g0 += 8) {
-        const int left = G - g0;
-        if (left >= 5) decode_split_kernel<HD, 8, KVT><<<grid, block, 0, s>>>(p, g0);
-        else if (left >= 3) decode_split_kernel<HD, 4, KVT><<<grid, block, 0, s>>>(p, g0);
-        else if (left == 2) decode_split_kernel<HD, 2, KVT><<<grid, block, 0, s>>>(p, g0);
-        else decode_split_kernel<HD, 1, KVT><<<grid, block, 0, s>>>(p, g0);
+    if constexpr (sizeof(KVT) == 2) {
+        if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2>(p, s);
     }
+    launch_split_hpb<HD, KVT, 1>(p, s);
 }
 
 template <int HD>
@@ -617,21 +639,21 @@ hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
 }  // namespace
 
 namespace {
-// Rows per step of the split kernel for a query-head group of GP: a wave covers 64 * dims
-// / hd_kv rows per unrolled row.
+// Rows per step of the split kernel for a query-head group of GP with hpb kv heads per
+// workgroup: each of a head's 4 / hpb waves covers 64 * dims / hd_kv rows per unrolled row.
 template <int GP, typename KVT>
-int32_t step_rows(int32_t hd_kv)
+int32_t step_rows(int32_t hd_kv, int32_t hpb)
 {
-    return kWaves * (64 * dims_per_lane<GP, KVT>() / hd_kv) * rows_per_step<GP, KVT>();
+    return kWaves / hpb * (64 * dims_per_lane<GP, KVT>() / hd_kv) * rows_per_step<GP, KVT>();
 }
 template <typename KVT>
-int32_t step_rows_fmt(int32_t hd_kv, int32_t G)
+int32_t step_rows_fmt(int32_t hd_kv, int32_t G, int32_t hpb)
 {
     // The group of the first pass (launch_split): 8 heads from 5 up, then 4, 2, 1.
-    if (G >= 5) return step_rows<8, KVT>(hd_kv);
-    if (G >= 3) return step_rows<4, KVT>(hd_kv);
-    if (G == 2) return step_rows<2, KVT>(hd_kv);
-    return step_rows<1, KVT>(hd_kv);
+    if (G >= 5) return step_rows<8, KVT>(hd_kv, hpb);
+    if (G >= 3) return step_rows<4, KVT>(hd_kv, hpb);
+    if (G == 2) return step_rows<2, KVT>(hd_kv, hpb);
+    return step_rows<1, KVT>(hd_kv, hpb);
 }
 }  // namespace
 
@@ -673,11 +695,16 @@ hipError_t static_scratch_addr(int device, float **addr)
     return hipSuccess;
 }
 
-int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt)
+int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv)
 {
-    if (kv_fmt == kFmtQ8) return step_rows_fmt<int8_t>(hd_kv, G);
-    if (kv_fmt == kFmtF16) return step_rows_fmt<_Float16>(hd_kv, G);
-    return step_rows_fmt<float>(hd_kv, G);
+    return kv_fmt == kFmtF16 && n_head_kv % 2 == 0 ? 2 : 1;
+}
+
+int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt, int32_t hpb)
+{
+    if (kv_fmt == kFmtQ8) return step_rows_fmt<int8_t>(hd_kv, G, hpb);
+    if (kv_fmt == kFmtF16) return step_rows_fmt<_Float16>(hd_kv, G, hpb);
+    return step_rows_fmt<float>(hd_kv, G, hpb);
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)

@@ -262,10 +262,12 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         return t;
     };
     // Chunk size (plan.cpp); KVC_SPLIT_ROWS overrides it (tuning only, never the result).
-    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, n_head / c->g.n_head_kv, c->kv_fmt);
+    const int32_t hpb = kvc::decode_heads_per_block(c->kv_fmt, c->g.n_head_kv);
+    const int32_t br = kvc::decode_block_rows(c->g.hd_kv, n_head / c->g.n_head_kv, c->kv_fmt, hpb);
     int64_t total_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) total_rows += window_rows(b);
-    const int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, env_split_rows());
+    const int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, hpb,
+                                                env_split_rows());
     // Chunks of entry b: its window cut into pieces of at most `rows` rows (each run on
     // its own for an explicit window).
     auto chunks_of = [&](int32_t b) -> int64_t {
@@ -331,6 +333,7 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         p.layer = layer;
         p.kv_fmt = c->kv_fmt;
         p.rows_per_chunk = (int32_t)rows;
+        p.hpb = hpb;
         p.qscale = log2e_times(scale);
         int32_t chunks = 0;
         for (int32_t i = 0; i < n; i++) {

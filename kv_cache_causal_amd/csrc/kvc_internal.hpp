@@ -95,6 +95,7 @@ struct DecodeParams {
     int64_t region_bytes, scale_off;
     int32_t n, n_head, hd, n_head_kv, hd_kv, n_layer, layer, kv_fmt;
     int32_t rows_per_chunk, total_chunks;
+    int32_t hpb;             // kv heads per split-K workgroup (decode_heads_per_block)
     float qscale;            // scale * log2(e): scores are kept in base-2 units
     int32_t pos[kInlineEntries];
     int32_t seq[kInlineEntries];
@@ -107,10 +108,13 @@ struct DecodeParams {
 constexpr size_t kStaticScratchFloats = size_t(4) << 20;
 hipError_t static_scratch_addr(int device, float **addr);
 
+// kv heads per split-K workgroup for a region format: 2 for binary16 regions with an even
+// n_head_kv, else 1.
+int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv);
 // Rows per step of the split-K kernel that a call with query-head group G (n_head /
-// n_head_kv) launches first, for a kv head dim and region format (chunks should be a
-// multiple of it).
-int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt);
+// n_head_kv) launches first, for a kv head dim, region format and heads per workgroup
+// (chunks should be a multiple of it).
+int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt, int32_t hpb);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 
 // ---- K4: causal prefill with fp32 MFMA -------------------------------------------------

@@ -76,7 +76,7 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
     return pl;
 }
 
-int64_t decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
+int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
 {
     // A workgroup streams its chunk in steps of br rows, each step a memory round trip,
     // so a chunk of many steps is latency-bound unless many workgroups run.  Large work:
@@ -90,6 +90,9 @@ int64_t decode_chunk_rows(int64_t work, int32_t br, int64_t forced)
         if (work > 2048 * 512) rows = work / 2048;
         else if (work > 131072) rows = 512;
         else rows = work / 512;
+        // A workgroup of hpb kv heads gives each head 1/hpb of its waves: chunks 1/hpb as
+        // long keep the rows per wave, and the workgroup count, of one head per workgroup.
+        rows /= std::max<int32_t>(1, hpb);
     }
     return std::max<int64_t>(br, (rows + br - 1) / br * br);
 }

@@ -39,7 +39,8 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
                          int32_t hd_kv, int32_t force_seg);
 
 // Rows per decode chunk (a multiple of br, at least br) for `work` = total window rows x
-// kv heads of one call; forced > 0 overrides the choice (then rounded up to br).
-int64_t decode_chunk_rows(int64_t work, int32_t br, int64_t forced);
+// kv heads of one call, with hpb kv heads per workgroup; forced > 0 overrides the choice
+// (then rounded up to br).
+int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced);
 
 }  // namespace kvc

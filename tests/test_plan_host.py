@@ -24,7 +24,7 @@ def hc():
     L = ctypes.CDLL(HOSTCHECK)
     p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.hc_plan_prefill.argtypes = [p, i32, i32, i32, i32, i32, p, p, i32]
-    L.hc_decode_chunk_rows.argtypes = [i64, i32, i64]
+    L.hc_decode_chunk_rows.argtypes = [i64, i32, i32, i64]
     L.hc_decode_chunk_rows.restype = i64
     L.hc_max_part_bytes.restype = i64
     return L
@@ -181,17 +181,20 @@ def test_partial_records_stay_within_the_cap(hc):
 
 def test_decode_chunk_rows(hc):
     f = hc.hc_decode_chunk_rows
-    for br in (32, 64, 128):
-        prev = 0
-        for work in (1, 100, 10_000, 131_072, 131_073, 500_000, 1 << 20, (1 << 20) + 1, 1 << 26):
-            r = f(work, br, 0)
-            assert r >= br and r % br == 0
-            assert r >= prev                                  # never shrinks with work
-            prev = r
-        assert f(131_073, br, 0) == max(br, 512 // br * br)   # middle range: 512 rows
-        assert f(1 << 26, br, 0) == (1 << 26) // 2048         # large: ~2048 workgroups
-        assert f(512 * 40, br, 0) == max(br, -(-40 // br) * br)   # small: ~512 workgroups
-        assert f(10_000, br, 100) == -(-100 // br) * br        # forced, rounded up to br
+    for br in (16, 32, 64, 128):
+        for hpb in (1, 2, 4):
+            prev = 0
+            for work in (1, 100, 10_000, 131_072, 131_073, 500_000, 1 << 20, (1 << 20) + 1,
+                         1 << 26):
+                r = f(work, br, hpb, 0)
+                assert r >= br and r % br == 0
+                assert r >= prev                              # never shrinks with work
+                prev = r
+            up = lambda x: max(br, -(-x // br) * br)          # noqa: E731 (round up to br)
+            assert f(131_073, br, hpb, 0) == up(512 // hpb)        # middle range: 512 rows
+            assert f(1 << 26, br, hpb, 0) == up((1 << 26) // 2048 // hpb)   # ~2048 workgroups
+            assert f(512 * 40, br, hpb, 0) == up(40 // hpb)        # small: ~512 workgroups
+            assert f(10_000, br, hpb, 100) == up(100)              # forced, rounded up to br
 
 
 def test_rope_exact_evaluation_constants(hc):
