@@ -119,7 +119,9 @@ def _dev(t, name, numel=0):
 
 
 def _host_i32(a):
-    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    if not (type(a) is np.ndarray and a.dtype == np.int32 and a.ndim == 1
+            and a.flags.c_contiguous):
+        a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
     return a, a.ctypes.data
 
 

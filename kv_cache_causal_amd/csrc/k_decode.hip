@@ -258,8 +258,8 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
     m = mn;
 }
 
-template <int HD, int GP, typename KVT, int HPB>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32_t g0)
+template <int HD, int GP, typename KVT, int HPB, int E>
+__global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, int32_t g0)
 {
     constexpr int kDimsPerLane = dims_per_lane<GP, KVT>();
     constexpr int kUnroll = rows_per_step<GP, KVT>();
@@ -521,8 +521,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, int32
 // loads are independent, so they are in flight together); the slices are then merged
 // the same way through LDS.  A window of up to 8 x slices chunks (64 for head dim 128)
 // is merged in one trip of loads.
-template <int HD>
-__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
+template <int HD, int E>
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParamsT<E> p)
 {
     constexpr int QPR = HD / 4;                          // dim quads per record
     constexpr int SLICES = 256 / QPR;                    // chunk slices
@@ -598,42 +598,55 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams p)
     }
 }
 
-template <int HD, typename KVT, int HPB>
-void launch_split_hpb(const DecodeParams &p, hipStream_t s)
+template <int HD, typename KVT, int HPB, int E>
+void launch_split_hpb(const DecodeParamsT<E> &p, hipStream_t s)
 {
     const int G = p.n_head / p.n_head_kv;
     const dim3 grid((unsigned)p.total_chunks * (unsigned)(p.n_head_kv / HPB)), block(256);
     for (int g0 = 0; g0 < G; g0 += 8) {
         const int left = G - g0;
-        if (left >= 5) decode_split_kernel<HD, 8, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
-        else if (left >= 3) decode_split_kernel<HD, 4, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
-        else if (left == 2) decode_split_kernel<HD, 2, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
-        else decode_split_kernel<HD, 1, KVT, HPB><<<grid, block, 0, s>>>(p, g0);
+        if (left >= 5) decode_split_kernel<HD, 8, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
+        else if (left >= 3) decode_split_kernel<HD, 4, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
+        else if (left == 2) decode_split_kernel<HD, 2, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
+        else decode_split_kernel<HD, 1, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
     }
 }
 
-template <int HD, typename KVT>
-void launch_split(const DecodeParams &p, hipStream_t s)
+template <int HD, typename KVT, int E>
+void launch_split(const DecodeParamsT<E> &p, hipStream_t s)
 {
     if constexpr (sizeof(KVT) == 2) {
-        if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2>(p, s);
+        if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2, E>(p, s);
     }
-    launch_split_hpb<HD, KVT, 1>(p, s);
+    launch_split_hpb<HD, KVT, 1, E>(p, s);
 }
 
-template <int HD>
-hipError_t launch_hd(const DecodeParams &p, hipStream_t s)
+template <int HD, int E>
+hipError_t launch_hd(const DecodeParamsT<E> &p, hipStream_t s)
 {
     if constexpr (HD % kQ8Block == 0) {
-        if (p.kv_fmt == kFmtQ8) launch_split<HD, int8_t>(p, s);
+        if (p.kv_fmt == kFmtQ8) launch_split<HD, int8_t, E>(p, s);
     }
-    if (p.kv_fmt == kFmtF16) launch_split<HD, _Float16>(p, s);
-    else if (p.kv_fmt == kFmtF32) launch_split<HD, float>(p, s);
+    if (p.kv_fmt == kFmtF16) launch_split<HD, _Float16, E>(p, s);
+    else if (p.kv_fmt == kFmtF32) launch_split<HD, float, E>(p, s);
     if (p.total_chunks > p.n) {  // some entry spans several chunks
         const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head);
-        decode_combine_kernel<HD><<<cgrid, 256, 0, s>>>(p);
+        decode_combine_kernel<HD, E><<<cgrid, 256, 0, s>>>(p);
     }
     return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_by_hd(const DecodeParamsT<E> &p, hipStream_t s)
+{
+    switch (p.hd_kv) {
+    case 16: return launch_hd<16, E>(p, s);
+    case 32: return launch_hd<32, E>(p, s);
+    case 64: return launch_hd<64, E>(p, s);
+    case 128: return launch_hd<128, E>(p, s);
+    case 256: return launch_hd<256, E>(p, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -709,14 +722,18 @@ int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt, int32_t hpb)
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
 {
-    switch (p.hd_kv) {
-    case 16: return launch_hd<16>(p, s);
-    case 32: return launch_hd<32>(p, s);
-    case 64: return launch_hd<64>(p, s);
-    case 128: return launch_hd<128>(p, s);
-    case 256: return launch_hd<256>(p, s);
-    default: return hipErrorInvalidValue;
+    if (p.n <= kSmallInline) {
+        // Few entries: the same launches with an argument block sized for them.
+        DecodeParamsT<kSmallInline> sp;
+        static_cast<DecodeArgs &>(sp) = p;
+        for (int i = 0; i < kSmallInline; i++) {
+            sp.pos[i] = i < p.n ? p.pos[i] : 0;
+            sp.seq[i] = i < p.n ? p.seq[i] : 0;
+        }
+        for (int i = 0; i <= kSmallInline; i++) sp.cbase[i] = p.cbase[i < p.n ? i : p.n];
+        return launch_by_hd(sp, s);
     }
+    return launch_by_hd(p, s);
 }
 
 }  // namespace kvc

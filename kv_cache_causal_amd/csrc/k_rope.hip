@@ -374,7 +374,7 @@ __device__ __forceinline__ void rotate_heads_vec(const float *src, DT *dst, int3
 // multiple of 16).
 // Rotate q of token t in place (f32, whatever the region format).
 template <int STYLE, bool QVEC>
-__device__ __forceinline__ void rotate_q(const AppendParams &p, int32_t t, int32_t pos)
+__device__ __forceinline__ void rotate_q(const AppendArgs &p, int32_t t, int32_t pos)
 {
     if (STYLE != kNone && p.q) {
         float *qt = p.q + (int64_t)t * p.n_head * p.hd;
@@ -384,8 +384,8 @@ __device__ __forceinline__ void rotate_q(const AppendParams &p, int32_t t, int32
     }
 }
 
-template <int STYLE, bool QVEC, typename KVT>
-__global__ void __launch_bounds__(256) append_kernel(AppendParams p)
+template <int STYLE, bool QVEC, typename KVT, int E>
+__global__ void __launch_bounds__(256) append_kernel(AppendParamsT<E> p)
 {
     const int32_t t = blockIdx.x;
     const int32_t pos = p.pos ? p.pos[t] : p.ipos[t];
@@ -447,8 +447,8 @@ __device__ __forceinline__ float4 rotated4(const float *x, int32_t e, int32_t w,
 // block as it is stored.  Thread idx handles values 4 idx .. 4 idx + 3 of the row;
 // nkt / 4 is a multiple of 8 and so is the block size, so the 8 lanes of a block are
 // always active together.
-template <int STYLE, bool QVEC>
-__global__ void __launch_bounds__(256) append_q8_kernel(AppendParams p)
+template <int STYLE, bool QVEC, int E>
+__global__ void __launch_bounds__(256) append_q8_kernel(AppendParamsT<E> p)
 {
     const int32_t t = blockIdx.x;
     const int32_t pos = p.pos ? p.pos[t] : p.ipos[t];
@@ -490,45 +490,63 @@ hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_b
     return hipGetLastError();
 }
 
-template <typename KVT>
-void launch_append_t(const AppendParams &p, hipStream_t s)
+template <typename KVT, int E>
+void launch_append_t(const AppendParamsT<E> &p, hipStream_t s)
 {
     const dim3 grid((unsigned)p.nt), block(256);
     switch (p.style) {
     case kNeox:
-        if (p.hd % 8 == 0) append_kernel<kNeox, true, KVT><<<grid, block, 0, s>>>(p);
-        else append_kernel<kNeox, false, KVT><<<grid, block, 0, s>>>(p);
+        if (p.hd % 8 == 0) append_kernel<kNeox, true, KVT, E><<<grid, block, 0, s>>>(p);
+        else append_kernel<kNeox, false, KVT, E><<<grid, block, 0, s>>>(p);
         break;
     case kInterleaved:
-        if (p.hd % 4 == 0) append_kernel<kInterleaved, true, KVT><<<grid, block, 0, s>>>(p);
-        else append_kernel<kInterleaved, false, KVT><<<grid, block, 0, s>>>(p);
+        if (p.hd % 4 == 0) append_kernel<kInterleaved, true, KVT, E><<<grid, block, 0, s>>>(p);
+        else append_kernel<kInterleaved, false, KVT, E><<<grid, block, 0, s>>>(p);
         break;
-    default: append_kernel<kNone, false, KVT><<<grid, block, 0, s>>>(p); break;
+    default: append_kernel<kNone, false, KVT, E><<<grid, block, 0, s>>>(p); break;
     }
 }
 
-void launch_append_q8(const AppendParams &p, hipStream_t s)
+template <int E>
+void launch_append_q8(const AppendParamsT<E> &p, hipStream_t s)
 {
     const dim3 grid((unsigned)p.nt), block(256);
     switch (p.style) {
     case kNeox:
-        if (p.hd % 8 == 0) append_q8_kernel<kNeox, true><<<grid, block, 0, s>>>(p);
-        else append_q8_kernel<kNeox, false><<<grid, block, 0, s>>>(p);
+        if (p.hd % 8 == 0) append_q8_kernel<kNeox, true, E><<<grid, block, 0, s>>>(p);
+        else append_q8_kernel<kNeox, false, E><<<grid, block, 0, s>>>(p);
         break;
     case kInterleaved:
-        if (p.hd % 4 == 0) append_q8_kernel<kInterleaved, true><<<grid, block, 0, s>>>(p);
-        else append_q8_kernel<kInterleaved, false><<<grid, block, 0, s>>>(p);
+        if (p.hd % 4 == 0) append_q8_kernel<kInterleaved, true, E><<<grid, block, 0, s>>>(p);
+        else append_q8_kernel<kInterleaved, false, E><<<grid, block, 0, s>>>(p);
         break;
-    default: append_q8_kernel<kNone, false><<<grid, block, 0, s>>>(p); break;
+    default: append_q8_kernel<kNone, false, E><<<grid, block, 0, s>>>(p); break;
     }
+}
+
+template <int E>
+void launch_append_fmt(const AppendParamsT<E> &p, hipStream_t s)
+{
+    if (p.kv_fmt == kFmtQ8) launch_append_q8<E>(p, s);
+    else if (p.kv_fmt == kFmtF16) launch_append_t<_Float16, E>(p, s);
+    else launch_append_t<float, E>(p, s);
 }
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s)
 {
     if (p.nt <= 0) return hipSuccess;
-    if (p.kv_fmt == kFmtQ8) launch_append_q8(p, s);
-    else if (p.kv_fmt == kFmtF16) launch_append_t<_Float16>(p, s);
-    else launch_append_t<float>(p, s);
+    if (!p.pos && !p.seq && p.nt <= kSmallInline) {
+        // Few inline tokens: the same launch with an argument block sized for them.
+        AppendParamsT<kSmallInline> sp;
+        static_cast<AppendArgs &>(sp) = p;
+        for (int i = 0; i < kSmallInline; i++) {
+            sp.ipos[i] = i < p.nt ? p.ipos[i] : 0;
+            sp.iseq[i] = i < p.nt ? p.iseq[i] : 0;
+        }
+        launch_append_fmt(sp, s);
+    } else {
+        launch_append_fmt(p, s);
+    }
     return hipGetLastError();
 }
 

@@ -42,11 +42,17 @@ __host__ __device__ inline int64_t q8_scale_index(int64_t row, int32_t j, int32_
 hipError_t launch_rope_table(float2 *tab, int32_t rows, int32_t hd, float freq_base,
                              float freq_scale, bool exact, hipStream_t s);
 
+// Kernel arguments cost host time at every launch: on MI355X a launch with 16 bytes of
+// arguments took 2.6 us of host time, one with 816 bytes 3.8 us.  The arrays a call passes
+// in the arguments therefore come in two capacities, and a call with up to kSmallInline
+// tokens or entries launches kernels whose arguments hold only that many.
+constexpr int kSmallInline = 8;
+
 // ---- K1: RoPE(q, k) + in-place K/V row store ------------------------------------------
 // Up to kInlineTokens positions / sequence ids ride in the kernel arguments (no upload);
 // longer appends pass them through device memory (pos/seq non-null).
 constexpr int kInlineTokens = 64;
-struct AppendParams {
+struct AppendArgs {
     float *q;               // [nt][n_head][hd] or nullptr
     const float *k, *v;     // [nt][n_head_kv][hd_kv]
     void *kc, *vc;          // cache bases
@@ -57,8 +63,12 @@ struct AppendParams {
     int64_t region_bytes, scale_off;
     int32_t nt, n_head, hd, n_head_kv, hd_kv, n_layer, layer, style;
     int32_t kv_fmt;         // KvFmt: the store rounds to binary16 or quantizes to Q8_0
-    int32_t ipos[kInlineTokens], iseq[kInlineTokens];
 };
+template <int E>
+struct AppendParamsT : AppendArgs {
+    int32_t ipos[E], iseq[E];
+};
+using AppendParams = AppendParamsT<kInlineTokens>;
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 
 // ---- Fused decode step: q/k/v projections + biases + RoPE + K/V store -------------------
@@ -83,7 +93,7 @@ hipError_t launch_qkv(const QkvParams &p, hipStream_t s);
 // One launch covers up to kInlineEntries batch entries, whose positions, sequence ids
 // and chunk offsets ride in the kernel arguments.
 constexpr int kInlineEntries = 64;
-struct DecodeParams {
+struct DecodeArgs {
     const float *q;          // [n][n_head][hd] (this launch's entries)
     float *out;              // [n][n_head][hd_kv]
     float *part;             // [total_chunks][n_head][hd_kv + 4]: m, l, -, -, acc[hd_kv]
@@ -97,10 +107,14 @@ struct DecodeParams {
     int32_t rows_per_chunk, total_chunks;
     int32_t hpb;             // kv heads per split-K workgroup (decode_heads_per_block)
     float qscale;            // scale * log2(e): scores are kept in base-2 units
-    int32_t pos[kInlineEntries];
-    int32_t seq[kInlineEntries];
-    int32_t cbase[kInlineEntries + 1];  // first chunk of entry b; cbase[n] = total_chunks
 };
+template <int E>
+struct DecodeParamsT : DecodeArgs {
+    int32_t pos[E];
+    int32_t seq[E];
+    int32_t cbase[E + 1];    // first chunk of entry b; cbase[n] = total_chunks
+};
+using DecodeParams = DecodeParamsT<kInlineEntries>;
 // The allocation-free decode keeps its split-K records in a fixed device array of this
 // many floats (16 MiB per GPU).  static_scratch_addr returns the device address of the
 // array's copy on `device`; the first lookup for a device must run with that device
