@@ -54,9 +54,9 @@
  *     kv_last_error() then returns a message for the calling thread.
  *   - nt == 0 / n_seq == 0 is an OK no-op (after the handle and layer are checked).
  *
- * Limits of this implementation: hd_kv (the KV head dim) must be one of 16, 32, 64, 128,
- * 256; the query head dim hd must be even, <= 256 and >= hd_kv; positions < capacity
- * <= 2^24.
+ * Limits of this implementation: hd_kv (the KV head dim) must be one of 16, 32, 64, 80, 96,
+ * 112, 128, 160, 192, 256 (a Q8_0 cache: 32, 64, 128 or 256); the query head dim hd must
+ * be even, <= 256 and >= hd_kv; positions < capacity <= 2^24.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -118,7 +118,7 @@ typedef enum kvc_kv_dtype {
  *   n_seq      independent sequences (>= 1).
  *   n_layer    layers (>= 1).
  *   n_head_kv  KV heads per row (>= 1).
- *   hd_kv      KV head dim, one of 16, 32, 64, 128, 256.
+ *   hd_kv      KV head dim, one of 16, 32, 64, 80, 96, 112, 128, 160, 192, 256.
  *   capacity   rows per (sequence, layer) region, 1 .. 2^24.  Fixed for the handle's
  *              life: the regions never grow, move or get copied.
  *   stream     used for the zero fill; kv_alloc waits for it before returning.
@@ -146,7 +146,8 @@ kvc_status kv_alloc(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_h
  * with the scales of one block for 4 consecutive rows (4q .. 4q+3) in 8 contiguous bytes.
  * Zero bytes decode to +0.0.
  * Errors: as kv_alloc, plus KVC_E_ARG for an unknown format and KVC_E_GEOMETRY for a
- * Q8_0 cache whose hd_kv is not a multiple of 32.
+ * Q8_0 cache whose hd_kv is not a multiple of 32, or is 96, 160 or 192 (this library's
+ * Q8_0 kernels take the power-of-two head dims only).
  */
 kvc_status kv_alloc_typed(kvc_cache **out, int32_t n_seq, int32_t n_layer, int32_t n_head_kv,
                           int32_t hd_kv, int32_t capacity, kvc_kv_dtype dtype, void *stream);

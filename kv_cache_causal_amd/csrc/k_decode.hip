@@ -104,12 +104,13 @@ typedef int32_t intx2 __attribute__((ext_vector_type(2)));
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
 
 // Where one kv head's slices live in a region: row r's values start at element
-// r * nkt + hk * HD; a Q8_0 region's scales start at `scales` (q8_scale_index: head-major,
-// `rows` rows per head, interleaved by row quads).
+// r * nkt + hk * hd; a Q8_0 region's scales start at `scales` (q8_scale_index: head-major,
+// `rows` rows per head, interleaved by row quads).  hd is the kv head dim; the lane layout
+// may be laid out for a wider power of two (padded lanes load nothing and hold zeros).
 struct Slice {
     const char *region, *scales;
     int64_t rows;
-    int32_t nkt, hk;
+    int32_t nkt, hk, hd;
 };
 
 // How a lane group reads its DPL dims of a row slice (LPR lanes per row).  Raw is what
@@ -145,20 +146,30 @@ __device__ __forceinline__ T stream_load(const void *p)
 }
 
 template <typename KVT>
-__device__ __forceinline__ const KVT *slice_row(const Slice &s, int64_t row, int hd)
+__device__ __forceinline__ const KVT *slice_row(const Slice &s, int64_t row)
 {
-    return reinterpret_cast<const KVT *>(s.region) + row * s.nkt + (int64_t)s.hk * hd;
+    return reinterpret_cast<const KVT *>(s.region) + row * s.nkt + (int64_t)s.hk * s.hd;
+}
+
+// PAD: the head dim is below the lane layout's; a lane loads only the pieces that start
+// inside the head (head dims are multiples of 16, so a piece is wholly in or out).
+template <bool PAD, typename T>
+__device__ __forceinline__ T load_if(const void *p, bool inside)
+{
+    if (!PAD || inside) return stream_load<T>(p);
+    return T{};
 }
 
 template <int LPR>
 struct RowIO<float, 8, LPR> : NoRowScale {
     struct Raw { floatx4 a, b; };
+    template <bool PAD>
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        const float *p = slice_row<float>(s, row, 8 * LPR);
+        const float *p = slice_row<float>(s, row);
         Raw r;
-        r.a = stream_load<floatx4>(p + li * 4);
-        r.b = stream_load<floatx4>(p + 4 * LPR + li * 4);
+        r.a = load_if<PAD, floatx4>(p + li * 4, li * 4 < s.hd);
+        r.b = load_if<PAD, floatx4>(p + 4 * LPR + li * 4, 4 * LPR + li * 4 < s.hd);
         return r;
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
@@ -167,9 +178,10 @@ struct RowIO<float, 8, LPR> : NoRowScale {
 template <int LPR>
 struct RowIO<float, 4, LPR> : NoRowScale {
     typedef floatx4 Raw;
+    template <bool PAD>
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return stream_load<floatx4>(slice_row<float>(s, row, 4 * LPR) + li * 4);
+        return load_if<PAD, floatx4>(slice_row<float>(s, row) + li * 4, li * 4 < s.hd);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return r[i]; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
@@ -177,9 +189,10 @@ struct RowIO<float, 4, LPR> : NoRowScale {
 template <int LPR>
 struct RowIO<_Float16, 8, LPR> : NoRowScale {
     typedef half8_t Raw;
+    template <bool PAD>
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return stream_load<half8_t>(slice_row<_Float16>(s, row, 8 * LPR) + li * 8);
+        return load_if<PAD, half8_t>(slice_row<_Float16>(s, row) + li * 8, li * 8 < s.hd);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 8 + i; }
@@ -187,9 +200,10 @@ struct RowIO<_Float16, 8, LPR> : NoRowScale {
 template <int LPR>
 struct RowIO<_Float16, 4, LPR> : NoRowScale {
     typedef half4_t Raw;
+    template <bool PAD>
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
-        return stream_load<half4_t>(slice_row<_Float16>(s, row, 4 * LPR) + li * 4);
+        return load_if<PAD, half4_t>(slice_row<_Float16>(s, row) + li * 4, li * 4 < s.hd);
     }
     static __device__ __forceinline__ float get(const Raw &r, int i) { return (float)r[i]; }
     static __device__ __forceinline__ int dim(int li, int i) { return li * 4 + i; }
@@ -223,8 +237,10 @@ struct RowIO<int8_t, DPL, LPR> {
     struct Raw { Codes c; };
     static constexpr bool kQuads = true;
     typedef half4_t Quad;   // the scales of the lane's block for 4 consecutive rows
+    template <bool PAD>
     static __device__ __forceinline__ Raw load(const Slice &s, int64_t row, int li)
     {
+        static_assert(!PAD, "Q8_0 head dims fill the lane layout");
         const int64_t v0 = row * s.nkt + (int64_t)s.hk * HD + li * DPL;   // first value
         return Raw{stream_load<Codes>(s.region + v0)};
     }
@@ -258,7 +274,9 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float m2, float l2
     m = mn;
 }
 
-template <int HD, int GP, typename KVT, int HPB, int E>
+// HD is the lane layout's head dim; PAD: the kv head dim p.hd_kv is below it (a multiple
+// of 16), and the lanes past it load nothing.
+template <int HD, int GP, typename KVT, int HPB, int E, bool PAD>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, int32_t g0)
 {
     constexpr int kDimsPerLane = dims_per_lane<GP, KVT>();
@@ -302,13 +320,14 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
         r1 = min(r0 + p.rows_per_chunk, p.pos[b] + 1);
     }
     const int seq = p.seq[b];
-    const int nkt = p.n_head_kv * HD;
+    const int hdr = PAD ? p.hd_kv : HD;   // the kv head dim
+    const int nkt = p.n_head_kv * hdr;
     const int64_t reg = ((int64_t)seq * p.n_layer + p.layer) * p.region_bytes;
     const int64_t qrows = p.scale_off / nkt;   // region rows (Q8_0 only)
     const char *kreg = static_cast<const char *>(p.kc) + reg;
     const char *vreg = static_cast<const char *>(p.vc) + reg;
-    const Slice K{kreg, kreg + p.scale_off, qrows, nkt, hk};
-    const Slice V{vreg, vreg + p.scale_off, qrows, nkt, hk};
+    const Slice K{kreg, kreg + p.scale_off, qrows, nkt, hk, hdr};
+    const Slice V{vreg, vreg + p.scale_off, qrows, nkt, hk, hdr};
 
     // The lane's query values in the order its row values arrive (IO::dim).  Loaded here,
     // scaled only after the first step's row loads are issued (below), so that the query
@@ -319,7 +338,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
         const bool ok = g0 + g < G;
         const float *qrow = p.q + ((int64_t)b * p.n_head + (hk * G + (ok ? g0 + g : 0))) * p.hd;
 #pragma unroll
-        for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = qrow[IO::dim(li, i)];
+        for (int i = 0; i < kDimsPerLane; i++)
+            qf[g][i] = (!PAD || IO::dim(li, i) < hdr) ? qrow[IO::dim(li, i)] : 0.0f;
     }
 
     float m[GP], l[GP], acc[GP][kDimsPerLane];
@@ -355,8 +375,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
         for (int u = 0; u < kUnroll; u++) {
             int row = row_of(rb, u);
             row = row < r1 ? row : r0;  // rows past the chunk re-read row r0 and are masked
-            kf[u] = IO::load(K, row, li);
-            vf[u] = IO::load(V, row, li);
+            kf[u] = IO::template load<PAD>(K, row, li);
+            vf[u] = IO::template load<PAD>(V, row, li);
         }
         if constexpr (kQuads) {
             // A quad wholly past the chunk re-reads r0's quad (inside the region).
@@ -483,11 +503,11 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
     __syncthreads();
 
     const int ngp = min(GP, G - g0);   // heads of this pass that exist
-    float *out_b = p.out + (int64_t)b * p.n_head * HD;
-    for (int idx = threadIdx.x; idx < HPB * ngp * HD; idx += blockDim.x) {
-        const int bh = idx / (ngp * HD);   // kv head of the block
-        const int g = (idx - bh * ngp * HD) / HD;
-        const int d = idx - (bh * ngp + g) * HD;
+    float *out_b = p.out + (int64_t)b * p.n_head * hdr;
+    for (int idx = threadIdx.x; idx < HPB * ngp * hdr; idx += blockDim.x) {
+        const int bh = idx / (ngp * hdr);   // kv head of the block
+        const int g = (idx - bh * ngp * hdr) / hdr;
+        const int d = idx - (bh * ngp + g) * hdr;
         const int w0 = bh * WPH;
         float M = -INFINITY;
 #pragma unroll
@@ -502,9 +522,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
         }
         const int h = (hk - wh + bh) * G + g0 + g;
         if (nchunks == 1) {
-            out_b[(int64_t)h * HD + d] = A / L;
+            out_b[(int64_t)h * hdr + d] = A / L;
         } else {
-            float *rec = p.part + ((int64_t)cg * p.n_head + h) * (HD + 4);
+            float *rec = p.part + ((int64_t)cg * p.n_head + h) * (hdr + 4);
             if (d == 0) {
                 rec[0] = M;
                 rec[1] = L;
@@ -598,40 +618,42 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParamsT<E> p)
     }
 }
 
-template <int HD, typename KVT, int HPB, int E>
+template <int HD, typename KVT, int HPB, int E, bool PAD>
 void launch_split_hpb(const DecodeParamsT<E> &p, hipStream_t s)
 {
     const int G = p.n_head / p.n_head_kv;
     const dim3 grid((unsigned)p.total_chunks * (unsigned)(p.n_head_kv / HPB)), block(256);
     for (int g0 = 0; g0 < G; g0 += 8) {
         const int left = G - g0;
-        if (left >= 5) decode_split_kernel<HD, 8, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
-        else if (left >= 3) decode_split_kernel<HD, 4, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
-        else if (left == 2) decode_split_kernel<HD, 2, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
-        else decode_split_kernel<HD, 1, KVT, HPB, E><<<grid, block, 0, s>>>(p, g0);
+        if (left >= 5) decode_split_kernel<HD, 8, KVT, HPB, E, PAD><<<grid, block, 0, s>>>(p, g0);
+        else if (left >= 3) decode_split_kernel<HD, 4, KVT, HPB, E, PAD><<<grid, block, 0, s>>>(p, g0);
+        else if (left == 2) decode_split_kernel<HD, 2, KVT, HPB, E, PAD><<<grid, block, 0, s>>>(p, g0);
+        else decode_split_kernel<HD, 1, KVT, HPB, E, PAD><<<grid, block, 0, s>>>(p, g0);
     }
 }
 
-template <int HD, typename KVT, int E>
+template <int HD, typename KVT, int E, bool PAD>
 void launch_split(const DecodeParamsT<E> &p, hipStream_t s)
 {
     if constexpr (sizeof(KVT) == 2) {
-        if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2, E>(p, s);
+        if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2, E, PAD>(p, s);
     }
-    launch_split_hpb<HD, KVT, 1, E>(p, s);
+    launch_split_hpb<HD, KVT, 1, E, PAD>(p, s);
 }
 
-template <int HD, int E>
+// HDL: the lane layout's head dim (a power of two); HDR: the kv head dim (HDR <= HDL).
+template <int HDL, int HDR, int E>
 hipError_t launch_hd(const DecodeParamsT<E> &p, hipStream_t s)
 {
-    if constexpr (HD % kQ8Block == 0) {
-        if (p.kv_fmt == kFmtQ8) launch_split<HD, int8_t, E>(p, s);
+    constexpr bool PAD = HDR != HDL;
+    if constexpr (!PAD && HDL % kQ8Block == 0) {
+        if (p.kv_fmt == kFmtQ8) launch_split<HDL, int8_t, E, false>(p, s);
     }
-    if (p.kv_fmt == kFmtF16) launch_split<HD, _Float16, E>(p, s);
-    else if (p.kv_fmt == kFmtF32) launch_split<HD, float, E>(p, s);
+    if (p.kv_fmt == kFmtF16) launch_split<HDL, _Float16, E, PAD>(p, s);
+    else if (p.kv_fmt == kFmtF32) launch_split<HDL, float, E, PAD>(p, s);
     if (p.total_chunks > p.n) {  // some entry spans several chunks
         const dim3 cgrid((unsigned)p.n, (unsigned)p.n_head);
-        decode_combine_kernel<HD, E><<<cgrid, 256, 0, s>>>(p);
+        decode_combine_kernel<HDR, E><<<cgrid, 256, 0, s>>>(p);
     }
     return hipGetLastError();
 }
@@ -640,11 +662,16 @@ template <int E>
 hipError_t launch_by_hd(const DecodeParamsT<E> &p, hipStream_t s)
 {
     switch (p.hd_kv) {
-    case 16: return launch_hd<16, E>(p, s);
-    case 32: return launch_hd<32, E>(p, s);
-    case 64: return launch_hd<64, E>(p, s);
-    case 128: return launch_hd<128, E>(p, s);
-    case 256: return launch_hd<256, E>(p, s);
+    case 16: return launch_hd<16, 16, E>(p, s);
+    case 32: return launch_hd<32, 32, E>(p, s);
+    case 64: return launch_hd<64, 64, E>(p, s);
+    case 80: return launch_hd<128, 80, E>(p, s);
+    case 96: return launch_hd<128, 96, E>(p, s);
+    case 112: return launch_hd<128, 112, E>(p, s);
+    case 128: return launch_hd<128, 128, E>(p, s);
+    case 160: return launch_hd<256, 160, E>(p, s);
+    case 192: return launch_hd<256, 192, E>(p, s);
+    case 256: return launch_hd<256, 256, E>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -652,12 +679,19 @@ hipError_t launch_by_hd(const DecodeParamsT<E> &p, hipStream_t s)
 }  // namespace
 
 namespace {
+// The decode lane layout's head dim for a kv head dim: the next power of two from 16.
+constexpr int32_t decode_lane_dim(int32_t hd_kv)
+{
+    return hd_kv <= 16 ? 16 : hd_kv <= 32 ? 32 : hd_kv <= 64 ? 64 : hd_kv <= 128 ? 128 : 256;
+}
+
 // Rows per step of the split kernel for a query-head group of GP with hpb kv heads per
 // workgroup: each of a head's 4 / hpb waves covers 64 * dims / hd_kv rows per unrolled row.
 template <int GP, typename KVT>
 int32_t step_rows(int32_t hd_kv, int32_t hpb)
 {
-    return kWaves / hpb * (64 * dims_per_lane<GP, KVT>() / hd_kv) * rows_per_step<GP, KVT>();
+    const int32_t hdl = decode_lane_dim(hd_kv);
+    return kWaves / hpb * (64 * dims_per_lane<GP, KVT>() / hdl) * rows_per_step<GP, KVT>();
 }
 template <typename KVT>
 int32_t step_rows_fmt(int32_t hd_kv, int32_t G, int32_t hpb)

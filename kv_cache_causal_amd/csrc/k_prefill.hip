@@ -75,10 +75,16 @@ struct PrefillCfg {
     // pieces) are conflict-free unpadded.
     static constexpr int KSTR = HD;
     static constexpr int VSTR = HD;
-    // K swizzle: 16-byte chunk c of tile row r sits at chunk position c ^ (r mod KSWZ).
-    static constexpr int KSWZ = (HD / 4) < 16 ? (HD / 4) : 16;
+    // K swizzle: 16-byte chunk c of tile row r sits at chunk position c ^ (r mod KSWZ),
+    // KSWZ the largest power of two up to 16 that divides the row's HD / 4 chunks (so the
+    // swizzle stays inside the row: 16 for head dims that are multiples of 64, 8 for 96
+    // and 160, 4 for 80 and 112).
+    static constexpr int KSWZ = (HD / 4) % 16 == 0 ? 16 : (HD / 4) % 8 == 0 ? 8
+                              : (HD / 4) % 4 == 0 ? 4 : (HD / 4) % 2 == 0 ? 2 : 1;
     static constexpr int NDB = HD / 16;             // 16-dim output blocks
-    static constexpr int VEC = NDB >= 4 ? 4 : NDB;  // output blocks fed by one V read
+    // Output blocks fed by one V read: 4 when they group by 4, else 2 or 1.
+    static constexpr int VEC = NDB % 4 == 0 ? 4 : NDB % 2 == 0 ? 2 : 1;
+    static_assert(HD % 16 == 0 && (HD / 4) % KSWZ == 0 && NDB % VEC == 0, "head dim");
 };
 
 typedef int32_t intx4 __attribute__((ext_vector_type(4)));
@@ -461,8 +467,10 @@ template <int HD>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillParams p)
 {
     constexpr int TPR = HD / 4;           // threads per record
+    constexpr int RPB = 256 / TPR;        // records per workgroup
     constexpr int kBatch = 8;
-    const int rec = (int)blockIdx.x * (256 / TPR) + (int)threadIdx.x / TPR;
+    if ((int)threadIdx.x >= RPB * TPR) return;   // head dims that do not divide 1,024
+    const int rec = (int)blockIdx.x * RPB + (int)threadIdx.x / TPR;
     const int d = ((int)threadIdx.x % TPR) * 4;
     if (rec >= p.nt * p.n_head) return;
     const int t = rec / p.n_head, h = rec - t * p.n_head;
@@ -571,7 +579,12 @@ hipError_t launch_by_hd(const PrefillParams &p, hipStream_t s)
     case 16: return launch_hd<16>(p, s);
     case 32: return launch_hd<32>(p, s);
     case 64: return launch_hd<64>(p, s);
+    case 80: return launch_hd<80>(p, s);
+    case 96: return launch_hd<96>(p, s);
+    case 112: return launch_hd<112>(p, s);
     case 128: return launch_hd<128>(p, s);
+    case 160: return launch_hd<160>(p, s);
+    case 192: return launch_hd<192>(p, s);
     case 256: return launch_hd<256>(p, s);
     default: return hipErrorInvalidValue;
     }

@@ -8,8 +8,9 @@
 
 namespace kvc {
 
-// Keys per prefill tile for a kv head dim (the prefill kernel's tile height).
-constexpr int prefill_key_tile(int hd_kv) { return hd_kv >= 256 ? 32 : 64; }
+// Keys per prefill tile for a kv head dim (the prefill kernel's tile height): K and V
+// tiles of 64 keys up to head dim 128 (64 KB of LDS), of 32 keys beyond.
+constexpr int prefill_key_tile(int hd_kv) { return hd_kv > 128 ? 32 : 64; }
 
 // A prefill workgroup owns 64 query rows (GB heads of one kv group x TQ tokens: a "query
 // tile") and scans key tiles of KT keys.  When there are too few query tiles to fill the

@@ -61,7 +61,11 @@ kvc_status check_seq_ids(const Geometry &g, int32_t n, const int32_t *seq_ids, s
 
 bool supported_kv_head_dim(int32_t hd_kv)
 {
-    return hd_kv == 16 || hd_kv == 32 || hd_kv == 64 || hd_kv == 128 || hd_kv == 256;
+    switch (hd_kv) {
+    case 16: case 32: case 64: case 80: case 96: case 112: case 128: case 160: case 192:
+    case 256: return true;
+    default: return false;
+    }
 }
 
 kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_t hd_kv,
@@ -72,7 +76,8 @@ kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_
         return KVC_E_ARG;
     }
     if (!supported_kv_head_dim(hd_kv)) {
-        msg = "kv head dim " + s(hd_kv) + " unsupported (16, 32, 64, 128 or 256)";
+        msg = "kv head dim " + s(hd_kv) +
+              " unsupported (16, 32, 64, 80, 96, 112, 128, 160, 192 or 256)";
         return KVC_E_ARG;
     }
     if (capacity <= 0 || capacity > KVC_MAX_CAPACITY) {
@@ -83,9 +88,14 @@ kvc_status check_alloc(int32_t n_seq, int32_t n_layer, int32_t n_head_kv, int32_
         msg = "unknown region format " + s(dtype);
         return KVC_E_ARG;
     }
-    // Q8_0 blocks of 32 run along a row; each must lie within one kv head.
+    // Q8_0 blocks of 32 run along a row; each must lie within one kv head.  This library's
+    // Q8_0 kernels further take only the power-of-two head dims 32 .. 256.
     if (dtype == KVC_KV_Q8_0 && hd_kv % 32 != 0) {
         msg = "a Q8_0 cache needs hd_kv a multiple of 32, got " + s(hd_kv);
+        return KVC_E_GEOMETRY;
+    }
+    if (dtype == KVC_KV_Q8_0 && (hd_kv & (hd_kv - 1)) != 0) {
+        msg = "a Q8_0 cache here needs hd_kv of 32, 64, 128 or 256, got " + s(hd_kv);
         return KVC_E_GEOMETRY;
     }
     // Row width and region sizes must fit the 64-bit offsets the kernels use.

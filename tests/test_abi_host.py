@@ -223,14 +223,23 @@ def test_alloc_checks(hc):
     # lie inside one kv head (hd_kv a multiple of 32).
     from oracle import Oracle
     L = Oracle().L
-    for hdk in (16, 32, 64, 128, 256):
+    for hdk in (16, 32, 64, 80, 96, 112, 128, 160, 192, 256):
         for dt in (kvc.KV_F32, kvc.KV_F16, kvc.KV_Q8_0):
             lib_ok = hc.hc_check_alloc(1, 1, 2, hdk, 8, dt) == kvc.OK
             h = L.orc_cache_new_typed(1, 1, 2, hdk, 8, dt)
-            assert lib_ok == bool(h), (hdk, dt)
+            if dt == kvc.KV_Q8_0 and hdk in (96, 160, 192):
+                # The oracle's Q8_0 takes any multiple of 32; the library's kernels only
+                # the power-of-two head dims (a documented limit).
+                assert bool(h) and not lib_ok, hdk
+                assert hc.hc_check_alloc(1, 1, 2, hdk, 8, dt) == kvc.E_GEOMETRY
+            else:
+                assert lib_ok == bool(h), (hdk, dt)
             if h:
                 L.orc_cache_free(h)
     assert hc.hc_check_alloc(1, 1, 2, 16, 8, kvc.KV_Q8_0) == kvc.E_GEOMETRY
+    # Head dims the library does not run (the oracle takes any even one up to 256).
+    for hdk in (24, 48, 144, 208, 240, 250):
+        assert hc.hc_check_alloc(1, 1, 2, hdk, 8, kvc.KV_F32) == kvc.E_ARG, hdk
 
 
 RUNS_CASES = [
