@@ -11,16 +11,17 @@ from tests.gpu_util import Pair, assert_bitwise, assert_close, compare_cache, de
 pytestmark = pytest.mark.gpu
 
 HD_KV = [16, 32, 64, 128, 256]
+HD_KV_BETWEEN = [80, 96, 112, 160, 192]   # f32 and binary16 regions only
 GROUPS = [1, 2, 3, 4, 7, 8]
 
 
-def case(seed):
+def case(seed, dims=HD_KV):
     rng = np.random.default_rng(10_000 + seed)
-    hdk = int(rng.choice(HD_KV))
+    hdk = int(rng.choice(dims))
     nkv = int(rng.choice([1, 2, 4, 8] if hdk <= 128 else [1, 2]))
     g = int(rng.choice(GROUPS))
     hd = min(256, hdk + 2 * int(rng.integers(0, 3)) * int(rng.integers(0, 2)))   # sometimes > hd_kv
-    fmts = [0, 1] + ([2] if hdk % 32 == 0 else [])
+    fmts = [0, 1] + ([2] if hdk % 32 == 0 and (hdk & (hdk - 1)) == 0 else [])
     return dict(n_seq=int(rng.integers(1, 4)), n_layer=int(rng.integers(1, 3)), nkv=nkv,
                 nh=nkv * g, hd=hd, hdk=hdk, cap=int(rng.integers(1, 1500)),
                 kv=int(rng.choice(fmts)), style=int(rng.integers(0, 3)), rng=rng)
@@ -28,7 +29,16 @@ def case(seed):
 
 @pytest.mark.parametrize("seed", range(200))
 def test_random_case(seed):
-    c = case(seed)
+    run_case(seed, case(seed))
+
+
+@pytest.mark.parametrize("seed", range(200, 260))
+def test_random_case_between_dims(seed):
+    """The same sweep over the kv head dims between the powers of two."""
+    run_case(seed, case(seed, HD_KV_BETWEEN))
+
+
+def run_case(seed, c):
     rng = c.pop("rng")
     say(f"random case {seed}: " + ", ".join(f"{k}={v}" for k, v in c.items()))
     n_seq, n_layer, nkv, nh, hd, hdk, cap = (c[k] for k in ("n_seq", "n_layer", "nkv", "nh", "hd",
