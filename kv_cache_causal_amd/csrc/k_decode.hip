@@ -462,12 +462,22 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParamsT<E> p, i
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; i++) qf[g][i] = ok ? qf[g][i] * p.qscale : 0.0f;
     }
-    for (int st = 0; st < nsteps; st += 2) {
-        if (st + 1 < nsteps) load(kB, vB, kqB, vqB, st + 1);
+    // The loads inside the loop are unconditional: with a load that a branch may skip, the
+    // compiler's wait counts must hold on the path without it, and consuming one set then
+    // also waits for the other set's loads, so the two sets never overlap.
+    int st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+        load(kB, vB, kqB, vqB, st + 1);
         consume(kA, vA, kqA, vqA, st);
-        if (st + 1 >= nsteps) break;
-        if (st + 2 < nsteps) load(kA, vA, kqA, vqA, st + 2);
+        load(kA, vA, kqA, vqA, st + 2);
         consume(kB, vB, kqB, vqB, st + 1);
+    }
+    if (st + 1 < nsteps) {
+        load(kB, vB, kqB, vqB, st + 1);
+        consume(kA, vA, kqA, vqA, st);
+        consume(kB, vB, kqB, vqB, st + 1);
+    } else if (st < nsteps) {
+        consume(kA, vA, kqA, vqA, st);
     }
 
     // Merge the row groups of the wave (lanes that share li).
