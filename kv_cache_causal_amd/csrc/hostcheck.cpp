@@ -109,4 +109,10 @@ int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forc
     return kvc::decode_chunk_rows(work, br, hpb, forced);
 }
 
+int64_t hc_decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
+                                 int64_t slots, int32_t br, int64_t rows)
+{
+    return kvc::decode_one_round_rows(len, m, n_head_kv, hpb, slots, br, rows);
+}
+
 }  // extern "C"

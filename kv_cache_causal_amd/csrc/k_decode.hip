@@ -645,10 +645,28 @@ void launch_split_hpb(const DecodeParamsT<E> &p, hipStream_t s)
 template <int HD, typename KVT, int E, bool PAD>
 void launch_split(const DecodeParamsT<E> &p, hipStream_t s)
 {
-    if constexpr (sizeof(KVT) == 2) {
+    if constexpr (sizeof(KVT) <= 2) {
         if (p.hpb == 2) return launch_split_hpb<HD, KVT, 2, E, PAD>(p, s);
     }
     launch_split_hpb<HD, KVT, 1, E, PAD>(p, s);
+}
+
+// The split kernel that launch_split launches first (the pass of the first 8 heads).
+template <int HD, typename KVT, int HPB, int E, bool PAD>
+const void *first_split_kernel(int32_t G)
+{
+    if (G >= 5) return reinterpret_cast<const void *>(decode_split_kernel<HD, 8, KVT, HPB, E, PAD>);
+    if (G >= 3) return reinterpret_cast<const void *>(decode_split_kernel<HD, 4, KVT, HPB, E, PAD>);
+    if (G == 2) return reinterpret_cast<const void *>(decode_split_kernel<HD, 2, KVT, HPB, E, PAD>);
+    return reinterpret_cast<const void *>(decode_split_kernel<HD, 1, KVT, HPB, E, PAD>);
+}
+template <int HD, typename KVT, int E, bool PAD>
+const void *first_split_kernel_hpb(int32_t G, int32_t hpb)
+{
+    if constexpr (sizeof(KVT) <= 2) {
+        if (hpb == 2) return first_split_kernel<HD, KVT, 2, E, PAD>(G);
+    }
+    return first_split_kernel<HD, KVT, 1, E, PAD>(G);
 }
 
 // HDL: the lane layout's head dim (a power of two); HDR: the kv head dim (HDR <= HDL).
@@ -666,6 +684,55 @@ hipError_t launch_hd(const DecodeParamsT<E> &p, hipStream_t s)
         decode_combine_kernel<HDR, E><<<cgrid, 256, 0, s>>>(p);
     }
     return hipGetLastError();
+}
+
+template <int HDL, int HDR, int E>
+const void *first_split_kernel_hd(int32_t G, int32_t kv_fmt, int32_t hpb)
+{
+    constexpr bool PAD = HDR != HDL;
+    if constexpr (!PAD && HDL % kQ8Block == 0) {
+        if (kv_fmt == kFmtQ8) return first_split_kernel_hpb<HDL, int8_t, E, false>(G, hpb);
+    }
+    if (kv_fmt == kFmtF16) return first_split_kernel_hpb<HDL, _Float16, E, PAD>(G, hpb);
+    if (kv_fmt == kFmtF32) return first_split_kernel_hpb<HDL, float, E, PAD>(G, hpb);
+    return nullptr;
+}
+
+// Index of a supported kv head dim (0 .. kNumHd - 1), and the kernel of launch_hd's first
+// launch for it.
+constexpr int kNumHd = 10;
+int hd_index(int32_t hd_kv)
+{
+    switch (hd_kv) {
+    case 16: return 0;
+    case 32: return 1;
+    case 64: return 2;
+    case 80: return 3;
+    case 96: return 4;
+    case 112: return 5;
+    case 128: return 6;
+    case 160: return 7;
+    case 192: return 8;
+    case 256: return 9;
+    default: return -1;
+    }
+}
+template <int E>
+const void *first_split_kernel_any(int32_t hd_kv, int32_t G, int32_t kv_fmt, int32_t hpb)
+{
+    switch (hd_kv) {
+    case 16: return first_split_kernel_hd<16, 16, E>(G, kv_fmt, hpb);
+    case 32: return first_split_kernel_hd<32, 32, E>(G, kv_fmt, hpb);
+    case 64: return first_split_kernel_hd<64, 64, E>(G, kv_fmt, hpb);
+    case 80: return first_split_kernel_hd<128, 80, E>(G, kv_fmt, hpb);
+    case 96: return first_split_kernel_hd<128, 96, E>(G, kv_fmt, hpb);
+    case 112: return first_split_kernel_hd<128, 112, E>(G, kv_fmt, hpb);
+    case 128: return first_split_kernel_hd<128, 128, E>(G, kv_fmt, hpb);
+    case 160: return first_split_kernel_hd<256, 160, E>(G, kv_fmt, hpb);
+    case 192: return first_split_kernel_hd<256, 192, E>(G, kv_fmt, hpb);
+    case 256: return first_split_kernel_hd<256, 256, E>(G, kv_fmt, hpb);
+    default: return nullptr;
+    }
 }
 
 template <int E>
@@ -752,9 +819,53 @@ hipError_t static_scratch_addr(int device, float **addr)
     return hipSuccess;
 }
 
-int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv)
+int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv, int32_t G)
 {
-    return kv_fmt == kFmtF16 && n_head_kv % 2 == 0 ? 2 : 1;
+    if (n_head_kv % 2 != 0) return 1;
+    if (kv_fmt == kFmtF16) return 2;
+    return kv_fmt == kFmtQ8 && G == 2 ? 2 : 1;
+}
+
+namespace {
+// Resident workgroups per CU of each first-pass split kernel (0: not looked up yet), by
+// kv head dim, query-head group class, format, heads per workgroup and argument block.
+// The library holds gfx950 code only, so the count is the same on every device it runs on.
+std::atomic<int32_t> g_blocks_per_cu[kNumHd][4][3][2][2];
+std::atomic<int32_t> g_cus[kMaxDevices];
+}  // namespace
+
+int32_t decode_resident_blocks(int32_t device, int32_t hd_kv, int32_t G, int32_t kv_fmt,
+                               int32_t hpb, int32_t n)
+{
+    const int hi = hd_index(hd_kv);
+    if (hi < 0 || kv_fmt < 0 || kv_fmt > 2 || hpb < 1 || hpb > 2 || device < 0 ||
+        device >= kMaxDevices)
+        return 0;
+    const int gc = G >= 5 ? 3 : G >= 3 ? 2 : G == 2 ? 1 : 0;
+    const bool small = n <= kSmallInline;
+    std::atomic<int32_t> &slot = g_blocks_per_cu[hi][gc][kv_fmt][hpb - 1][small ? 1 : 0];
+    int32_t per_cu = slot.load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        const void *k = small ? first_split_kernel_any<kSmallInline>(hd_kv, G, kv_fmt, hpb)
+                              : first_split_kernel_any<kInlineEntries>(hd_kv, G, kv_fmt, hpb);
+        int nb = 0;
+        if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, 256, 0) != hipSuccess ||
+            nb <= 0)
+            return 0;
+        per_cu = nb;
+        slot.store(per_cu, std::memory_order_relaxed);
+    }
+    int32_t cus = g_cus[device].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device) !=
+                hipSuccess ||
+            c <= 0)
+            return 0;
+        cus = c;
+        g_cus[device].store(cus, std::memory_order_relaxed);
+    }
+    return per_cu * cus;
 }
 
 int32_t decode_block_rows(int32_t hd_kv, int32_t G, int32_t kv_fmt, int32_t hpb)

@@ -262,12 +262,27 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         return t;
     };
     // Chunk size (plan.cpp); KVC_SPLIT_ROWS overrides it (tuning only, never the result).
-    const int32_t hpb = kvc::decode_heads_per_block(c->kv_fmt, c->g.n_head_kv);
+    const int32_t hpb = kvc::decode_heads_per_block(c->kv_fmt, c->g.n_head_kv,
+                                                    n_head / c->g.n_head_kv);
     const int32_t br = kvc::decode_block_rows(c->g.hd_kv, n_head / c->g.n_head_kv, c->kv_fmt, hpb);
     int64_t total_rows = 0;
     for (int32_t b = 0; b < n_seq; b++) total_rows += window_rows(b);
-    const int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, hpb,
-                                                env_split_rows());
+    const int32_t forced = env_split_rows();
+    int64_t rows = kvc::decode_chunk_rows(total_rows * c->g.n_head_kv, br, hpb, forced);
+    if (forced <= 0 && n_seq <= kvc::kInlineEntries) {
+        // One launch: chunks whose workgroups all run at once, when such chunks balance.
+        const int32_t slots = kvc::decode_resident_blocks(
+            c->device, c->g.hd_kv, n_head / c->g.n_head_kv, c->kv_fmt, hpb, n_seq);
+        if (!runs) {
+            int64_t len[kvc::kInlineEntries];
+            for (int32_t b = 0; b < n_seq; b++) len[b] = (int64_t)pos[b] + 1;
+            rows = kvc::decode_one_round_rows(len, n_seq, c->g.n_head_kv, hpb, slots, br, rows);
+        } else {
+            std::vector<int64_t> len(run_len + run_off[0], run_len + run_off[n_seq]);
+            rows = kvc::decode_one_round_rows(len.data(), (int32_t)len.size(), c->g.n_head_kv,
+                                              hpb, slots, br, rows);
+        }
+    }
     // Chunks of entry b: its window cut into pieces of at most `rows` rows (each run on
     // its own for an explicit window).
     auto chunks_of = [&](int32_t b) -> int64_t {

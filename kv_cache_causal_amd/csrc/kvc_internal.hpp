@@ -122,9 +122,15 @@ using DecodeParams = DecodeParamsT<kInlineEntries>;
 constexpr size_t kStaticScratchFloats = size_t(4) << 20;
 hipError_t static_scratch_addr(int device, float **addr);
 
-// kv heads per split-K workgroup for a region format: 2 for binary16 regions with an even
-// n_head_kv, else 1.
-int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv);
+// kv heads per split-K workgroup for a region format and query-head group G: 2 for
+// binary16 regions, and for Q8_0 regions at G = 2, with an even n_head_kv; else 1.
+int32_t decode_heads_per_block(int32_t kv_fmt, int32_t n_head_kv, int32_t G);
+// Workgroups of the split kernel that a call launches first (for this kv head dim,
+// query-head group G, format, heads per workgroup and n entries in the launch) that
+// `device` holds resident at once: resident workgroups per CU (HIP's occupancy query,
+// looked up once per kernel) x CUs.  0 if a lookup fails.
+int32_t decode_resident_blocks(int32_t device, int32_t hd_kv, int32_t G, int32_t kv_fmt,
+                               int32_t hpb, int32_t n);
 // Rows per step of the split-K kernel that a call with query-head group G (n_head /
 // n_head_kv) launches first, for a kv head dim, region format and heads per workgroup
 // (chunks should be a multiple of it).

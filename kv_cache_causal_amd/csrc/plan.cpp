@@ -76,6 +76,11 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
     return pl;
 }
 
+namespace {
+constexpr int64_t kDecodeLargeWork = 2048 * 512;   // ~2048 workgroups of >= 512 rows
+constexpr int64_t kDecodeSmallWork = 131072;       // up to here: ~512 short chunks
+}  // namespace
+
 int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
 {
     // A workgroup streams its chunk in steps of br rows, each step a memory round trip,
@@ -87,14 +92,45 @@ int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
     // costs two short launches instead of one long chain of dependent loads.
     int64_t rows = forced;
     if (rows <= 0) {
-        if (work > 2048 * 512) rows = work / 2048;
-        else if (work > 131072) rows = 512;
+        if (work > kDecodeLargeWork) rows = work / 2048;
+        else if (work > kDecodeSmallWork) rows = 512;
         else rows = work / 512;
         // A workgroup of hpb kv heads gives each head 1/hpb of its waves: chunks 1/hpb as
         // long keep the rows per wave, and the workgroup count, of one head per workgroup.
         rows /= std::max<int32_t>(1, hpb);
     }
     return std::max<int64_t>(br, (rows + br - 1) / br * br);
+}
+
+int64_t decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
+                              int64_t slots, int32_t br, int64_t rows)
+{
+    // With the chunks of decode_chunk_rows (512 rows, or ~2048 workgroups), a launch of
+    // more than small work runs in several rounds of resident workgroups, and the last
+    // round leaves part of the device idle.  One round of chunks that fill the device and
+    // are about equally long keeps every resident workgroup streaming to the end.
+    int64_t total = 0, longest = 0;
+    for (int32_t i = 0; i < m; i++) {
+        total += len[i];
+        longest = std::max(longest, len[i]);
+    }
+    if (m <= 0 || slots <= 0 || br <= 0 || total * n_head_kv <= kDecodeSmallWork) return rows;
+    const int64_t blocks = n_head_kv / std::max<int32_t>(1, hpb);   // head blocks per chunk
+    auto workgroups = [&](int64_t r) {
+        int64_t c = 0;
+        for (int32_t i = 0; i < m; i++) c += (len[i] + r - 1) / r;
+        return c * blocks;
+    };
+    int64_t lo = (rows + br - 1) / br, hi = std::max(lo, (longest + br - 1) / br);
+    if (workgroups(hi * br) > slots) return rows;   // no chunk length fits one round
+    while (lo < hi) {   // workgroups(r) does not grow with r
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (workgroups(mid * br) <= slots) hi = mid;
+        else lo = mid + 1;
+    }
+    const int64_t r = lo * br;
+    if (r * slots * 20 > total * blocks * 23) return rows;   // over 15% above the balance
+    return r;
 }
 
 }  // namespace kvc

@@ -44,4 +44,14 @@ PrefillPlan plan_prefill(const int32_t *pos, int32_t nt, int32_t n_head, int32_t
 // (then rounded up to br).
 int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced);
 
+// A chunk length for one launch whose workgroups all run at once: given the lengths of
+// the m pieces a launch cuts into chunks (window or run lengths), n_head_kv kv heads in
+// workgroups of hpb, `slots` workgroups resident at once on the device and the chunk
+// length `rows` of decode_chunk_rows, returns the shortest multiple of br, at least rows,
+// with (sum of chunks) x n_head_kv / hpb <= slots, if the work is above the small range
+// of decode_chunk_rows (131,072 row-heads) and that length is within 15% of a perfect
+// balance (total rows x n_head_kv / hpb / slots per workgroup); otherwise rows.
+int64_t decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
+                              int64_t slots, int32_t br, int64_t rows);
+
 }  // namespace kvc

@@ -26,6 +26,8 @@ def hc():
     L.hc_plan_prefill.argtypes = [p, i32, i32, i32, i32, i32, p, p, i32]
     L.hc_decode_chunk_rows.argtypes = [i64, i32, i32, i64]
     L.hc_decode_chunk_rows.restype = i64
+    L.hc_decode_one_round_rows.argtypes = [p, i32, i32, i32, i64, i32, i64]
+    L.hc_decode_one_round_rows.restype = i64
     L.hc_max_part_bytes.restype = i64
     return L
 
@@ -195,6 +197,59 @@ def test_decode_chunk_rows(hc):
             assert f(1 << 26, br, hpb, 0) == up((1 << 26) // 2048 // hpb)   # ~2048 workgroups
             assert f(512 * 40, br, hpb, 0) == up(40 // hpb)        # small: ~512 workgroups
             assert f(10_000, br, hpb, 100) == up(100)              # forced, rounded up to br
+
+
+def one_round(hc, lens, n_head_kv, hpb, slots, br, rows):
+    a = np.ascontiguousarray(np.asarray(lens, np.int64))
+    return hc.hc_decode_one_round_rows(a.ctypes.data, len(a), n_head_kv, hpb, slots, br, rows)
+
+
+def test_decode_one_round_rows(hc):
+    """The one-round chunk length: the shortest multiple of br (from the rule's length up)
+    whose chunks x head blocks fit the resident workgroups, taken only above the small
+    range (131,072 row-heads) and within 15% of a perfect balance; anything else keeps the
+    rule's length."""
+    from tests.workloads import batch_n_past
+    lens = batch_n_past().astype(np.int64) + 1         # the 32-sequence batch's windows
+    blocks = lambda r, nkv, hpb: int(np.sum((lens + r - 1) // r)) * (nkv // hpb)  # noqa: E731
+    # binary16 / Q8_0 at 2 kv heads per workgroup, 3 resident workgroups per CU: 768 rows
+    # (748 workgroups), 12% above the balance of 685 rows per workgroup.
+    assert one_round(hc, lens, 8, 2, 768, 32, 288) == 768
+    assert blocks(768, 8, 2) <= 768 < blocks(736, 8, 2)
+    # One kv head per workgroup (1,664 rows: 21% above the balance) and f32 at 2 resident
+    # workgroups per CU (2,944 rows: 43% above): the rule's length stays.
+    assert one_round(hc, lens, 8, 1, 768, 64, 576) == 576
+    assert one_round(hc, lens, 8, 1, 512, 128, 640) == 640
+    # Small work, unknown occupancy, or no length that fits: unchanged.
+    assert one_round(hc, [16384], 8, 2, 768, 32, 256) == 256   # 131,072 row-heads: small
+    assert one_round(hc, [16385], 8, 2, 768, 32, 256) == 256   # the rule's 260 fit already
+    assert one_round(hc, [8193] * 8, 8, 2, 768, 32, 256) == 352   # 8 x 24 chunks x 4 blocks
+    assert one_round(hc, lens, 8, 2, 0, 32, 288) == 288
+    assert one_round(hc, lens, 8, 2, 100, 32, 288) == 288
+    # Random cases against a direct search.
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        m = int(rng.integers(1, 65))
+        ls = rng.integers(1, 40000, m).astype(np.int64)
+        nkv, hpb = [(8, 2), (8, 1), (2, 2), (4, 1), (16, 2)][int(rng.integers(0, 5))]
+        br = int(rng.choice([16, 32, 64, 128]))
+        slots = int(rng.choice([256, 512, 768, 1024, 2048]))
+        rows = br * int(rng.integers(1, 40))
+        got = one_round(hc, ls, nkv, hpb, slots, br, rows)
+        if int(ls.sum()) * nkv <= 131072:
+            assert got == rows
+            continue
+        wg = lambda r: int(np.sum((ls + r - 1) // r)) * (nkv // hpb)  # noqa: E731
+        want = rows
+        top = max(rows, -(-int(ls.max()) // br) * br)
+        if wg(top) <= slots:
+            r = rows
+            while wg(r) > slots:
+                r += br
+            if r * slots * 20 <= int(ls.sum()) * (nkv // hpb) * 23:
+                want = r
+        assert got == want, (m, nkv, hpb, br, slots, rows, got, want)
+        assert got % br == 0 and got >= rows
 
 
 def test_rope_exact_evaluation_constants(hc):
