@@ -315,10 +315,12 @@ kvc_status gqa_attn_decode(const kvc_cache *c, int32_t layer, int32_t n_seq,
  * kernels.
  *
  * Limit: the records of one launch (up to 64 entries) must fit the fixed scratch,
- * KVC_STATIC_SCRATCH_BYTES (16 MiB): chunks x n_head x (hd_kv + 4) floats, where a
- * window of L rows takes about L x n_head_kv x n_seq / 2048 / 512 chunks when large
- * (e.g. 32 Qwen3-0.6B-shaped sequences of 8,192 rows: about 2.3 MB).  A call that needs
- * more is refused with KVC_E_ARG before anything is queued.
+ * KVC_STATIC_SCRATCH_BYTES (16 MiB): chunks x n_head x (hd_kv + 4) floats.  The windows
+ * of a call are cut into at most about 2048 x HPB / n_head_kv + n_seq chunks in all
+ * (HPB, kv heads per workgroup: 2 for binary16 regions, and for Q8_0 regions with
+ * n_head = 2 n_head_kv, when n_head_kv is even; else 1), fewer when longer chunks fill the
+ * device in one round (e.g. 32 Qwen3-0.6B-shaped sequences of 8,192 rows, f32: about
+ * 2.3 MB).  A call that needs more is refused with KVC_E_ARG before anything is queued.
  * Every call on one GPU shares that GPU's one copy of the array (it is held until the
  * process ends), so calls that overlap on one GPU -- on different streams, or from
  * different threads or handles without ordering -- race on it; calls ordered on one
