@@ -110,9 +110,11 @@ int64_t hc_decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forc
 }
 
 int64_t hc_decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
-                                 int64_t slots, int32_t br, int64_t rows)
+                                 int64_t slots, int32_t br, int64_t rows, int32_t excess_pct)
 {
-    return kvc::decode_one_round_rows(len, m, n_head_kv, hpb, slots, br, rows);
+    return kvc::decode_one_round_rows(len, m, n_head_kv, hpb, slots, br, rows, excess_pct);
 }
+
+int32_t hc_decode_one_round_excess(int32_t kv_fmt) { return kvc::decode_one_round_excess(kv_fmt); }
 
 }  // extern "C"

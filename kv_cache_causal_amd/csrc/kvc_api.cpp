@@ -276,11 +276,13 @@ kvc_status decode_driver(const kvc_cache *c, int32_t layer, int32_t n_seq, const
         if (!runs) {
             int64_t len[kvc::kInlineEntries];
             for (int32_t b = 0; b < n_seq; b++) len[b] = (int64_t)pos[b] + 1;
-            rows = kvc::decode_one_round_rows(len, n_seq, c->g.n_head_kv, hpb, slots, br, rows);
+            rows = kvc::decode_one_round_rows(len, n_seq, c->g.n_head_kv, hpb, slots, br, rows,
+                                              kvc::decode_one_round_excess(c->kv_fmt));
         } else {
             std::vector<int64_t> len(run_len + run_off[0], run_len + run_off[n_seq]);
             rows = kvc::decode_one_round_rows(len.data(), (int32_t)len.size(), c->g.n_head_kv,
-                                              hpb, slots, br, rows);
+                                              hpb, slots, br, rows,
+                                              kvc::decode_one_round_excess(c->kv_fmt));
         }
     }
     // Chunks of entry b: its window cut into pieces of at most `rows` rows (each run on

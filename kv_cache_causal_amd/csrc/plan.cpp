@@ -103,7 +103,7 @@ int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
 }
 
 int64_t decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
-                              int64_t slots, int32_t br, int64_t rows)
+                              int64_t slots, int32_t br, int64_t rows, int32_t excess_pct)
 {
     // With the chunks of decode_chunk_rows (512 rows, or ~2048 workgroups), a launch of
     // more than small work runs in several rounds of resident workgroups, and the last
@@ -129,7 +129,7 @@ int64_t decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, 
         else lo = mid + 1;
     }
     const int64_t r = lo * br;
-    if (r * slots * 20 > total * blocks * 23) return rows;   // over 15% above the balance
+    if (r * slots * 100 > total * blocks * (100 + excess_pct)) return rows;   // off balance
     return r;
 }
 

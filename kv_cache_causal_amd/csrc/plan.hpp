@@ -49,9 +49,13 @@ int64_t decode_chunk_rows(int64_t work, int32_t br, int32_t hpb, int64_t forced)
 // workgroups of hpb, `slots` workgroups resident at once on the device and the chunk
 // length `rows` of decode_chunk_rows, returns the shortest multiple of br, at least rows,
 // with (sum of chunks) x n_head_kv / hpb <= slots, if the work is above the small range
-// of decode_chunk_rows (131,072 row-heads) and that length is within 15% of a perfect
-// balance (total rows x n_head_kv / hpb / slots per workgroup); otherwise rows.
+// of decode_chunk_rows (131,072 row-heads) and that length is at most excess_pct percent
+// above a perfect balance (total rows x n_head_kv / hpb / slots per workgroup); otherwise
+// rows.  decode_one_round_excess gives the limit measured best for a region format.
 int64_t decode_one_round_rows(const int64_t *len, int32_t m, int32_t n_head_kv, int32_t hpb,
-                              int64_t slots, int32_t br, int64_t rows);
+                              int64_t slots, int32_t br, int64_t rows, int32_t excess_pct);
+// 20 for binary16 regions (one round gained up to 15-20% off balance), 15 for f32 and
+// Q8_0 (f32 lost 3% at 18%; Q8_0 neither gained nor lost there).
+inline int32_t decode_one_round_excess(int32_t kv_fmt) { return kv_fmt == 1 /* binary16 */ ? 20 : 15; }
 
 }  // namespace kvc

@@ -26,8 +26,10 @@ def hc():
     L.hc_plan_prefill.argtypes = [p, i32, i32, i32, i32, i32, p, p, i32]
     L.hc_decode_chunk_rows.argtypes = [i64, i32, i32, i64]
     L.hc_decode_chunk_rows.restype = i64
-    L.hc_decode_one_round_rows.argtypes = [p, i32, i32, i32, i64, i32, i64]
+    L.hc_decode_one_round_rows.argtypes = [p, i32, i32, i32, i64, i32, i64, i32]
     L.hc_decode_one_round_rows.restype = i64
+    L.hc_decode_one_round_excess.argtypes = [i32]
+    L.hc_decode_one_round_excess.restype = i32
     L.hc_max_part_bytes.restype = i64
     return L
 
@@ -199,16 +201,18 @@ def test_decode_chunk_rows(hc):
             assert f(10_000, br, hpb, 100) == up(100)              # forced, rounded up to br
 
 
-def one_round(hc, lens, n_head_kv, hpb, slots, br, rows):
+def one_round(hc, lens, n_head_kv, hpb, slots, br, rows, excess=15):
     a = np.ascontiguousarray(np.asarray(lens, np.int64))
-    return hc.hc_decode_one_round_rows(a.ctypes.data, len(a), n_head_kv, hpb, slots, br, rows)
+    return hc.hc_decode_one_round_rows(a.ctypes.data, len(a), n_head_kv, hpb, slots, br, rows,
+                                       excess)
 
 
 def test_decode_one_round_rows(hc):
     """The one-round chunk length: the shortest multiple of br (from the rule's length up)
     whose chunks x head blocks fit the resident workgroups, taken only above the small
-    range (131,072 row-heads) and within 15% of a perfect balance; anything else keeps the
-    rule's length."""
+    range (131,072 row-heads) and within the format's limit above a perfect balance (20%
+    for binary16, 15% for f32 and Q8_0); anything else keeps the rule's length."""
+    assert [hc.hc_decode_one_round_excess(f) for f in (0, 1, 2)] == [15, 20, 15]
     from tests.workloads import batch_n_past
     lens = batch_n_past().astype(np.int64) + 1         # the 32-sequence batch's windows
     blocks = lambda r, nkv, hpb: int(np.sum((lens + r - 1) // r)) * (nkv // hpb)  # noqa: E731
@@ -216,10 +220,12 @@ def test_decode_one_round_rows(hc):
     # (748 workgroups), 12% above the balance of 685 rows per workgroup.
     assert one_round(hc, lens, 8, 2, 768, 32, 288) == 768
     assert blocks(768, 8, 2) <= 768 < blocks(736, 8, 2)
-    # One kv head per workgroup (1,664 rows: 21% above the balance) and f32 at 2 resident
+    # One kv head per workgroup (1,664 rows: 21.4% above the balance) and f32 at 2 resident
     # workgroups per CU (2,944 rows: 43% above): the rule's length stays.
     assert one_round(hc, lens, 8, 1, 768, 64, 576) == 576
+    assert one_round(hc, lens, 8, 1, 768, 64, 576, 20) == 576
     assert one_round(hc, lens, 8, 1, 512, 128, 640) == 640
+    assert one_round(hc, lens, 8, 1, 768, 64, 576, 22) == 1664   # within a 22% limit
     # Small work, unknown occupancy, or no length that fits: unchanged.
     assert one_round(hc, [16384], 8, 2, 768, 32, 256) == 256   # 131,072 row-heads: small
     assert one_round(hc, [16385], 8, 2, 768, 32, 256) == 256   # the rule's 260 fit already
@@ -235,7 +241,8 @@ def test_decode_one_round_rows(hc):
         br = int(rng.choice([16, 32, 64, 128]))
         slots = int(rng.choice([256, 512, 768, 1024, 2048]))
         rows = br * int(rng.integers(1, 40))
-        got = one_round(hc, ls, nkv, hpb, slots, br, rows)
+        excess = int(rng.choice([15, 20]))
+        got = one_round(hc, ls, nkv, hpb, slots, br, rows, excess)
         if int(ls.sum()) * nkv <= 131072:
             assert got == rows
             continue
@@ -246,7 +253,7 @@ def test_decode_one_round_rows(hc):
             r = rows
             while wg(r) > slots:
                 r += br
-            if r * slots * 20 <= int(ls.sum()) * (nkv // hpb) * 23:
+            if r * slots * 100 <= int(ls.sum()) * (nkv // hpb) * (100 + excess):
                 want = r
         assert got == want, (m, nkv, hpb, br, slots, rows, got, want)
         assert got % br == 0 and got >= rows
