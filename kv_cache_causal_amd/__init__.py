@@ -118,10 +118,29 @@ def _dev(t, name, numel=0):
     return t.data_ptr()
 
 
+# Data pointers of the last few small int32 arrays passed (id -> (array, pointer)).
+# Reading ndarray.ctypes.data costs ~1 us, a large share of a small call's host time, and
+# callers pass the same position / sequence arrays call after call.  The entry holds a
+# reference, so the id cannot be reused and the buffer cannot move (an in-place resize
+# refuses while another reference exists) until the entry is dropped.
+_PTRS = {}
+_PTRS_MAX = 16
+_PTRS_MAX_SIZE = 64
+
+
 def _host_i32(a):
-    if not (type(a) is np.ndarray and a.dtype == np.int32 and a.ndim == 1
-            and a.flags.c_contiguous):
-        a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    """(a contiguous 1-D int32 array holding a's values, its data pointer)."""
+    if type(a) is np.ndarray and a.dtype == np.int32 and a.ndim == 1 and a.flags.c_contiguous:
+        hit = _PTRS.get(id(a))
+        if hit is not None and hit[0] is a:
+            return a, hit[1]
+        ptr = a.ctypes.data
+        if a.size <= _PTRS_MAX_SIZE:
+            if len(_PTRS) >= _PTRS_MAX:
+                _PTRS.clear()
+            _PTRS[id(a)] = (a, ptr)
+        return a, ptr
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
     return a, a.ctypes.data
 
 
